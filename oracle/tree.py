@@ -1,0 +1,221 @@
+"""Draft-tree construction (TEST INFRASTRUCTURE).
+
+What the pages fix: the draft proposes tokens greedily (vLLM Neuron design
+page, "Design Choices": the draft always takes the argmax; "The propose()
+Method": a prefill pass on the shifted ids gives the first draft token, then
+K-1 recurrent passes at positions +1 each give the rest, returning
+[batch, num_speculative_tokens]); a tree is described by draft_top_k,
+draft_depth and total_draft_tokens ("Eaglet" page, "Approach 1: YAML Recipe"),
+verified by the target as 1 + total_draft_tokens tokens ("Block Efficiency
+(BE) Evaluation": eval_tm_arn [128, 32]).
+
+Expansion rule (a reading; the pages give only the three parameters):
+  * the root pass runs the n_new new rows of each sequence at positions
+    ctx .. ctx+n_new-1 (slots equal to positions); the top-k of its last row
+    are the depth-1 candidates, scored by their log-probabilities;
+  * for depth d = 2..D the beam is the top-k depth-(d-1) candidates by
+    (score desc, candidate index asc); beam node j of depth d-1 sits at
+    position ctx+n_new-1+(d-1) and slot ctx+n_new+(d-2)*k+j, runs in recurrent
+    mode on its parent's pre-norm state and its own token, sees the context,
+    the root rows, its ancestors' slots and its own slot, and appends its top-k
+    children with score = parent score + log-prob (float32 add);
+  * candidate index is append order (depth-major, beam order, child rank);
+  * the tree is the top-N candidates by (score desc, index asc), emitted in
+    index order as nodes 1..N; node 0 is the root (the last input token).
+    Parents precede children and the set is ancestor-closed because
+    log-probabilities are <= 0 and a parent's index is smaller.
+  * a sequence with ctx + n_new + (D-1)*k > kv_capacity gets no drafts (the
+    position-aware cutoff of the vLLM Neuron design page, "Design Choices").
+  * top_k = 1 is the chain of "The propose() Method".
+
+Top-k order is (value desc, id asc) over draft ids; log-probs are
+z - logsumexp(z), with logsumexp accumulated in float64 and rounded to
+float32 once, then the subtraction in float32.
+
+Pinned by tests/test_oracle_tree.py: brute-force enumeration of every token
+sequence on tiny vocabularies, the structural invariants (ancestor closure,
+scores non-increasing along paths, depth and position of every node), the
+D = 1 and k = 1 reductions, and numpy sorting of the log-probs.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .draft import draft_pass, topk_desc
+
+
+def topk_logprobs(z, k: int, ids=None):
+    """Top-k of one row of logits and their log-probabilities.
+
+    Returns (positions in z of the k best by (z desc, tie id asc), their
+    float32 log-probs).  ``ids`` are the tie-break ids (default: positions)."""
+    z = np.asarray(z, dtype=np.float32)
+    top = topk_desc(z, k, ids)
+    z64 = z.astype(np.float64)
+    m = float(np.max(z64))
+    lse = np.float32(m + np.log(np.sum(np.exp(z64 - m))))
+    return top, (z[top] - lse).astype(np.float32)
+
+
+def _ancestor_slots(cands, ci):
+    out = []
+    p = cands[ci]["parent"]
+    while p >= 0:
+        out.append(cands[p]["slot"])
+        p = cands[p]["parent"]
+    return out[::-1]
+
+
+def build_tree_core(cfg, B, n_new, ctx_len, in_tokens, pass_fn):
+    """Tree construction with a pluggable draft.
+
+    ``pass_fn(d, rows)`` runs draft pass d (1 = root) over ``rows`` (dicts with
+    b, token, pos, slot, anc, src, cand, rank, i, path) and returns one
+    (ids[k], logp[k]) pair per row, ids in the target vocabulary."""
+    k, D, N = cfg["top_k"], cfg["depth"], cfg["total_tokens"]
+    cap = cfg["kv_capacity"]
+    ctx_len = np.asarray(ctx_len)
+    active = [b for b in range(B) if ctx_len[b] + n_new + (D - 1) * k <= cap]
+    cands = {b: [] for b in active}
+
+    rows = []
+    for b in active:
+        c0 = int(ctx_len[b])
+        for i in range(n_new):
+            rows.append(dict(b=b, i=i, token=int(in_tokens[b, i]), pos=c0 + i, slot=c0 + i,
+                             anc=[c0 + j for j in range(i + 1)], src=None, cand=-1, rank=0,
+                             path=()))
+    res = pass_fn(1, rows) if rows else []
+    for idx, r in enumerate(rows):
+        if r["i"] != n_new - 1:
+            continue
+        ids, lp = res[idx]
+        for t, l in zip(ids, lp):
+            cands[r["b"]].append(dict(token=int(t), parent=-1, depth=1, score=np.float32(l),
+                                      slot=-1, src=idx, path=(int(t),)))
+
+    for d in range(2, D + 1):
+        rows = []
+        for b in active:
+            c0 = int(ctx_len[b])
+            C = cands[b]
+            pool = [ci for ci, c in enumerate(C) if c["depth"] == d - 1]
+            beam = sorted(pool, key=lambda ci: (-float(C[ci]["score"]), ci))[:k]
+            for j, ci in enumerate(beam):
+                C[ci]["slot"] = c0 + n_new + (d - 2) * k + j
+                anc = [c0 + i for i in range(n_new)] + _ancestor_slots(C, ci) + [C[ci]["slot"]]
+                rows.append(dict(b=b, i=0, token=C[ci]["token"], pos=c0 + n_new - 1 + (d - 1),
+                                 slot=C[ci]["slot"], anc=anc, src=C[ci]["src"], cand=ci, rank=j,
+                                 path=C[ci]["path"]))
+        res = pass_fn(d, rows) if rows else []
+        for idx, r in enumerate(rows):
+            ids, lp = res[idx]
+            C = cands[r["b"]]
+            ps = C[r["cand"]]["score"]
+            for t, l in zip(ids, lp):
+                C.append(dict(token=int(t), parent=r["cand"], depth=d,
+                              score=np.float32(np.float32(ps) + np.float32(l)), slot=-1, src=idx,
+                              path=r["path"] + (int(t),)))
+
+    n1 = N + 1
+    tree = {
+        "tokens": np.full((B, n1), -1, np.int32),
+        "parent": np.full((B, n1), -1, np.int32),
+        "depth": np.full((B, n1), -1, np.int32),
+        "position": np.full((B, n1), -1, np.int32),
+        "draft_slot": np.full((B, n1), -1, np.int32),
+        "score": np.zeros((B, n1), np.float32),
+        "anc_mask": np.zeros((B, n1), np.uint64),
+        "num_nodes": np.zeros(B, np.int32),
+        "cands": cands,
+    }
+    for b in range(B):
+        c0 = int(ctx_len[b])
+        tree["tokens"][b, 0] = in_tokens[b, n_new - 1]
+        tree["depth"][b, 0] = 0
+        tree["position"][b, 0] = c0 + n_new - 1
+        tree["anc_mask"][b, 0] = 1
+        if b not in cands:
+            continue
+        tree["draft_slot"][b, 0] = c0 + n_new - 1
+        C = cands[b]
+        best = sorted(range(len(C)), key=lambda ci: (-float(C[ci]["score"]), ci))[:N]
+        sel = sorted(best)
+        node_of = {ci: n + 1 for n, ci in enumerate(sel)}
+        tree["num_nodes"][b] = len(sel)
+        for ci in sel:
+            n = node_of[ci]
+            c = C[ci]
+            par = 0 if c["parent"] < 0 else node_of[c["parent"]]
+            tree["tokens"][b, n] = c["token"]
+            tree["parent"][b, n] = par
+            tree["depth"][b, n] = c["depth"]
+            tree["position"][b, n] = c0 + n_new - 1 + c["depth"]
+            tree["draft_slot"][b, n] = c["slot"]
+            tree["score"][b, n] = c["score"]
+            tree["anc_mask"][b, n] = tree["anc_mask"][b, par] | np.uint64(1 << n)
+    return tree
+
+
+def model_pass_fn(cfg, W, kcache, vcache, aux, ctx_len, record=None):
+    """The draft model as a pass function for build_tree_core.
+
+    ``record``, if given, is a list that receives each pass's rows and output
+    dict (for tests that compare stage by stage)."""
+    k = cfg["top_k"]
+    d2t = W.get("d2t")
+    state = {}
+
+    def fn(d, rows):
+        M = len(rows)
+        if d == 1:
+            hidden = np.stack([aux[r["b"], r["i"]] for r in rows])
+        else:
+            hidden = state["h"][[r["src"] for r in rows]]
+        A = max(len(r["anc"]) for r in rows)
+        anc = np.full((M, A), -1, np.int64)
+        for i, r in enumerate(rows):
+            anc[i, : len(r["anc"])] = r["anc"]
+        out = draft_pass(cfg, W, kcache, vcache, 0 if d == 1 else 1, hidden,
+                         [r["token"] for r in rows], [r["b"] for r in rows],
+                         [r["pos"] for r in rows], [r["slot"] for r in rows], ctx_len, anc)
+        state["h"] = out["h_out"]
+        if record is not None:
+            record.append((rows, out))
+        res = []
+        for i in range(M):
+            if cfg["cand_rank"]:
+                pos, lp = topk_logprobs(out["cand_logits"][i], k, ids=out["cand_ids"][i])
+                ids = out["cand_ids"][i][pos]
+            else:
+                pos, lp = topk_logprobs(out["logits"][i], k)
+                ids = d2t[pos] if d2t is not None else pos
+            res.append((np.asarray(ids, np.int64), lp))
+        return res
+
+    return fn
+
+
+def build_tree(cfg, W, kcache, vcache, aux, in_tokens, ctx_len, record=None):
+    """Full draft side of one speculation step: root pass, D-1 expansions and
+    the final selection.  kcache/vcache are updated in place."""
+    in_tokens = np.asarray(in_tokens)
+    B, n_new = in_tokens.shape
+    fn = model_pass_fn(cfg, W, kcache, vcache, aux, ctx_len, record)
+    return build_tree_core(cfg, B, n_new, ctx_len, in_tokens, fn)
+
+
+def table_pass_fn(ids_tab, lp_tab):
+    """A draft given as a table: pass d, sequence b and beam rank j produce
+    ids_tab[d-1, b, j] and lp_tab[d-1, b, j] (the root pass uses rank 0)."""
+    def fn(d, rows):
+        return [(np.asarray(ids_tab[d - 1, r["b"], r["rank"]], np.int64),
+                 np.asarray(lp_tab[d - 1, r["b"], r["rank"]], np.float32)) for r in rows]
+    return fn
+
+
+def build_tree_from_topk(cfg, ctx_len, in_tokens, ids_tab, lp_tab):
+    in_tokens = np.asarray(in_tokens)
+    B, n_new = in_tokens.shape
+    return build_tree_core(cfg, B, n_new, ctx_len, in_tokens, table_pass_fn(ids_tab, lp_tab))
