@@ -1,0 +1,224 @@
+"""Benchmark of one speculation step (draft tree + verify + KV compaction).
+
+A step is spec_build_tree + spec_verify_tree + spec_compact_kv for the whole
+batch, on inputs already resident in HBM.  Default workload: the
+Llama-3.1-8B-shaped EAGLE-3 chain (batch 4, context 256, 5 draft tokens,
+greedy), on synthetic seeded inputs.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+                    [--graph] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "speculation steps/sec (draft tree + verify) at 1 GPU; HBM GB/s & MFMA util vs peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama8b_chain")
+    ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=2)
+    return ap.parse_args()
+
+
+def lm_head_bytes(cfg, M):
+    """Algorithmic bytes of one LM-head launch: the weight stream, the normed
+    rows in and the float32 logits out (EAGLE-4: the low-rank score GEMM)."""
+    H = cfg["hidden"]
+    if cfg["cand_rank"]:
+        r, V = cfg["cand_rank"], cfg["vocab"]
+        return V * r * 2 + M * r * 2 + M * V * 4
+    Vd = cfg["draft_vocab"]
+    return Vd * H * 2 + M * H * 2 + M * Vd * 4
+
+
+def pass_rows(cfg):
+    B, k, D, n_new = cfg["batch"], cfg["top_k"], cfg["depth"], cfg["n_new"]
+    return [B * n_new] + [B * k] * (D - 1)
+
+
+def cpu_baseline(cfg, W, inp, seed, steps):
+    """The oracle, as it stands, on a bounded sample: whole steps of the same
+    workload (same weights and inputs), timed on the host cores."""
+    from oracle import compact as oc
+    from oracle import tree as ot
+    from oracle import verify as ov
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    times = []
+    for s in range(steps):
+        kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
+        t0 = time.perf_counter()
+        tree = ot.build_tree(cfg, W, kc, vc, inp["aux"], inp["in_tokens"], inp["ctx_len"])
+        t1 = time.perf_counter()
+        logits = gen.plant_target_logits(cfg, tree, seed)
+        t2 = time.perf_counter()
+        if cfg["verify"] == "greedy":
+            out, alen, nodes = ov.verify_greedy(tree, logits, cfg["depth"])
+        else:
+            u = gen.make_accept_u(cfg, seed)
+            out, alen, nodes = ov.verify_stochastic(tree, logits, cfg["depth"], cfg["temperature"], u,
+                                                    gen.philox_seed(seed))
+        base = inp["ctx_len"] + cfg["n_new"] - 1
+        tk = np.zeros((1, cfg["batch"], cfg["n_kv_heads"], cfg["kv_capacity"], cfg["head_dim"]), np.float32)
+        oc.compact_kv(tk, tk.copy(), base, nodes, alen)
+        t3 = time.perf_counter()
+        times.append((t1 - t0) + (t3 - t2))  # input planting excluded
+    med = float(np.median(times))
+    return {"value": 1.0 / med, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} whole steps of the same workload (batch {cfg['batch']}); "
+                      f"median {med:.3f} s per step; compaction on a 1-layer cache"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              "(the step is data-parallel over sequences and would shard by batch)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from speculative_decoding_aux_amd import spec as S
+    from speculative_decoding_aux_amd import _lib as L
+    from speculative_decoding_aux_amd.tensors import to_device, upload_kv, upload_weights
+    from synth import configs, gen
+
+    cfg = configs.get(args.config)
+    seed = configs.SEEDS[args.config]
+    B = cfg["batch"]
+    print(f"[bench] generating inputs for {args.config}", file=sys.stderr, flush=True)
+    W = gen.make_weights(cfg, seed)
+    inp = gen.make_step_inputs(cfg, seed)
+    dev = "cuda"
+    w = upload_weights(cfg, W)
+    draft_kv = upload_kv(cfg, inp["k_cache"], inp["v_cache"])
+    aux = to_device(inp["aux"], cfg["dtype"])
+    in_tok = torch.from_numpy(inp["in_tokens"]).to(dev)
+    ctx_len = torch.from_numpy(inp["ctx_len"]).to(dev)
+    # target-shaped KV for compaction: target_layers x [B, nkv, ctx + N + 1 (+pad), hd]
+    t_slots = cfg["ctx"] + cfg["n_new"] + cfg["total_tokens"] + 8
+    tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(seed)
+    tshape = (cfg["target_layers"], B, cfg["n_kv_heads"], t_slots, cfg["head_dim"])
+    target_kv = S.KVCache(torch.randn(tshape, generator=g, device=dev).to(tdt),
+                          torch.randn(tshape, generator=g, device=dev).to(tdt))
+    tree_base = (ctx_len + cfg["n_new"] - 1).to(torch.int32)
+    ctx = S.SpecContext(cfg, max_batch=B, max_new=cfg["n_new"])
+    tree = S.Tree(B, cfg["total_tokens"] + 1, dev)
+    D = cfg["depth"]
+    vout = (torch.empty(B, D + 1, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev),
+            torch.empty(B, D, dtype=torch.int32, device=dev))
+    # target logits planted on this run's own tree (one untimed draft pass)
+    S.spec_build_tree(ctx, w, draft_kv, aux, in_tok, ctx_len, tree=tree)
+    torch.cuda.synchronize()
+    tnp = tree.numpy()
+    if cfg["target_logits"] == "planted":
+        tl = gen.plant_target_logits(cfg, tnp, seed)
+    else:
+        base = gen.random_logits(seed, "bench_draft_like", (B, cfg["total_tokens"] + 1, cfg["vocab"]))
+        tl = gen.add_noise_logits(base, seed)
+    target_logits = torch.from_numpy(tl).to(dev)
+    mode = 0 if cfg["verify"] == "greedy" else 1
+    accept_u = torch.from_numpy(gen.make_accept_u(cfg, seed)).to(dev) if mode else None
+    pseed = gen.philox_seed(seed)
+
+    def step():
+        S.spec_build_tree(ctx, w, draft_kv, aux, in_tok, ctx_len, tree=tree)
+        S.spec_verify_tree(ctx, tree, target_logits, mode, cfg["temperature"], accept_u, pseed, out=vout)
+        S.spec_compact_kv(ctx, target_kv, tree_base, vout[2], vout[1])
+
+    stream = torch.cuda.current_stream()
+    graph = None
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    if graph is None:
+        ctx.profile(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    roof = None
+    if graph is None:
+        n, ms = ctx.profile_read(L.SPEC_PROF_LM_HEAD)
+        na, msa = ctx.profile_read(L.SPEC_PROF_ATTENTION)
+        nv, msv = ctx.profile_read(L.SPEC_PROF_VERIFY)
+        ctx.profile(False)
+        rows = pass_rows(cfg)
+        byts = sum(lm_head_bytes(cfg, m) for m in rows) / len(rows)
+        avg_ms = ms / max(n, 1)
+        achieved = byts / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemm_bf16_stream<*,1> (LM head)" if cfg["dtype"] == "bf16" else "gemm_f32_rows",
+                "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n,
+                "algorithmic_bytes_per_launch": int(byts)}
+        print(f"[bench] lm_head {n} launches avg {avg_ms*1e3:.1f} us; attention avg "
+              f"{msa / max(na, 1) * 1e3:.1f} us; verify avg {msv / max(nv, 1) * 1e3:.1f} us",
+              file=sys.stderr, flush=True)
+    res = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.config, "batch": B, "ctx": cfg["ctx"], "top_k": cfg["top_k"],
+                   "depth": cfg["depth"], "total_tokens": cfg["total_tokens"], "verify": cfg["verify"],
+                   "graph": bool(graph is not None), "wall_s": round(wall, 3)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, W, inp, seed, args.cpu_steps)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

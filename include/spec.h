@@ -1,0 +1,254 @@
+/*
+ * spec.h - C ABI of the MI355X speculation-step library (libspec_mi355x.so).
+ *
+ * One speculation step of EAGLE-3 (and its EAGLE-4 variant) on one GPU:
+ *   spec_build_tree   draft side: FC fusion of the three auxiliary target
+ *                     hidden states, one draft decoder layer, LM head (or the
+ *                     EAGLE-4 low-rank candidate head), top-k tree expansion;
+ *   spec_verify_tree  greedy longest-accepted-path or stochastic rejection
+ *                     sampling against the target's logits;
+ *   spec_compact_kv   move the accepted nodes' K/V next to the root.
+ * Stage-level entry points expose single steps of the same path:
+ *   spec_draft_step, spec_topk_logprobs, spec_tree_from_topk.
+ *
+ * Sources: "Speculative Decoding (EAGLE3) in the vLLM Neuron Framework"
+ * (sections "What is EAGLE3?", "Eagle3 Draft Model Architecture", "The
+ * propose() Method", "Rejection Sampling", "KV Cache Sharing", "Design
+ * Choices"); "Eaglet" (section "Approach 1: YAML Recipe": draft_top_k,
+ * draft_depth, total_draft_tokens); NeMo AutoModel "eagle4" page
+ * (Eagle4CandidateHeadConfig rank / num_candidates, Eagle4Config
+ * sliding_window).
+ *
+ * Conventions for every call
+ *  - All tensors are caller-owned DEVICE memory unless a parameter says host.
+ *    Matrices are row-major [rows, cols]; linear weights are [out, in].
+ *  - Floating tensors are float32 or bfloat16 according to spec_config.dtype
+ *    ("storage type"); logits, log-probs, scores and uniforms are float32;
+ *    ids, positions, slots and counts are int32.
+ *  - `stream` is a hipStream_t (void* here so the header needs no HIP headers);
+ *    NULL is the default stream.  Calls only enqueue work: they never
+ *    allocate, free or synchronise after spec_create.
+ *  - Return codes: SPEC_OK, or SPEC_EINVAL (null pointer, bad size) /
+ *    SPEC_EUNSUPPORTED (a size outside the compiled limits) detected on the
+ *    host before anything is launched, or SPEC_EHIP if a launch failed;
+ *    spec_last_error() then holds a message.  Device-side ids and slots are
+ *    preconditions; kernels clamp them so that bad values cannot fault, but
+ *    results are then unspecified.
+ *  - One context per stream: a context's workspace is reused by every call.
+ */
+#ifndef SPEC_MI355X_H
+#define SPEC_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,
+  SPEC_EUNSUPPORTED = -2,
+  SPEC_EHIP = -3,
+  SPEC_ENOMEM = -4
+} spec_status;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+typedef enum { SPEC_VERIFY_GREEDY = 0, SPEC_VERIFY_STOCHASTIC = 1 } spec_verify_mode;
+
+typedef struct spec_ctx spec_ctx;
+
+/* Shapes of the draft and of the tree; copied by spec_create.
+ * Limits: head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads with
+ * n_q_heads/n_kv_heads * max(top_k, max_new) <= 64; top_k <= 16;
+ * total_tokens + 1 <= 64; depth <= total_tokens; hidden, 3*hidden,
+ * intermediate and n_q_heads*head_dim multiples of 128 for bf16 (of 4 for
+ * f32); num_candidates <= 256 and a multiple of 32 when cand_rank > 0. */
+typedef struct spec_config {
+  int32_t hidden;          /* H */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t intermediate;    /* I: MLP width */
+  int32_t vocab;           /* V: target vocabulary (embedding rows, verify width) */
+  int32_t draft_vocab;     /* Vd: LM-head rows; < V for a trimmed vocabulary with d2t */
+  int32_t cand_rank;       /* r of the EAGLE-4 candidate head; 0 = EAGLE-3 head */
+  int32_t num_candidates;  /* K candidates kept from the low-rank scores */
+  int32_t sliding_window;  /* W keys per query including itself; 0 = full causal */
+  float rope_base;         /* RoPE base (rotate-half form) */
+  float rms_eps;           /* RMSNorm epsilon */
+  int32_t top_k;           /* draft_top_k (1 = chain) */
+  int32_t depth;           /* draft_depth (chain: num_speculative_tokens) */
+  int32_t total_tokens;    /* total_draft_tokens N; the tree has N+1 nodes */
+  int32_t max_batch;       /* largest B any call will pass */
+  int32_t max_new;         /* largest n_new (rows per sequence in the root pass) */
+  int32_t kv_capacity;     /* S: draft-KV slots per sequence */
+  int32_t dtype;           /* spec_dtype: storage type of weights/activations/KV */
+} spec_config;
+
+/* Draft weights (device, storage type unless stated).  The QKV rows are
+ * [q heads | k heads | v heads], each head_dim wide; w_gate_up rows are
+ * [gate (I) | up (I)]. */
+typedef struct spec_weights {
+  const void* fc;             /* [H, 3H]  fusion of the low|mid|high aux states */
+  const void* embed;          /* [V, H]   token embedding */
+  const void* input_norm;     /* [H]      RMSNorm gain on the embedding */
+  const void* hidden_norm;    /* [H]      RMSNorm gain on the hidden input */
+  const void* post_attn_norm; /* [H] */
+  const void* final_norm;     /* [H] */
+  const void* wqkv;           /* [(nq+2nkv)*hd, 2H] */
+  const void* wo;             /* [H, nq*hd] */
+  const void* w_gate_up;      /* [2I, H] */
+  const void* w_down;         /* [H, I] */
+  const void* lm_head;        /* [Vd, H]; with a candidate head [V, H] */
+  const int32_t* d2t;         /* [Vd] draft id -> target id, or NULL when Vd == V */
+  const void* cand_down;      /* [r, H]  efficient_lm_head_down_proj, or NULL */
+  const void* cand_up;        /* [V, r]  efficient_lm_head, or NULL */
+} spec_weights;
+
+/* A KV cache laid out [layers][batch][n_kv_heads][slots][head_dim] in the
+ * storage type; the strides (in elements) allow any layout whose rows of
+ * head_dim are contiguous.  The draft KV has one layer; keys are stored
+ * after RoPE. */
+typedef struct spec_kv {
+  void* k;
+  void* v;
+  int32_t num_layers;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t slots;
+  int32_t head_dim;
+  int64_t stride_layer;
+  int64_t stride_seq;
+  int64_t stride_head;
+} spec_kv;
+
+/* The draft tree of each sequence, N+1 nodes; node 0 is the root (the last
+ * input token), nodes 1..num_nodes are drafts in candidate order (parents
+ * before children).  Unused nodes hold -1 (tokens, parent, depth, position,
+ * draft_slot), 0 (score) and 0 (anc_mask). */
+typedef struct spec_tree {
+  int32_t* tokens;      /* [B, N+1] target-vocabulary ids */
+  int32_t* parent;      /* [B, N+1] node index, -1 for the root */
+  int32_t* depth;       /* [B, N+1] root 0 */
+  int32_t* position;    /* [B, N+1] ctx_len + n_new - 1 + depth */
+  int32_t* draft_slot;  /* [B, N+1] draft-KV slot of nodes that were expanded, else -1 */
+  int32_t* num_nodes;   /* [B] drafts kept (0 when the sequence is past the capacity cutoff) */
+  float* score;         /* [B, N+1] cumulative draft log-prob, root 0 */
+  uint64_t* anc_mask;   /* [B, N+1] bit j set iff node j is the node, an ancestor or the root */
+} spec_tree;
+
+/* Allocate a context and its workspace (the only allocation of the library). */
+spec_status spec_create(const spec_config* cfg, spec_ctx** out);
+void spec_destroy(spec_ctx* ctx);
+const char* spec_last_error(const spec_ctx* ctx);
+int64_t spec_workspace_bytes(const spec_ctx* ctx);
+const char* spec_version(void);
+
+/* One draft pass over M = B * rows_per_seq rows (vLLM Neuron page, "Eagle3
+ * Draft Model Architecture": initial and recurrent forward modes).  Row r
+ * belongs to sequence r / rows_per_seq.
+ *   mode 0: hidden_in is [M, 3H], the concatenated low|mid|high aux states;
+ *   mode 1: hidden_in is [M, H], the pre-norm state of an earlier pass.
+ *   tokens[M], positions[M]: input token and RoPE position of each row;
+ *   kv_slot[M]: draft-KV slot the row's K/V is written to (-1: not written);
+ *   ctx_len[B]: context slots [0, ctx_len) every row of the sequence sees;
+ *   anc_slots[M, anc_width]: further visible slots, -1 padded; the valid
+ *     entries of a row hold consecutive positions ending at the row's own
+ *     position, in order (root rows, ancestors, the row itself);
+ *   k_out <= top_k: outputs topk_ids[M, k_out] (target ids, d2t applied) and
+ *     topk_logp[M, k_out] (float32 log-probs), ordered by (logit desc, id asc);
+ *   hidden_out[M, H]: pre-norm output state (storage type);
+ *   logits_out: NULL, or [M, Vd] float32 logits (EAGLE-3 head) / [M, V]
+ *     low-rank scores (candidate head);
+ *   cand_ids_out / cand_logits_out: NULL, or [M, num_candidates] retrieved
+ *     candidate ids and their exact logits (candidate head only).
+ * K/V of all rows are written before any row attends. */
+spec_status spec_draft_step(spec_ctx* ctx, const spec_weights* w, const spec_kv* draft_kv,
+                            int32_t B, int32_t rows_per_seq, int32_t mode, const void* hidden_in,
+                            const int32_t* tokens, const int32_t* positions, const int32_t* kv_slot,
+                            const int32_t* ctx_len, const int32_t* anc_slots, int32_t anc_width,
+                            int32_t k_out, int32_t* topk_ids, float* topk_logp, void* hidden_out,
+                            float* logits_out, int32_t* cand_ids_out, float* cand_logits_out,
+                            void* stream);
+
+/* Top-k and log-probabilities of M rows of float32 logits [M, n]:
+ * ids ordered by (value desc, position asc), log-prob = z - logsumexp(row)
+ * with the sum accumulated in float64; ids_out = id_map[position] when
+ * id_map (device, [n]) is given, else the position.  k <= 16. */
+spec_status spec_topk_logprobs(spec_ctx* ctx, int32_t M, int32_t n, const float* logits, int32_t k,
+                               const int32_t* id_map, int32_t* ids_out, float* logp_out, void* stream);
+
+/* Tree expansion and selection with the draft given as a table: pass d
+ * (1 = root), sequence b and beam rank j produce topk_ids[d-1][b][j][:] and
+ * topk_logp[d-1][b][j][:] (arrays [depth, B, top_k, top_k]; the root pass
+ * uses rank 0).  Same selection rule and outputs as spec_build_tree. */
+spec_status spec_tree_from_topk(spec_ctx* ctx, int32_t B, int32_t n_new, const int32_t* in_tokens,
+                                const int32_t* ctx_len, const int32_t* topk_ids,
+                                const float* topk_logp, spec_tree* out, void* stream);
+
+/* Draft side of one step for B sequences ("Eaglet": tree of draft_top_k,
+ * draft_depth, total_draft_tokens; vLLM Neuron page, "The propose() Method").
+ *   aux_hidden[B, n_new, 3H]: concatenated aux states of the new rows;
+ *   in_tokens[B, n_new]: their (shifted) input ids; the last one is the root;
+ *   ctx_len[B]: tokens already in the draft KV.
+ * The root pass runs the new rows at positions/slots ctx_len + i; each of
+ * the depth-1 expansion passes runs the top_k beam nodes of the previous
+ * depth; the tree is the best total_tokens candidates by cumulative log-prob.
+ * A sequence with ctx_len + n_new + (depth-1)*top_k > kv_capacity gets no
+ * drafts and no KV writes (the page's position-aware cutoff). */
+spec_status spec_build_tree(spec_ctx* ctx, const spec_weights* w, const spec_kv* draft_kv,
+                            int32_t B, int32_t n_new, const void* aux_hidden,
+                            const int32_t* in_tokens, const int32_t* ctx_len, spec_tree* out,
+                            void* stream);
+
+/* Verification of the trees against target logits [B, N+1, V] float32 (row
+ * n = tree node n) (vLLM Neuron page, "Rejection Sampling").
+ *   mode SPEC_VERIFY_GREEDY: walk from the root to the child whose token is
+ *     the current node's argmax (first index on ties); emit the accepted
+ *     tokens, then the argmax at the last accepted node.
+ *   mode SPEC_VERIFY_STOCHASTIC: at the current node test the children in
+ *     node order with Z = 1: accept child c_i iff accept_u[b, cur, i] <=
+ *     p(c_i) / Z, else Z -= p(c_i), with p = softmax(logits / temperature);
+ *     if none is accepted emit argmax over non-children of
+ *     l/T - log(-log U) with U from Philox4x32-10 keyed by seed and counter
+ *     (v >> 2, cur, b, 0), word v & 3, U = ((x >> 8) + 0.5) * 2^-24.
+ *   accept_u: [B, N+1, top_k] float32 (stochastic only, else NULL).
+ * Outputs: out_tokens[B, depth+1] (-1 padded), accepted_len[B],
+ * accepted_nodes[B, depth] (-1 padded). */
+spec_status spec_verify_tree(spec_ctx* ctx, int32_t B, const spec_tree* tree,
+                             const float* target_logits, int32_t mode, float temperature,
+                             const float* accept_u, uint64_t seed, int32_t* out_tokens,
+                             int32_t* accepted_len, int32_t* accepted_nodes, void* stream);
+
+/* KV compaction of the accepted path, every layer of `kv`: for each
+ * sequence b and j < accepted_len[b], the row at slot tree_base[b] +
+ * accepted_nodes[b, j] moves to slot tree_base[b] + 1 + j.  All rows of a
+ * sequence are read before any is written, so overlapping source and
+ * destination slots are safe.  accepted_nodes is [B, max_accept]. */
+spec_status spec_compact_kv(spec_ctx* ctx, const spec_kv* kv, int32_t B, const int32_t* tree_base,
+                            const int32_t* accepted_nodes, const int32_t* accepted_len,
+                            int32_t max_accept, void* stream);
+
+/* Kernel timing for measurement tools.  While enabled, every launch of a
+ * labelled kernel is bracketed by a pair of hipEvents recorded on the stream
+ * it is launched on (at most 4096 launches per label are kept).  Enabling
+ * resets the counts and creates the event pool on first use (the only other
+ * host-side allocation of the library); spec_profile_read waits for the
+ * recorded events and returns the number of timed launches and their summed
+ * duration in milliseconds. */
+typedef enum {
+  SPEC_PROF_LM_HEAD = 0,    /* LM-head GEMM (EAGLE-3) or low-rank score GEMM (EAGLE-4) */
+  SPEC_PROF_ATTENTION = 1,  /* context attention + combine */
+  SPEC_PROF_VERIFY = 2,     /* verify statistics + walk */
+  SPEC_PROF_TOPK = 3,       /* vocab top-k + log-probs */
+  SPEC_PROF_NLABELS = 4
+} spec_prof_label;
+spec_status spec_profile_enable(spec_ctx* ctx, int32_t enable);
+spec_status spec_profile_read(spec_ctx* ctx, int32_t label, int32_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_MI355X_H */

@@ -1,0 +1,113 @@
+// Shared device helpers for the gfx950 speculation-step kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SPEC_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte load unit
+
+constexpr int kWave = 64;
+
+SPEC_DEV float bf16_to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// float -> bfloat16, round to nearest even (NaN stays NaN).
+SPEC_DEV bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+// Storage-type traits: T is float (fp32 workloads) or bf16_t.
+template <typename T> struct St;
+template <> struct St<float> {
+  static SPEC_DEV float load(const float* p, int64_t i) { return p[i]; }
+  static SPEC_DEV void store(float* p, int64_t i, float v) { p[i] = v; }
+  static SPEC_DEV float round(float v) { return v; }
+};
+template <> struct St<bf16_t> {
+  static SPEC_DEV float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static SPEC_DEV void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+  static SPEC_DEV float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+};
+
+// ---- wavefront reductions (64 lanes) --------------------------------------
+SPEC_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+SPEC_DEV double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+SPEC_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum of one float (blockDim.x a multiple of 64, <= 1024).
+SPEC_DEV float block_sum(float v, float* red /* >= 16 floats of LDS */) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  const int nw = blockDim.x >> 6;
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+SPEC_DEV double block_sum(double v, double* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  const int nw = blockDim.x >> 6;
+  double t = 0.0;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// (value desc, id asc) ordering used by every top-k and argmax.
+SPEC_DEV bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw; SC'11) ----------------------
+struct u32x4 { uint32_t x, y, z, w; };
+SPEC_DEV u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = u32x4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+// Gumbel noise -log(-log U) for U = ((x >> 8) + 0.5) * 2^-24 in (0, 1).
+// U = (2m+1) * 2^-25 with m = x >> 8.  Below 1/2 that value is exact in
+// float32 and -log U is taken directly; above, 1 - U = (2^25 - 2m - 1) * 2^-25
+// is exact and -log U = -log1p(-(1 - U)) avoids the cancellation near 1.
+SPEC_DEV float gumbel_from_bits(uint32_t x) {
+  const uint32_t m = x >> 8;
+  float e;
+  if (m < (1u << 23)) {
+    e = -logf(float(2u * m + 1u) * 2.98023223876953125e-8f);
+  } else {
+    e = -log1pf(-float((1u << 25) - 2u * m - 1u) * 2.98023223876953125e-8f);
+  }
+  return -logf(e);
+}
+
+SPEC_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }

@@ -1,0 +1,122 @@
+// Internal launch interface of the speculation-step kernels (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spec {
+
+// ---------------------------------------------------------------- GEMM
+// P[split][M][N] (float32) = X[M, K] . W[N, K]^T over the split's K range.
+struct GemmPlan {
+  int nsplit = 1;
+  int kc = 0;  // K elements per split (multiple of 128 for bf16)
+};
+GemmPlan gemm_plan(int M, int N, int K, bool bf16);
+// tag 1 launches a separately named instance (the LM head and score GEMMs).
+hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
+                int K, const GemmPlan& plan, hipStream_t s, int tag = 0);
+
+enum EpiOp { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_F32 = 3 };
+// Sum the nsplit partials and apply the op.  EPI_SWIGLU reads 2N columns of P
+// (gate | up) and writes N; EPI_F32 writes float32 sums to Y.
+hipError_t gemm_epilogue(bool bf16, int op, void* Y, const void* R, const float* P, int nsplit,
+                         int M, int N, hipStream_t s);
+
+struct KvView {
+  void* k;
+  void* v;
+  int64_t stride_seq, stride_head;  // elements
+  int slots;
+};
+// QKV epilogue: sum partials, round, RoPE on q and k at pos[m], store q to
+// qout[M, nq, hd], k/v to the cache at (m / rows_per_seq, head, slot[m]).
+hipError_t qkv_epilogue(bool bf16, const float* P, int nsplit, int M, int nq, int nkv, int hd,
+                        const int* pos, const int* slot, int rows_per_seq, float rope_base,
+                        void* qout, KvView kv, hipStream_t s);
+
+// ------------------------------------------------------------- norms
+// c[r] = [rms(embed[tok[r]]) * w_in | rms(g[r]) * w_hid];  g[r] = hid[src ? src[r] : r]
+// is also copied to gout (the residual of the layer).
+hipError_t prologue(bool bf16, const void* embed, int V, const int* tok, const void* hid,
+                    const int* src, const void* w_in, const void* w_hid, float eps, int M, int H,
+                    void* gout, void* cout, hipStream_t s);
+hipError_t rmsnorm(bool bf16, const void* x, const void* w, float eps, int M, int H, void* y,
+                   hipStream_t s);
+
+// --------------------------------------------------------- attention
+struct AttnArgs {
+  const void* q;        // [M, nq, hd]
+  KvView kv;
+  const int* ctx_len;   // [B]
+  const int* pos;       // [M]
+  const int* anc;       // [M, A]
+  int A;
+  int B, R, nq, nkv, hd, window;
+  void* out;            // [M, nq*hd]
+  float* part;          // workspace
+  int nchunks, chunk;
+};
+void attn_plan(int B, int nkv, int slots, int window, int* nchunks, int* chunk);
+size_t attn_part_floats(int B, int nkv, int R, int nq, int hd, int nchunks);
+hipError_t attention(bool bf16, const AttnArgs& a, hipStream_t s);
+
+// -------------------------------------------------------------- top-k
+void topk_plan(int M, int n, int* nch, int* chunk);
+size_t topk_part_bytes(int M, int nch, int kmax);
+// ids = id_map ? id_map[pos] : pos, logp = z - lse.
+hipError_t topk(const float* z, int M, int n, int ldz, int k, const int* id_map, int* ids,
+                int ldi, float* logp, int ldl, void* part, int nch, int chunk, hipStream_t s);
+// As topk, with per-row ids rowmap[M, n] used as tie-break and as output ids.
+hipError_t topk_rows(const float* z, int M, int n, int ldz, int k, const int* id_map,
+                     const int* rowmap, int* ids, int ldi, float* logp, int ldl, void* part,
+                     int nch, int chunk, hipStream_t s);
+// Candidate retrieval: the best K (value desc, id asc) of each row, K <= 256.
+hipError_t topk_large(const float* z, int M, int n, int K, int* ids, void* part, hipStream_t s);
+// Gathered exact rescoring: out[m, j] = dot(x[m], W[ids[m, j]]) (float32 accumulate).
+hipError_t gather_dot(bool bf16, const void* x, const void* W, int H, int V, const int* ids, int M,
+                      int K, float* out, hipStream_t s);
+
+// --------------------------------------------------------------- tree
+struct TreeState {   // workspace arrays, per sequence CMAX candidates
+  int* tok;
+  int* parent;
+  int* slot;
+  int* src;
+  float* score;
+  int* active;      // [B]
+  int* beam;        // [B, k] candidate index of each beam node of the current pass
+  int cmax;
+};
+struct TreeOut {
+  int* tokens; int* parent; int* depth; int* position; int* draft_slot; int* num_nodes;
+  float* score; uint64_t* anc_mask;
+};
+struct PassRows {    // inputs of the next draft pass
+  int* tok; int* pos; int* slot; int* src; int* anc; int A;
+};
+hipError_t tree_root_setup(int B, int n_new, const int* in_tokens, const int* ctx_len, int k, int D,
+                           int cap, TreeState st, PassRows rows, hipStream_t s);
+// Consume pass d's top-k (ids/logp rows of width ld), append candidates,
+// select the next beam (writes `next`) or, at d == D, the final tree.
+hipError_t tree_expand(int d, int B, int n_new, const int* ctx_len, const int* in_tokens, int k,
+                       int D, int N, const int* ids, const float* logp, int ld, int root_stride,
+                       int root_off, TreeState st, PassRows next, TreeOut out, hipStream_t s);
+
+// ------------------------------------------------------------- verify
+void verify_plan(int rows, int V, int* nch, int* chunk);
+size_t verify_part_bytes(int rows, int nch);
+hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const int* parent,
+                  const int* num_nodes, const float* logits, int mode, float temperature,
+                  const float* accept_u, uint64_t seed, int* out_tokens, int* accepted_len,
+                  int* accepted_nodes, void* part, int nch, int chunk, hipStream_t s);
+
+// ------------------------------------------------------------ compact
+struct KvFull {
+  void* k; void* v; int layers; int batch; int nkv; int slots; int hd;
+  int64_t stride_layer, stride_seq, stride_head;
+};
+hipError_t compact(bool bf16, KvFull kv, int B, const int* base, const int* nodes,
+                   const int* alen, int max_accept, hipStream_t s);
+
+}  // namespace spec

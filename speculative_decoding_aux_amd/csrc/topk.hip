@@ -1,0 +1,426 @@
+// Vocabulary-wide top-k with log-probabilities, candidate retrieval and the
+// gathered exact rescoring of the EAGLE-4 candidate head.
+//
+// topk: rows are split into chunks; a workgroup scans one chunk with a sorted
+// register list of KM (value, id) per thread plus an online (max, sum exp)
+// (sum in float64), merges the 256 lists by k rounds of wave-wide "best head"
+// selection, and writes a partial record; a second kernel merges the chunk
+// records of a row, takes logsumexp = max + log(sum) in float64 rounded once to
+// float32, and emits log-prob = z - lse.  Order is (value desc, id asc).
+#include "common.h"
+#include "kernels.h"
+
+namespace spec {
+
+namespace {
+
+constexpr int kIdNone = 0x7fffffff;
+
+template <int KM>
+struct List {
+  float v[KM];
+  int i[KM];
+  SPEC_DEV void init() {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      v[j] = -INFINITY;
+      i[j] = kIdNone;
+    }
+  }
+  SPEC_DEV void insert(float x, int id) {
+    if (!better(x, id, v[KM - 1], i[KM - 1])) return;
+#pragma unroll
+    for (int j = KM - 1; j >= 1; --j) {
+      const bool bp = better(x, id, v[j - 1], i[j - 1]);
+      const bool bc = better(x, id, v[j], i[j]);
+      const float nv = bp ? v[j - 1] : (bc ? x : v[j]);
+      const int ni = bp ? i[j - 1] : (bc ? id : i[j]);
+      v[j] = nv;
+      i[j] = ni;
+    }
+    if (better(x, id, v[0], i[0])) {
+      v[0] = x;
+      i[0] = id;
+    }
+  }
+  SPEC_DEV void pop() {
+#pragma unroll
+    for (int j = 0; j < KM - 1; ++j) {
+      v[j] = v[j + 1];
+      i[j] = i[j + 1];
+    }
+    v[KM - 1] = -INFINITY;
+    i[KM - 1] = kIdNone;
+  }
+};
+
+// Wave-wide best (value, id) of each lane's head.
+SPEC_DEV void wave_best(float& v, int& id) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oi = __shfl_xor(id, o, 64);
+    if (better(ov, oi, v, id)) {
+      v = ov;
+      id = oi;
+    }
+  }
+}
+
+// Merge the lists of the wave: the k best go to (outv, outi) (valid in every lane).
+template <int KM, int KO>
+SPEC_DEV void wave_merge(List<KM>& L, int k, float (&outv)[KO], int (&outi)[KO]) {
+#pragma unroll
+  for (int r = 0; r < KO; ++r) {
+    if (r < k) {
+      float bv = L.v[0];
+      int bi = L.i[0];
+      wave_best(bv, bi);
+      outv[r] = bv;
+      outi[r] = bi;
+      if (L.i[0] == bi && L.v[0] == bv) L.pop();
+    }
+  }
+}
+
+struct Part {   // per (row, chunk)
+  double s;
+  float m;
+  int pad;
+};
+
+template <int KM>
+__global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restrict__ z, int n,
+                                                           int ldz, int k, int chunk,
+                                                           const int* __restrict__ rowmap,
+                                                           float* __restrict__ pv,
+                                                           int* __restrict__ pi,
+                                                           Part* __restrict__ pp) {
+  __shared__ float sv[4 * KM];
+  __shared__ int si[4 * KM];
+  __shared__ float smax[4];
+  __shared__ double ssum[4];
+  const int c = blockIdx.x, r = blockIdx.y, nch = gridDim.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float* row = z + (int64_t)r * ldz;
+  const int* rm = rowmap ? rowmap + (int64_t)r * n : nullptr;
+  const int lo = c * chunk, hi = min(n, lo + chunk);
+  List<KM> L;
+  L.init();
+  float m = -INFINITY;
+  double s = 0.0;
+  for (int x = lo + threadIdx.x; x < hi; x += 256) {
+    const float v = row[x];
+    L.insert(v, rm ? rm[x] : x);
+    if (v > m) {
+      s = (m == -INFINITY ? 0.0 : s * (double)expf(m - v)) + 1.0;
+      m = v;
+    } else {
+      s += (double)expf(v - m);
+    }
+  }
+  // block max / sum
+  float wm = wave_max(m);
+  double ws = (m == -INFINITY) ? 0.0 : s * (double)expf(m - wm);
+  ws = wave_sum(ws);
+  if (lane == 0) {
+    smax[wave] = wm;
+    ssum[wave] = ws;
+  }
+  float wv[KM];
+  int wi[KM];
+  wave_merge<KM, KM>(L, k, wv, wi);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < k) {
+        sv[wave * KM + j] = wv[j];
+        si[wave * KM + j] = wi[j];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float bm = -INFINITY;
+    for (int w = 0; w < 4; ++w) bm = fmaxf(bm, smax[w]);
+    double bs = 0.0;
+    for (int w = 0; w < 4; ++w)
+      if (smax[w] != -INFINITY) bs += ssum[w] * (double)expf(smax[w] - bm);
+    List<1> one;
+    one.init();
+    if (lane < 4 * KM && (lane % KM) < k) {
+      one.v[0] = sv[lane];
+      one.i[0] = si[lane];
+    }
+    float ov[KM];
+    int oi[KM];
+    wave_merge<1, KM>(one, k, ov, oi);
+    const int64_t base = ((int64_t)r * nch + c) * KM;
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j < k) {
+          pv[base + j] = ov[j];
+          pi[base + j] = oi[j];
+        }
+      }
+      pp[(int64_t)r * nch + c] = Part{bs, bm, 0};
+    }
+  }
+}
+
+template <int KM>
+__global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict__ z, int ldz,
+                                                        int n, int k, int nch,
+                                                        const float* __restrict__ pv,
+                                                        const int* __restrict__ pi,
+                                                        const Part* __restrict__ pp,
+                                                        const int* __restrict__ id_map,
+                                                        const int* __restrict__ rowmap,
+                                                        int* __restrict__ ids, int ldi,
+                                                        float* __restrict__ logp, int ldl) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  List<KM> L;
+  L.init();
+  for (int x = lane; x < nch * KM; x += 64) {
+    if ((x % KM) < k) L.insert(pv[(int64_t)r * nch * KM + x], pi[(int64_t)r * nch * KM + x]);
+  }
+  float m = -INFINITY;
+  for (int c = lane; c < nch; c += 64) m = fmaxf(m, pp[(int64_t)r * nch + c].m);
+  m = wave_max(m);
+  double s = 0.0;
+  for (int c = lane; c < nch; c += 64) {
+    const Part p = pp[(int64_t)r * nch + c];
+    if (p.m != -INFINITY) s += p.s * exp((double)p.m - (double)m);
+  }
+  s = wave_sum(s);
+  const float lse = (float)((double)m + log(s));
+  float ov[KM];
+  int oi[KM];
+  wave_merge<KM, KM>(L, k, ov, oi);
+  if (lane < k) {
+    float v = 0.f;
+    int id = 0;
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j == lane) {
+        v = ov[j];
+        id = oi[j];
+      }
+    int out;
+    if (rowmap) {
+      out = id;  // the tie-break id is already the target id
+    } else {
+      out = id_map ? id_map[clampi(id, 0, n - 1)] : id;
+    }
+    (void)z;
+    (void)ldz;
+    ids[(int64_t)r * ldi + lane] = out;
+    logp[(int64_t)r * ldl + lane] = v - lse;
+  }
+}
+
+// ---- candidate retrieval: radix select of the K best per row ---------------
+SPEC_DEV uint32_t okey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict__ z, int n,
+                                                         int K, int* __restrict__ ids) {
+  __shared__ int hist[256];
+  __shared__ int sel_cnt, need_s, take_all;
+  __shared__ uint32_t prefix_s, mask_s;
+  __shared__ float cv[256];
+  __shared__ int ci[256];
+  __shared__ int scan[256];
+  const int r = blockIdx.x, t = threadIdx.x;
+  const float* row = z + (int64_t)r * n;
+  if (t == 0) {
+    prefix_s = 0;
+    mask_s = 0;
+    need_s = K;
+  }
+  __syncthreads();
+  for (int p = 24; p >= 0; p -= 8) {
+    hist[t] = 0;
+    __syncthreads();
+    const uint32_t pre = prefix_s, msk = mask_s;
+    for (int x = t; x < n; x += 256) {
+      const uint32_t key = okey(row[x]);
+      if ((key & msk) == pre) atomicAdd(&hist[(key >> p) & 255], 1);
+    }
+    __syncthreads();
+    if (t == 0) {
+      int need = need_s, above = 0;
+      int dd = 0;
+      for (int d = 255; d >= 0; --d) {
+        if (above + hist[d] >= need) {
+          dd = d;
+          break;
+        }
+        above += hist[d];
+      }
+      need_s = need - above;
+      prefix_s = pre | ((uint32_t)dd << p);
+      mask_s = msk | (255u << p);
+      take_all = (p == 0) && (hist[dd] == need - above);
+    }
+    __syncthreads();
+  }
+  const uint32_t T = prefix_s;
+  const int need_eq = need_s;
+  if (t == 0) sel_cnt = 0;
+  cv[t] = -INFINITY;
+  ci[t] = kIdNone;
+  __syncthreads();
+  // strictly above the threshold: order does not matter (sorted below)
+  for (int x = t; x < n; x += 256) {
+    const float v = row[x];
+    const uint32_t key = okey(v);
+    if (key > T || (take_all && key == T)) {
+      const int slot = atomicAdd(&sel_cnt, 1);
+      cv[slot] = v;
+      ci[slot] = x;
+    }
+  }
+  __syncthreads();
+  if (!take_all) {
+    // ties at the threshold: the smallest ids first, in row order
+    int taken = 0;
+    const int base = sel_cnt;
+    for (int x0 = 0; x0 < n && taken < need_eq; x0 += 256) {
+      const int x = x0 + t;
+      const int eq = (x < n && okey(row[x]) == T) ? 1 : 0;
+      scan[t] = eq;
+      __syncthreads();
+      for (int o = 1; o < 256; o <<= 1) {
+        const int add = t >= o ? scan[t - o] : 0;
+        __syncthreads();
+        scan[t] += add;
+        __syncthreads();
+      }
+      const int before = scan[t] - eq;
+      if (eq && taken + before < need_eq) {
+        cv[base + taken + before] = row[x];
+        ci[base + taken + before] = x;
+      }
+      const int tot = scan[255];
+      __syncthreads();
+      taken += tot;
+    }
+    __syncthreads();
+  }
+  // bitonic sort of 256 (value desc, id asc)
+  for (int size = 2; size <= 256; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int partner = t ^ stride;
+      if (partner > t) {
+        const bool desc = (t & size) == 0;
+        const bool pb = better(cv[partner], ci[partner], cv[t], ci[t]);
+        if (pb == desc) {
+          const float tv = cv[t];
+          cv[t] = cv[partner];
+          cv[partner] = tv;
+          const int ti = ci[t];
+          ci[t] = ci[partner];
+          ci[partner] = ti;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (t < K) ids[(int64_t)r * K + t] = ci[t];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_dot_kernel(const T* __restrict__ x,
+                                                         const T* __restrict__ W, int H, int V,
+                                                         const int* __restrict__ ids, int K,
+                                                         float* __restrict__ out) {
+  const int m = blockIdx.y, j = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (j >= K) return;
+  const int row = clampi(ids[(int64_t)m * K + j], 0, V - 1);
+  const T* w = W + (int64_t)row * H;
+  const T* xr = x + (int64_t)m * H;
+  float a = 0.f;
+  for (int i = lane; i < H; i += 64) a += St<T>::load(w, i) * St<T>::load(xr, i);
+  a = wave_sum(a);
+  if (lane == 0) out[(int64_t)m * K + j] = a;
+}
+
+template <int KM>
+hipError_t launch_topk(const float* z, int M, int n, int ldz, int k, const int* id_map,
+                       const int* rowmap, int* ids, int ldi, float* logp, int ldl, void* part,
+                       int nch, int chunk, hipStream_t s) {
+  float* pv = (float*)part;
+  int* pi = (int*)(pv + (size_t)M * nch * KM);
+  Part* pp = (Part*)(pi + (size_t)M * nch * KM);
+  hipLaunchKernelGGL(topk_partial_kernel<KM>, dim3(nch, M), dim3(256), 0, s, z, n, ldz, k, chunk,
+                     rowmap, pv, pi, pp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_merge_kernel<KM>, dim3(M), dim3(64), 0, s, z, ldz, n, k, nch, pv, pi,
+                     pp, id_map, rowmap, ids, ldi, logp, ldl);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void topk_plan(int M, int n, int* nch, int* chunk) {
+  int c = (2048 + M - 1) / M;
+  const int maxc = std::max(1, (n + 1023) / 1024);
+  c = std::max(1, std::min(c, maxc));
+  int ch = (n + c - 1) / c;
+  ch = (ch + 255) / 256 * 256;
+  *chunk = ch;
+  *nch = (n + ch - 1) / ch;
+}
+
+size_t topk_part_bytes(int M, int nch, int kmax) {
+  // 8-byte aligned: values + ids, then one Part per (row, chunk)
+  size_t b = (size_t)M * nch * kmax * 8;
+  b = (b + 15) / 16 * 16;
+  return b + (size_t)M * nch * sizeof(Part);
+}
+
+hipError_t topk(const float* z, int M, int n, int ldz, int k, const int* id_map, int* ids,
+                int ldi, float* logp, int ldl, void* part, int nch, int chunk, hipStream_t s) {
+  return topk_rows(z, M, n, ldz, k, id_map, nullptr, ids, ldi, logp, ldl, part, nch, chunk, s);
+}
+
+// rowmap (optional, [M, n]): per-row ids used both as tie-break and as output.
+hipError_t topk_rows(const float* z, int M, int n, int ldz, int k, const int* id_map,
+                     const int* rowmap, int* ids, int ldi, float* logp, int ldl, void* part,
+                     int nch, int chunk, hipStream_t s) {
+  if (k <= 1)
+    return launch_topk<1>(z, M, n, ldz, k, id_map, rowmap, ids, ldi, logp, ldl, part, nch, chunk, s);
+  if (k <= 2)
+    return launch_topk<2>(z, M, n, ldz, k, id_map, rowmap, ids, ldi, logp, ldl, part, nch, chunk, s);
+  if (k <= 4)
+    return launch_topk<4>(z, M, n, ldz, k, id_map, rowmap, ids, ldi, logp, ldl, part, nch, chunk, s);
+  if (k <= 8)
+    return launch_topk<8>(z, M, n, ldz, k, id_map, rowmap, ids, ldi, logp, ldl, part, nch, chunk, s);
+  return launch_topk<16>(z, M, n, ldz, k, id_map, rowmap, ids, ldi, logp, ldl, part, nch, chunk, s);
+}
+
+hipError_t topk_large(const float* z, int M, int n, int K, int* ids, void* part, hipStream_t s) {
+  (void)part;
+  hipLaunchKernelGGL(topk_large_kernel, dim3(M), dim3(256), 0, s, z, n, K, ids);
+  return hipGetLastError();
+}
+
+hipError_t gather_dot(bool bf16, const void* x, const void* W, int H, int V, const int* ids, int M,
+                      int K, float* out, hipStream_t s) {
+  dim3 grid((K + 3) / 4, M);
+  if (bf16) {
+    hipLaunchKernelGGL(gather_dot_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,
+                       (const bf16_t*)W, H, V, ids, K, out);
+  } else {
+    hipLaunchKernelGGL(gather_dot_kernel<float>, grid, dim3(256), 0, s, (const float*)x,
+                       (const float*)W, H, V, ids, K, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace spec

@@ -1,0 +1,226 @@
+// Draft-tree bookkeeping: one workgroup per sequence.
+//
+// Candidates of a sequence are stored in append order (depth-major, beam
+// order, child rank): depth 1 at [0, k), depth d >= 2 at
+// [k + (d-2) k^2, k + (d-1) k^2).  After pass d the children of that pass are
+// appended with score = parent score + log-prob (float32); the beam of the
+// next pass is the top-k depth-d candidates by (score desc, index asc); beam
+// node j runs at position ctx + n_new - 1 + d and slot ctx + n_new + (d-1) k + j
+// and sees the root rows, its ancestors' slots and its own slot.  After the
+// last pass the tree is the top-N candidates by (score desc, index asc),
+// emitted in index order (parents precede children; log-probs <= 0 make the
+// set ancestor-closed).  A sequence past the capacity cutoff keeps only its
+// root and writes no KV.
+#include "common.h"
+#include "kernels.h"
+
+namespace spec {
+
+namespace {
+
+SPEC_DEV int cand_depth(int c, int k) { return c < k ? 1 : 2 + (c - k) / (k * k); }
+
+__global__ void root_setup_kernel(int B, int n_new, const int* __restrict__ in_tokens,
+                                  const int* __restrict__ ctx_len, int k, int D, int cap,
+                                  int* __restrict__ active, int* __restrict__ tok,
+                                  int* __restrict__ pos, int* __restrict__ slot,
+                                  int* __restrict__ src, int* __restrict__ anc, int A) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * n_new) return;
+  const int b = idx / n_new, i = idx % n_new;
+  const int ctx = ctx_len[b];
+  const int act = (ctx >= 0 && ctx + n_new + (D - 1) * k <= cap) ? 1 : 0;
+  if (i == 0) active[b] = act;
+  tok[idx] = in_tokens[idx];
+  pos[idx] = ctx + i;
+  slot[idx] = act ? ctx + i : -1;
+  src[idx] = idx;
+  for (int j = 0; j < A; ++j) anc[(int64_t)idx * A + j] = (act && j <= i) ? ctx + j : -1;
+}
+
+__global__ __launch_bounds__(256) void tree_expand_kernel(
+    int d, int n_new, const int* __restrict__ ctx_len, const int* __restrict__ in_tokens, int k,
+    int D, int N, const int* __restrict__ ids, const float* __restrict__ logp, int ld,
+    int root_stride, int root_off, TreeState st, int* __restrict__ beam, PassRows nx,
+    TreeOut out) {
+  extern __shared__ int sh[];  // node_of[cmax] | counts[256] | scores[cmax]
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int cmax = st.cmax;
+  int* ctok = st.tok + (int64_t)b * cmax;
+  int* cpar = st.parent + (int64_t)b * cmax;
+  int* cslot = st.slot + (int64_t)b * cmax;
+  int* csrc = st.src + (int64_t)b * cmax;
+  float* csc = st.score + (int64_t)b * cmax;
+  int* bm = beam + (int64_t)b * k;
+  const int act = st.active[b];
+  const int ctx = ctx_len[b];
+  const int K2 = k * k;
+
+  if (act) {
+    // 1. append the children produced by pass d
+    if (d == 1) {
+      const int row = b * root_stride + root_off;
+      if (t < k) {
+        ctok[t] = ids[(int64_t)row * ld + t];
+        cpar[t] = -1;
+        cslot[t] = -1;
+        csrc[t] = row;
+        csc[t] = logp[(int64_t)row * ld + t];
+      }
+    } else {
+      const int base = k + (d - 2) * K2;
+      for (int x = t; x < K2; x += blockDim.x) {
+        const int jb = x / k, jc = x % k;
+        const int row = b * k + jb;
+        const int p = bm[jb];
+        ctok[base + x] = ids[(int64_t)row * ld + jc];
+        cpar[base + x] = p;
+        cslot[base + x] = -1;
+        csrc[base + x] = row;
+        csc[base + x] = csc[p] + logp[(int64_t)row * ld + jc];
+      }
+    }
+    __syncthreads();
+  }
+
+  if (d < D) {
+    // 2. beam of the next pass among the depth-d candidates
+    const int lo = d == 1 ? 0 : k + (d - 2) * K2;
+    const int cnt = d == 1 ? k : K2;
+    if (act) {
+      float* ss = (float*)(sh + cmax + 256);
+      for (int x = t; x < cnt; x += blockDim.x) ss[x] = csc[lo + x];
+      __syncthreads();
+      for (int x = t; x < cnt; x += blockDim.x) {
+        const float sc = ss[x];
+        int rank = 0;
+        for (int y = 0; y < cnt; ++y) rank += better(ss[y], y, sc, x) ? 1 : 0;
+        if (rank < k) bm[rank] = lo + x;
+      }
+      __syncthreads();
+    }
+    for (int j = t; j < k; j += blockDim.x) {
+      const int r = b * k + j;
+      nx.pos[r] = ctx + n_new - 1 + d;
+      if (act) {
+        const int c = bm[j];
+        const int sl = ctx + n_new + (d - 1) * k + j;
+        cslot[c] = sl;
+        nx.tok[r] = ctok[c];
+        nx.slot[r] = sl;
+        nx.src[r] = csrc[c];
+        int* a = nx.anc + (int64_t)r * nx.A;
+        for (int i = 0; i < n_new; ++i) a[i] = ctx + i;
+        // ancestors of a depth-d candidate sit at depths 1 .. d-1, then itself
+        for (int p = cpar[c]; p >= 0; p = cpar[p]) a[n_new + cand_depth(p, k) - 1] = cslot[p];
+        a[n_new + d - 1] = sl;
+        int na = n_new + d;
+        for (; na < nx.A; ++na) a[na] = -1;
+      } else {
+        nx.tok[r] = 0;
+        nx.slot[r] = -1;
+        nx.src[r] = d == 1 ? b * root_stride : b * k;
+        int* a = nx.anc + (int64_t)r * nx.A;
+        for (int i = 0; i < nx.A; ++i) a[i] = -1;
+      }
+    }
+    return;
+  }
+
+  // 3. final selection (d == D)
+  const int n1 = N + 1;
+  const int ncand = act ? k + (D - 1) * K2 : 0;
+  int* node_of = sh;
+  int* counts = sh + cmax;
+  float* ss = (float*)(sh + cmax + 256);
+  for (int c = t; c < ncand; c += blockDim.x) ss[c] = csc[c];
+  __syncthreads();
+  for (int c = t; c < ncand; c += blockDim.x) {
+    const float sc = ss[c];
+    int rank = 0;
+    for (int y = 0; y < ncand; ++y) rank += better(ss[y], y, sc, c) ? 1 : 0;
+    node_of[c] = rank < N ? 1 : 0;
+  }
+  __syncthreads();
+  // exclusive scan of the selection flags in index order
+  const int seg = (ncand + blockDim.x - 1) / blockDim.x;
+  int local = 0;
+  for (int c = t * seg; c < min(ncand, (t + 1) * seg); ++c) local += node_of[c];
+  counts[t] = local;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < (int)blockDim.x; ++i) {
+      const int v = counts[i];
+      counts[i] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int next = counts[t];
+  for (int c = t * seg; c < min(ncand, (t + 1) * seg); ++c) {
+    if (node_of[c]) {
+      node_of[c] = 1 + next;
+      ++next;
+    } else {
+      node_of[c] = -1;
+    }
+  }
+  __syncthreads();
+  const int64_t ob = (int64_t)b * n1;
+  for (int n = t; n < n1; n += blockDim.x) {
+    out.tokens[ob + n] = -1;
+    out.parent[ob + n] = -1;
+    out.depth[ob + n] = -1;
+    out.position[ob + n] = -1;
+    out.draft_slot[ob + n] = -1;
+    out.score[ob + n] = 0.f;
+    out.anc_mask[ob + n] = 0ull;
+  }
+  __syncthreads();
+  if (t == 0) {
+    out.tokens[ob] = in_tokens[b * n_new + n_new - 1];
+    out.depth[ob] = 0;
+    out.position[ob] = ctx + n_new - 1;
+    out.draft_slot[ob] = act ? ctx + n_new - 1 : -1;
+    out.anc_mask[ob] = 1ull;
+    out.num_nodes[b] = min(N, ncand);
+  }
+  for (int c = t; c < ncand; c += blockDim.x) {
+    const int n = node_of[c];
+    if (n < 0) continue;
+    const int pc = cpar[c];
+    const int dep = cand_depth(c, k);
+    out.tokens[ob + n] = ctok[c];
+    out.parent[ob + n] = pc < 0 ? 0 : node_of[pc];
+    out.depth[ob + n] = dep;
+    out.position[ob + n] = ctx + n_new - 1 + dep;
+    out.draft_slot[ob + n] = cslot[c];
+    out.score[ob + n] = csc[c];
+    uint64_t mask = 1ull | (1ull << n);
+    for (int p = pc; p >= 0; p = cpar[p]) mask |= 1ull << node_of[p];
+    out.anc_mask[ob + n] = mask;
+  }
+}
+
+}  // namespace
+
+hipError_t tree_root_setup(int B, int n_new, const int* in_tokens, const int* ctx_len, int k, int D,
+                           int cap, TreeState st, PassRows rows, hipStream_t s) {
+  const int n = B * n_new;
+  hipLaunchKernelGGL(root_setup_kernel, dim3((n + 255) / 256), dim3(256), 0, s, B, n_new,
+                     in_tokens, ctx_len, k, D, cap, st.active, rows.tok, rows.pos, rows.slot,
+                     rows.src, rows.anc, rows.A);
+  return hipGetLastError();
+}
+
+hipError_t tree_expand(int d, int B, int n_new, const int* ctx_len, const int* in_tokens, int k,
+                       int D, int N, const int* ids, const float* logp, int ld, int root_stride,
+                       int root_off, TreeState st, PassRows next, TreeOut out, hipStream_t s) {
+  const size_t lds = (size_t)(2 * st.cmax + 256) * sizeof(int);
+  hipLaunchKernelGGL(tree_expand_kernel, dim3(B), dim3(256), lds, s, d, n_new, ctx_len, in_tokens,
+                     k, D, N, ids, logp, ld, root_stride, root_off, st, st.beam, next, out);
+  return hipGetLastError();
+}
+
+}  // namespace spec

@@ -1,0 +1,368 @@
+// Verification of the draft trees against the target logits, and KV
+// compaction of the accepted path.
+//
+// Stage 1 (data-parallel over every tree node and a chunk of the vocabulary,
+// the target logits are read exactly once): greedy keeps the argmax (first
+// index on ties); stochastic keeps the running max m of l/T, the sum of
+// exp(l/T - m) in float64 and the Gumbel-max candidate l/T - log(-log U)
+// over tokens that are not children of the node, with U drawn in-kernel from
+// Philox4x32-10 (key = seed, counter = (v >> 2, node, b, 0), word v & 3), so
+// the noise costs no memory traffic.
+// Stage 2 (one wave per sequence): merge the chunk records of the nodes on
+// the walk and run the acceptance walk from the root.
+#include "common.h"
+#include "kernels.h"
+
+namespace spec {
+
+namespace {
+
+struct VPart {       // per (tree node, vocab chunk)
+  double z;          // sum exp(l/T - m)
+  float m;           // max l/T   (greedy: max l)
+  float gs;          // best Gumbel score
+  int arg;           // greedy argmax id
+  int gid;           // Gumbel argmax id
+  int pad0, pad1;
+};
+
+__global__ __launch_bounds__(256) void verify_stats_kernel(
+    int N, int k, int V, const int* __restrict__ tokens, const int* __restrict__ parent,
+    const int* __restrict__ num_nodes, const float* __restrict__ logits, int mode, float temp,
+    uint32_t seed_lo, uint32_t seed_hi, int chunk, VPart* __restrict__ part) {
+  __shared__ int kids[64];
+  __shared__ int nkids;
+  __shared__ float rf[4];
+  __shared__ int ri[4];
+  __shared__ float rg[4];
+  __shared__ int rgi[4];
+  __shared__ double rz[4];
+  const int c = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
+  const int n1 = N + 1;
+  const int b = row / n1, n = row % n1;
+  const int nn = num_nodes[b];
+  if (n > nn) return;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const float* lrow = logits + (int64_t)row * V;
+  const int lo = c * chunk, hi = min(V, lo + chunk);
+  VPart rec;
+  rec.pad0 = rec.pad1 = 0;
+  if (mode == 0) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int x = lo + t; x < hi; x += 256) {
+      const float v = lrow[x];
+      if (better(v, x, bv, bi)) {
+        bv = v;
+        bi = x;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      rf[wave] = bv;
+      ri[wave] = bi;
+    }
+    __syncthreads();
+    if (t == 0) {
+      for (int w = 1; w < 4; ++w)
+        if (better(rf[w], ri[w], rf[0], ri[0])) {
+          rf[0] = rf[w];
+          ri[0] = ri[w];
+        }
+      rec.m = rf[0];
+      rec.arg = ri[0];
+      rec.z = 0.0;
+      rec.gs = -INFINITY;
+      rec.gid = 0x7fffffff;
+      part[(int64_t)row * nch + c] = rec;
+    }
+    return;
+  }
+  // stochastic: children tokens of node n
+  if (t == 0) {
+    int cnt = 0;
+    for (int x = 1; x <= nn && cnt < 64; ++x)
+      if (parent[(int64_t)b * n1 + x] == n) kids[cnt++] = tokens[(int64_t)b * n1 + x];
+    nkids = cnt;
+  }
+  __syncthreads();
+  const int nk = nkids;
+  const float invT = 1.0f / temp;
+  float m = -INFINITY;
+  double zs = 0.0;
+  float gs = -INFINITY;
+  int gi = 0x7fffffff;
+  // 4 consecutive ids share one Philox block
+  const int q0 = lo >> 2, q1 = (hi + 3) >> 2;
+  for (int qd = q0 + t; qd < q1; qd += 256) {
+    const u32x4 rnd = philox4x32_10(u32x4{(uint32_t)qd, (uint32_t)n, (uint32_t)b, 0u}, seed_lo,
+                                    seed_hi);
+    const uint32_t w[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x = qd * 4 + e;
+      if (x < lo || x >= hi) continue;
+      const float zv = temp == 1.0f ? lrow[x] : lrow[x] * invT;
+      if (zv > m) {
+        zs = (m == -INFINITY ? 0.0 : zs * exp((double)m - (double)zv)) + 1.0;
+        m = zv;
+      } else {
+        zs += (double)expf(zv - m);
+      }
+      const float sc = zv + gumbel_from_bits(w[e]);
+      if (better(sc, x, gs, gi)) {
+        bool child = false;
+        for (int j = 0; j < nk; ++j) child |= kids[j] == x;
+        if (!child) {
+          gs = sc;
+          gi = x;
+        }
+      }
+    }
+  }
+  const float wm = wave_max(m);
+  double wz = m == -INFINITY ? 0.0 : zs * exp((double)m - (double)wm);
+  wz = wave_sum(wz);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float og = __shfl_xor(gs, o, 64);
+    const int oi = __shfl_xor(gi, o, 64);
+    if (better(og, oi, gs, gi)) {
+      gs = og;
+      gi = oi;
+    }
+  }
+  if (lane == 0) {
+    rf[wave] = wm;
+    rz[wave] = wz;
+    rg[wave] = gs;
+    rgi[wave] = gi;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float bm = -INFINITY;
+    for (int w2 = 0; w2 < 4; ++w2) bm = fmaxf(bm, rf[w2]);
+    double bz = 0.0;
+    for (int w2 = 0; w2 < 4; ++w2)
+      if (rf[w2] != -INFINITY) bz += rz[w2] * exp((double)rf[w2] - (double)bm);
+    float bg = rg[0];
+    int bgi = rgi[0];
+    for (int w2 = 1; w2 < 4; ++w2)
+      if (better(rg[w2], rgi[w2], bg, bgi)) {
+        bg = rg[w2];
+        bgi = rgi[w2];
+      }
+    rec.m = bm;
+    rec.z = bz;
+    rec.gs = bg;
+    rec.gid = bgi;
+    rec.arg = 0;
+    part[(int64_t)row * nch + c] = rec;
+  }
+}
+
+__global__ __launch_bounds__(64) void verify_walk_kernel(
+    int N, int D, int k, int V, const int* __restrict__ tokens, const int* __restrict__ parent,
+    const int* __restrict__ num_nodes, const float* __restrict__ logits, int mode, float temp,
+    const float* __restrict__ accept_u, int nch, const VPart* __restrict__ part,
+    int* __restrict__ out_tokens, int* __restrict__ accepted_len, int* __restrict__ accepted_nodes) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int n1 = N + 1;
+  const int nn = min(num_nodes[b], N);
+  const int* tk = tokens + (int64_t)b * n1;
+  const int* pr = parent + (int64_t)b * n1;
+  int cur = 0, depth = 0, emit = 0;
+  for (int j = lane; j <= D; j += 64) out_tokens[(int64_t)b * (D + 1) + j] = -1;
+  for (int j = lane; j < D; j += 64) accepted_nodes[(int64_t)b * D + j] = -1;
+  while (true) {
+    const VPart* pb = part + (int64_t)(b * n1 + cur) * nch;
+    // merge the chunk records of node cur
+    float m = -INFINITY, gs = -INFINITY;
+    int arg = 0x7fffffff, gid = 0x7fffffff;
+    for (int c = lane; c < nch; c += 64) {
+      const VPart p = pb[c];
+      if (mode == 0) {
+        if (better(p.m, p.arg, m, arg)) {
+          m = p.m;
+          arg = p.arg;
+        }
+      } else {
+        m = fmaxf(m, p.m);
+        if (better(p.gs, p.gid, gs, gid)) {
+          gs = p.gs;
+          gid = p.gid;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float om = __shfl_xor(m, o, 64);
+      const int oa = __shfl_xor(arg, o, 64);
+      const float og = __shfl_xor(gs, o, 64);
+      const int oi = __shfl_xor(gid, o, 64);
+      if (mode == 0) {
+        if (better(om, oa, m, arg)) {
+          m = om;
+          arg = oa;
+        }
+      } else {
+        m = fmaxf(m, om);
+        if (better(og, oi, gs, gid)) {
+          gs = og;
+          gid = oi;
+        }
+      }
+    }
+    int next = -1;
+    if (mode == 0) {
+      // child whose token is the argmax (first in node order)
+      for (int x0 = 1; x0 <= nn && next < 0; x0 += 64) {
+        const int x = x0 + lane;
+        const bool hit = x <= nn && pr[x] == cur && tk[x] == arg;
+        const unsigned long long bal = __ballot(hit);
+        if (bal) next = x0 + __ffsll((long long)bal) - 1;
+      }
+      emit = arg;
+    } else {
+      double z = 0.0;
+      for (int c = lane; c < nch; c += 64) {
+        const VPart p = pb[c];
+        if (p.m != -INFINITY) z += p.z * exp((double)p.m - (double)m);
+      }
+      z = wave_sum(z);
+      // children in node order, tested one after another
+      double zrem = 1.0;
+      int ord = 0;
+      for (int x = 1; x <= nn && next < 0; ++x) {
+        if (pr[x] != cur) continue;
+        const int tok = clampi(tk[x], 0, V - 1);
+        const float l = logits[(int64_t)(b * n1 + cur) * V + tok];
+        const float zv = temp == 1.0f ? l : l * (1.0f / temp);
+        const double p = exp((double)zv - (double)m) / z;
+        const float u = accept_u[((int64_t)(b * n1 + cur)) * k + min(ord, k - 1)];
+        if ((double)u <= p / zrem) {
+          next = x;
+        } else {
+          zrem -= p;
+        }
+        ++ord;
+      }
+      emit = gid;
+    }
+    if (next < 0 || depth >= D) break;
+    if (lane == 0) {
+      out_tokens[(int64_t)b * (D + 1) + depth] = tk[next];
+      accepted_nodes[(int64_t)b * D + depth] = next;
+    }
+    ++depth;
+    cur = next;
+  }
+  if (lane == 0) {
+    out_tokens[(int64_t)b * (D + 1) + depth] = emit;
+    accepted_len[b] = depth;
+  }
+}
+
+// One block per (sequence, layer, kv-head): read every accepted row, then write.
+template <int VEC_PER_ROW>
+__global__ __launch_bounds__(256) void compact_kernel(char* __restrict__ kb, char* __restrict__ vb,
+                                                      int64_t sl_bytes, int64_t ss_bytes,
+                                                      int64_t sh_bytes, int slots,
+                                                      const int* __restrict__ base,
+                                                      const int* __restrict__ nodes,
+                                                      const int* __restrict__ alen, int max_accept) {
+  const int b = blockIdx.x, layer = blockIdx.y, h = blockIdx.z, t = threadIdx.x;
+  const int a = clampi(alen[b], 0, max_accept);
+  const int bs = base[b];
+  const int64_t off = layer * sl_bytes + b * ss_bytes + h * sh_bytes;
+  constexpr int kPer = (2 * 64 * VEC_PER_ROW + 255) / 256;  // up to 64 rows of K and V
+  u32x4_t buf[kPer];
+  const int total = 2 * a * VEC_PER_ROW;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = t + 256 * i;
+    if (e < total) {
+      const int kv = e / (a * VEC_PER_ROW), rem = e % (a * VEC_PER_ROW);
+      const int j = rem / VEC_PER_ROW, q = rem % VEC_PER_ROW;
+      const int src = bs + nodes[(int64_t)b * max_accept + j];
+      if (src >= 0 && src < slots) {
+        const char* p = (kv ? vb : kb) + off + (int64_t)src * VEC_PER_ROW * 16 + q * 16;
+        buf[i] = *(const u32x4_t*)p;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = t + 256 * i;
+    if (e < total) {
+      const int kv = e / (a * VEC_PER_ROW), rem = e % (a * VEC_PER_ROW);
+      const int j = rem / VEC_PER_ROW, q = rem % VEC_PER_ROW;
+      const int src = bs + nodes[(int64_t)b * max_accept + j];
+      const int dst = bs + 1 + j;
+      if (src >= 0 && src < slots && dst >= 0 && dst < slots) {
+        char* p = (kv ? vb : kb) + off + (int64_t)dst * VEC_PER_ROW * 16 + q * 16;
+        *(u32x4_t*)p = buf[i];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+void verify_plan(int rows, int V, int* nch, int* chunk) {
+  int c = (2048 + rows - 1) / std::max(1, rows);
+  const int maxc = std::max(1, (V + 4095) / 4096);
+  c = std::max(1, std::min(c, maxc));
+  int ch = (V + c - 1) / c;
+  ch = (ch + 1023) / 1024 * 1024;
+  *chunk = ch;
+  *nch = (V + ch - 1) / ch;
+}
+
+size_t verify_part_bytes(int rows, int nch) { return (size_t)rows * nch * sizeof(VPart); }
+
+hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const int* parent,
+                  const int* num_nodes, const float* logits, int mode, float temperature,
+                  const float* accept_u, uint64_t seed, int* out_tokens, int* accepted_len,
+                  int* accepted_nodes, void* part, int nch, int chunk, hipStream_t s) {
+  const int rows = B * (N + 1);
+  hipLaunchKernelGGL(verify_stats_kernel, dim3(nch, rows), dim3(256), 0, s, N, k, V, tokens,
+                     parent, num_nodes, logits, mode, temperature, (uint32_t)(seed & 0xffffffffu),
+                     (uint32_t)(seed >> 32), chunk, (VPart*)part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_walk_kernel, dim3(B), dim3(64), 0, s, N, D, k, V, tokens, parent,
+                     num_nodes, logits, mode, temperature, accept_u, nch, (const VPart*)part,
+                     out_tokens, accepted_len, accepted_nodes);
+  return hipGetLastError();
+}
+
+hipError_t compact(bool bf16, KvFull kv, int B, const int* base, const int* nodes,
+                   const int* alen, int max_accept, hipStream_t s) {
+  const int esz = bf16 ? 2 : 4;
+  const int row_bytes = kv.hd * esz;
+  const dim3 grid(B, kv.layers, kv.nkv);
+  const int64_t sl = kv.stride_layer * esz, ss = kv.stride_seq * esz, sh = kv.stride_head * esz;
+  if (row_bytes == 256) {
+    hipLaunchKernelGGL(compact_kernel<16>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
+                       sh, kv.slots, base, nodes, alen, max_accept);
+  } else if (row_bytes == 128) {
+    hipLaunchKernelGGL(compact_kernel<8>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
+                       sh, kv.slots, base, nodes, alen, max_accept);
+  } else {
+    hipLaunchKernelGGL(compact_kernel<32>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
+                       sh, kv.slots, base, nodes, alen, max_accept);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace spec

@@ -1,0 +1,213 @@
+"""Python binding of the speculation-step library.
+
+Argument marshalling only: every function below passes device pointers and
+sizes to the C ABI of the same name (include/spec.h) and allocates its output
+tensors with torch.  Every step of the path runs in the HIP kernels of
+libspec_mi355x.so; there is no CPU or torch fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+_DT = {"f32": (L.SPEC_F32, torch.float32), "bf16": (L.SPEC_BF16, torch.bfloat16)}
+
+
+class SpecError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"spec error {code}: {msg}")
+        self.code = code
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _i32(x, device):
+    if isinstance(x, torch.Tensor):
+        assert x.dtype == torch.int32 and x.is_cuda and x.is_contiguous()
+        return x
+    return torch.as_tensor(x, dtype=torch.int32, device=device).contiguous()
+
+
+class Weights:
+    """Draft weights resident on the GPU, in the workload's storage type."""
+
+    NAMES = ("fc", "embed", "input_norm", "hidden_norm", "post_attn_norm", "final_norm", "wqkv", "wo",
+             "w_gate_up", "w_down", "lm_head", "cand_down", "cand_up")
+
+    def __init__(self, tensors: dict):
+        self.t = tensors
+        s = L.SpecWeights()
+        for n in self.NAMES + ("d2t",):
+            v = tensors.get(n)
+            setattr(s, n, None if v is None else v.data_ptr())
+        self.struct = s
+
+
+class KVCache:
+    """K and V tensors [layers, B, n_kv, slots, head_dim] (contiguous)."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor):
+        assert k.shape == v.shape and k.dim() == 5 and k.is_contiguous() and v.is_contiguous()
+        self.k, self.v = k, v
+        Lr, B, H, S, D = k.shape
+        self.struct = L.SpecKV(k.data_ptr(), v.data_ptr(), Lr, B, H, S, D,
+                               k.stride(0), k.stride(1), k.stride(2))
+
+
+class Tree:
+    FIELDS = ("tokens", "parent", "depth", "position", "draft_slot", "num_nodes", "score", "anc_mask")
+
+    def __init__(self, B, n1, device):
+        z = lambda dt, *shape: torch.empty(*shape, dtype=dt, device=device)
+        self.tokens = z(torch.int32, B, n1)
+        self.parent = z(torch.int32, B, n1)
+        self.depth = z(torch.int32, B, n1)
+        self.position = z(torch.int32, B, n1)
+        self.draft_slot = z(torch.int32, B, n1)
+        self.num_nodes = z(torch.int32, B)
+        self.score = z(torch.float32, B, n1)
+        self.anc_mask = z(torch.int64, B, n1)  # uint64 bit pattern
+        self.struct = L.SpecTree(*[getattr(self, f).data_ptr() for f in self.FIELDS])
+
+    def numpy(self) -> dict:
+        out = {f: getattr(self, f).cpu().numpy() for f in self.FIELDS}
+        out["anc_mask"] = out["anc_mask"].view("uint64")
+        return out
+
+
+class SpecContext:
+    """One spec_ctx (workspace) bound to the workload's shapes."""
+
+    def __init__(self, cfg: dict, max_batch: int, max_new: int = 1, device="cuda"):
+        self.lib = L.load()
+        self.cfg = dict(cfg)
+        self.device = torch.device(device)
+        code, self.tdtype = _DT[cfg["dtype"]]
+        c = L.SpecConfig(hidden=cfg["hidden"], n_q_heads=cfg["n_q_heads"], n_kv_heads=cfg["n_kv_heads"],
+                         head_dim=cfg["head_dim"], intermediate=cfg["intermediate"], vocab=cfg["vocab"],
+                         draft_vocab=cfg["draft_vocab"], cand_rank=cfg.get("cand_rank", 0),
+                         num_candidates=cfg.get("num_candidates", 0),
+                         sliding_window=cfg.get("sliding_window", 0), rope_base=cfg["rope_base"],
+                         rms_eps=cfg["rms_eps"], top_k=cfg["top_k"], depth=cfg["depth"],
+                         total_tokens=cfg["total_tokens"], max_batch=max_batch, max_new=max_new,
+                         kv_capacity=cfg["kv_capacity"], dtype=code)
+        h = ctypes.c_void_p()
+        st = self.lib.spec_create(ctypes.byref(c), ctypes.byref(h))
+        if st != L.SPEC_OK:
+            raise SpecError(st, "spec_create rejected the configuration")
+        self.h = h
+        self.max_batch, self.max_new = max_batch, max_new
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.spec_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+    def _check(self, st):
+        if st != L.SPEC_OK:
+            raise SpecError(st, self.lib.spec_last_error(self.h).decode())
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self.lib.spec_workspace_bytes(self.h))
+
+    def profile(self, enable: bool):
+        self._check(self.lib.spec_profile_enable(self.h, 1 if enable else 0))
+
+    def profile_read(self, label: int):
+        n, ms = ctypes.c_int32(), ctypes.c_double()
+        self._check(self.lib.spec_profile_read(self.h, label, ctypes.byref(n), ctypes.byref(ms)))
+        return int(n.value), float(ms.value)
+
+
+# --------------------------------------------------------------- entry points
+def spec_draft_step(ctx: SpecContext, w: Weights, kv: KVCache, B, rows_per_seq, mode, hidden_in,
+                    tokens, positions, kv_slot, ctx_len, anc_slots, k_out, want_logits=False,
+                    want_candidates=False):
+    cfg, dev = ctx.cfg, ctx.device
+    M = B * rows_per_seq
+    tokens, positions, kv_slot, ctx_len = (_i32(x, dev) for x in (tokens, positions, kv_slot, ctx_len))
+    anc = _i32(anc_slots, dev).reshape(M, -1)
+    ids = torch.empty(M, k_out, dtype=torch.int32, device=dev)
+    logp = torch.empty(M, k_out, dtype=torch.float32, device=dev)
+    hid = torch.empty(M, cfg["hidden"], dtype=ctx.tdtype, device=dev)
+    width = cfg["vocab"] if cfg.get("cand_rank") else cfg["draft_vocab"]
+    logits = torch.empty(M, width, dtype=torch.float32, device=dev) if want_logits else None
+    K = cfg.get("num_candidates", 0)
+    cids = torch.empty(M, K, dtype=torch.int32, device=dev) if want_candidates else None
+    cz = torch.empty(M, K, dtype=torch.float32, device=dev) if want_candidates else None
+    st = ctx.lib.spec_draft_step(ctx.h, ctypes.byref(w.struct), ctypes.byref(kv.struct), B, rows_per_seq,
+                                 mode, _p(hidden_in), _p(tokens), _p(positions), _p(kv_slot), _p(ctx_len),
+                                 _p(anc), anc.shape[1], k_out, _p(ids), _p(logp), _p(hid), _p(logits),
+                                 _p(cids), _p(cz), _stream())
+    ctx._check(st)
+    return {"ids": ids, "logp": logp, "h_out": hid, "logits": logits, "cand_ids": cids, "cand_logits": cz}
+
+
+def spec_topk_logprobs(ctx: SpecContext, logits: torch.Tensor, k: int, id_map=None):
+    M, n = logits.shape
+    ids = torch.empty(M, k, dtype=torch.int32, device=logits.device)
+    logp = torch.empty(M, k, dtype=torch.float32, device=logits.device)
+    st = ctx.lib.spec_topk_logprobs(ctx.h, M, n, _p(logits), k, _p(id_map), _p(ids), _p(logp), _stream())
+    ctx._check(st)
+    return ids, logp
+
+
+def spec_tree_from_topk(ctx: SpecContext, B, n_new, in_tokens, ctx_len, ids_tab, lp_tab) -> Tree:
+    dev = ctx.device
+    tree = Tree(B, ctx.cfg["total_tokens"] + 1, dev)
+    in_tokens, ctx_len, ids_tab = (_i32(x, dev) for x in (in_tokens, ctx_len, ids_tab))
+    lp_tab = lp_tab.contiguous()
+    st = ctx.lib.spec_tree_from_topk(ctx.h, B, n_new, _p(in_tokens), _p(ctx_len), _p(ids_tab),
+                                     _p(lp_tab), ctypes.byref(tree.struct), _stream())
+    ctx._check(st)
+    return tree
+
+
+def spec_build_tree(ctx: SpecContext, w: Weights, kv: KVCache, aux, in_tokens, ctx_len, tree=None) -> Tree:
+    dev = ctx.device
+    B, n_new = in_tokens.shape
+    if tree is None:
+        tree = Tree(B, ctx.cfg["total_tokens"] + 1, dev)
+    in_tokens, ctx_len = _i32(in_tokens, dev), _i32(ctx_len, dev)
+    st = ctx.lib.spec_build_tree(ctx.h, ctypes.byref(w.struct), ctypes.byref(kv.struct), B, n_new,
+                                 _p(aux), _p(in_tokens), _p(ctx_len), ctypes.byref(tree.struct), _stream())
+    ctx._check(st)
+    return tree
+
+
+def spec_verify_tree(ctx: SpecContext, tree: Tree, target_logits, mode, temperature=1.0, accept_u=None,
+                     seed=0, out=None):
+    B = tree.tokens.shape[0]
+    D = ctx.cfg["depth"]
+    dev = target_logits.device
+    if out is None:
+        out = (torch.empty(B, D + 1, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, D, dtype=torch.int32, device=dev))
+    st = ctx.lib.spec_verify_tree(ctx.h, B, ctypes.byref(tree.struct), _p(target_logits), mode,
+                                  float(temperature), _p(accept_u), int(seed) & (2**64 - 1), _p(out[0]),
+                                  _p(out[1]), _p(out[2]), _stream())
+    ctx._check(st)
+    return out
+
+
+def spec_compact_kv(ctx: SpecContext, kv: KVCache, tree_base, accepted_nodes, accepted_len):
+    B, max_accept = accepted_nodes.shape
+    dev = ctx.device
+    tree_base = _i32(tree_base, dev)
+    st = ctx.lib.spec_compact_kv(ctx.h, ctypes.byref(kv.struct), B, _p(tree_base), _p(accepted_nodes),
+                                 _p(accepted_len), max_accept, _stream())
+    ctx._check(st)

@@ -1,0 +1,179 @@
+"""GPU parity of one draft pass (S1-S9, S8') and of the whole draft side
+(spec_build_tree) against the oracle on the same seeded inputs.
+
+Tolerances: float32 workloads 1e-4 on logits; bf16 workloads 2e-2 absolute on
+logits (bf16 operands, float32 accumulation), and relative 1e-2 on bf16
+activations and cache rows (a one-ulp rounding flip).  Token ids must match
+the oracle wherever the oracle's logits leave a gap wider than the tolerance;
+end-to-end trees are compared bit-exactly on seeds whose every decision has
+such a gap (checked from the oracle's own values)."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, announce, compare_tree, ids_match_where_gap_allows
+from oracle import draft as od
+from oracle import tree as ot
+from speculative_decoding_aux_amd import spec as S
+from speculative_decoding_aux_amd.tensors import from_device, to_device, upload_kv, upload_weights
+from synth import configs, gen
+
+pytestmark = pytest.mark.gpu
+
+SMALL = dict(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, intermediate=512, vocab=2048,
+             draft_vocab=2048, top_k=3, depth=3, total_tokens=8, dtype="bf16", batch=2, ctx=40)
+
+CASES = {
+    "tiny_chain_f32": (configs.get("tiny_chain"), 1e-4),
+    "small_bf16": (configs.get("tiny_chain", **SMALL), 2e-2),
+    "small_bf16_window": (configs.get("tiny_chain", **dict(SMALL, sliding_window=8)), 2e-2),
+    "small_bf16_trimmed": (configs.get("tiny_chain", **dict(SMALL, vocab=4096, draft_vocab=1024)), 2e-2),
+    "small_f32_hd128": (configs.get("tiny_chain", **dict(SMALL, head_dim=128, dtype="f32", n_q_heads=8,
+                                                         n_kv_heads=2)), 1e-4),
+    "small_eagle4": (configs.get("tiny_chain", **dict(SMALL, cand_rank=32, num_candidates=64)), 2e-2),
+}
+
+
+def _act_tol(cfg):
+    return dict(rtol=1e-2, atol=1e-2) if cfg["dtype"] == "bf16" else dict(rtol=1e-5, atol=1e-5)
+
+
+def _rows_root(cfg, inp):
+    B, ctx = cfg["batch"], inp["ctx_len"]
+    seq = np.arange(B)
+    pos = ctx.astype(np.int32)
+    anc = pos[:, None].astype(np.int32)
+    return seq, pos, pos.copy(), anc
+
+
+def _run_both(name):
+    cfg, tol = CASES[name]
+    B, k, H = cfg["batch"], cfg["top_k"], cfg["hidden"]
+    seed = 500 + len(name)
+    W = gen.make_weights(cfg, seed)
+    inp = gen.make_step_inputs(cfg, seed, ctx_len=[cfg["ctx"] - i * 3 for i in range(B)])
+    kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
+    ctx = S.SpecContext(cfg, max_batch=B, max_new=1)
+    w = upload_weights(cfg, W)
+    cache = upload_kv(cfg, inp["k_cache"], inp["v_cache"])
+    ctx_len = inp["ctx_len"]
+    # pass 1: root rows, initial mode
+    seq, pos, slot, anc = _rows_root(cfg, inp)
+    toks = inp["in_tokens"][:, 0]
+    o1 = od.draft_pass(cfg, W, kc, vc, 0, inp["aux"][:, 0], toks, seq, pos, slot, ctx_len, anc)
+    aux = to_device(np.ascontiguousarray(inp["aux"][:, 0]), cfg["dtype"])
+    g1 = S.spec_draft_step(ctx, w, cache, B, 1, 0, aux, toks, pos, slot, ctx_len, anc, k,
+                           want_logits=True, want_candidates=bool(cfg["cand_rank"]))
+    # pass 2: k recurrent rows per sequence on the root state, slots after the root
+    rng = np.random.default_rng(seed)
+    seq2 = np.repeat(np.arange(B), k)
+    pos2 = np.repeat(pos + 1, k).astype(np.int32)
+    slot2 = (np.repeat(pos + 1, k) + np.tile(np.arange(k), B)).astype(np.int32)
+    anc2 = np.stack([np.repeat(pos, k), slot2], axis=1).astype(np.int32)
+    toks2 = rng.integers(0, cfg["vocab"], size=B * k).astype(np.int32)
+    hid2 = o1["h_out"][seq2]
+    o2 = od.draft_pass(cfg, W, kc, vc, 1, hid2, toks2, seq2, pos2, slot2, ctx_len, anc2)
+    hid2_dev = g1["h_out"][torch.from_numpy(seq2).to(DEV)].contiguous()
+    g2 = S.spec_draft_step(ctx, w, cache, B, k, 1, hid2_dev, toks2, pos2, slot2, ctx_len, anc2, k,
+                           want_logits=True, want_candidates=bool(cfg["cand_rank"]))
+    torch.cuda.synchronize()
+    return cfg, tol, W, (o1, g1), (o2, g2), (kc, vc), cache
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_draft_step_matches_oracle(name):
+    announce(f"draft step {name}")
+    cfg, tol, W, p1, p2, (kc, vc), cache = _run_both(name)
+    at = _act_tol(cfg)
+    k = cfg["top_k"]
+    d2t = W.get("d2t")
+    for o, g in (p1, p2):
+        np.testing.assert_allclose(from_device(g["h_out"]), o["h_out"], **at)
+        if cfg["cand_rank"]:
+            np.testing.assert_allclose(g["logits"].cpu().numpy(), o["scores"], atol=tol, rtol=0)
+            ids_match_where_gap_allows(g["cand_ids"].cpu().numpy(), o["scores"], cfg["num_candidates"], tol)
+            gi, gz = g["cand_ids"].cpu().numpy(), g["cand_logits"].cpu().numpy()
+            for r in range(gi.shape[0]):
+                common = {int(c): j for j, c in enumerate(o["cand_ids"][r])}
+                for j, c in enumerate(gi[r]):
+                    if int(c) in common:
+                        assert abs(gz[r, j] - o["cand_logits"][r, common[int(c)]]) <= tol
+        else:
+            np.testing.assert_allclose(g["logits"].cpu().numpy(), o["logits"], atol=tol, rtol=0)
+            ids_match_where_gap_allows(g["ids"].cpu().numpy(), o["logits"], k, tol, d2t)
+        assert np.all(g["logp"].cpu().numpy() <= 0)
+    np.testing.assert_allclose(from_device(cache.k)[0], kc, **at)
+    np.testing.assert_allclose(from_device(cache.v)[0], vc, **at)
+
+
+# ------------------------------------------------------------ whole draft side
+def _decision_gaps(cfg, record, tree):
+    """Smallest margin of every discrete choice the oracle made: the order of
+    each row's top-k (and its boundary), each beam's order and boundary, and
+    the boundary of the final selection."""
+    k, N = cfg["top_k"], cfg["total_tokens"]
+    gaps = []
+    for rows, out in record:
+        z = out["cand_logits"] if cfg["cand_rank"] else out["logits"]
+        for r in range(z.shape[0]):
+            s = np.sort(z[r].astype(np.float64))[::-1][: k + 1]
+            gaps.extend(np.abs(np.diff(s)).tolist())
+    for b, C in tree["cands"].items():
+        sc = np.array([c["score"] for c in C], np.float64)
+        depth = np.array([c["depth"] for c in C])
+        for d in np.unique(depth):
+            s = np.sort(sc[depth == d])[::-1][: k + 1]
+            gaps.extend(np.abs(np.diff(s)).tolist())
+        s = np.sort(sc)[::-1]
+        if len(s) > N:
+            gaps.append(s[N - 1] - s[N])
+    return min(gaps) if gaps else np.inf
+
+
+# End-to-end trees: a small vocabulary and tree keep the number of discrete
+# decisions low enough that seeds with no near-tie exist.
+SMALLB = dict(SMALL, vocab=512, draft_vocab=512, top_k=2, depth=3, total_tokens=5)
+BUILD = {
+    "tiny_chain_f32": (configs.get("tiny_chain"), 1e-4),
+    "small_bf16_tree": (configs.get("tiny_chain", **SMALLB), 2e-2),
+    "small_bf16_window_tree": (configs.get("tiny_chain", **dict(SMALLB, sliding_window=16, depth=4,
+                                                               total_tokens=6)), 2e-2),
+    "small_trimmed_tree": (configs.get("tiny_chain", **dict(SMALLB, vocab=4096, draft_vocab=512)), 2e-2),
+    "small_eagle4_tree": (configs.get("tiny_chain", **dict(SMALLB, cand_rank=32, num_candidates=64)), 2e-2),
+    "small_two_new_rows": (configs.get("tiny_chain", **dict(SMALLB, n_new=2)), 2e-2),
+}
+
+
+@pytest.mark.parametrize("name", list(BUILD))
+def test_build_tree_matches_oracle(name):
+    announce(f"build tree {name}")
+    cfg, tol = BUILD[name]
+    B, n_new = cfg["batch"], cfg["n_new"]
+    margin = 2e-3 if cfg["dtype"] == "bf16" else 1e-5
+    # first seed (of a fixed list) on which every oracle decision has a safe margin
+    for seed in range(700, 760):
+        W = gen.make_weights(cfg, seed)
+        ctx_len = [cfg["ctx"] - 3 * i for i in range(B)]
+        inp = gen.make_step_inputs(cfg, seed, ctx_len=ctx_len)
+        kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
+        rec = []
+        want = ot.build_tree(cfg, W, kc, vc, inp["aux"], inp["in_tokens"], inp["ctx_len"], record=rec)
+        if _decision_gaps(cfg, rec, want) > margin:
+            break
+    else:
+        pytest.fail("no seed with safe decision margins")
+    ctx = S.SpecContext(cfg, max_batch=B, max_new=n_new)
+    w = upload_weights(cfg, W)
+    cache = upload_kv(cfg, inp["k_cache"], inp["v_cache"])
+    aux = to_device(inp["aux"], cfg["dtype"])
+    tr = S.spec_build_tree(ctx, w, cache, aux, torch.from_numpy(inp["in_tokens"]).to(DEV),
+                           torch.from_numpy(inp["ctx_len"]).to(DEV))
+    torch.cuda.synchronize()
+    got = tr.numpy()
+    compare_tree(got, want, fields=("tokens", "parent", "depth", "position", "draft_slot", "num_nodes",
+                                    "anc_mask"))
+    np.testing.assert_allclose(got["score"], want["score"], atol=5e-3 if cfg["dtype"] == "bf16" else 1e-5)
+    at = _act_tol(cfg)
+    np.testing.assert_allclose(from_device(cache.k)[0], kc, **at)
+    np.testing.assert_allclose(from_device(cache.v)[0], vc, **at)

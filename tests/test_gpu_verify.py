@@ -1,0 +1,166 @@
+"""GPU parity of verification (S11-S12) and compaction (S13) against the oracle.
+
+Greedy verification and compaction are bit-exact (identical float32 logits
+and integer trees in, integer results out).  Stochastic verification must
+make the same accept decisions and draw the same Gumbel tokens; the seeds used
+here keep every decision farther than 1e-6 from its threshold (checked)."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, announce, tree_to_device
+from oracle import compact as oc
+from oracle import verify as ov
+from speculative_decoding_aux_amd import spec as S
+from speculative_decoding_aux_amd.tensors import to_device, upload_kv
+from synth import configs, gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _chain_tree(cfg, seed, B):
+    """A chain of K drafts per sequence (the chain workloads' tree shape)."""
+    rng = np.random.default_rng(seed)
+    K, V = cfg["total_tokens"], cfg["vocab"]
+    toks = rng.integers(0, V, size=(B, K + 1)).astype(np.int32)
+    parent = np.tile(np.arange(-1, K, dtype=np.int32), (B, 1))
+    return {"tokens": toks, "parent": parent, "num_nodes": np.full(B, K, np.int32)}
+
+
+CASES = [
+    ("tiny_chain", 1, "chain"),
+    ("llama8b_chain", 4, "chain"),
+    ("qwen4b_tree", 1, "tree"),
+    ("qwen4b_tree", 6, "tree"),
+    ("qwen8b_tree", 32, "tree"),
+    ("eagle4_llama8b", 64, "tree"),
+]
+
+
+@pytest.mark.parametrize("name,B,shape", CASES)
+def test_greedy_verify_bit_exact(name, B, shape):
+    announce(f"greedy verify {name} B={B}")
+    cfg = configs.get(name, batch=B)
+    seed = configs.SEEDS[name] + 7
+    tree = _chain_tree(cfg, seed, B) if shape == "chain" else gen.random_tree(cfg, seed)
+    logits = gen.plant_target_logits(cfg, tree, seed)
+    # exact ties at the argmax exercise the first-index rule
+    logits[0, 0, 5] = logits[0, 0].max()
+    want = ov.verify_greedy(tree, logits, cfg["depth"])
+    ctx = S.SpecContext(cfg, max_batch=B)
+    tr = tree_to_device(tree, ctx)
+    lg = torch.from_numpy(logits).to(DEV)
+    out, alen, nodes = S.spec_verify_tree(ctx, tr, lg, 0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), want[0])
+    np.testing.assert_array_equal(alen.cpu().numpy(), want[1])
+    np.testing.assert_array_equal(nodes.cpu().numpy(), want[2])
+    if shape == "chain":
+        assert want[1].max() > 0  # planted acceptance happened
+
+
+def _boost_children(tree, logits, amount):
+    B = logits.shape[0]
+    for b in range(B):
+        for c in range(1, int(tree["num_nodes"][b]) + 1):
+            logits[b, tree["parent"][b, c], tree["tokens"][b, c]] += amount
+
+
+def _check_margins(tree, logits, u, T, seed, out_alen):
+    """Every accept test the oracle makes is farther than 1e-6 from its
+    threshold, and the Gumbel winner beats the runner-up by more than 1e-5."""
+    B = logits.shape[0]
+    for b in range(B):
+        cur = 0
+        while True:
+            ch = ov.children(tree, b, cur)
+            p = ov.node_probs(logits[b, cur], T)
+            z, acc = 1.0, None
+            for i, c in enumerate(ch):
+                r = p[tree["tokens"][b, c]] / z
+                assert abs(float(u[b, cur, i]) - r) > 1e-6
+                if float(u[b, cur, i]) <= r:
+                    acc = c
+                    break
+                z -= p[tree["tokens"][b, c]]
+            if acc is None:
+                V = logits.shape[-1]
+                sc = logits[b, cur].astype(np.float64) / T - np.log(-np.log(ov.uniforms(seed, b, cur, np.arange(V))))
+                sc[[tree["tokens"][b, c] for c in ch]] = -np.inf
+                top2 = np.sort(sc)[-2:]
+                assert top2[1] - top2[0] > 1e-5
+                break
+            cur = acc
+
+
+@pytest.mark.parametrize("name,B,T,boost", [
+    ("tiny_chain", 8, 1.0, 3.0),
+    ("qwen4b_tree", 4, 0.7, 12.0),
+    ("qwen8b_tree", 32, 1.0, 12.0),
+])
+def test_stochastic_verify_matches_oracle(name, B, T, boost):
+    announce(f"stochastic verify {name} B={B} T={T}")
+    cfg = configs.get(name, batch=B)
+    seed = configs.SEEDS[name] + 11
+    tree = gen.random_tree(cfg, seed)
+    logits = gen.random_logits(seed, "stoch", (B, cfg["total_tokens"] + 1, cfg["vocab"]))
+    _boost_children(tree, logits, boost)
+    u = gen.make_accept_u(cfg, seed, batch=B)
+    pseed = gen.philox_seed(seed)
+    want = ov.verify_stochastic(tree, logits, cfg["depth"], T, u, pseed)
+    _check_margins(tree, logits, u, T, pseed, want[1])
+    ctx = S.SpecContext(cfg, max_batch=B)
+    tr = tree_to_device(tree, ctx)
+    out, alen, nodes = S.spec_verify_tree(ctx, tr, torch.from_numpy(logits).to(DEV), 1, T,
+                                          torch.from_numpy(u).to(DEV), pseed)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(alen.cpu().numpy(), want[1])
+    np.testing.assert_array_equal(nodes.cpu().numpy(), want[2])
+    np.testing.assert_array_equal(out.cpu().numpy(), want[0])
+    assert want[1].max() > 0
+
+
+def test_capacity_cutoff_sequence_emits_one_token():
+    cfg = configs.get("qwen4b_tree", batch=2)
+    tree = gen.random_tree(cfg, 5)
+    tree["num_nodes"][1] = 0
+    tree["tokens"][1, 1:] = -1
+    tree["parent"][1, 1:] = -1
+    logits = gen.plant_target_logits(cfg, tree, 5)
+    want = ov.verify_greedy(tree, logits, cfg["depth"])
+    ctx = S.SpecContext(cfg, max_batch=2)
+    out, alen, _ = S.spec_verify_tree(ctx, tree_to_device(tree, ctx), torch.from_numpy(logits).to(DEV), 0)
+    torch.cuda.synchronize()
+    assert alen[1].item() == 0 and (out[1, 1:] == -1).all()
+    np.testing.assert_array_equal(out.cpu().numpy(), want[0])
+
+
+@pytest.mark.parametrize("name,layers,B", [("tiny_chain", 1, 1), ("llama8b_chain", 32, 4),
+                                           ("qwen8b_tree", 3, 32)])
+def test_compaction_bit_exact(name, layers, B):
+    announce(f"compaction {name} layers={layers} B={B}")
+    cfg = configs.get(name, batch=B)
+    D = cfg["depth"]
+    slots = cfg["ctx"] + cfg["total_tokens"] + 8
+    kv = gen.make_target_kv(cfg, 3, slots, layers)
+    rng = np.random.default_rng(4)
+    base = np.full(B, cfg["ctx"], np.int32)
+    base[0] = 0
+    nodes = np.full((B, D), -1, np.int32)
+    alen = rng.integers(0, D + 1, size=B).astype(np.int32)
+    alen[0] = D
+    for b in range(B):
+        path = np.sort(rng.choice(np.arange(1, cfg["total_tokens"] + 1), size=alen[b], replace=False))
+        nodes[b, : alen[b]] = path
+    k_ref, v_ref = kv["k"].copy(), kv["v"].copy()
+    oc.compact_kv(k_ref, v_ref, base, nodes, alen)
+    ctx = S.SpecContext(cfg, max_batch=B)
+    cache = upload_kv(cfg, kv["k"], kv["v"])
+    S.spec_compact_kv(ctx, cache, torch.from_numpy(base).to(DEV), torch.from_numpy(nodes).to(DEV),
+                      torch.from_numpy(alen).to(DEV))
+    torch.cuda.synchronize()
+    got_k = cache.k.float().cpu().numpy()
+    got_v = cache.v.float().cpu().numpy()
+    np.testing.assert_array_equal(got_k, k_ref)
+    np.testing.assert_array_equal(got_v, v_ref)
