@@ -61,9 +61,10 @@ typedef struct spec_ctx spec_ctx;
 /* Shapes of the draft and of the tree; copied by spec_create.
  * Limits: head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads with
  * n_q_heads/n_kv_heads * max(top_k, max_new) <= 64; top_k <= 16;
- * total_tokens + 1 <= 64; depth <= total_tokens; hidden, 3*hidden,
- * intermediate and n_q_heads*head_dim multiples of 128 for bf16 (of 4 for
- * f32); num_candidates <= 256 and a multiple of 32 when cand_rank > 0. */
+ * total_tokens + 1 <= 64; depth <= total_tokens; max_new + depth <= 64;
+ * hidden, intermediate, n_q_heads*head_dim and cand_rank multiples of 32 for
+ * bf16 (of 4 for f32); hidden <= 8192 (bf16) / 4096 (f32);
+ * top_k <= num_candidates <= 256 when cand_rank > 0. */
 typedef struct spec_config {
   int32_t hidden;          /* H */
   int32_t n_q_heads;

@@ -9,6 +9,8 @@
 // kv-head (online softmax in float32, partial (max, sum, O) per query vector).
 // A combine kernel merges the chunk partials with the few extra keys of each
 // row and normalises.  Scores are q.k / sqrt(hd).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -17,6 +19,14 @@ namespace spec {
 namespace {
 
 constexpr int kTile = 64;  // keys per tile (one per lane)
+
+// Element e of a 16-byte vector holding 8 bf16 or 4 float32 values.
+template <typename T> SPEC_DEV float unpack(const u32x4_t& w, int e);
+template <> SPEC_DEV float unpack<float>(const u32x4_t& w, int e) { return __uint_as_float(w[e]); }
+template <> SPEC_DEV float unpack<bf16_t>(const u32x4_t& w, int e) {
+  const uint32_t x = w[e >> 1];
+  return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+}
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
@@ -74,9 +84,15 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
     const bool kok = key < k1;
     float kv[HD];
     if (kok) {
-      const T* kr = kb + (int64_t)key * HD;
+      // 16-byte loads of the key row
+      const u32x4_t* kr = (const u32x4_t*)(kb + (int64_t)key * HD);
+      constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
 #pragma unroll
-      for (int e = 0; e < HD; ++e) kv[e] = St<T>::load(kr, e);
+      for (int vq = 0; vq < HD / EPV; ++vq) {
+        const u32x4_t w = kr[vq];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) kv[vq * EPV + e] = unpack<T>(w, e);
+      }
     }
     for (int qv = wave; qv < QV; qv += 4) {
       float s = -INFINITY;
@@ -108,12 +124,20 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
       const int qv = grp + j * NG;
       if (qv < QV) acc[j] *= srow[qv];
     }
-    for (int kk = 0; kk < nk; ++kk) {
-      const float v = St<T>::load(vb, (int64_t)(t0 + kk) * HD + d);
+    // V rows in batches of 8 keys: the loads of a batch are independent
+    for (int kk0 = 0; kk0 < nk; kk0 += 8) {
+      float v8[8];
 #pragma unroll
-      for (int j = 0; j < (64 + NG - 1) / NG; ++j) {
-        const int qv = grp + j * NG;
-        if (qv < QV) acc[j] += sc[qv * kTile + kk] * v;
+      for (int u = 0; u < 8; ++u)
+        v8[u] = kk0 + u < nk ? St<T>::load(vb, (int64_t)(t0 + kk0 + u) * HD + d) : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (kk0 + u >= nk) break;
+#pragma unroll
+        for (int j = 0; j < (64 + NG - 1) / NG; ++j) {
+          const int qv = grp + j * NG;
+          if (qv < QV) acc[j] += sc[qv * kTile + kk0 + u] * v8[u];
+        }
       }
     }
     __syncthreads();
@@ -128,6 +152,192 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
   for (int i = threadIdx.x; i < QV; i += blockDim.x) {
     pb[i * (HD + 2) + HD] = mrow[i];
     pb[i * (HD + 2) + HD + 1] = lrow[i];
+  }
+}
+
+
+// ---- bf16 context attention on MFMA -----------------------------------------
+// Each wave takes blocks of 32 keys (two 16-key tiles).  S^T = K . Q^T uses K
+// rows as the A operand (lane: key = lane&15, 8 dims at 8*(lane>>4)) and the
+// query vectors as B, so the score tile lands with key 4*(lane>>4)+i and query
+// column lane&15 - exactly the B-operand layout of O^T = V^T . P^T over the 32
+// keys (element e<4: tile 0 key 4g+e, e>=4: tile 1 key 16+4g+e-4).  V^T
+// fragments gather those 8 keys at dim lane&15.  Online softmax runs per query
+// column (shuffles across the four lane groups); the four waves of a block are
+// merged pairwise through LDS.
+SPEC_DEV u32x4_t ld16(const bf16_t* p) { return *(const u32x4_t*)p; }
+
+SPEC_DEV u32x4_t pack8(const float (&v)[8]) {
+  u32x4_t w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
+  return w;
+}
+
+template <int HD, int QT>
+__global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    int64_t sseq, int64_t shead, int S, const int* __restrict__ ctx_len, const int* __restrict__ pos,
+    int R, int nq, int nkv, int window, int chunk, float* __restrict__ part) {
+  constexpr int DS = HD / 32;  // 32-dim steps of S^T
+  constexpr int DT = HD / 16;  // 16-dim tiles of O^T
+  __shared__ f32x4 mo[2][QT][DT][64];
+  __shared__ float mm[2][QT][64], ml[2][QT][64];
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int nch = gridDim.x;
+  const int G = nq / nkv, QV = R * G;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  const float scale = 1.0f / sqrtf((float)HD);
+
+  const int ctx = clampi(ctx_len[b], 0, S);
+  int minpos = 0x7fffffff;
+  for (int r = 0; r < R; ++r) minpos = min(minpos, pos[b * R + r]);
+  const int start = window > 0 ? max(0, minpos - window + 1) : 0;
+  const int k0 = start + c * chunk;
+  const int k1 = min(ctx, k0 + chunk);
+
+  u32x4_t qf[QT][DS];
+  int loq[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int qv = t * 16 + col;
+    const bool ok = qv < QV;
+    const int r = ok ? qv / G : 0, h = kvh * G + (ok ? qv % G : 0);
+    const bf16_t* qp = q + ((int64_t)(b * R + r) * nq + h) * HD + g * 8;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[t][ds] = ok ? ld16(qp + ds * 32) : u32x4_t{0u, 0u, 0u, 0u};
+    loq[t] = ok ? (window > 0 ? max(0, pos[b * R + r] - window + 1) : 0) : 0x7fffffff;
+  }
+  float mrun[QT], lrun[QT];
+  f32x4 o[QT][DT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    mrun[t] = -INFINITY;
+    lrun[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const bf16_t* kb = kc + b * sseq + kvh * shead;
+  const bf16_t* vb = vc + b * sseq + kvh * shead;
+
+  for (int kb0 = k0 + wave * 32; kb0 < k1; kb0 += 128) {
+    f32x4 sc[2][QT];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = kb0 + kt * 16 + col;
+      u32x4_t kf[DS];
+      const bf16_t* kp = kb + (int64_t)key * HD + g * 8;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) kf[ds] = key < k1 ? ld16(kp + ds * 32) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        sc[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+          sc[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ds]),
+                                                              __builtin_bit_cast(bf16x8, qf[t][ds]),
+                                                              sc[kt][t], 0, 0, 0);
+      }
+    }
+    // V^T fragments of the 32 keys, one per 16-dim tile
+    u32x4_t vf[DT];
+    {
+      int keyv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) keyv[e] = kb0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint32_t h16[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          h16[e] = keyv[e] < k1 ? (uint32_t)vb[(int64_t)keyv[e] * HD + dt * 16 + col] : 0u;
+        vf[dt] = u32x4_t{h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16), h16[4] | (h16[5] << 16),
+                         h16[6] | (h16[7] << 16)};
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      float v[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kb0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+        const float x = (e < 4 ? sc[0][t][e] : sc[1][t][e - 4]) * scale;
+        v[e] = (key < k1 && key >= loq[t]) ? x : -INFINITY;
+        tmax = fmaxf(tmax, v[e]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun[t], tmax);
+      const float alpha =
+          mrun[t] == -INFINITY ? (mnew == -INFINITY ? 1.f : 0.f) : expf(mrun[t] - mnew);
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = v[e] == -INFINITY ? 0.f : expf(v[e] - mnew);
+        psum += v[e];
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      lrun[t] = lrun[t] * alpha + psum;
+      mrun[t] = mnew;
+      const u32x4_t pf = pack8(v);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[t][dt] *= alpha;
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
+                                                           __builtin_bit_cast(bf16x8, pf), o[t][dt],
+                                                           0, 0, 0);
+      }
+    }
+  }
+  // merge waves pairwise: (2,3) -> (0,1), then 1 -> 0
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const int half = round == 0 ? 2 : 1;
+    if (wave >= half && wave < 2 * half) {
+      const int slot = wave - half;
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        mm[slot][t][lane] = mrun[t];
+        ml[slot][t][lane] = lrun[t];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) mo[slot][t][dt][lane] = o[t][dt];
+      }
+    }
+    __syncthreads();
+    if (wave < half) {
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        const float mb = mm[wave][t][lane], lb = ml[wave][t][lane];
+        const float M = fmaxf(mrun[t], mb);
+        const float ea = mrun[t] == -INFINITY ? 0.f : expf(mrun[t] - M);
+        const float eb = mb == -INFINITY ? 0.f : expf(mb - M);
+        lrun[t] = lrun[t] * ea + lb * eb;
+        mrun[t] = M;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[t][dt] = o[t][dt] * ea + mo[wave][t][dt][lane] * eb;
+      }
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+    float* pb = part + (((int64_t)(b * nkv + kvh) * nch + c) * QV) * (HD + 2);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int qv = t * 16 + col;
+      if (qv >= QV) continue;
+      float* rec = pb + (int64_t)qv * (HD + 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rec[dt * 16 + 4 * g + i] = o[t][dt][i];
+      if (g == 0) {
+        rec[HD] = mrun[t];
+        rec[HD + 1] = lrun[t];
+      }
+    }
   }
 }
 
@@ -213,11 +423,25 @@ template <typename T, int HD>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int G = a.nq / a.nkv;
   const int QV = a.R * G;
-  const size_t lds = (size_t)QV * (HD + kTile + 3) * sizeof(float) + QV * sizeof(int);
-  hipLaunchKernelGGL((attn_ctx_kernel<T, HD>), dim3(a.nchunks, a.nkv, a.B), dim3(256), lds, s,
-                     (const T*)a.q, (const T*)a.kv.k, (const T*)a.kv.v, a.kv.stride_seq,
-                     a.kv.stride_head, a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv, a.window,
-                     a.chunk, a.part);
+  const dim3 grid(a.nchunks, a.nkv, a.B);
+  if (std::is_same<T, bf16_t>::value && QV <= 32) {
+    if (QV <= 16) {
+      hipLaunchKernelGGL((attn_ctx_mfma_kernel<HD, 1>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
+                         (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq,
+                         a.kv.stride_head, a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
+                         a.window, a.chunk, a.part);
+    } else {
+      hipLaunchKernelGGL((attn_ctx_mfma_kernel<HD, 2>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
+                         (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq,
+                         a.kv.stride_head, a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
+                         a.window, a.chunk, a.part);
+    }
+  } else {
+    const size_t lds = (size_t)QV * (HD + kTile + 3) * sizeof(float) + QV * sizeof(int);
+    hipLaunchKernelGGL((attn_ctx_kernel<T, HD>), grid, dim3(256), lds, s, (const T*)a.q,
+                       (const T*)a.kv.k, (const T*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
+                       a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv, a.window, a.chunk, a.part);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(a.B * a.R, a.nq), dim3(64), 0, s,
@@ -233,10 +457,10 @@ void attn_plan(int B, int nkv, int slots, int window, int* nchunks, int* chunk) 
   const int span = window > 0 ? std::min(window, slots) : slots;
   const int units = std::max(1, B * nkv);
   int nc = (1024 + units - 1) / units;
-  const int max_nc = std::max(1, (span + 255) / 256);
+  const int max_nc = std::max(1, (span + 127) / 128);  // at least one 32-key block per wave
   nc = std::max(1, std::min(nc, max_nc));
   int ch = (span + nc - 1) / nc;
-  ch = (ch + kTile - 1) / kTile * kTile;
+  ch = (ch + 127) / 128 * 128;  // whole 32-key blocks for each of the 4 waves
   *chunk = ch;
   *nchunks = (span + ch - 1) / ch;
 }

@@ -21,15 +21,20 @@ namespace {
 // v_mfma_f32_16x16x32_bf16 operand layout: lane l holds row (l & 15) of A
 // (column (l & 15) of B) and K elements 8*(l >> 4) .. +8; the 4 accumulators
 // of lane l are rows 4*(l >> 4) .. +4 of column (l & 15).
+//
+// A wave owns CW tiles of 16 output columns; each 128-K step issues 4*CW
+// 16-byte loads per lane, and two steps are issued before their MFMAs, so a
+// wave keeps 8*CW loads of the weight stream in flight.  Plain (temporal)
+// loads measured faster than nontemporal ones on this stream.
 // TAG only separates kernel symbols (0: layer GEMMs, 1: LM head / scores) so
 // that per-kernel traces attribute time to the dominant contraction.
-template <int MT, int TAG>
+template <int MT, int TAG, int CW>
 __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict__ X, int ldx,
                                                          const bf16_t* __restrict__ W, int ldw,
                                                          float* __restrict__ P, int M, int N, int K,
                                                          int kc) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * 64 + wave * 16;
+  const int n0 = blockIdx.x * (64 * CW) + wave * (16 * CW);
   if (n0 >= N) return;
   const int split = blockIdx.y;
   const int k0 = split * kc;
@@ -37,7 +42,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict
   const int m0 = blockIdx.z * (16 * MT);
   const int g = lane >> 4, c = lane & 15;
 
-  const bf16_t* wp = W + (int64_t)min(n0 + c, N - 1) * ldw + g * 8;
+  const bf16_t* wp[CW];
+#pragma unroll
+  for (int w = 0; w < CW; ++w) wp[w] = W + (int64_t)min(n0 + 16 * w + c, N - 1) * ldw + g * 8;
   const bf16_t* xp[MT];
   bool xv[MT];
 #pragma unroll
@@ -46,17 +53,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict
     xv[t] = m < M;
     xp[t] = X + (int64_t)(xv[t] ? m : 0) * ldx + g * 8;
   }
-  f32x4 acc[MT];
+  f32x4 acc[CW][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < CW; ++w)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // 128 K elements per step: 4 MFMAs, each over 32 consecutive K.
-  int k = k0;
-#pragma unroll 2
-  for (; k + 128 <= k1; k += 128) {
-    u32x4_t wr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wr[j] = __builtin_nontemporal_load((const u32x4_t*)(wp + k + j * 32));
+  auto step = [&](const u32x4_t (&wr)[CW][4], int k) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       u32x4_t xr[4];
@@ -64,35 +67,63 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict
       for (int j = 0; j < 4; ++j)
         xr[j] = xv[t] ? *(const u32x4_t*)(xp[t] + k + j * 32) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[j]),
-                                                         __builtin_bit_cast(bf16x8, xr[j]), acc[t],
-                                                         0, 0, 0);
+      for (int w = 0; w < CW; ++w)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[w][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr[w][j]),
+                                                              __builtin_bit_cast(bf16x8, xr[j]),
+                                                              acc[w][t], 0, 0, 0);
     }
+  };
+  int k = k0;
+  // two 128-K steps per iteration: all their weight loads first
+  for (; k + 256 <= k1; k += 256) {
+    u32x4_t wa[CW][4], wb[CW][4];
+#pragma unroll
+    for (int w = 0; w < CW; ++w)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wa[w][j] = *(const u32x4_t*)(wp[w] + k + j * 32);
+        wb[w][j] = *(const u32x4_t*)(wp[w] + k + 128 + j * 32);
+      }
+    step(wa, k);
+    step(wb, k + 128);
+  }
+  for (; k + 128 <= k1; k += 128) {
+    u32x4_t wa[CW][4];
+#pragma unroll
+    for (int w = 0; w < CW; ++w)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wa[w][j] = *(const u32x4_t*)(wp[w] + k + j * 32);
+    step(wa, k);
   }
   // K tail in steps of 32
   for (; k < k1; k += 32) {
-    const u32x4_t wr = *(const u32x4_t*)(wp + k);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const u32x4_t xr = xv[t] ? *(const u32x4_t*)(xp[t] + k) : u32x4_t{0u, 0u, 0u, 0u};
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wr),
-                                                       __builtin_bit_cast(bf16x8, xr), acc[t], 0, 0,
-                                                       0);
+#pragma unroll
+      for (int w = 0; w < CW; ++w)
+        acc[w][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, *(const u32x4_t*)(wp[w] + k)), __builtin_bit_cast(bf16x8, xr),
+            acc[w][t], 0, 0, 0);
     }
   }
-  // lane holds Y[n0 + 4g + r][m0 + 16t + c], r = 0..3
-  const int nb = n0 + 4 * g;
+  // lane holds Y[n0 + 16w + 4g + r][m0 + 16t + c], r = 0..3
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int m = m0 + t * 16 + c;
-    if (m >= M) continue;
-    float* dst = P + ((int64_t)split * M + m) * N + nb;
-    if (nb + 3 < N && (N & 3) == 0) {
-      *(float4*)dst = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-    } else {
-      for (int r = 0; r < 4; ++r)
-        if (nb + r < N) dst[r] = acc[t][r];
+  for (int w = 0; w < CW; ++w) {
+    const int nb = n0 + 16 * w + 4 * g;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int m = m0 + t * 16 + c;
+      if (m >= M || nb >= N) continue;
+      float* dst = P + ((int64_t)split * M + m) * N + nb;
+      if (nb + 3 < N && (N & 3) == 0) {
+        *(float4*)dst = make_float4(acc[w][t][0], acc[w][t][1], acc[w][t][2], acc[w][t][3]);
+      } else {
+        for (int r = 0; r < 4; ++r)
+          if (nb + r < N) dst[r] = acc[w][t][r];
+      }
     }
   }
 }
@@ -132,60 +163,90 @@ __global__ __launch_bounds__(256) void gemm_f32_rows(const float* __restrict__ X
   }
 }
 
+// Split-K reduction: a block covers 32 consecutive outputs; thread group
+// sg = threadIdx.x / 32 (8 groups) sums splits sg, sg+8, ... and the groups are
+// combined through LDS in a fixed order, so results are deterministic.
+constexpr int kEpiCols = 32, kEpiGroups = 8;
+
+SPEC_DEV float split_sum(const float* __restrict__ p, int64_t sstride, int nsplit, int sg) {
+  float a = 0.f;
+  for (int s = sg; s < nsplit; s += kEpiGroups) a += p[s * sstride];
+  return a;
+}
+
 template <typename T, int OP>
 __global__ __launch_bounds__(256) void epi_kernel(T* __restrict__ Y, const T* __restrict__ R,
                                                    const float* __restrict__ P, int nsplit, int M,
                                                    int N) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)M * N) return;
-  const int m = int(idx / N), n = int(idx % N);
+  __shared__ float red[2][kEpiGroups][kEpiCols];
+  const int e = threadIdx.x % kEpiCols, sg = threadIdx.x / kEpiCols;
+  const int64_t idx = (int64_t)blockIdx.x * kEpiCols + e;
+  const bool ok = idx < (int64_t)M * N;
+  const int m = ok ? int(idx / N) : 0, n = ok ? int(idx % N) : 0;
   const int ldp = OP == EPI_SWIGLU ? 2 * N : N;
   const int64_t ss = (int64_t)M * ldp;
+  const float* p = P + (int64_t)m * ldp + n;
+  red[0][sg][e] = ok ? split_sum(p, ss, nsplit, sg) : 0.f;
+  if (OP == EPI_SWIGLU) red[1][sg][e] = ok ? split_sum(p + N, ss, nsplit, sg) : 0.f;
+  __syncthreads();
+  if (sg != 0 || !ok) return;
+  float a = 0.f, u = 0.f;
+#pragma unroll
+  for (int j = 0; j < kEpiGroups; ++j) {
+    a += red[0][j][e];
+    if (OP == EPI_SWIGLU) u += red[1][j][e];
+  }
   if (OP == EPI_SWIGLU) {
-    float gsum = 0.f, usum = 0.f;
-    const float* p = P + (int64_t)m * ldp + n;
-    for (int s = 0; s < nsplit; ++s) {
-      gsum += p[s * ss];
-      usum += p[s * ss + N];
-    }
-    const float silu = gsum / (1.f + expf(-gsum));
-    St<T>::store(Y, idx, silu * usum);
+    const float silu = a / (1.f + expf(-a));
+    St<T>::store(Y, idx, silu * u);
     return;
   }
-  float sum = 0.f;
-  const float* p = P + (int64_t)m * ldp + n;
-  for (int s = 0; s < nsplit; ++s) sum += p[s * ss];
-  if (OP == EPI_RESID) sum += St<T>::load(R, idx);
-  St<T>::store(Y, idx, sum);
+  if (OP == EPI_RESID) a += St<T>::load(R, idx);
+  St<T>::store(Y, idx, a);
 }
 
 __global__ __launch_bounds__(256) void epi_f32(float* __restrict__ Y, const float* __restrict__ P,
                                                int nsplit, int64_t MN) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= MN) return;
-  float sum = 0.f;
-  for (int s = 0; s < nsplit; ++s) sum += P[s * MN + idx];
-  Y[idx] = sum;
+  __shared__ float red[kEpiGroups][kEpiCols];
+  const int e = threadIdx.x % kEpiCols, sg = threadIdx.x / kEpiCols;
+  const int64_t idx = (int64_t)blockIdx.x * kEpiCols + e;
+  const bool ok = idx < MN;
+  red[sg][e] = ok ? split_sum(P + idx, MN, nsplit, sg) : 0.f;
+  __syncthreads();
+  if (sg != 0 || !ok) return;
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < kEpiGroups; ++j) a += red[j][e];
+  Y[idx] = a;
 }
 
-// One block per (row, head): thread i < hd/2 owns the rotation pair (i, i + hd/2).
+// One block per (row, head): 4 split groups x 64 threads; thread i < hd/2 of
+// group 0 owns the rotation pair (i, i + hd/2).
 template <typename T>
-__global__ void qkv_epi_kernel(const float* __restrict__ P, int nsplit, int M, int nq, int nkv,
-                               int hd, const int* __restrict__ pos, const int* __restrict__ slot,
-                               int rows_per_seq, float rope_base, T* __restrict__ qout,
-                               T* __restrict__ kc, T* __restrict__ vc, int64_t stride_seq,
-                               int64_t stride_head, int slots) {
-  const int m = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+__global__ __launch_bounds__(256) void qkv_epi_kernel(
+    const float* __restrict__ P, int nsplit, int M, int nq, int nkv, int hd,
+    const int* __restrict__ pos, const int* __restrict__ slot, int rows_per_seq, float rope_base,
+    T* __restrict__ qout, T* __restrict__ kc, T* __restrict__ vc, int64_t stride_seq,
+    int64_t stride_head, int slots) {
+  __shared__ float red[2][4][64];
+  const int m = blockIdx.x, h = blockIdx.y, i = threadIdx.x & 63, sg = threadIdx.x >> 6;
   const int half = hd >> 1;
-  if (i >= half) return;
   const int N = (nq + 2 * nkv) * hd;
   const int64_t ss = (int64_t)M * N;
   const float* p = P + (int64_t)m * N + h * hd;
   float x1 = 0.f, x2 = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    x1 += p[s * ss + i];
-    x2 += p[s * ss + i + half];
+  if (i < half) {
+    for (int s = sg; s < nsplit; s += 4) {
+      x1 += p[s * ss + i];
+      x2 += p[s * ss + i + half];
+    }
   }
+  red[0][sg][i] = x1;
+  red[1][sg][i] = x2;
+  __syncthreads();
+  if (sg != 0 || i >= half) return;
+  x1 = red[0][0][i] + red[0][1][i] + red[0][2][i] + red[0][3][i];
+  x2 = red[1][0][i] + red[1][1][i] + red[1][2][i] + red[1][3][i];
   x1 = St<T>::round(x1);
   x2 = St<T>::round(x2);
   const int seq = m / rows_per_seq;
@@ -215,6 +276,12 @@ __global__ void qkv_epi_kernel(const float* __restrict__ P, int nsplit, int M, i
 
 }  // namespace
 
+// Columns per wave: 16 for the very wide LM head at M <= 16 (one long K sweep
+// per wave, no split), 32 otherwise (twice the loads in flight, and at M > 16
+// each activation fragment feeds two weight tiles).
+static constexpr int kMaxSplit = 32;  // bounds the epilogue's reduction depth
+static int gemm_cw(int M, int N) { return (M <= 16 && N >= 65536) ? 1 : 2; }
+
 GemmPlan gemm_plan(int M, int N, int K, bool bf16) {
   GemmPlan p;
   if (!bf16) {
@@ -222,30 +289,31 @@ GemmPlan gemm_plan(int M, int N, int K, bool bf16) {
     p.kc = K;
     return p;
   }
-  const int strips = (N + 63) / 64;
+  const int cw = gemm_cw(M, N);
+  const int strips = (N + 64 * cw - 1) / (64 * cw);
   const int mblocks = (M + 63) / 64;
-  const int target = 2048;
+  const int target = cw == 1 ? 1024 : 2048;  // workgroups in flight
   int ns = (target + strips * mblocks - 1) / (strips * mblocks);
   const int kblocks = (K + 127) / 128;
-  ns = std::max(1, std::min(ns, kblocks));
+  ns = std::max(1, std::min(std::min(ns, kblocks), kMaxSplit));
   const int kc = ((kblocks + ns - 1) / ns) * 128;
   p.kc = kc;
   p.nsplit = (K + kc - 1) / kc;
   return p;
 }
 
-template <int TAG>
+template <int TAG, int CW>
 static void launch_stream(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
                           int K, const GemmPlan& plan, hipStream_t s) {
-  const int strips = (N + 63) / 64;
+  const int strips = (N + 64 * CW - 1) / (64 * CW);
   if (M <= 16) {
-    hipLaunchKernelGGL((gemm_bf16_stream<1, TAG>), dim3(strips, plan.nsplit, 1), dim3(256), 0, s,
-                       (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc);
+    hipLaunchKernelGGL((gemm_bf16_stream<1, TAG, CW>), dim3(strips, plan.nsplit, 1), dim3(256), 0,
+                       s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc);
   } else if (M <= 32) {
-    hipLaunchKernelGGL((gemm_bf16_stream<2, TAG>), dim3(strips, plan.nsplit, 1), dim3(256), 0, s,
-                       (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc);
+    hipLaunchKernelGGL((gemm_bf16_stream<2, TAG, CW>), dim3(strips, plan.nsplit, 1), dim3(256), 0,
+                       s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc);
   } else {
-    hipLaunchKernelGGL((gemm_bf16_stream<4, TAG>), dim3(strips, plan.nsplit, (M + 63) / 64),
+    hipLaunchKernelGGL((gemm_bf16_stream<4, TAG, CW>), dim3(strips, plan.nsplit, (M + 63) / 64),
                        dim3(256), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K,
                        plan.kc);
   }
@@ -259,10 +327,13 @@ hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float
                        (const float*)W, ldw, P, M, N, K);
     return hipGetLastError();
   }
+  const bool cw1 = gemm_cw(M, N) == 1;
   if (tag == 1) {
-    launch_stream<1>(X, ldx, W, ldw, P, M, N, K, plan, s);
+    if (cw1) launch_stream<1, 1>(X, ldx, W, ldw, P, M, N, K, plan, s);
+    else launch_stream<1, 2>(X, ldx, W, ldw, P, M, N, K, plan, s);
   } else {
-    launch_stream<0>(X, ldx, W, ldw, P, M, N, K, plan, s);
+    if (cw1) launch_stream<0, 1>(X, ldx, W, ldw, P, M, N, K, plan, s);
+    else launch_stream<0, 2>(X, ldx, W, ldw, P, M, N, K, plan, s);
   }
   return hipGetLastError();
 }
@@ -270,7 +341,7 @@ hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float
 hipError_t gemm_epilogue(bool bf16, int op, void* Y, const void* R, const float* P, int nsplit,
                          int M, int N, hipStream_t s) {
   const int64_t total = (int64_t)M * N;
-  const dim3 grid((unsigned)((total + 255) / 256));
+  const dim3 grid((unsigned)((total + kEpiCols - 1) / kEpiCols));
   if (op == EPI_F32) {
     hipLaunchKernelGGL(epi_f32, grid, dim3(256), 0, s, (float*)Y, P, nsplit, total);
     return hipGetLastError();
@@ -302,7 +373,7 @@ hipError_t qkv_epilogue(bool bf16, const float* P, int nsplit, int M, int nq, in
                         const int* pos, const int* slot, int rows_per_seq, float rope_base,
                         void* qout, KvView kv, hipStream_t s) {
   dim3 grid(M, nq + 2 * nkv);
-  dim3 block(hd / 2);
+  dim3 block(256);
   if (bf16) {
     hipLaunchKernelGGL(qkv_epi_kernel<bf16_t>, grid, block, 0, s, P, nsplit, M, nq, nkv, hd, pos,
                        slot, rows_per_seq, rope_base, (bf16_t*)qout, (bf16_t*)kv.k,

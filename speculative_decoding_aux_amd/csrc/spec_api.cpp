@@ -148,7 +148,7 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
   if ((c.head_dim != 64 && c.head_dim != 128) || c.top_k > 16 || c.total_tokens + 1 > 64 ||
       c.depth > c.total_tokens || G * r_max > 64 || c.hidden % kmul ||
       c.intermediate % kmul || (c.n_q_heads * c.head_dim) % kmul ||
-      c.max_new + c.depth > 64)
+      c.max_new + c.depth > 64 || c.hidden > (bf16 ? 8192 : 4096))
     return SPEC_EUNSUPPORTED;
   if (c.cand_rank) {
     if (c.cand_rank % kmul || c.num_candidates <= 0 || c.num_candidates > 256 ||

@@ -45,8 +45,8 @@ def test_greedy_verify_bit_exact(name, B, shape):
     seed = configs.SEEDS[name] + 7
     tree = _chain_tree(cfg, seed, B) if shape == "chain" else gen.random_tree(cfg, seed)
     logits = gen.plant_target_logits(cfg, tree, seed)
-    # exact ties at the argmax exercise the first-index rule
-    logits[0, 0, 5] = logits[0, 0].max()
+    # an exact tie at the argmax of the last node exercises the first-index rule
+    logits[-1, -1, 5] = logits[-1, -1].max()
     want = ov.verify_greedy(tree, logits, cfg["depth"])
     ctx = S.SpecContext(cfg, max_batch=B)
     tr = tree_to_device(tree, ctx)
