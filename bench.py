@@ -36,18 +36,43 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
 
 
 def lm_head_bytes(cfg, M):
-    """Algorithmic bytes of one LM-head launch: the weight stream, the normed
-    rows in and the float32 logits out (EAGLE-4: the low-rank score GEMM)."""
+    """Algorithmic bytes of one LM-head launch: the weight stream and the
+    normed rows in; out, the float32 logits, or - when the vocab top-k is fused
+    into the launch (bf16, unsplit: M <= 16 with Vd >= 65536, or enough
+    64-row blocks x 128-column strips to fill 2048 workgroups) - one
+    (top-k list, max, sum) record per row and column strip.  EAGLE-4: the
+    low-rank score GEMM, scores out."""
     H = cfg["hidden"]
     if cfg["cand_rank"]:
         r, V = cfg["cand_rank"], cfg["vocab"]
         return V * r * 2 + M * r * 2 + M * V * 4
-    Vd = cfg["draft_vocab"]
-    return Vd * H * 2 + M * H * 2 + M * Vd * 4
+    Vd, k = cfg["draft_vocab"], cfg["top_k"]
+    cols = 64 if (M <= 16 and Vd >= 65536) else 128
+    strips = -(-Vd // cols)
+    fused = cfg["dtype"] == "bf16" and k <= 8 and (cols == 64 or strips * -(-M // 64) >= 2048)
+    out = M * strips * (8 * (1 if k == 1 else 8) + 16) if fused else M * Vd * 4
+    return Vd * H * 2 + M * H * 2 + out
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the LM head from the committed counter profile
+    (FETCH_SIZE and WRITE_SIZE scaled by a copy of known size), or None when
+    the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_lm_head_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for src in rec["kernel_sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["kernel_source_sha256"] else None
 
 
 def pass_rows(cfg):
@@ -99,6 +124,16 @@ def main():
               "(the step is data-parallel over sequences and would shard by batch)", file=sys.stderr)
         sys.exit(2)
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 3}))
+        return
 
     from speculative_decoding_aux_amd import spec as S
     from speculative_decoding_aux_amd import _lib as L
@@ -189,8 +224,8 @@ def main():
         avg_ms = ms / max(n, 1)
         achieved = byts / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemm_bf16_stream<*,1> (LM head)" if cfg["dtype"] == "bf16" else "gemm_f32_rows",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
+                "kernel": "LM head (gemm_lmhead_topk_kernel / gemm_bf16_stream<*,1,*>)" if cfg["dtype"] == "bf16" else "gemm_f32_rows",
                 "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n,
                 "algorithmic_bytes_per_launch": int(byts)}
         print(f"[bench] lm_head {n} launches avg {avg_ms*1e3:.1f} us; attention avg "

@@ -28,6 +28,112 @@ template <> SPEC_DEV float unpack<bf16_t>(const u32x4_t& w, int e) {
   return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
 }
 
+// Final attention output of one query vector (row r, q-head h), computed by
+// one wave: merge the context-chunk records with the row's extra keys.  Lane j
+// scores extra key j (its own 16-byte key loads, q from LDS); each lane then
+// accumulates its dims over the chunk records and the extra keys' values.
+template <typename T, int HD>
+SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restrict__ kc,
+                         const T* __restrict__ vc, int64_t sseq, int64_t shead, int S,
+                         const int* __restrict__ pos, const int* __restrict__ anc, int A, int R,
+                         int nq, int nkv, int window, int nch, const float* __restrict__ part,
+                         T* __restrict__ out, float* qs /* LDS, HD floats for this wave */) {
+  constexpr int DPL = HD / 64;  // dims per lane
+  constexpr int EPV = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int G = nq / nkv, kvh = h / G;
+  const int b = r / R, qv = (r % R) * G + h % G, QV = R * G;
+  const float inv_sqrt = 1.0f / sqrtf((float)HD);
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) qs[lane + 64 * i] = St<T>::load(q, ((int64_t)r * nq + h) * HD + lane + 64 * i);
+  const float* pb = part + ((int64_t)(b * nkv + kvh) * nch * QV + qv) * (HD + 2);
+  const int64_t cstride = (int64_t)QV * (HD + 2);
+  float m = -INFINITY;
+  for (int c = lane; c < nch; c += 64) m = fmaxf(m, pb[c * cstride + HD]);
+  // extra keys: valid entries hold consecutive positions ending at pos[r]
+  const int sl = lane < A ? anc[(int64_t)r * A + lane] : -1;
+  const unsigned long long vmask = __ballot(sl >= 0);
+  const int nvalid = __popcll(vmask);
+  const int rank = __popcll(vmask & ((1ull << lane) - 1ull));
+  const int pq = pos[r];
+  const T* kb = kc + b * sseq + kvh * shead;
+  const T* vb = vc + b * sseq + kvh * shead;
+  float s = -INFINITY;
+  const bool vis = sl >= 0 && sl < S && (window <= 0 || pq - (nvalid - 1 - rank) > pq - window);
+  if (vis) {
+    const u32x4_t* kr = (const u32x4_t*)(kb + (int64_t)sl * HD);
+    float a = 0.f;
+#pragma unroll
+    for (int vq = 0; vq < HD / EPV; ++vq) {
+      const u32x4_t w = kr[vq];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) a += qs[vq * EPV + e] * unpack<T>(w, e);
+    }
+    s = a * inv_sqrt;
+  }
+  m = wave_max(fmaxf(m, s));
+  float l = 0.f;
+  float o[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[i] = 0.f;
+  if (m != -INFINITY) {
+    const float p = s == -INFINITY ? 0.f : expf(s - m);
+    l = wave_sum(p);
+    float lc = 0.f;
+    for (int c = lane; c < nch; c += 64) {
+      const float mc = pb[c * cstride + HD];
+      if (mc != -INFINITY) lc += pb[c * cstride + HD + 1] * expf(mc - m);
+    }
+    l += wave_sum(lc);
+    for (int c = 0; c < nch; ++c) {
+      const float mc = pb[c * cstride + HD];
+      if (mc == -INFINITY) continue;
+      const float w = expf(mc - m);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) o[i] += pb[c * cstride + lane + 64 * i] * w;
+    }
+    // extra keys' values, eight keys' loads in flight at a time
+    for (int j0 = 0; j0 < 64; j0 += 8) {
+      if (!(vmask >> j0)) break;
+      float vv[8][DPL], pj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        const int slj = __shfl(sl, j, 64);
+        pj[u] = __shfl(p, j, 64);
+        const bool ok = ((vmask >> j) & 1ull) && pj[u] > 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i)
+          vv[u][i] = ok ? St<T>::load(vb, (int64_t)slj * HD + lane + 64 * i) : 0.f;
+        if (!ok) pj[u] = 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o[i] += pj[u] * vv[u][i];
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) St<T>::store(out, ((int64_t)r * nq + h) * HD + lane + 64 * i, o[i] * inv);
+}
+
+// One wave per (row, q-head).
+template <typename T, int HD>
+__global__ __launch_bounds__(64) void attn_combine_kernel(const T* __restrict__ q,
+                                                          const T* __restrict__ kc,
+                                                          const T* __restrict__ vc, int64_t sseq,
+                                                          int64_t shead, int S,
+                                                          const int* __restrict__ pos,
+                                                          const int* __restrict__ anc, int A,
+                                                          int R, int nq, int nkv, int window,
+                                                          int nch, const float* __restrict__ part,
+                                                          T* __restrict__ out) {
+  __shared__ float qs[HD];
+  combine_qv<T, HD>(blockIdx.x, blockIdx.y, q, kc, vc, sseq, shead, S, pos, anc, A, R, nq, nkv,
+                    window, nch, part, out, qs);
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ kc,
@@ -222,6 +328,23 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
   const bf16_t* vb = vc + b * sseq + kvh * shead;
 
   for (int kb0 = k0 + wave * 32; kb0 < k1; kb0 += 128) {
+    // V^T fragments of the 32 keys, one per 16-dim tile (loaded first: they do
+    // not depend on the scores)
+    u32x4_t vf[DT];
+    {
+      int keyv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) keyv[e] = kb0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint32_t h16[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          h16[e] = keyv[e] < k1 ? (uint32_t)vb[(int64_t)keyv[e] * HD + dt * 16 + col] : 0u;
+        vf[dt] = u32x4_t{h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16), h16[4] | (h16[5] << 16),
+                         h16[6] | (h16[7] << 16)};
+      }
+    }
     f32x4 sc[2][QT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -238,22 +361,6 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
           sc[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ds]),
                                                               __builtin_bit_cast(bf16x8, qf[t][ds]),
                                                               sc[kt][t], 0, 0, 0);
-      }
-    }
-    // V^T fragments of the 32 keys, one per 16-dim tile
-    u32x4_t vf[DT];
-    {
-      int keyv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) keyv[e] = kb0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        uint32_t h16[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          h16[e] = keyv[e] < k1 ? (uint32_t)vb[(int64_t)keyv[e] * HD + dt * 16 + col] : 0u;
-        vf[dt] = u32x4_t{h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16), h16[4] | (h16[5] << 16),
-                         h16[6] | (h16[7] << 16)};
       }
     }
 #pragma unroll
@@ -339,84 +446,6 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
       }
     }
   }
-}
-
-// One wave per (row, q-head).
-template <typename T, int HD>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const T* __restrict__ q,
-                                                          const T* __restrict__ kc,
-                                                          const T* __restrict__ vc, int64_t sseq,
-                                                          int64_t shead, int S,
-                                                          const int* __restrict__ pos,
-                                                          const int* __restrict__ anc, int A,
-                                                          int R, int nq, int nkv, int window,
-                                                          int nch, const float* __restrict__ part,
-                                                          T* __restrict__ out) {
-  constexpr int DPL = HD / 64;  // dims per lane
-  const int r = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int G = nq / nkv, kvh = h / G;
-  const int b = r / R, qv = (r % R) * G + h % G, QV = R * G;
-  const float inv_sqrt = 1.0f / sqrtf((float)HD);
-  float qd[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) qd[i] = St<T>::load(q, ((int64_t)r * nq + h) * HD + lane + 64 * i);
-
-  const float* pb = part + ((int64_t)(b * nkv + kvh) * nch * QV + qv) * (HD + 2);
-  const int64_t cstride = (int64_t)QV * (HD + 2);
-  float m = -INFINITY;
-  for (int c = 0; c < nch; ++c) m = fmaxf(m, pb[c * cstride + HD]);
-
-  // extra keys: valid entries hold consecutive positions ending at pos[r]
-  const int* ar = anc + (int64_t)r * A;
-  int nvalid = 0;
-  for (int j = 0; j < A; ++j) nvalid += ar[j] >= 0;
-  const int pq = pos[r];
-  const T* kb = kc + b * sseq + kvh * shead;
-  const T* vb = vc + b * sseq + kvh * shead;
-  __shared__ float sx[64];
-  int jv = 0;
-  for (int j = 0; j < A && jv < 64; ++j) {
-    const int sl = ar[j];
-    if (sl < 0) continue;
-    const int pk = pq - (nvalid - 1 - jv);
-    float s = -INFINITY;
-    if (sl < S && (window <= 0 || pk > pq - window)) {
-      float a = 0.f;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) a += qd[i] * St<T>::load(kb, (int64_t)sl * HD + lane + 64 * i);
-      s = wave_sum(a) * inv_sqrt;
-    }
-    sx[jv++] = s;
-    m = fmaxf(m, s);
-  }
-  float l = 0.f;
-  float o[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) o[i] = 0.f;
-  if (m != -INFINITY) {
-    for (int c = 0; c < nch; ++c) {
-      const float mc = pb[c * cstride + HD];
-      if (mc == -INFINITY) continue;
-      const float w = expf(mc - m);
-      l += pb[c * cstride + HD + 1] * w;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) o[i] += pb[c * cstride + lane + 64 * i] * w;
-    }
-    jv = 0;
-    for (int j = 0; j < A && jv < 64; ++j) {
-      const int sl = ar[j];
-      if (sl < 0) continue;
-      const float s = sx[jv++];
-      if (s == -INFINITY) continue;
-      const float w = expf(s - m);
-      l += w;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) o[i] += w * St<T>::load(vb, (int64_t)sl * HD + lane + 64 * i);
-    }
-  }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) St<T>::store(out, ((int64_t)r * nq + h) * HD + lane + 64 * i, o[i] * inv);
 }
 
 template <typename T, int HD>

@@ -13,6 +13,7 @@
 // is deterministic).
 #include "common.h"
 #include "kernels.h"
+#include "topk_common.h"
 
 namespace spec {
 
@@ -28,20 +29,12 @@ namespace {
 // loads measured faster than nontemporal ones on this stream.
 // TAG only separates kernel symbols (0: layer GEMMs, 1: LM head / scores) so
 // that per-kernel traces attribute time to the dominant contraction.
-template <int MT, int TAG, int CW>
-__global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict__ X, int ldx,
-                                                         const bf16_t* __restrict__ W, int ldw,
-                                                         float* __restrict__ P, int M, int N, int K,
-                                                         int kc) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * (64 * CW) + wave * (16 * CW);
-  if (n0 >= N) return;
-  const int split = blockIdx.y;
-  const int k0 = split * kc;
-  const int k1 = min(K, k0 + kc);
-  const int m0 = blockIdx.z * (16 * MT);
+template <int MT, int CW>
+SPEC_DEV void stream_acc(const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W,
+                         int ldw, int M, int N, int k0, int k1, int m0, int n0,
+                         f32x4 (&acc)[CW][MT]) {
+  const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
-
   const bf16_t* wp[CW];
 #pragma unroll
   for (int w = 0; w < CW; ++w) wp[w] = W + (int64_t)min(n0 + 16 * w + c, N - 1) * ldw + g * 8;
@@ -53,7 +46,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict
     xv[t] = m < M;
     xp[t] = X + (int64_t)(xv[t] ? m : 0) * ldx + g * 8;
   }
-  f32x4 acc[CW][MT];
 #pragma unroll
   for (int w = 0; w < CW; ++w)
 #pragma unroll
@@ -109,7 +101,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict
             acc[w][t], 0, 0, 0);
     }
   }
-  // lane holds Y[n0 + 16w + 4g + r][m0 + 16t + c], r = 0..3
+}
+
+// lane holds Y[n0 + 16w + 4g + r][m0 + 16t + c], r = 0..3
+template <int MT, int CW>
+SPEC_DEV void store_tiles(const f32x4 (&acc)[CW][MT], float* __restrict__ P, int M, int N, int m0,
+                          int n0) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, c = lane & 15;
 #pragma unroll
   for (int w = 0; w < CW; ++w) {
     const int nb = n0 + 16 * w + 4 * g;
@@ -117,7 +116,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict
     for (int t = 0; t < MT; ++t) {
       const int m = m0 + t * 16 + c;
       if (m >= M || nb >= N) continue;
-      float* dst = P + ((int64_t)split * M + m) * N + nb;
+      float* dst = P + (int64_t)m * N + nb;
       if (nb + 3 < N && (N & 3) == 0) {
         *(float4*)dst = make_float4(acc[w][t][0], acc[w][t][1], acc[w][t][2], acc[w][t][3]);
       } else {
@@ -125,6 +124,125 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict
           if (nb + r < N) dst[r] = acc[w][t][r];
       }
     }
+  }
+}
+
+template <int MT, int TAG, int CW>
+__global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict__ X, int ldx,
+                                                         const bf16_t* __restrict__ W, int ldw,
+                                                         float* __restrict__ P, int M, int N, int K,
+                                                         int kc) {
+  const int wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * (64 * CW) + wave * (16 * CW);
+  if (n0 >= N) return;
+  const int split = blockIdx.y;
+  const int k0 = split * kc;
+  const int k1 = min(K, k0 + kc);
+  const int m0 = blockIdx.z * (16 * MT);
+  f32x4 acc[CW][MT];
+  stream_acc<MT, CW>(X, ldx, W, ldw, M, N, k0, k1, m0, n0, acc);
+  store_tiles<MT, CW>(acc, P + (int64_t)split * M * N, M, N, m0, n0);
+}
+
+// LM head with the vocab top-k fused: after the (unsplit) contraction each
+// lane reduces its CW*4 columns of a row to a top-KM list and a (max, sum exp)
+// pair, the four lane groups of a wave merge by shuffles, and the four waves
+// through LDS; one record per (row, workgroup) goes to the partial buffer in
+// the layout the record merge reads (pv/pi [M][nch][KM], pp [M][nch]).
+template <int MT, int CW, int KM>
+__global__ __launch_bounds__(256) void gemm_lmhead_topk_kernel(
+    const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W, int ldw,
+    float* __restrict__ z, int M, int N, int K, float* __restrict__ pv, int* __restrict__ pi,
+    topkdev::Part* __restrict__ pp) {
+  using topkdev::List;
+  __shared__ float tv[4][16 * MT][KM];
+  __shared__ int ti[4][16 * MT][KM];
+  __shared__ float tm[4][16 * MT];
+  __shared__ float ts[4][16 * MT];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int strip = blockIdx.x, nch = gridDim.x;
+  const int n0 = strip * (64 * CW) + wave * (16 * CW);
+  const int m0 = blockIdx.z * (16 * MT);
+  const bool active = n0 < N;  // no early return: the block meets at a barrier
+  f32x4 acc[CW][MT];
+  if (active) {
+    stream_acc<MT, CW>(X, ldx, W, ldw, M, N, 0, K, m0, n0, acc);
+    if (z) store_tiles<MT, CW>(acc, z, M, N, m0, n0);
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    List<KM> L;
+    L.init();
+    float lm = -INFINITY, ls = 0.f;
+    if (active) {
+#pragma unroll
+      for (int w = 0; w < CW; ++w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + 16 * w + 4 * g + r;
+          if (n < N) {
+            L.insert(acc[w][t][r], n);
+            lm = fmaxf(lm, acc[w][t][r]);
+          }
+        }
+#pragma unroll
+      for (int w = 0; w < CW; ++w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n0 + 16 * w + 4 * g + r < N) ls += expf(acc[w][t][r] - lm);
+    }
+    // merge the four lane groups holding the same row
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float om = __shfl_xor(lm, o, 64), os = __shfl_xor(ls, o, 64);
+      const float mx = fmaxf(lm, om);
+      ls = (lm == -INFINITY ? 0.f : ls * expf(lm - mx)) + (om == -INFINITY ? 0.f : os * expf(om - mx));
+      lm = mx;
+      float pvv[KM];
+      int pii[KM];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        pvv[j] = __shfl_xor(L.v[j], o, 64);
+        pii[j] = __shfl_xor(L.i[j], o, 64);
+      }
+#pragma unroll
+      for (int j = 0; j < KM; ++j) L.insert(pvv[j], pii[j]);
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        tv[wave][16 * t + c][j] = L.v[j];
+        ti[wave][16 * t + c][j] = L.i[j];
+      }
+      tm[wave][16 * t + c] = lm;
+      ts[wave][16 * t + c] = ls;
+    }
+  }
+  __syncthreads();
+  const int row = threadIdx.x;
+  if (row < 16 * MT && m0 + row < M) {
+    List<KM> L;
+    L.init();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mx = fmaxf(mx, tm[w][row]);
+#pragma unroll
+      for (int j = 0; j < KM; ++j) L.insert(tv[w][row][j], ti[w][row][j]);
+    }
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (tm[w][row] != -INFINITY) sum += (double)ts[w][row] * exp((double)tm[w][row] - (double)mx);
+    const int m = m0 + row;
+    const int64_t base = ((int64_t)m * nch + strip) * KM;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      pv[base + j] = L.v[j];
+      pi[base + j] = L.i[j];
+    }
+    pp[(int64_t)m * nch + strip] = topkdev::Part{sum, mx, 0};
   }
 }
 
@@ -334,6 +452,46 @@ hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float
   } else {
     if (cw1) launch_stream<0, 1>(X, ldx, W, ldw, P, M, N, K, plan, s);
     else launch_stream<0, 2>(X, ldx, W, ldw, P, M, N, K, plan, s);
+  }
+  return hipGetLastError();
+}
+
+int gemm_strips(int M, int N) {
+  const int cw = gemm_cw(M, N);
+  return (N + 64 * cw - 1) / (64 * cw);
+}
+
+template <int MT, int CW>
+static void launch_lmhead(const void* X, int ldx, const void* W, int ldw, float* z, int M, int N,
+                          int K, int km, float* pv, int* pi, topkdev::Part* pp, hipStream_t s) {
+  const dim3 grid((N + 64 * CW - 1) / (64 * CW), 1, (M + 16 * MT - 1) / (16 * MT));
+  if (km == 1) {
+    hipLaunchKernelGGL((gemm_lmhead_topk_kernel<MT, CW, 1>), grid, dim3(256), 0, s,
+                       (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, z, M, N, K, pv, pi, pp);
+  } else {
+    hipLaunchKernelGGL((gemm_lmhead_topk_kernel<MT, CW, 8>), grid, dim3(256), 0, s,
+                       (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, z, M, N, K, pv, pi, pp);
+  }
+}
+
+hipError_t gemm_lmhead_topk(const void* X, int ldx, const void* W, int ldw, float* z, int M, int N,
+                            int K, int km, void* part, hipStream_t s) {
+  const GemmPlan plan = gemm_plan(M, N, K, true);
+  if (plan.nsplit != 1 || (km != 1 && km != 8)) return hipErrorInvalidValue;
+  const int nch = gemm_strips(M, N);
+  float* pv = (float*)part;
+  int* pi = (int*)(pv + (size_t)M * nch * km);
+  topkdev::Part* pp = (topkdev::Part*)(pi + (size_t)M * nch * km);
+  const bool cw1 = gemm_cw(M, N) == 1;
+  if (M <= 16) {
+    if (cw1) launch_lmhead<1, 1>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
+    else launch_lmhead<1, 2>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
+  } else if (M <= 32) {
+    if (cw1) launch_lmhead<2, 1>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
+    else launch_lmhead<2, 2>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
+  } else {
+    if (cw1) launch_lmhead<4, 1>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
+    else launch_lmhead<4, 2>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
   }
   return hipGetLastError();
 }

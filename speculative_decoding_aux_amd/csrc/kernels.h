@@ -17,6 +17,14 @@ GemmPlan gemm_plan(int M, int N, int K, bool bf16);
 hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
                 int K, const GemmPlan& plan, hipStream_t s, int tag = 0);
 
+// LM head with the vocab top-k fused into its epilogue (nsplit must be 1):
+// each workgroup writes, per row, its columns' top-km list and (sum exp, max)
+// record into `part` (km = 1 or 8 >= k); logits are also stored when z != null.
+// Returns hipErrorInvalidValue when the shape does not run unsplit.
+int gemm_strips(int M, int N);
+hipError_t gemm_lmhead_topk(const void* X, int ldx, const void* W, int ldw, float* z, int M, int N,
+                            int K, int km, void* part, hipStream_t s);
+
 enum EpiOp { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_F32 = 3 };
 // Sum the nsplit partials and apply the op.  EPI_SWIGLU reads 2N columns of P
 // (gate | up) and writes N; EPI_F32 writes float32 sums to Y.
@@ -71,6 +79,10 @@ hipError_t topk(const float* z, int M, int n, int ldz, int k, const int* id_map,
 hipError_t topk_rows(const float* z, int M, int n, int ldz, int k, const int* id_map,
                      const int* rowmap, int* ids, int ldi, float* logp, int ldl, void* part,
                      int nch, int chunk, hipStream_t s);
+// Merge of the per-strip records written by the fused LM-head GEMM (km = 1 or 8
+// entries per record, layout as the topk partials): ids and log-probs per row.
+hipError_t topk_merge_records(int M, int n, int k, int km, int nch, void* part, const int* id_map,
+                              int* ids, int ldi, float* logp, int ldl, hipStream_t s);
 // Candidate retrieval: the best K (value desc, id asc) of each row, K <= 256.
 hipError_t topk_large(const float* z, int M, int n, int K, int* ids, void* part, hipStream_t s);
 // Gathered exact rescoring: out[m, j] = dot(x[m], W[ids[m, j]]) (float32 accumulate).

@@ -182,6 +182,9 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
     int nch, ch;
     topk_plan(m, nmax, &nch, &ch);
     tk = std::max(tk, topk_part_bytes(m, nch, 16));
+    // records of the fused LM-head top-k (one per row and workgroup strip)
+    if (bf16 && !c.cand_rank && gemm_plan(m, c.draft_vocab, H, true).nsplit == 1)
+      tk = std::max(tk, topk_part_bytes(m, gemm_strips(m, c.draft_vocab), 8));
   }
   ctx->topk_bytes = tk;
   {
@@ -420,8 +423,21 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
   SPEC_HIP(ctx, rmsnorm(bf, io.hidden_out, w->final_norm, c.rms_eps, M, H, ws.nrm, s));
   if (!c.cand_rank) {
     const int Vd = c.draft_vocab;
-    float* z = io.logits_out ? io.logits_out : ws.logits;
     const GemmPlan p = gemm_plan(M, Vd, H, bf);
+    const int km = io.k_out == 1 ? 1 : (io.k_out <= 8 ? 8 : 0);
+    if (bf && p.nsplit == 1 && km) {
+      // LM head with the top-k fused into its epilogue; logits only if asked for
+      {
+        ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
+        SPEC_HIP(ctx, gemm_lmhead_topk(ws.nrm, H, w->lm_head, H, io.logits_out, M, Vd, H, km,
+                                       ws.topk_part, s));
+      }
+      ProfScope ps(ctx, SPEC_PROF_TOPK, s);
+      SPEC_HIP(ctx, topk_merge_records(M, Vd, io.k_out, km, gemm_strips(M, Vd), ws.topk_part,
+                                       w->d2t, io.ids, io.ld_out, io.logp, io.ld_out, s));
+      return SPEC_OK;
+    }
+    float* z = io.logits_out ? io.logits_out : ws.logits;
     if (p.nsplit == 1) {
       ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
       SPEC_HIP(ctx, gemm(bf, ws.nrm, H, w->lm_head, H, z, M, Vd, H, p, s, 1));

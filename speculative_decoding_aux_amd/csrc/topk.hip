@@ -9,85 +9,13 @@
 // float32, and emits log-prob = z - lse.  Order is (value desc, id asc).
 #include "common.h"
 #include "kernels.h"
+#include "topk_common.h"
 
 namespace spec {
 
 namespace {
 
-constexpr int kIdNone = 0x7fffffff;
-
-template <int KM>
-struct List {
-  float v[KM];
-  int i[KM];
-  SPEC_DEV void init() {
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      v[j] = -INFINITY;
-      i[j] = kIdNone;
-    }
-  }
-  SPEC_DEV void insert(float x, int id) {
-    if (!better(x, id, v[KM - 1], i[KM - 1])) return;
-#pragma unroll
-    for (int j = KM - 1; j >= 1; --j) {
-      const bool bp = better(x, id, v[j - 1], i[j - 1]);
-      const bool bc = better(x, id, v[j], i[j]);
-      const float nv = bp ? v[j - 1] : (bc ? x : v[j]);
-      const int ni = bp ? i[j - 1] : (bc ? id : i[j]);
-      v[j] = nv;
-      i[j] = ni;
-    }
-    if (better(x, id, v[0], i[0])) {
-      v[0] = x;
-      i[0] = id;
-    }
-  }
-  SPEC_DEV void pop() {
-#pragma unroll
-    for (int j = 0; j < KM - 1; ++j) {
-      v[j] = v[j + 1];
-      i[j] = i[j + 1];
-    }
-    v[KM - 1] = -INFINITY;
-    i[KM - 1] = kIdNone;
-  }
-};
-
-// Wave-wide best (value, id) of each lane's head.
-SPEC_DEV void wave_best(float& v, int& id) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(id, o, 64);
-    if (better(ov, oi, v, id)) {
-      v = ov;
-      id = oi;
-    }
-  }
-}
-
-// Merge the lists of the wave: the k best go to (outv, outi) (valid in every lane).
-template <int KM, int KO>
-SPEC_DEV void wave_merge(List<KM>& L, int k, float (&outv)[KO], int (&outi)[KO]) {
-#pragma unroll
-  for (int r = 0; r < KO; ++r) {
-    if (r < k) {
-      float bv = L.v[0];
-      int bi = L.i[0];
-      wave_best(bv, bi);
-      outv[r] = bv;
-      outi[r] = bi;
-      if (L.i[0] == bi && L.v[0] == bv) L.pop();
-    }
-  }
-}
-
-struct Part {   // per (row, chunk)
-  double s;
-  float m;
-  int pad;
-};
+using namespace topkdev;
 
 template <int KM>
 __global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restrict__ z, int n,
@@ -169,35 +97,97 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restri
   }
 }
 
+// Merge of per-chunk records (top-KM lists with ids, and (sum exp, max)) of
+// a row: a 256-thread block, four records per thread per round.
 template <int KM>
-__global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict__ z, int ldz,
-                                                        int n, int k, int nch,
-                                                        const float* __restrict__ pv,
-                                                        const int* __restrict__ pi,
-                                                        const Part* __restrict__ pp,
-                                                        const int* __restrict__ id_map,
-                                                        const int* __restrict__ rowmap,
-                                                        int* __restrict__ ids, int ldi,
-                                                        float* __restrict__ logp, int ldl) {
-  const int r = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void topk_merge_kernel(int n, int k, int nch,
+                                                         const float* __restrict__ pv,
+                                                         const int* __restrict__ pi,
+                                                         const Part* __restrict__ pp,
+                                                         const int* __restrict__ id_map,
+                                                         const int* __restrict__ rowmap,
+                                                         int* __restrict__ ids, int ldi,
+                                                         float* __restrict__ logp, int ldl) {
+  __shared__ float sv[4 * KM];
+  __shared__ int si[4 * KM];
+  __shared__ float smax[4];
+  __shared__ double ssum[4];
+  const int r = blockIdx.x, t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int total = nch * KM;
+  const float* rv = pv + (int64_t)r * total;
+  const int* ri = pi + (int64_t)r * total;
   List<KM> L;
   L.init();
-  for (int x = lane; x < nch * KM; x += 64) {
-    if ((x % KM) < k) L.insert(pv[(int64_t)r * nch * KM + x], pi[(int64_t)r * nch * KM + x]);
+  for (int x0 = t; x0 < total; x0 += 1024) {
+    float v[4];
+    int id[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = x0 + 256 * u;
+      const bool ok = x < total && (x % KM) < k;
+      v[u] = ok ? rv[x] : -INFINITY;
+      id[u] = ok ? ri[x] : kIdNone;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) L.insert(v[u], id[u]);
   }
   float m = -INFINITY;
-  for (int c = lane; c < nch; c += 64) m = fmaxf(m, pp[(int64_t)r * nch + c].m);
-  m = wave_max(m);
   double s = 0.0;
-  for (int c = lane; c < nch; c += 64) {
-    const Part p = pp[(int64_t)r * nch + c];
-    if (p.m != -INFINITY) s += p.s * exp((double)p.m - (double)m);
+  for (int c0 = t; c0 < nch; c0 += 1024) {
+    Part q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 256 * u;
+      q[u] = c < nch ? pp[(int64_t)r * nch + c] : Part{0.0, -INFINITY, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const Part p = q[u];
+      if (p.m == -INFINITY) continue;
+      if (p.m > m) {
+        s = (m == -INFINITY ? 0.0 : s * exp((double)m - (double)p.m)) + p.s;
+        m = p.m;
+      } else {
+        s += p.s * exp((double)p.m - (double)m);
+      }
+    }
   }
-  s = wave_sum(s);
-  const float lse = (float)((double)m + log(s));
+  const float wm = wave_max(m);
+  double ws = m == -INFINITY ? 0.0 : s * exp((double)m - (double)wm);
+  ws = wave_sum(ws);
+  if (lane == 0) {
+    smax[wave] = wm;
+    ssum[wave] = ws;
+  }
+  float wv[KM];
+  int wi[KM];
+  wave_merge<KM, KM>(L, k, wv, wi);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (j < k) {
+        sv[wave * KM + j] = wv[j];
+        si[wave * KM + j] = wi[j];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float bm = -INFINITY;
+  for (int w = 0; w < 4; ++w) bm = fmaxf(bm, smax[w]);
+  double bs = 0.0;
+  for (int w = 0; w < 4; ++w)
+    if (smax[w] != -INFINITY) bs += ssum[w] * exp((double)smax[w] - (double)bm);
+  const float lse = (float)((double)bm + log(bs));
+  List<1> one;
+  one.init();
+  if (lane < 4 * KM && (lane % KM) < k) {
+    one.v[0] = sv[lane];
+    one.i[0] = si[lane];
+  }
   float ov[KM];
   int oi[KM];
-  wave_merge<KM, KM>(L, k, ov, oi);
+  wave_merge<1, KM>(one, k, ov, oi);
   if (lane < k) {
     float v = 0.f;
     int id = 0;
@@ -207,14 +197,8 @@ __global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict_
         v = ov[j];
         id = oi[j];
       }
-    int out;
-    if (rowmap) {
-      out = id;  // the tie-break id is already the target id
-    } else {
-      out = id_map ? id_map[clampi(id, 0, n - 1)] : id;
-    }
-    (void)z;
-    (void)ldz;
+    // with per-row ids the tie-break id is already the output id
+    const int out = rowmap ? id : (id_map ? id_map[clampi(id, 0, n - 1)] : id);
     ids[(int64_t)r * ldi + lane] = out;
     logp[(int64_t)r * ldl + lane] = v - lse;
   }
@@ -360,8 +344,8 @@ hipError_t launch_topk(const float* z, int M, int n, int ldz, int k, const int* 
                      rowmap, pv, pi, pp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel<KM>, dim3(M), dim3(64), 0, s, z, ldz, n, k, nch, pv, pi,
-                     pp, id_map, rowmap, ids, ldi, logp, ldl);
+  hipLaunchKernelGGL(topk_merge_kernel<KM>, dim3(M), dim3(256), 0, s, n, k, nch, pv, pi, pp,
+                     id_map, rowmap, ids, ldi, logp, ldl);
   return hipGetLastError();
 }
 
@@ -402,6 +386,21 @@ hipError_t topk_rows(const float* z, int M, int n, int ldz, int k, const int* id
   if (k <= 8)
     return launch_topk<8>(z, M, n, ldz, k, id_map, rowmap, ids, ldi, logp, ldl, part, nch, chunk, s);
   return launch_topk<16>(z, M, n, ldz, k, id_map, rowmap, ids, ldi, logp, ldl, part, nch, chunk, s);
+}
+
+hipError_t topk_merge_records(int M, int n, int k, int km, int nch, void* part, const int* id_map,
+                              int* ids, int ldi, float* logp, int ldl, hipStream_t s) {
+  float* pv = (float*)part;
+  int* pi = (int*)(pv + (size_t)M * nch * km);
+  Part* pp = (Part*)(pi + (size_t)M * nch * km);
+  if (km == 1) {
+    hipLaunchKernelGGL(topk_merge_kernel<1>, dim3(M), dim3(256), 0, s, n, k, nch, pv, pi, pp, id_map,
+                       nullptr, ids, ldi, logp, ldl);
+  } else {
+    hipLaunchKernelGGL(topk_merge_kernel<8>, dim3(M), dim3(256), 0, s, n, k, nch, pv, pi, pp, id_map,
+                       nullptr, ids, ldi, logp, ldl);
+  }
+  return hipGetLastError();
 }
 
 hipError_t topk_large(const float* z, int M, int n, int K, int* ids, void* part, hipStream_t s) {
