@@ -402,6 +402,11 @@ static int gemm_cw(int M, int N) { return (M <= 16 && N >= 65536) ? 1 : 2; }
 
 GemmPlan gemm_plan(int M, int N, int K, bool bf16) {
   GemmPlan p;
+  if (bf16 && gemm_tile_ok(M, K)) {
+    p = gemm_tile_plan(M, N, K);
+    p.tile = true;
+    return p;
+  }
   if (!bf16) {
     p.nsplit = 1;
     p.kc = K;
@@ -445,6 +450,7 @@ hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float
                        (const float*)W, ldw, P, M, N, K);
     return hipGetLastError();
   }
+  if (plan.tile) return gemm_tile(X, ldx, W, ldw, P, M, N, K, plan, s);
   const bool cw1 = gemm_cw(M, N) == 1;
   if (tag == 1) {
     if (cw1) launch_stream<1, 1>(X, ldx, W, ldw, P, M, N, K, plan, s);
@@ -477,7 +483,7 @@ static void launch_lmhead(const void* X, int ldx, const void* W, int ldw, float*
 hipError_t gemm_lmhead_topk(const void* X, int ldx, const void* W, int ldw, float* z, int M, int N,
                             int K, int km, void* part, hipStream_t s) {
   const GemmPlan plan = gemm_plan(M, N, K, true);
-  if (plan.nsplit != 1 || (km != 1 && km != 8)) return hipErrorInvalidValue;
+  if (plan.nsplit != 1 || plan.tile || (km != 1 && km != 8)) return hipErrorInvalidValue;
   const int nch = gemm_strips(M, N);
   float* pv = (float*)part;
   int* pi = (int*)(pv + (size_t)M * nch * km);

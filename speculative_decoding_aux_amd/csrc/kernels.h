@@ -10,9 +10,15 @@ namespace spec {
 // P[split][M][N] (float32) = X[M, K] . W[N, K]^T over the split's K range.
 struct GemmPlan {
   int nsplit = 1;
-  int kc = 0;  // K elements per split (multiple of 128 for bf16)
+  int kc = 0;         // K elements per split
+  bool tile = false;  // LDS-tiled kernel (beam passes, M > 64) instead of weight streaming
 };
 GemmPlan gemm_plan(int M, int N, int K, bool bf16);
+// LDS-tiled GEMM for M > 64 (gemm_tile.hip).
+bool gemm_tile_ok(int M, int K);
+GemmPlan gemm_tile_plan(int M, int N, int K);
+hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N, int K,
+                     const GemmPlan& plan, hipStream_t s);
 // tag 1 launches a separately named instance (the LM head and score GEMMs).
 hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
                 int K, const GemmPlan& plan, hipStream_t s, int tag = 0);

@@ -183,7 +183,8 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
     topk_plan(m, nmax, &nch, &ch);
     tk = std::max(tk, topk_part_bytes(m, nch, 16));
     // records of the fused LM-head top-k (one per row and workgroup strip)
-    if (bf16 && !c.cand_rank && gemm_plan(m, c.draft_vocab, H, true).nsplit == 1)
+    const GemmPlan lp = gemm_plan(m, c.draft_vocab, H, true);
+    if (bf16 && !c.cand_rank && lp.nsplit == 1 && !lp.tile)
       tk = std::max(tk, topk_part_bytes(m, gemm_strips(m, c.draft_vocab), 8));
   }
   ctx->topk_bytes = tk;
@@ -425,7 +426,7 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
     const int Vd = c.draft_vocab;
     const GemmPlan p = gemm_plan(M, Vd, H, bf);
     const int km = io.k_out == 1 ? 1 : (io.k_out <= 8 ? 8 : 0);
-    if (bf && p.nsplit == 1 && km) {
+    if (bf && p.nsplit == 1 && !p.tile && km) {
       // LM head with the top-k fused into its epilogue; logits only if asked for
       {
         ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);

@@ -43,6 +43,10 @@ CASES = {
                                                      total_tokens=3)), 2e-2),
     "bigvocab_trimmed_k8": (configs.get("tiny_chain", **dict(SMALL, vocab=90000, draft_vocab=70000,
                                                              top_k=8, total_tokens=20)), 2e-2),
+    # 72 beam rows: the LDS-tiled GEMM with ragged row and column tiles; K = 480 of the
+    # down projection is not a multiple of 64 and takes the streaming kernel
+    "tile_rows72_ragged": (configs.get("tiny_chain", **dict(SMALL, batch=9, top_k=8, total_tokens=20,
+                                                            intermediate=480)), 2e-2),
     "bigvocab_k8_rows512": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
                                                              top_k=8, total_tokens=20, batch=64, ctx=24)), 2e-2),
 }
