@@ -1,13 +1,11 @@
 // LDS-tiled MFMA GEMM for the beam passes of tree workloads (M > 64 rows):
 // P[split][M][N] = X[M, K] . W[N, K]^T over the split's K range.
 //
-// A 256-thread block owns a BN x BM output tile (BN weight rows x BM X rows)
-// and walks K in 64-wide tiles staged through LDS; while the MFMAs consume the
-// current tile, each thread's 16-byte global loads of the next tile are in
-// flight.  Four waves in a 2 x 2 layout each own a 64 (N) x BM/2 (M) tile of
-// v_mfma_f32_16x16x32_bf16 accumulators, so every weight tile of the block is
-// read from HBM once for all BM rows.  LDS rows are padded to 72 elements
-// (144 B), which makes the 16-lane 16-byte fragment reads conflict-free.
+// A 512-thread block owns a BN x BM output tile (BN weight rows x BM X rows),
+// so each weight tile is read from HBM once for all BM rows, and walks K in
+// BK-wide stages that global_load_lds_dwordx4 brings straight into LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -15,92 +13,175 @@ namespace spec {
 
 namespace {
 
-constexpr int kBK = 64;
-constexpr int kPitch = kBK + 8;  // bf16 elements per LDS row
+// NTH threads own a BN x BM output tile and walk K in BK-wide stages.  Each
+// stage is brought into LDS by global_load_lds_dwordx4 (no staging registers),
+// NS stages deep: NS - 1 are in flight while the MFMAs consume one.  A stage
+// row is BK * 2 bytes (CH = BK / 8 chunks of 16 bytes); chunk j of row r is
+// stored at position j ^ swz(r), swz(r) = (r >> 2) & 3 for 4 chunks and
+// (r >> 1) & 7 for 8, so the 16-lane fragment reads of 16 consecutive rows hit
+// 16 distinct 16-byte bank groups.
+// Synchronisation is a raw s_waitcnt vmcnt + s_barrier (a workgroup fence
+// would drain every stage in flight), with compiler fences so that no LDS
+// access moves across the barrier.  Each stage lives in its own LDS object
+// and every wave issues the same DMA count per stage, unconditionally (past
+// the end the last stage is loaded again), so the compiler can tell a stage's
+// reads from the other stages' DMA and adds no wait of its own.
+#define SPEC_LDS __attribute__((address_space(3)))
 
-template <int BN, int BM>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(const bf16_t* __restrict__ X, int ldx,
-                                                         const bf16_t* __restrict__ W, int ldw,
-                                                         float* __restrict__ P, int M, int N, int K,
-                                                         int kc) {
-  constexpr int WN = BN / 2, WM = BM / 2;  // wave tile
-  constexpr int FA = WN / 16, FB = WM / 16;
-  constexpr int CW = BN * kBK / 8 / 256;   // 16-byte chunks per thread per tile
-  constexpr int CX = BM * kBK / 8 / 256;
-  __shared__ bf16_t ws[BN * kPitch];
-  __shared__ bf16_t xs[BM * kPitch];
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int wn = wave & 1, wm = wave >> 1;
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits [3:0] and
+// [15:14], expcnt [6:4], lgkmcnt [11:8]); the LDS reads of the stage before
+// have completed too, so the refill after the next barrier cannot overtake them.
+template <int N>
+SPEC_DEV void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// 16 bytes per lane from global memory to LDS (lane i lands at dst + 16 i).
+SPEC_DEV void dma16(const bf16_t* src, SPEC_LDS void* dst) {
+  __builtin_amdgcn_global_load_lds((const void*)src, dst, 16, 0, 0);
+}
+
+template <int CH>
+SPEC_DEV int chunk_swz(int row) {
+  return CH == 4 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
+
+template <int BN, int BM, int BK, int NTH, int NS>
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
+    const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W, int ldw,
+    float* __restrict__ P, int M, int N, int K, int kc) {
+  constexpr int NWAVE = NTH / 64;
+  constexpr int WGN = BN / 64, WGM = NWAVE / WGN;  // wave grid
+  constexpr int WM = BM / WGM;                     // X rows per wave
+  constexpr int FA = 4, FB = WM / 16;
+  constexpr int CH = BK / 8;                       // 16-byte chunks per stage row
+  // wave-level DMA instructions per stage, dealt round-robin to the waves
+  // (repeats load the same bytes)
+  constexpr int IW = BN * CH / 64, IX = BM * CH / 64;
+  constexpr int NW = (IW + NWAVE - 1) / NWAVE, NX = (IX + NWAVE - 1) / NWAVE, NI = NW + NX;
+  static_assert(FB >= 1 && WGN * WGM == NWAVE && BM % (16 * WGM) == 0, "tile shape");
+  static_assert((BK == 32 || BK == 64) && NS >= 2 && NS <= 4, "stages");
+  // one LDS object per stage
+  __shared__ u32x4_t w0[BN * CH], w1[BN * CH], w2[NS > 2 ? BN * CH : 1], w3[NS > 3 ? BN * CH : 1];
+  __shared__ u32x4_t x0[BM * CH], x1[BM * CH], x2[NS > 2 ? BM * CH : 1], x3[NS > 3 ? BM * CH : 1];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wn = wave % WGN, wm = wave / WGN;
   const int g = lane >> 4, c = lane & 15;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.z * BM;
   const int k0 = blockIdx.y * kc, k1 = min(K, k0 + kc);
+  const int T = max(0, (k1 - k0) / BK);
+
+  // DMA sources: LDS unit u (row u / CH, position u % CH) holds chunk
+  // (u % CH) ^ swz(row)
+  const bf16_t* gw[NW];
+  const bf16_t* gx[NX];
+  int uw[NW], ux[NX];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    uw[j] = ((wave * NW + j) % IW) * 64;
+    const int u = uw[j] + lane, row = u / CH;
+    const int ch = (u % CH) ^ chunk_swz<CH>(row);
+    gw[j] = W + (int64_t)min(n0 + row, N - 1) * ldw + k0 + ch * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < NX; ++j) {
+    ux[j] = ((wave * NX + j) % IX) * 64;
+    const int u = ux[j] + lane, row = u / CH;
+    const int ch = (u % CH) ^ chunk_swz<CH>(row);
+    gx[j] = X + (int64_t)min(m0 + row, M - 1) * ldx + k0 + ch * 8;
+  }
+  auto wbuf = [](auto sc) -> SPEC_LDS u32x4_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return (SPEC_LDS u32x4_t*)w0;
+    else if constexpr (S == 1) return (SPEC_LDS u32x4_t*)w1;
+    else if constexpr (S == 2) return (SPEC_LDS u32x4_t*)w2;
+    else return (SPEC_LDS u32x4_t*)w3;
+  };
+  auto xbuf = [](auto sc) -> SPEC_LDS u32x4_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return (SPEC_LDS u32x4_t*)x0;
+    else if constexpr (S == 1) return (SPEC_LDS u32x4_t*)x1;
+    else if constexpr (S == 2) return (SPEC_LDS u32x4_t*)x2;
+    else return (SPEC_LDS u32x4_t*)x3;
+  };
+  auto issue = [&](auto sc, int i) {
+    const int k = min(i, T - 1) * BK;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) dma16(gw[j] + k, wbuf(sc) + uw[j]);
+#pragma unroll
+    for (int j = 0; j < NX; ++j) dma16(gx[j] + k, xbuf(sc) + ux[j]);
+  };
 
   f32x4 acc[FA][FB];
 #pragma unroll
   for (int a = 0; a < FA; ++a)
 #pragma unroll
     for (int b = 0; b < FB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int sw = chunk_swz<CH>(c);  // rows of a fragment start at multiples of 16
+  const int rowa = (wn * 64 + c) * CH, rowb = (wm * WM + c) * CH;
 
-  u32x4_t rw[CW], rx[CX];
-  auto load = [&](int k) {
+  // stage i: wait for this wave's DMA of stage i (the NS - 2 stages after it
+  // may still be pending), barrier (every wave's DMA of stage i has landed and
+  // every wave is done reading stage i - 1), refill stage i - 1's buffer with
+  // stage i + NS - 1, compute stage i.  Past T only the refill runs.
+  auto step = [&](auto sc, auto sn, int i) {
+    wait_vm<(NS - 2) * NI>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(sn, i + NS - 1);
+    if (i < T) {
 #pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const int q = t + 256 * i, row = q >> 3, ch = q & 7;
-      const int n = n0 + row;
-      rw[i] = n < N ? *(const u32x4_t*)(W + (int64_t)n * ldw + k + ch * 8) : u32x4_t{0u, 0u, 0u, 0u};
-    }
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        const int pos = (ks * 4 + g) ^ sw;
+        u32x4_t fa[FA], fb[FB];
 #pragma unroll
-    for (int i = 0; i < CX; ++i) {
-      const int q = t + 256 * i, row = q >> 3, ch = q & 7;
-      const int m = m0 + row;
-      rx[i] = m < M ? *(const u32x4_t*)(X + (int64_t)m * ldx + k + ch * 8) : u32x4_t{0u, 0u, 0u, 0u};
+        for (int a = 0; a < FA; ++a) fa[a] = wbuf(sc)[rowa + a * 16 * CH + pos];
+#pragma unroll
+        for (int b = 0; b < FB; ++b) fb[b] = xbuf(sc)[rowb + b * 16 * CH + pos];
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+          for (int b = 0; b < FB; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[a]),
+                                                                __builtin_bit_cast(bf16x8, fb[b]),
+                                                                acc[a][b], 0, 0, 0);
+      }
     }
+    asm volatile("" ::: "memory");
   };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < CW; ++i) {
-      const int q = t + 256 * i, row = q >> 3, ch = q & 7;
-      *(u32x4_t*)(ws + row * kPitch + ch * 8) = rw[i];
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  if (T > 0) {
+    issue(S0{}, 0);
+    if constexpr (NS == 4) {
+      issue(S1{}, 1);
+      issue(S2{}, 2);
+      for (int i = 0; i < T; i += 4) {
+        step(S0{}, S3{}, i);
+        step(S1{}, S0{}, i + 1);
+        step(S2{}, S1{}, i + 2);
+        step(S3{}, S2{}, i + 3);
+      }
+    } else if constexpr (NS == 3) {
+      issue(S1{}, 1);
+      for (int i = 0; i < T; i += 3) {
+        step(S0{}, S2{}, i);
+        step(S1{}, S0{}, i + 1);
+        step(S2{}, S1{}, i + 2);
+      }
+    } else {
+      for (int i = 0; i < T; i += 2) {
+        step(S0{}, S1{}, i);
+        step(S1{}, S0{}, i + 1);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < CX; ++i) {
-      const int q = t + 256 * i, row = q >> 3, ch = q & 7;
-      *(u32x4_t*)(xs + row * kPitch + ch * 8) = rx[i];
-    }
-  };
-
-  if (k0 < k1) {
-    load(k0);
-    stash();
+    wait_vm<0>();  // the repeated loads past the end
   }
-  __syncthreads();
-  for (int k = k0; k < k1; k += kBK) {
-    const bool more = k + kBK < k1;
-    if (more) load(k + kBK);
-#pragma unroll
-    for (int s = 0; s < kBK / 32; ++s) {
-      u32x4_t fa[FA], fb[FB];
-#pragma unroll
-      for (int a = 0; a < FA; ++a)
-        fa[a] = *(const u32x4_t*)(ws + (wn * WN + a * 16 + c) * kPitch + s * 32 + g * 8);
-#pragma unroll
-      for (int b = 0; b < FB; ++b)
-        fb[b] = *(const u32x4_t*)(xs + (wm * WM + b * 16 + c) * kPitch + s * 32 + g * 8);
-#pragma unroll
-      for (int a = 0; a < FA; ++a)
-#pragma unroll
-        for (int b = 0; b < FB; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[a]),
-                                                              __builtin_bit_cast(bf16x8, fb[b]),
-                                                              acc[a][b], 0, 0, 0);
-    }
-    __syncthreads();
-    if (more) {
-      stash();
-      __syncthreads();
-    }
-  }
-  // lane holds Y[m0 + wm*WM + 16b + c][n0 + wn*WN + 16a + 4g + r]
+  // lane holds Y[m0 + wm*WM + 16b + c][n0 + wn*64 + 16a + 4g + r]
   float* Pb = P + (int64_t)blockIdx.y * M * N;
 #pragma unroll
   for (int b = 0; b < FB; ++b) {
@@ -108,7 +189,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const bf16_t* __restrict
     if (m >= M) continue;
 #pragma unroll
     for (int a = 0; a < FA; ++a) {
-      const int n = n0 + wn * WN + 16 * a + 4 * g;
+      const int n = n0 + wn * 64 + 16 * a + 4 * g;
       float* dst = Pb + (int64_t)m * N + n;
       if (n + 3 < N && (N & 3) == 0) {
         *(float4*)dst = make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
@@ -122,29 +203,34 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const bf16_t* __restrict
 
 }  // namespace
 
-constexpr int kTileBN = 128, kTileBM = 256;
+// Beam-pass tile: 128 weight rows x 256 X rows, K stages of 64, three stages
+// (144 KB of LDS, one block per CU, two waves per SIMD).
+constexpr int kTileBN = 128, kTileBM = 256, kTileBK = 64, kTileThreads = 512, kTileStages = 3;
 
-bool gemm_tile_ok(int M, int K) { return M > 64 && K % kBK == 0; }
+bool gemm_tile_ok(int M, int K) { return M > 64 && K % kTileBK == 0; }
 
 GemmPlan gemm_tile_plan(int M, int N, int K) {
   GemmPlan p;
   const int strips = (N + kTileBN - 1) / kTileBN;
   const int mblocks = (M + kTileBM - 1) / kTileBM;
-  const int ktiles = K / kBK;
-  // enough blocks for 256 CUs, but at least 8 K tiles per split
-  int ns = (512 + strips * mblocks - 1) / (strips * mblocks);
-  ns = std::max(1, std::min(ns, std::max(1, ktiles / 8)));
+  const int ktiles = K / kTileBK;
+  // One block per CU: split K only while the grid is short of 256 blocks
+  // (every split costs an M x N float32 partial), keeping >= 4 stages per split.
+  int ns = 256 / std::max(1, strips * mblocks);
+  ns = std::max(1, std::min(ns, std::max(1, ktiles / 4)));
   const int per = (ktiles + ns - 1) / ns;
-  p.kc = per * kBK;
+  p.kc = per * kTileBK;
   p.nsplit = (ktiles + per - 1) / per;
   return p;
 }
 
 hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N, int K,
                      const GemmPlan& plan, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K % kTileBK != 0 || plan.kc % kTileBK != 0) return hipErrorInvalidValue;
   const dim3 grid((N + kTileBN - 1) / kTileBN, plan.nsplit, (M + kTileBM - 1) / kTileBM);
-  hipLaunchKernelGGL((gemm_tile_kernel<kTileBN, kTileBM>), grid, dim3(256), 0, s, (const bf16_t*)X,
-                     ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc);
+  hipLaunchKernelGGL((gemm_dma_kernel<kTileBN, kTileBM, kTileBK, kTileThreads, kTileStages>), grid,
+                     dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M,
+                     N, K, plan.kc);
   return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ struct GemmPlan {
   bool tile = false;  // LDS-tiled kernel (beam passes, M > 64) instead of weight streaming
 };
 GemmPlan gemm_plan(int M, int N, int K, bool bf16);
-// LDS-tiled GEMM for M > 64 (gemm_tile.hip).
+// LDS-tiled GEMM for M > 64 and K % 64 == 0 (gemm_tile.hip).
 bool gemm_tile_ok(int M, int K);
 GemmPlan gemm_tile_plan(int M, int N, int K);
 hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N, int K,
@@ -122,12 +122,16 @@ hipError_t tree_expand(int d, int B, int n_new, const int* ctx_len, const int* i
                        int root_off, TreeState st, PassRows next, TreeOut out, hipStream_t s);
 
 // ------------------------------------------------------------- verify
-void verify_plan(int rows, int V, int* nch, int* chunk);
-size_t verify_part_bytes(int rows, int nch);
+struct VerifyPlan {
+  int nch, chunk;    // statistics pass: vocab chunks per node row
+  int gch, gchunk;   // Gumbel pass: vocab chunks per stop row
+};
+VerifyPlan verify_plan(int B, int N, int V);
+size_t verify_ws_bytes(const VerifyPlan& p, int B, int N);
 hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const int* parent,
                   const int* num_nodes, const float* logits, int mode, float temperature,
                   const float* accept_u, uint64_t seed, int* out_tokens, int* accepted_len,
-                  int* accepted_nodes, void* part, int nch, int chunk, hipStream_t s);
+                  int* accepted_nodes, void* ws, const VerifyPlan& p, hipStream_t s);
 
 // ------------------------------------------------------------ compact
 struct KvFull {

@@ -189,14 +189,10 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
   }
   ctx->topk_bytes = tk;
   {
-    int nch, ch;
-    const int rows = c.max_batch * (c.total_tokens + 1);
     size_t vb = 0;
-    for (int b = 1; b <= c.max_batch; ++b) {
-      verify_plan(b * (c.total_tokens + 1), c.vocab, &nch, &ch);
-      vb = std::max(vb, verify_part_bytes(b * (c.total_tokens + 1), nch));
-    }
-    (void)rows;
+    for (int b = 1; b <= c.max_batch; ++b)
+      vb = std::max(vb, verify_ws_bytes(verify_plan(b, c.total_tokens, c.vocab), b,
+                                        c.total_tokens));
     ctx->verify_bytes = vb;
   }
   const int nc = c.cand_rank ? c.num_candidates : 1;
@@ -674,15 +670,13 @@ spec_status spec_verify_tree(spec_ctx* ctx, int32_t B, const spec_tree* tree,
   if (mode == SPEC_VERIFY_STOCHASTIC)
     SPEC_REQ(ctx, accept_u && temperature > 0.f, SPEC_EINVAL,
              "stochastic verification needs accept_u and temperature > 0");
-  const int rows = B * (c.total_tokens + 1);
-  int nch, ch;
-  verify_plan(rows, c.vocab, &nch, &ch);
-  SPEC_REQ(ctx, verify_part_bytes(rows, nch) <= ctx->verify_bytes, SPEC_EUNSUPPORTED,
+  const VerifyPlan vp = verify_plan(B, c.total_tokens, c.vocab);
+  SPEC_REQ(ctx, verify_ws_bytes(vp, B, c.total_tokens) <= ctx->verify_bytes, SPEC_EUNSUPPORTED,
            "workspace too small");
   ProfScope ps(ctx, SPEC_PROF_VERIFY, STREAM(stream));
   SPEC_HIP(ctx, verify(B, c.total_tokens, c.depth, c.top_k, c.vocab, tree->tokens, tree->parent,
                        tree->num_nodes, target_logits, mode, temperature, accept_u, seed,
-                       out_tokens, accepted_len, accepted_nodes, ctx->ws.verify_part, nch, ch,
+                       out_tokens, accepted_len, accepted_nodes, ctx->ws.verify_part, vp,
                        STREAM(stream)));
   return SPEC_OK;
 }

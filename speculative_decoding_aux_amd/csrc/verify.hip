@@ -1,15 +1,18 @@
 // Verification of the draft trees against the target logits, and KV
 // compaction of the accepted path.
 //
-// Stage 1 (data-parallel over every tree node and a chunk of the vocabulary,
-// the target logits are read exactly once): greedy keeps the argmax (first
-// index on ties); stochastic keeps the running max m of l/T, the sum of
-// exp(l/T - m) in float64 and the Gumbel-max candidate l/T - log(-log U)
-// over tokens that are not children of the node, with U drawn in-kernel from
+// Stage 1, statistics (data-parallel over every tree node and a chunk of the
+// vocabulary; the target logits are read once with 16-byte loads): greedy
+// keeps the argmax (first index on ties), stochastic keeps the running max m
+// of l/T and the sum of exp(l/T - m) in float64.
+// Stage 2, walk (one wave per sequence): merge the chunk records of the nodes
+// on the walk and run the acceptance walk from the root; greedy writes the
+// bonus token, stochastic records the node where the walk stopped.
+// Stage 3, stochastic only: Gumbel-max over that node's row with its children
+// excluded, which samples the residual distribution (or the node's own
+// distribution when it has no children).  U is drawn in-kernel from
 // Philox4x32-10 (key = seed, counter = (v >> 2, node, b, 0), word v & 3), so
-// the noise costs no memory traffic.
-// Stage 2 (one wave per sequence): merge the chunk records of the nodes on
-// the walk and run the acceptance walk from the root.
+// the noise costs no memory traffic and is drawn for B rows, not B (N + 1).
 #include "common.h"
 #include "kernels.h"
 
@@ -17,46 +20,74 @@ namespace spec {
 
 namespace {
 
-struct VPart {       // per (tree node, vocab chunk)
-  double z;          // sum exp(l/T - m)
-  float m;           // max l/T   (greedy: max l)
-  float gs;          // best Gumbel score
-  int arg;           // greedy argmax id
-  int gid;           // Gumbel argmax id
-  int pad0, pad1;
+struct VPart {  // per (tree node, vocab chunk)
+  double z;     // stochastic: sum exp(l/T - m)
+  float m;      // stochastic: max l/T; greedy: max l
+  int arg;      // greedy argmax id
 };
 
-__global__ __launch_bounds__(256) void verify_stats_kernel(
-    int N, int k, int V, const int* __restrict__ tokens, const int* __restrict__ parent,
-    const int* __restrict__ num_nodes, const float* __restrict__ logits, int mode, float temp,
-    uint32_t seed_lo, uint32_t seed_hi, int chunk, VPart* __restrict__ part) {
-  __shared__ int kids[64];
-  __shared__ int nkids;
+struct GPart {  // per (sequence, vocab chunk) of the stop node's row
+  float gs;     // best Gumbel score
+  int gid;
+};
+
+constexpr int kUnroll = 4;  // float4 loads in flight per thread
+
+// Visit the values of lrow[lo, hi) owned by this thread, in increasing index
+// order per thread; lo must be a multiple of 4 when V is.
+template <typename F>
+SPEC_DEV void for_chunk(const float* lrow, int lo, int hi, bool vec, F&& f) {
+  const int t = threadIdx.x;
+  if (vec) {
+    for (int x0 = lo + 4 * t; x0 < hi; x0 += 1024 * kUnroll) {
+      float4 v[kUnroll];
+#pragma unroll
+      for (int i = 0; i < kUnroll; ++i) {
+        const int x = x0 + 1024 * i;
+        v[i] = x < hi ? *(const float4*)(lrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < kUnroll; ++i) {
+        const int x = x0 + 1024 * i;
+        if (x < hi) {
+          f(v[i].x, x);
+          f(v[i].y, x + 1);
+          f(v[i].z, x + 2);
+          f(v[i].w, x + 3);
+        }
+      }
+    }
+  } else {
+    for (int x = lo + t; x < hi; x += 256) f(lrow[x], x);
+  }
+}
+
+__global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
+                                                           const int* __restrict__ num_nodes,
+                                                           const float* __restrict__ logits,
+                                                           int mode, float temp, int chunk,
+                                                           VPart* __restrict__ part) {
   __shared__ float rf[4];
   __shared__ int ri[4];
-  __shared__ float rg[4];
-  __shared__ int rgi[4];
   __shared__ double rz[4];
   const int c = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
   const int n1 = N + 1;
   const int b = row / n1, n = row % n1;
-  const int nn = num_nodes[b];
-  if (n > nn) return;
+  if (n > num_nodes[b]) return;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const float* lrow = logits + (int64_t)row * V;
   const int lo = c * chunk, hi = min(V, lo + chunk);
+  const bool vec = (V & 3) == 0;
   VPart rec;
-  rec.pad0 = rec.pad1 = 0;
   if (mode == 0) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int x = lo + t; x < hi; x += 256) {
-      const float v = lrow[x];
+    for_chunk(lrow, lo, hi, vec, [&](float v, int x) {
       if (better(v, x, bv, bi)) {
         bv = v;
         bi = x;
       }
-    }
+    });
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float ov = __shfl_xor(bv, o, 64);
@@ -80,71 +111,28 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(
       rec.m = rf[0];
       rec.arg = ri[0];
       rec.z = 0.0;
-      rec.gs = -INFINITY;
-      rec.gid = 0x7fffffff;
       part[(int64_t)row * nch + c] = rec;
     }
     return;
   }
-  // stochastic: children tokens of node n
-  if (t == 0) {
-    int cnt = 0;
-    for (int x = 1; x <= nn && cnt < 64; ++x)
-      if (parent[(int64_t)b * n1 + x] == n) kids[cnt++] = tokens[(int64_t)b * n1 + x];
-    nkids = cnt;
-  }
-  __syncthreads();
-  const int nk = nkids;
   const float invT = 1.0f / temp;
   float m = -INFINITY;
   double zs = 0.0;
-  float gs = -INFINITY;
-  int gi = 0x7fffffff;
-  // 4 consecutive ids share one Philox block
-  const int q0 = lo >> 2, q1 = (hi + 3) >> 2;
-  for (int qd = q0 + t; qd < q1; qd += 256) {
-    const u32x4 rnd = philox4x32_10(u32x4{(uint32_t)qd, (uint32_t)n, (uint32_t)b, 0u}, seed_lo,
-                                    seed_hi);
-    const uint32_t w[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int x = qd * 4 + e;
-      if (x < lo || x >= hi) continue;
-      const float zv = temp == 1.0f ? lrow[x] : lrow[x] * invT;
-      if (zv > m) {
-        zs = (m == -INFINITY ? 0.0 : zs * exp((double)m - (double)zv)) + 1.0;
-        m = zv;
-      } else {
-        zs += (double)expf(zv - m);
-      }
-      const float sc = zv + gumbel_from_bits(w[e]);
-      if (better(sc, x, gs, gi)) {
-        bool child = false;
-        for (int j = 0; j < nk; ++j) child |= kids[j] == x;
-        if (!child) {
-          gs = sc;
-          gi = x;
-        }
-      }
+  for_chunk(lrow, lo, hi, vec, [&](float l, int) {
+    const float zv = temp == 1.0f ? l : l * invT;
+    if (zv > m) {
+      zs = (m == -INFINITY ? 0.0 : zs * exp((double)m - (double)zv)) + 1.0;
+      m = zv;
+    } else if (zv != -INFINITY) {
+      zs += (double)expf(zv - m);
     }
-  }
+  });
   const float wm = wave_max(m);
   double wz = m == -INFINITY ? 0.0 : zs * exp((double)m - (double)wm);
   wz = wave_sum(wz);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float og = __shfl_xor(gs, o, 64);
-    const int oi = __shfl_xor(gi, o, 64);
-    if (better(og, oi, gs, gi)) {
-      gs = og;
-      gi = oi;
-    }
-  }
   if (lane == 0) {
     rf[wave] = wm;
     rz[wave] = wz;
-    rg[wave] = gs;
-    rgi[wave] = gi;
   }
   __syncthreads();
   if (t == 0) {
@@ -153,17 +141,8 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(
     double bz = 0.0;
     for (int w2 = 0; w2 < 4; ++w2)
       if (rf[w2] != -INFINITY) bz += rz[w2] * exp((double)rf[w2] - (double)bm);
-    float bg = rg[0];
-    int bgi = rgi[0];
-    for (int w2 = 1; w2 < 4; ++w2)
-      if (better(rg[w2], rgi[w2], bg, bgi)) {
-        bg = rg[w2];
-        bgi = rgi[w2];
-      }
     rec.m = bm;
     rec.z = bz;
-    rec.gs = bg;
-    rec.gid = bgi;
     rec.arg = 0;
     part[(int64_t)row * nch + c] = rec;
   }
@@ -173,20 +152,21 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
     int N, int D, int k, int V, const int* __restrict__ tokens, const int* __restrict__ parent,
     const int* __restrict__ num_nodes, const float* __restrict__ logits, int mode, float temp,
     const float* __restrict__ accept_u, int nch, const VPart* __restrict__ part,
-    int* __restrict__ out_tokens, int* __restrict__ accepted_len, int* __restrict__ accepted_nodes) {
+    int* __restrict__ stop, int* __restrict__ out_tokens, int* __restrict__ accepted_len,
+    int* __restrict__ accepted_nodes) {
   const int b = blockIdx.x, lane = threadIdx.x;
   const int n1 = N + 1;
   const int nn = min(num_nodes[b], N);
   const int* tk = tokens + (int64_t)b * n1;
   const int* pr = parent + (int64_t)b * n1;
-  int cur = 0, depth = 0, emit = 0;
+  int cur = 0, depth = 0, emit = -1;
   for (int j = lane; j <= D; j += 64) out_tokens[(int64_t)b * (D + 1) + j] = -1;
   for (int j = lane; j < D; j += 64) accepted_nodes[(int64_t)b * D + j] = -1;
   while (true) {
     const VPart* pb = part + (int64_t)(b * n1 + cur) * nch;
     // merge the chunk records of node cur
-    float m = -INFINITY, gs = -INFINITY;
-    int arg = 0x7fffffff, gid = 0x7fffffff;
+    float m = -INFINITY;
+    int arg = 0x7fffffff;
     for (int c = lane; c < nch; c += 64) {
       const VPart p = pb[c];
       if (mode == 0) {
@@ -196,18 +176,12 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
         }
       } else {
         m = fmaxf(m, p.m);
-        if (better(p.gs, p.gid, gs, gid)) {
-          gs = p.gs;
-          gid = p.gid;
-        }
       }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float om = __shfl_xor(m, o, 64);
       const int oa = __shfl_xor(arg, o, 64);
-      const float og = __shfl_xor(gs, o, 64);
-      const int oi = __shfl_xor(gid, o, 64);
       if (mode == 0) {
         if (better(om, oa, m, arg)) {
           m = om;
@@ -215,10 +189,6 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
         }
       } else {
         m = fmaxf(m, om);
-        if (better(og, oi, gs, gid)) {
-          gs = og;
-          gid = oi;
-        }
       }
     }
     int next = -1;
@@ -255,7 +225,6 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
         }
         ++ord;
       }
-      emit = gid;
     }
     if (next < 0 || depth >= D) break;
     if (lane == 0) {
@@ -266,9 +235,111 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
     cur = next;
   }
   if (lane == 0) {
-    out_tokens[(int64_t)b * (D + 1) + depth] = emit;
+    if (mode == 0) out_tokens[(int64_t)b * (D + 1) + depth] = emit;
+    else stop[b] = cur;
     accepted_len[b] = depth;
   }
+}
+
+// Gumbel-max over a chunk of the stop node's row, children excluded.
+__global__ __launch_bounds__(256) void verify_gumbel_kernel(
+    int N, int V, const int* __restrict__ tokens, const int* __restrict__ parent,
+    const int* __restrict__ num_nodes, const float* __restrict__ logits, float temp,
+    uint32_t seed_lo, uint32_t seed_hi, int chunk, const int* __restrict__ stop,
+    GPart* __restrict__ gpart) {
+  __shared__ int kids[64];
+  __shared__ int nkids;
+  __shared__ float rg[4];
+  __shared__ int rgi[4];
+  const int c = blockIdx.x, b = blockIdx.y, nch = gridDim.x;
+  const int n1 = N + 1;
+  const int nn = min(num_nodes[b], N);
+  const int n = clampi(stop[b], 0, N);
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  if (t == 0) {
+    int cnt = 0;
+    for (int x = 1; x <= nn && cnt < 64; ++x)
+      if (parent[(int64_t)b * n1 + x] == n) kids[cnt++] = tokens[(int64_t)b * n1 + x];
+    nkids = cnt;
+  }
+  __syncthreads();
+  const int nk = nkids;
+  const float* lrow = logits + (int64_t)(b * n1 + n) * V;
+  const int lo = c * chunk, hi = min(V, lo + chunk);
+  const float invT = 1.0f / temp;
+  float gs = -INFINITY;
+  int gi = 0x7fffffff;
+  // 4 consecutive ids share one Philox block
+  const int q0 = lo >> 2, q1 = (hi + 3) >> 2;
+  for (int qd = q0 + t; qd < q1; qd += 256) {
+    const u32x4 rnd = philox4x32_10(u32x4{(uint32_t)qd, (uint32_t)n, (uint32_t)b, 0u}, seed_lo,
+                                    seed_hi);
+    const uint32_t w[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int x = qd * 4 + e;
+      if (x < lo || x >= hi) continue;
+      const float l = lrow[x];
+      const float sc = (temp == 1.0f ? l : l * invT) + gumbel_from_bits(w[e]);
+      if (better(sc, x, gs, gi)) {
+        bool child = false;
+        for (int j = 0; j < nk; ++j) child |= kids[j] == x;
+        if (!child) {
+          gs = sc;
+          gi = x;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float og = __shfl_xor(gs, o, 64);
+    const int oi = __shfl_xor(gi, o, 64);
+    if (better(og, oi, gs, gi)) {
+      gs = og;
+      gi = oi;
+    }
+  }
+  if (lane == 0) {
+    rg[wave] = gs;
+    rgi[wave] = gi;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int w2 = 1; w2 < 4; ++w2)
+      if (better(rg[w2], rgi[w2], rg[0], rgi[0])) {
+        rg[0] = rg[w2];
+        rgi[0] = rgi[w2];
+      }
+    gpart[(int64_t)b * nch + c] = GPart{rg[0], rgi[0]};
+  }
+}
+
+// One wave per sequence: merge the Gumbel records and write the bonus token.
+__global__ __launch_bounds__(64) void verify_emit_kernel(int D, int nch,
+                                                         const GPart* __restrict__ gpart,
+                                                         const int* __restrict__ accepted_len,
+                                                         int* __restrict__ out_tokens) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  float gs = -INFINITY;
+  int gi = 0x7fffffff;
+  for (int c = lane; c < nch; c += 64) {
+    const GPart p = gpart[(int64_t)b * nch + c];
+    if (better(p.gs, p.gid, gs, gi)) {
+      gs = p.gs;
+      gi = p.gid;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float og = __shfl_xor(gs, o, 64);
+    const int oi = __shfl_xor(gi, o, 64);
+    if (better(og, oi, gs, gi)) {
+      gs = og;
+      gi = oi;
+    }
+  }
+  if (lane == 0) out_tokens[(int64_t)b * (D + 1) + clampi(accepted_len[b], 0, D)] = gi;
 }
 
 // One block per (sequence, layer, kv-head): read every accepted row, then write.
@@ -318,31 +389,56 @@ __global__ __launch_bounds__(256) void compact_kernel(char* __restrict__ kb, cha
 
 }  // namespace
 
-void verify_plan(int rows, int V, int* nch, int* chunk) {
+VerifyPlan verify_plan(int B, int N, int V) {
+  VerifyPlan p;
+  const int rows = B * (N + 1);
+  // statistics: about 2048 blocks, chunks of at least 4096 ids
   int c = (2048 + rows - 1) / std::max(1, rows);
-  const int maxc = std::max(1, (V + 4095) / 4096);
-  c = std::max(1, std::min(c, maxc));
-  int ch = (V + c - 1) / c;
-  ch = (ch + 1023) / 1024 * 1024;
-  *chunk = ch;
-  *nch = (V + ch - 1) / ch;
+  c = std::max(1, std::min(c, std::max(1, (V + 4095) / 4096)));
+  p.chunk = ((V + c - 1) / c + 1023) / 1024 * 1024;
+  p.nch = (V + p.chunk - 1) / p.chunk;
+  // Gumbel pass: about 1024 blocks over the B stop rows, chunks of >= 2048 ids
+  int g = (1024 + B - 1) / std::max(1, B);
+  g = std::max(1, std::min(g, std::max(1, (V + 2047) / 2048)));
+  p.gchunk = ((V + g - 1) / g + 1023) / 1024 * 1024;
+  p.gch = (V + p.gchunk - 1) / p.gchunk;
+  return p;
 }
 
-size_t verify_part_bytes(int rows, int nch) { return (size_t)rows * nch * sizeof(VPart); }
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t verify_ws_bytes(const VerifyPlan& p, int B, int N) {
+  return align256((size_t)B * (N + 1) * p.nch * sizeof(VPart)) +
+         align256((size_t)B * p.gch * sizeof(GPart)) + align256((size_t)B * sizeof(int));
+}
 
 hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const int* parent,
                   const int* num_nodes, const float* logits, int mode, float temperature,
                   const float* accept_u, uint64_t seed, int* out_tokens, int* accepted_len,
-                  int* accepted_nodes, void* part, int nch, int chunk, hipStream_t s) {
+                  int* accepted_nodes, void* ws, const VerifyPlan& p, hipStream_t s) {
   const int rows = B * (N + 1);
-  hipLaunchKernelGGL(verify_stats_kernel, dim3(nch, rows), dim3(256), 0, s, N, k, V, tokens,
-                     parent, num_nodes, logits, mode, temperature, (uint32_t)(seed & 0xffffffffu),
-                     (uint32_t)(seed >> 32), chunk, (VPart*)part);
+  char* w = (char*)ws;
+  VPart* part = (VPart*)w;
+  w += align256((size_t)rows * p.nch * sizeof(VPart));
+  GPart* gpart = (GPart*)w;
+  w += align256((size_t)B * p.gch * sizeof(GPart));
+  int* stop = (int*)w;
+  hipLaunchKernelGGL(verify_stats_kernel, dim3(p.nch, rows), dim3(256), 0, s, N, V, num_nodes,
+                     logits, mode, temperature, p.chunk, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(verify_walk_kernel, dim3(B), dim3(64), 0, s, N, D, k, V, tokens, parent,
-                     num_nodes, logits, mode, temperature, accept_u, nch, (const VPart*)part,
-                     out_tokens, accepted_len, accepted_nodes);
+                     num_nodes, logits, mode, temperature, accept_u, p.nch, (const VPart*)part,
+                     stop, out_tokens, accepted_len, accepted_nodes);
+  e = hipGetLastError();
+  if (e != hipSuccess || mode == 0) return e;
+  hipLaunchKernelGGL(verify_gumbel_kernel, dim3(p.gch, B), dim3(256), 0, s, N, V, tokens, parent,
+                     num_nodes, logits, temperature, (uint32_t)(seed & 0xffffffffu),
+                     (uint32_t)(seed >> 32), p.gchunk, (const int*)stop, gpart);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_emit_kernel, dim3(B), dim3(64), 0, s, D, p.gch, (const GPart*)gpart,
+                     (const int*)accepted_len, out_tokens);
   return hipGetLastError();
 }
 
