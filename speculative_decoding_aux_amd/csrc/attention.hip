@@ -263,16 +263,23 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
 
 
 // ---- bf16 context attention on MFMA -----------------------------------------
-// Each wave takes blocks of 32 keys (two 16-key tiles).  S^T = K . Q^T uses K
-// rows as the A operand (lane: key = lane&15, 8 dims at 8*(lane>>4)) and the
-// query vectors as B, so the score tile lands with key 4*(lane>>4)+i and query
-// column lane&15 - exactly the B-operand layout of O^T = V^T . P^T over the 32
-// keys (element e<4: tile 0 key 4g+e, e>=4: tile 1 key 16+4g+e-4).  V^T
-// fragments gather those 8 keys at dim lane&15.  Online softmax runs per query
-// column (shuffles across the four lane groups); the four waves of a block are
-// merged pairwise through LDS.
-SPEC_DEV u32x4_t ld16(const bf16_t* p) { return *(const u32x4_t*)p; }
-
+// Each wave walks blocks of 32 keys (two 16-key tiles), wave w taking blocks
+// w, w + 4, ... of the chunk.  The K and V rows of a block (2 x 32 x HD bf16)
+// are brought into a wave-private LDS stage by global_load_lds_dwordx4, one
+// block ahead (two stages per wave), so the wave never waits on a barrier
+// and the loads stay 16 bytes wide and coalesced.
+// S^T = K . Q^T takes K rows as the A operand (lane: key = lane&15, 8 dims at
+// 8*(lane>>4)) and the query vectors as B, so the score tile lands with key
+// 4*(lane>>4)+i and query column lane&15 - the B-operand layout of
+// O^T = V^T . P^T over the 32 keys (element e<4: tile 0 key 4g+e, e>=4: tile 1
+// key 16+4g+e-4).  The V^T fragments gather those 8 keys at dim lane&15 from
+// LDS with 2-byte reads.
+// LDS layout: a row of CH = HD/8 16-byte chunks; K row r keeps chunk j at
+// position j ^ fk(r) (fk = r & 15 for 16 chunks, (r >> 1) & 7 for 8), so the
+// 16 rows of an A fragment hit 16 distinct bank groups; V row r keeps chunk j
+// at j ^ 2((r >> 2) & 3), so the four key rows 4g+e of a V^T read do too.
+// Online softmax runs per query column (shuffles across the four lane
+// groups); the four waves are merged pairwise through LDS at the end.
 SPEC_DEV u32x4_t pack8(const float (&v)[8]) {
   u32x4_t w;
 #pragma unroll
@@ -281,19 +288,31 @@ SPEC_DEV u32x4_t pack8(const float (&v)[8]) {
   return w;
 }
 
+template <int CH>
+SPEC_DEV int k_swz(int r) {
+  return CH == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+SPEC_DEV int v_swz(int r) { return 2 * ((r >> 2) & 3); }
+
 template <int HD, int QT>
 __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     int64_t sseq, int64_t shead, int S, const int* __restrict__ ctx_len, const int* __restrict__ pos,
     int R, int nq, int nkv, int window, int chunk, float* __restrict__ part) {
-  constexpr int DS = HD / 32;  // 32-dim steps of S^T
-  constexpr int DT = HD / 16;  // 16-dim tiles of O^T
-  __shared__ f32x4 mo[2][QT][DT][64];
-  __shared__ float mm[2][QT][64], ml[2][QT][64];
+  constexpr int DS = HD / 32;        // 32-dim steps of S^T
+  constexpr int DT = HD / 16;        // 16-dim tiles of O^T
+  constexpr int CH = HD / 8;         // 16-byte chunks per row
+  constexpr int BLK = 32 * CH;       // 16-byte units per 32-row block
+  constexpr int NI = BLK / 64;       // DMA instructions per block (K or V)
+  static_assert(HD == 64 || HD == 128, "head dim");
+  static_assert(2 * QT * DT * 64 * 16 <= 4 * BLK * 16, "merge buffer fits in a K stage");
+  // two stages, one LDS object each for K and V; a wave owns BLK units of each
+  __shared__ u32x4_t k0s[4 * BLK], k1s[4 * BLK], v0s[4 * BLK], v1s[4 * BLK];
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int nch = gridDim.x;
   const int G = nq / nkv, QV = R * G;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float scale = 1.0f / sqrtf((float)HD);
 
   const int ctx = clampi(ctx_len[b], 0, S);
@@ -302,6 +321,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
   const int start = window > 0 ? max(0, minpos - window + 1) : 0;
   const int k0 = start + c * chunk;
   const int k1 = min(ctx, k0 + chunk);
+  const int first = k0 + wave * 32;
+  const int nblk = first < k1 ? (k1 - first + 127) / 128 : 0;
 
   u32x4_t qf[QT][DS];
   int loq[QT];
@@ -312,7 +333,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
     const int r = ok ? qv / G : 0, h = kvh * G + (ok ? qv % G : 0);
     const bf16_t* qp = q + ((int64_t)(b * R + r) * nq + h) * HD + g * 8;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[t][ds] = ok ? ld16(qp + ds * 32) : u32x4_t{0u, 0u, 0u, 0u};
+    for (int ds = 0; ds < DS; ++ds)
+      qf[t][ds] = ok ? *(const u32x4_t*)(qp + ds * 32) : u32x4_t{0u, 0u, 0u, 0u};
     loq[t] = ok ? (window > 0 ? max(0, pos[b * R + r] - window + 1) : 0) : 0x7fffffff;
   }
   float mrun[QT], lrun[QT];
@@ -327,41 +349,76 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
   const bf16_t* kb = kc + b * sseq + kvh * shead;
   const bf16_t* vb = vc + b * sseq + kvh * shead;
 
-  for (int kb0 = k0 + wave * 32; kb0 < k1; kb0 += 128) {
-    // V^T fragments of the 32 keys, one per 16-dim tile (loaded first: they do
-    // not depend on the scores)
-    u32x4_t vf[DT];
-    {
-      int keyv[8];
+  // DMA sources: unit u of a block is row u / CH at position u % CH
+  int krow[NI], kch[NI], vch[NI];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) keyv[e] = kb0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+  for (int j = 0; j < NI; ++j) {
+    const int u = j * 64 + lane, row = u / CH, p = u % CH;
+    krow[j] = row;
+    kch[j] = p ^ k_swz<CH>(row);
+    vch[j] = p ^ v_swz(row);
+  }
+  auto kbuf = [](auto sc) -> SPEC_LDS u32x4_t* {
+    if constexpr (decltype(sc)::value == 0) return (SPEC_LDS u32x4_t*)k0s;
+    else return (SPEC_LDS u32x4_t*)k1s;
+  };
+  auto vbuf = [](auto sc) -> SPEC_LDS u32x4_t* {
+    if constexpr (decltype(sc)::value == 0) return (SPEC_LDS u32x4_t*)v0s;
+    else return (SPEC_LDS u32x4_t*)v1s;
+  };
+  // block i of this wave (past the end: the last block again, never read)
+  auto issue = [&](auto sc, int i) {
+    const int base = first + min(i, max(nblk - 1, 0)) * 128;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        uint32_t h16[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          h16[e] = keyv[e] < k1 ? (uint32_t)vb[(int64_t)keyv[e] * HD + dt * 16 + col] : 0u;
-        vf[dt] = u32x4_t{h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16), h16[4] | (h16[5] << 16),
-                         h16[6] | (h16[7] << 16)};
-      }
+    for (int j = 0; j < NI; ++j) {
+      const int key = min(base + krow[j], max(k1 - 1, 0));
+      dma16(kb + (int64_t)key * HD + kch[j] * 8, kbuf(sc) + wave * BLK + j * 64);
+      dma16(vb + (int64_t)key * HD + vch[j] * 8, vbuf(sc) + wave * BLK + j * 64);
     }
-    f32x4 sc[2][QT];
+  };
+
+  auto block = [&](auto sc, auto sn, int i) {
+    // refill the other stage (read by this wave's previous block, whose LDS
+    // reads have completed), then wait for this block's DMA only
+    wait_vm_lgkm0<2 * NI>();
+    asm volatile("" ::: "memory");
+    issue(sn, i + 1);
+    wait_vm_lgkm0<2 * NI>();
+    asm volatile("" ::: "memory");
+    if (i >= nblk) return;
+    const int kb0 = first + i * 128;
+    const SPEC_LDS u32x4_t* ks = kbuf(sc) + wave * BLK;
+    const SPEC_LDS bf16_t* vs = (const SPEC_LDS bf16_t*)(vbuf(sc) + wave * BLK);
+    f32x4 sc4[2][QT];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int key = kb0 + kt * 16 + col;
+      const int row = kt * 16 + col;
       u32x4_t kf[DS];
-      const bf16_t* kp = kb + (int64_t)key * HD + g * 8;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) kf[ds] = key < k1 ? ld16(kp + ds * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      for (int ds = 0; ds < DS; ++ds) kf[ds] = ks[row * CH + ((ds * 4 + g) ^ k_swz<CH>(row))];
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
-        sc[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sc4[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds)
-          sc[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ds]),
-                                                              __builtin_bit_cast(bf16x8, qf[t][ds]),
-                                                              sc[kt][t], 0, 0, 0);
+          sc4[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ds]),
+                                                               __builtin_bit_cast(bf16x8, qf[t][ds]),
+                                                               sc4[kt][t], 0, 0, 0);
       }
+    }
+    // V^T fragments: keys 4g+e (e < 4) and 16+4g+e-4 at dim dt*16 + col
+    u32x4_t vf[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int chn = (dt * 16 + col) >> 3, el = (dt * 16 + col) & 7;
+      uint32_t h16[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
+        h16[e] = vs[(row * CH + (chn ^ v_swz(row))) * 8 + el];
+      }
+      vf[dt] = u32x4_t{h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16), h16[4] | (h16[5] << 16),
+                       h16[6] | (h16[7] << 16)};
     }
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -370,7 +427,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = kb0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-        const float x = (e < 4 ? sc[0][t][e] : sc[1][t][e - 4]) * scale;
+        const float x = (e < 4 ? sc4[0][t][e] : sc4[1][t][e - 4]) * scale;
         v[e] = (key < k1 && key >= loq[t]) ? x : -INFINITY;
         tmax = fmaxf(tmax, v[e]);
       }
@@ -398,8 +455,23 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
                                                            0, 0, 0);
       }
     }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (nblk > 0) {
+    issue(S0{}, 0);
+    for (int i = 0; i < nblk; i += 2) {
+      block(S0{}, S1{}, i);
+      block(S1{}, S0{}, i + 1);
+    }
   }
-  // merge waves pairwise: (2,3) -> (0,1), then 1 -> 0
+  wait_vm_lgkm0<0>();  // the repeated loads past the end
+  __syncthreads();
+
+  // merge waves pairwise through LDS (the K stages are free now): (2,3) -> (0,1), then 1 -> 0
+  f32x4* mo = (f32x4*)k0s;    // [2][QT][DT][64]
+  float* mm = (float*)v0s;    // [2][QT][64]
+  float* ml = mm + 2 * QT * 64;
 #pragma unroll
   for (int round = 0; round < 2; ++round) {
     const int half = round == 0 ? 2 : 1;
@@ -407,24 +479,25 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
       const int slot = wave - half;
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
-        mm[slot][t][lane] = mrun[t];
-        ml[slot][t][lane] = lrun[t];
+        mm[(slot * QT + t) * 64 + lane] = mrun[t];
+        ml[(slot * QT + t) * 64 + lane] = lrun[t];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) mo[slot][t][dt][lane] = o[t][dt];
+        for (int dt = 0; dt < DT; ++dt) mo[((slot * QT + t) * DT + dt) * 64 + lane] = o[t][dt];
       }
     }
     __syncthreads();
     if (wave < half) {
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
-        const float mb = mm[wave][t][lane], lb = ml[wave][t][lane];
+        const float mb = mm[(wave * QT + t) * 64 + lane], lb = ml[(wave * QT + t) * 64 + lane];
         const float M = fmaxf(mrun[t], mb);
         const float ea = mrun[t] == -INFINITY ? 0.f : expf(mrun[t] - M);
         const float eb = mb == -INFINITY ? 0.f : expf(mb - M);
         lrun[t] = lrun[t] * ea + lb * eb;
         mrun[t] = M;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[t][dt] = o[t][dt] * ea + mo[wave][t][dt][lane] * eb;
+        for (int dt = 0; dt < DT; ++dt)
+          o[t][dt] = o[t][dt] * ea + mo[((wave * QT + t) * DT + dt) * 64 + lane] * eb;
       }
     }
     __syncthreads();
@@ -485,7 +558,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 void attn_plan(int B, int nkv, int slots, int window, int* nchunks, int* chunk) {
   const int span = window > 0 ? std::min(window, slots) : slots;
   const int units = std::max(1, B * nkv);
-  int nc = (1024 + units - 1) / units;
+  // about one workgroup per CU (the bf16 kernel holds 128 KB of LDS)
+  int nc = (256 + units - 1) / units;
   const int max_nc = std::max(1, (span + 127) / 128);  // at least one 32-key block per wave
   nc = std::max(1, std::min(nc, max_nc));
   int ch = (span + nc - 1) / nc;

@@ -13,6 +13,24 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // 16-byte lo
 
 constexpr int kWave = 64;
 
+#define SPEC_LDS __attribute__((address_space(3)))
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i's bytes land at dst + 16 i, dst uniform.
+// Completion is counted by vmcnt like any vector load.
+SPEC_DEV void dma16(const void* src, SPEC_LDS void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits [3:0] and
+// [15:14], expcnt [6:4], lgkmcnt [11:8]): at most N vector loads of this wave
+// outstanding, and every LDS access issued so far complete.
+template <int N>
+SPEC_DEV void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 SPEC_DEV float bf16_to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 
 // float -> bfloat16, round to nearest even (NaN stays NaN).
@@ -111,3 +129,34 @@ SPEC_DEV float gumbel_from_bits(uint32_t x) {
 }
 
 SPEC_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Visit f(value, index) for the float32 values row[lo, hi) owned by this
+// thread of a 256-thread block: 16-byte loads, four in flight per thread
+// (lo a multiple of 4 and row 16-byte aligned), indices increasing per thread.
+template <typename F>
+SPEC_DEV void for_row_chunk(const float* __restrict__ row, int lo, int hi, F&& f) {
+  constexpr int kU = 4;
+  for (int x0 = lo + 4 * (int)threadIdx.x; x0 < hi; x0 += 1024 * kU) {
+    float4 v[kU];
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int x = x0 + 1024 * i;
+      if (x + 3 < hi) {
+        v[i] = *(const float4*)(row + x);
+      } else {
+        v[i].x = x < hi ? row[x] : 0.f;
+        v[i].y = x + 1 < hi ? row[x + 1] : 0.f;
+        v[i].z = x + 2 < hi ? row[x + 2] : 0.f;
+        v[i].w = 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int x = x0 + 1024 * i;
+      if (x < hi) f(v[i].x, x);
+      if (x + 1 < hi) f(v[i].y, x + 1);
+      if (x + 2 < hi) f(v[i].z, x + 2);
+      if (x + 3 < hi) f(v[i].w, x + 3);
+    }
+  }
+}

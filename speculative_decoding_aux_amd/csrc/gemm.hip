@@ -338,6 +338,67 @@ __global__ __launch_bounds__(256) void epi_f32(float* __restrict__ Y, const floa
   Y[idx] = a;
 }
 
+// Few splits over many outputs: one thread per 4 consecutive outputs (16-byte
+// partial loads), splits summed in order from 0 - the same additions, in the
+// same order, as epi_kernel for nsplit <= kEpiGroups.
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  static SPEC_DEV float4 load(const float* p) { return *(const float4*)p; }
+  static SPEC_DEV void store(float* p, float4 v) { *(float4*)p = v; }
+};
+template <> struct Vec4<bf16_t> {
+  static SPEC_DEV float4 load(const bf16_t* p) {
+    const uint2 w = *(const uint2*)p;
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                       __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+  }
+  static SPEC_DEV void store(bf16_t* p, float4 v) {
+    uint2 w;
+    w.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    w.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    *(uint2*)p = w;
+  }
+};
+
+SPEC_DEV float4 split_sum4(const float* __restrict__ p, int64_t sstride, int nsplit) {
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nsplit; ++s) {
+    const float4 v = *(const float4*)(p + s * sstride);
+    a.x += v.x;
+    a.y += v.y;
+    a.z += v.z;
+    a.w += v.w;
+  }
+  return a;
+}
+
+template <typename T, int OP>
+__global__ __launch_bounds__(256) void epi_vec_kernel(T* __restrict__ Y, const T* __restrict__ R,
+                                                       const float* __restrict__ P, int nsplit,
+                                                       int M, int N) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= (int64_t)M * N) return;
+  const int m = int(e / N), n = int(e % N);
+  const int ldp = OP == EPI_SWIGLU ? 2 * N : N;
+  const int64_t ss = (int64_t)M * ldp;
+  const float* p = P + (int64_t)m * ldp + n;
+  float4 a = split_sum4(p, ss, nsplit);
+  if (OP == EPI_SWIGLU) {
+    const float4 u = split_sum4(p + N, ss, nsplit);
+    a.x = a.x / (1.f + expf(-a.x)) * u.x;
+    a.y = a.y / (1.f + expf(-a.y)) * u.y;
+    a.z = a.z / (1.f + expf(-a.z)) * u.z;
+    a.w = a.w / (1.f + expf(-a.w)) * u.w;
+  } else if (OP == EPI_RESID) {
+    const float4 r = Vec4<T>::load(R + e);
+    a.x += r.x;
+    a.y += r.y;
+    a.z += r.z;
+    a.w += r.w;
+  }
+  Vec4<T>::store(Y + e, a);
+}
+
 // One block per (row, head): 4 split groups x 64 threads; thread i < hd/2 of
 // group 0 owns the rotation pair (i, i + hd/2).
 template <typename T>
@@ -506,6 +567,25 @@ hipError_t gemm_epilogue(bool bf16, int op, void* Y, const void* R, const float*
                          int M, int N, hipStream_t s) {
   const int64_t total = (int64_t)M * N;
   const dim3 grid((unsigned)((total + kEpiCols - 1) / kEpiCols));
+  // vector path: few splits, many outputs, rows of whole 4-vectors, aligned
+  const auto al = [](const void* q, int b) { return ((uintptr_t)q & (b - 1)) == 0; };
+  const int eb = op == EPI_F32 || !bf16 ? 16 : 8;
+  if (nsplit <= kEpiGroups && total >= 65536 && N % 4 == 0 && al(P, 16) && al(Y, eb) &&
+      (op != EPI_RESID || al(R, eb))) {
+    const dim3 vgrid((unsigned)((total / 4 + 255) / 256));
+#define SPEC_EPIV(T, OPV)                                                                       \
+  hipLaunchKernelGGL((epi_vec_kernel<T, OPV>), vgrid, dim3(256), 0, s, (T*)Y, (const T*)R, P,  \
+                     nsplit, M, N)
+    if (op == EPI_F32) SPEC_EPIV(float, EPI_STORE);
+    else if (bf16 && op == EPI_STORE) SPEC_EPIV(bf16_t, EPI_STORE);
+    else if (bf16 && op == EPI_RESID) SPEC_EPIV(bf16_t, EPI_RESID);
+    else if (bf16) SPEC_EPIV(bf16_t, EPI_SWIGLU);
+    else if (op == EPI_STORE) SPEC_EPIV(float, EPI_STORE);
+    else if (op == EPI_RESID) SPEC_EPIV(float, EPI_RESID);
+    else SPEC_EPIV(float, EPI_SWIGLU);
+#undef SPEC_EPIV
+    return hipGetLastError();
+  }
   if (op == EPI_F32) {
     hipLaunchKernelGGL(epi_f32, grid, dim3(256), 0, s, (float*)Y, P, nsplit, total);
     return hipGetLastError();

@@ -20,27 +20,13 @@ namespace {
 // stored at position j ^ swz(r), swz(r) = (r >> 2) & 3 for 4 chunks and
 // (r >> 1) & 7 for 8, so the 16-lane fragment reads of 16 consecutive rows hit
 // 16 distinct 16-byte bank groups.
-// Synchronisation is a raw s_waitcnt vmcnt + s_barrier (a workgroup fence
-// would drain every stage in flight), with compiler fences so that no LDS
-// access moves across the barrier.  Each stage lives in its own LDS object
+// Synchronisation is a raw s_waitcnt vmcnt lgkmcnt(0) + s_barrier (a
+// workgroup fence would drain every stage in flight; lgkmcnt(0) makes the
+// reads of the stage before complete, so the refill after the barrier cannot
+// overtake them), with compiler fences so that no LDS access moves across it.  Each stage lives in its own LDS object
 // and every wave issues the same DMA count per stage, unconditionally (past
 // the end the last stage is loaded again), so the compiler can tell a stage's
 // reads from the other stages' DMA and adds no wait of its own.
-#define SPEC_LDS __attribute__((address_space(3)))
-
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits [3:0] and
-// [15:14], expcnt [6:4], lgkmcnt [11:8]); the LDS reads of the stage before
-// have completed too, so the refill after the next barrier cannot overtake them.
-template <int N>
-SPEC_DEV void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-// 16 bytes per lane from global memory to LDS (lane i lands at dst + 16 i).
-SPEC_DEV void dma16(const bf16_t* src, SPEC_LDS void* dst) {
-  __builtin_amdgcn_global_load_lds((const void*)src, dst, 16, 0, 0);
-}
-
 template <int CH>
 SPEC_DEV int chunk_swz(int row) {
   return CH == 4 ? (row >> 2) & 3 : (row >> 1) & 7;
@@ -126,7 +112,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   // every wave is done reading stage i - 1), refill stage i - 1's buffer with
   // stage i + NS - 1, compute stage i.  Past T only the refill runs.
   auto step = [&](auto sc, auto sn, int i) {
-    wait_vm<(NS - 2) * NI>();
+    wait_vm_lgkm0<(NS - 2) * NI>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -179,7 +165,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         step(S1{}, S0{}, i + 1);
       }
     }
-    wait_vm<0>();  // the repeated loads past the end
+    wait_vm_lgkm0<0>();  // the repeated loads past the end
   }
   // lane holds Y[m0 + wm*WM + 16b + c][n0 + wn*64 + 16a + 4g + r]
   float* Pb = P + (int64_t)blockIdx.y * M * N;

@@ -37,15 +37,19 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restri
   L.init();
   float m = -INFINITY;
   double s = 0.0;
-  for (int x = lo + threadIdx.x; x < hi; x += 256) {
-    const float v = row[x];
-    L.insert(v, rm ? rm[x] : x);
+  auto visit = [&](float v, int id) {
+    L.insert(v, id);
     if (v > m) {
       s = (m == -INFINITY ? 0.0 : s * (double)expf(m - v)) + 1.0;
       m = v;
     } else {
       s += (double)expf(v - m);
     }
+  };
+  if (!rm && ((uintptr_t)row & 15) == 0) {
+    for_row_chunk(row, lo, hi, visit);  // chunk starts are multiples of 256
+  } else {
+    for (int x = lo + threadIdx.x; x < hi; x += 256) visit(row[x], rm ? rm[x] : x);
   }
   // block max / sum
   float wm = wave_max(m);

@@ -31,37 +31,6 @@ struct GPart {  // per (sequence, vocab chunk) of the stop node's row
   int gid;
 };
 
-constexpr int kUnroll = 4;  // float4 loads in flight per thread
-
-// Visit the values of lrow[lo, hi) owned by this thread, in increasing index
-// order per thread; lo must be a multiple of 4 when V is.
-template <typename F>
-SPEC_DEV void for_chunk(const float* lrow, int lo, int hi, bool vec, F&& f) {
-  const int t = threadIdx.x;
-  if (vec) {
-    for (int x0 = lo + 4 * t; x0 < hi; x0 += 1024 * kUnroll) {
-      float4 v[kUnroll];
-#pragma unroll
-      for (int i = 0; i < kUnroll; ++i) {
-        const int x = x0 + 1024 * i;
-        v[i] = x < hi ? *(const float4*)(lrow + x) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int i = 0; i < kUnroll; ++i) {
-        const int x = x0 + 1024 * i;
-        if (x < hi) {
-          f(v[i].x, x);
-          f(v[i].y, x + 1);
-          f(v[i].z, x + 2);
-          f(v[i].w, x + 3);
-        }
-      }
-    }
-  } else {
-    for (int x = lo + t; x < hi; x += 256) f(lrow[x], x);
-  }
-}
-
 __global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
                                                            const int* __restrict__ num_nodes,
                                                            const float* __restrict__ logits,
@@ -77,17 +46,19 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const float* lrow = logits + (int64_t)row * V;
   const int lo = c * chunk, hi = min(V, lo + chunk);
-  const bool vec = (V & 3) == 0;
+  const bool vec = ((uintptr_t)lrow & 15) == 0;  // chunk starts are multiples of 1024
   VPart rec;
   if (mode == 0) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for_chunk(lrow, lo, hi, vec, [&](float v, int x) {
+    auto visit = [&](float v, int x) {
       if (better(v, x, bv, bi)) {
         bv = v;
         bi = x;
       }
-    });
+    };
+    if (vec) for_row_chunk(lrow, lo, hi, visit);
+    else for (int x = lo + t; x < hi; x += 256) visit(lrow[x], x);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float ov = __shfl_xor(bv, o, 64);
@@ -118,7 +89,7 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
   const float invT = 1.0f / temp;
   float m = -INFINITY;
   double zs = 0.0;
-  for_chunk(lrow, lo, hi, vec, [&](float l, int) {
+  auto visit = [&](float l, int) {
     const float zv = temp == 1.0f ? l : l * invT;
     if (zv > m) {
       zs = (m == -INFINITY ? 0.0 : zs * exp((double)m - (double)zv)) + 1.0;
@@ -126,7 +97,9 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
     } else if (zv != -INFINITY) {
       zs += (double)expf(zv - m);
     }
-  });
+  };
+  if (vec) for_row_chunk(lrow, lo, hi, visit);
+  else for (int x = lo + t; x < hi; x += 256) visit(lrow[x], x);
   const float wm = wave_max(m);
   double wz = m == -INFINITY ? 0.0 : zs * exp((double)m - (double)wm);
   wz = wave_sum(wz);
