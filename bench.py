@@ -44,18 +44,19 @@ def parse():
 def lm_head_bytes(cfg, M):
     """Algorithmic bytes of one LM-head launch: the weight stream and the
     normed rows in; out, the float32 logits, or - when the vocab top-k is fused
-    into the launch (bf16 weight streaming, unsplit: M <= 16 with Vd >= 65536,
-    or 128-column strips filling 2048 workgroups) - one (top-k list, max, sum)
-    record per row and column strip.  EAGLE-4: the low-rank score GEMM,
-    scores out."""
+    into the launch (bf16 weight streaming at M <= 64, unsplit: Vd >= 65536, or
+    column strips filling the grid) - one (top-k list, max, sum) record per row
+    and column strip.  EAGLE-4: the low-rank score GEMM, scores out."""
     H = cfg["hidden"]
     if cfg["cand_rank"]:
         r, V = cfg["cand_rank"], cfg["vocab"]
         return V * r * 2 + M * r * 2 + M * V * 4
     Vd, k = cfg["draft_vocab"], cfg["top_k"]
-    cols = 64 if (M <= 16 and Vd >= 65536) else 128
+    cw1 = M <= 16 and Vd >= 65536
+    cols = 64 if cw1 else 128
     strips = -(-Vd // cols)
-    fused = cfg["dtype"] == "bf16" and k <= 8 and M <= 64 and (cols == 64 or strips >= 2048)
+    unsplit = Vd >= 65536 or strips * -(-M // 64) >= (1024 if cw1 else 2048)
+    fused = cfg["dtype"] == "bf16" and k <= 8 and M <= 64 and unsplit
     out = M * strips * (8 * (1 if k == 1 else 8) + 16) if fused else M * Vd * 4
     return Vd * H * 2 + M * H * 2 + out
 

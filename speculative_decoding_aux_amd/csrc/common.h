@@ -130,33 +130,48 @@ SPEC_DEV float gumbel_from_bits(uint32_t x) {
 
 SPEC_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// Visit f(value, index) for the float32 values row[lo, hi) owned by this
-// thread of a 256-thread block: 16-byte loads, four in flight per thread
-// (lo a multiple of 4 and row 16-byte aligned), indices increasing per thread.
+// The float32 values row[lo, hi) owned by this thread of a 256-thread block,
+// in batches of 16 read by four 16-byte loads in flight (lo a multiple of 4,
+// row 16-byte aligned): f(v, x0) with v[4 i + e] = row[x0 + 1024 i + e], and
+// -inf where that index is >= hi.  Batches come in increasing x0.
 template <typename F>
-SPEC_DEV void for_row_chunk(const float* __restrict__ row, int lo, int hi, F&& f) {
-  constexpr int kU = 4;
-  for (int x0 = lo + 4 * (int)threadIdx.x; x0 < hi; x0 += 1024 * kU) {
-    float4 v[kU];
+SPEC_DEV void for_row_batches(const float* __restrict__ row, int lo, int hi, F&& f) {
+  for (int x0 = lo + 4 * (int)threadIdx.x; x0 < hi; x0 += 4096) {
+    float v[16];
 #pragma unroll
-    for (int i = 0; i < kU; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int x = x0 + 1024 * i;
+      float4 w;
       if (x + 3 < hi) {
-        v[i] = *(const float4*)(row + x);
+        w = *(const float4*)(row + x);
       } else {
-        v[i].x = x < hi ? row[x] : 0.f;
-        v[i].y = x + 1 < hi ? row[x + 1] : 0.f;
-        v[i].z = x + 2 < hi ? row[x + 2] : 0.f;
-        v[i].w = 0.f;
+        w.x = x < hi ? row[x] : -INFINITY;
+        w.y = x + 1 < hi ? row[x + 1] : -INFINITY;
+        w.z = x + 2 < hi ? row[x + 2] : -INFINITY;
+        w.w = -INFINITY;
       }
+      v[4 * i] = w.x;
+      v[4 * i + 1] = w.y;
+      v[4 * i + 2] = w.z;
+      v[4 * i + 3] = w.w;
     }
-#pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      const int x = x0 + 1024 * i;
-      if (x < hi) f(v[i].x, x);
-      if (x + 1 < hi) f(v[i].y, x + 1);
-      if (x + 2 < hi) f(v[i].z, x + 2);
-      if (x + 3 < hi) f(v[i].w, x + 3);
-    }
+    f(v, x0);
   }
+}
+
+// Online (max m, sum s of exp(v - m)) update with a batch of 16 values:
+// one rescale per batch at most; the batch's terms are summed in float64.
+SPEC_DEV void lse_update16(const float (&v)[16], float& m, double& s) {
+  float bm = v[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) bm = fmaxf(bm, v[e]);
+  if (bm == -INFINITY) return;
+  if (bm > m) {
+    s = m == -INFINITY ? 0.0 : s * exp((double)m - (double)bm);
+    m = bm;
+  }
+  double a = 0.0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) a += (double)expf(v[e] - m);
+  s += a;
 }

@@ -480,6 +480,9 @@ GemmPlan gemm_plan(int M, int N, int K, bool bf16) {
   int ns = (target + strips * mblocks - 1) / (strips * mblocks);
   const int kblocks = (K + 127) / 128;
   ns = std::max(1, std::min(std::min(ns, kblocks), kMaxSplit));
+  // vocab-wide heads have >= 1024 strips already: no split, so the top-k can
+  // be fused into the epilogue and no M x N partials are written
+  if (N >= 65536) ns = 1;
   const int kc = ((kblocks + ns - 1) / ns) * 128;
   p.kc = kc;
   p.nsplit = (K + kc - 1) / kc;

@@ -4,7 +4,8 @@
 // topk: rows are split into chunks; a workgroup scans one chunk with a sorted
 // register list of KM (value, id) per thread plus an online (max, sum exp)
 // (sum in float64), merges the 256 lists by k rounds of wave-wide "best head"
-// selection, and writes a partial record; a second kernel merges the chunk
+// selection, and writes a partial record (with 16-byte loads the lists hold
+// the best element of each 16-value batch, and the k best batches are rescanned); a second kernel merges the chunk
 // records of a row, takes logsumexp = max + log(sum) in float64 rounded once to
 // float32, and emits log-prob = z - lse.  Order is (value desc, id asc).
 #include "common.h"
@@ -46,8 +47,27 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restri
       s += (double)expf(v - m);
     }
   };
-  if (!rm && ((uintptr_t)row & 15) == 0) {
-    for_row_chunk(row, lo, hi, visit);  // chunk starts are multiples of 256
+  // 16-byte path: each thread sees its values in batches of 16 and keeps the
+  // KM best batches, ranked by their best element.  The k best elements of
+  // the chunk lie in the k best batches (a batch holding one of them has a
+  // best element at least as good; one holding none is worse than all of
+  // them), so the batch bests are merged and then their batches rescanned.
+  const bool vec = !rm && ((uintptr_t)row & 15) == 0;  // chunk starts are multiples of 256
+  if (vec) {
+    for_row_batches(row, lo, hi, [&](const float (&v)[16], int x0) {
+      float bv = -INFINITY;
+      int bi = kIdNone;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int x = x0 + 1024 * (e >> 2) + (e & 3);
+        if (x < hi && better(v[e], x, bv, bi)) {
+          bv = v[e];
+          bi = x;
+        }
+      }
+      if (bi != kIdNone) L.insert(bv, bi);
+      lse_update16(v, m, s);
+    });
   } else {
     for (int x = lo + threadIdx.x; x < hi; x += 256) visit(row[x], rm ? rm[x] : x);
   }
@@ -87,6 +107,26 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restri
     float ov[KM];
     int oi[KM];
     wave_merge<1, KM>(one, k, ov, oi);
+    if (vec) {
+      // rescan the k best batches: candidate q of lane = element q % 16 of batch q / 16
+      constexpr int CPL = KM >= 4 ? KM / 4 : 1;
+      List<CPL> cand;
+      cand.init();
+#pragma unroll
+      for (int h = 0; h < CPL; ++h) {
+        const int q = lane * CPL + h, j = q >> 4, e = q & 15;
+        int bid = kIdNone;
+#pragma unroll
+        for (int jj = 0; jj < KM; ++jj)
+          if (jj == j) bid = oi[jj];
+        if (j < k && bid != kIdNone) {
+          const int off = bid - lo;  // batch start: bid - 1024 i - e', i = (off >> 10) & 3, e' = off & 3
+          const int x = bid - 1024 * ((off >> 10) & 3) - (off & 3) + 1024 * (e >> 2) + (e & 3);
+          if (x < hi) cand.insert(row[x], x);
+        }
+      }
+      wave_merge<CPL, KM>(cand, k, ov, oi);
+    }
     const int64_t base = ((int64_t)r * nch + c) * KM;
     if (lane == 0) {
 #pragma unroll

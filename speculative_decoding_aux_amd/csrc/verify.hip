@@ -57,8 +57,17 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
         bi = x;
       }
     };
-    if (vec) for_row_chunk(lrow, lo, hi, visit);
-    else for (int x = lo + t; x < hi; x += 256) visit(lrow[x], x);
+    if (vec) {
+      for_row_batches(lrow, lo, hi, [&](const float (&v)[16], int x0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int x = x0 + 1024 * (e >> 2) + (e & 3);
+          if (x < hi) visit(v[e], x);
+        }
+      });
+    } else {
+      for (int x = lo + t; x < hi; x += 256) visit(lrow[x], x);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float ov = __shfl_xor(bv, o, 64);
@@ -89,17 +98,28 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
   const float invT = 1.0f / temp;
   float m = -INFINITY;
   double zs = 0.0;
-  auto visit = [&](float l, int) {
-    const float zv = temp == 1.0f ? l : l * invT;
-    if (zv > m) {
-      zs = (m == -INFINITY ? 0.0 : zs * exp((double)m - (double)zv)) + 1.0;
-      m = zv;
-    } else if (zv != -INFINITY) {
-      zs += (double)expf(zv - m);
+  if (vec) {
+    for_row_batches(lrow, lo, hi, [&](const float (&v)[16], int) {
+      if (temp == 1.0f) {
+        lse_update16(v, m, zs);
+      } else {
+        float zv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) zv[e] = v[e] * invT;
+        lse_update16(zv, m, zs);
+      }
+    });
+  } else {
+    for (int x = lo + t; x < hi; x += 256) {
+      const float zv = temp == 1.0f ? lrow[x] : lrow[x] * invT;
+      if (zv > m) {
+        zs = (m == -INFINITY ? 0.0 : zs * exp((double)m - (double)zv)) + 1.0;
+        m = zv;
+      } else if (zv != -INFINITY) {
+        zs += (double)expf(zv - m);
+      }
     }
-  };
-  if (vec) for_row_chunk(lrow, lo, hi, visit);
-  else for (int x = lo + t; x < hi; x += 256) visit(lrow[x], x);
+  }
   const float wm = wave_max(m);
   double wz = m == -INFINITY ? 0.0 : zs * exp((double)m - (double)wm);
   wz = wave_sum(wz);

@@ -37,6 +37,35 @@ def test_topk_logprobs_match_oracle(M, n, k, mapped):
         np.testing.assert_allclose(lp[r], want_lp, atol=2e-6, rtol=0)
 
 
+@pytest.mark.parametrize("n,k", [(151936, 8), (151936, 16), (5000, 8), (4999, 2)])
+def test_topk_adversarial_layouts(n, k):
+    """Value layouts aimed at the batched scan (a thread reads 16-value batches
+    at x0 + 1024 i + e): ramps, all-equal rows, the k best packed into one
+    batch, ties across chunks, -inf runs; rows of 4999 are not 16-byte aligned."""
+    announce(f"topk adversarial n={n} k={k}")
+    rng = np.random.default_rng(n + k)
+    M = 6
+    z = rng.normal(0, 2, (M, n)).astype(np.float32)
+    z[0] = np.linspace(-3, 3, n, dtype=np.float32)              # best values at the end
+    z[1] = np.linspace(3, -3, n, dtype=np.float32)              # best values at the start
+    z[2] = 0.25                                                 # all equal: lowest ids win
+    x0 = 4096 + 4 * 37                                          # one thread's batch
+    batch = [x0 + 1024 * i + e for i in range(4) for e in range(4)]
+    batch = [x for x in batch if x < n]
+    z[3, batch] = 10.0 + np.arange(len(batch), dtype=np.float32)[::-1] * 0.5
+    z[4, ::997] = z[4].max() + 1.0                              # ties spread over chunks
+    z[5, : n // 2] = -np.inf
+    cfg = configs.get("tiny_chain", top_k=min(k, 16), total_tokens=max(3, k), depth=3, vocab=n, draft_vocab=n)
+    ctx = S.SpecContext(cfg, max_batch=M)
+    ids, lp = S.spec_topk_logprobs(ctx, torch.from_numpy(z).to(DEV), k)
+    torch.cuda.synchronize()
+    ids, lp = ids.cpu().numpy(), lp.cpu().numpy()
+    for r in range(M):
+        top, want_lp = ot.topk_logprobs(z[r], k)
+        np.testing.assert_array_equal(ids[r], top, err_msg=f"row {r}")
+        np.testing.assert_allclose(lp[r], want_lp, atol=2e-6, rtol=0, err_msg=f"row {r}")
+
+
 def _table(cfg, B, seed, quantise):
     """Per-pass top-k tables: distinct ids per row, log-probs sorted
     descending; quantised log-probs create exact score ties."""
