@@ -9,7 +9,8 @@
  *                     sampling against the target's logits;
  *   spec_compact_kv   move the accepted nodes' K/V next to the root.
  * Stage-level entry points expose single steps of the same path:
- *   spec_draft_step, spec_topk_logprobs, spec_tree_from_topk.
+ *   spec_draft_step, spec_topk_logprobs, spec_retrieve_candidates,
+ *   spec_tree_from_topk.
  *
  * Sources: "Speculative Decoding (EAGLE3) in the vLLM Neuron Framework"
  * (sections "What is EAGLE3?", "Eagle3 Draft Model Architecture", "The
@@ -179,6 +180,15 @@ spec_status spec_draft_step(spec_ctx* ctx, const spec_weights* w, const spec_kv*
  * id_map (device, [n]) is given, else the position.  k <= 16. */
 spec_status spec_topk_logprobs(spec_ctx* ctx, int32_t M, int32_t n, const float* logits, int32_t k,
                                const int32_t* id_map, int32_t* ids_out, float* logp_out, void* stream);
+
+/* Candidate retrieval of the EAGLE-4 head (NeMo AutoModel "eagle4" page,
+ * Eagle4CandidateHeadConfig: the num_candidates best of the low-rank scores
+ * are kept for exact rescoring): for each of M rows of float32 scores [M, n]
+ * (device), the positions of the K best, best first by (score desc,
+ * position asc), into ids_out [M, K] (device).  K <= 256 and K <= n.  Uses
+ * no workspace; asynchronous on stream. */
+spec_status spec_retrieve_candidates(spec_ctx* ctx, int32_t M, int32_t n, const float* scores,
+                                     int32_t K, int32_t* ids_out, void* stream);
 
 /* Tree expansion and selection with the draft given as a table: pass d
  * (1 = root), sequence b and beam rank j produce topk_ids[d-1][b][j][:] and

@@ -44,7 +44,7 @@ class SpecTree(ctypes.Structure):
 
 
 EXPORTS = ["spec_create", "spec_destroy", "spec_last_error", "spec_workspace_bytes", "spec_version",
-           "spec_draft_step", "spec_topk_logprobs", "spec_tree_from_topk", "spec_build_tree",
+           "spec_draft_step", "spec_topk_logprobs", "spec_retrieve_candidates", "spec_tree_from_topk", "spec_build_tree",
            "spec_verify_tree", "spec_compact_kv", "spec_profile_enable", "spec_profile_read"]
 SPEC_PROF_LM_HEAD, SPEC_PROF_ATTENTION, SPEC_PROF_VERIFY, SPEC_PROF_TOPK = 0, 1, 2, 3
 
@@ -77,6 +77,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_draft_step.restype = c_i32
     lib.spec_topk_logprobs.argtypes = [c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp]
     lib.spec_topk_logprobs.restype = c_i32
+    lib.spec_retrieve_candidates.argtypes = [c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_vp]
+    lib.spec_retrieve_candidates.restype = c_i32
     lib.spec_tree_from_topk.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, P(SpecTree), c_vp]
     lib.spec_tree_from_topk.restype = c_i32
     lib.spec_build_tree.argtypes = [c_vp, P(SpecWeights), P(SpecKV), c_i32, c_i32, c_vp, c_vp, c_vp,

@@ -273,7 +273,8 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
 // 4*(lane>>4)+i and query column lane&15 - the B-operand layout of
 // O^T = V^T . P^T over the 32 keys (element e<4: tile 0 key 4g+e, e>=4: tile 1
 // key 16+4g+e-4).  The V^T fragments gather those 8 keys at dim lane&15 from
-// LDS with 2-byte reads.
+// LDS with 2-byte reads.  P goes in as two bf16 parts (hi + lo), keeping the
+// float32 softmax weights to about 16 bits.
 // LDS layout: a row of CH = HD/8 16-byte chunks; K row r keeps chunk j at
 // position j ^ fk(r) (fk = r & 15 for 16 chunks, (r >> 1) & 7 for 8), so the
 // 16 rows of an A fragment hit 16 distinct bank groups; V row r keeps chunk j
@@ -446,12 +447,24 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
       psum += __shfl_xor(psum, 32, 64);
       lrun[t] = lrun[t] * alpha + psum;
       mrun[t] = mnew;
+      // P = P_hi + P_lo in two bf16 parts (about 16 significant bits), so the
+      // products with V carry the float32 softmax weights, not bf16-rounded ones
+      float vlo[8];
       const u32x4_t pf = pack8(v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (pf[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        vlo[e] = v[e] - __uint_as_float(h << 16);
+      }
+      const u32x4_t pl = pack8(vlo);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         o[t][dt] *= alpha;
         o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
                                                            __builtin_bit_cast(bf16x8, pf), o[t][dt],
+                                                           0, 0, 0);
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
+                                                           __builtin_bit_cast(bf16x8, pl), o[t][dt],
                                                            0, 0, 0);
       }
     }

@@ -581,6 +581,15 @@ spec_status spec_topk_logprobs(spec_ctx* ctx, int32_t M, int32_t n, const float*
   return SPEC_OK;
 }
 
+spec_status spec_retrieve_candidates(spec_ctx* ctx, int32_t M, int32_t n, const float* scores,
+                                     int32_t K, int32_t* ids_out, void* stream) {
+  if (!ctx) return SPEC_EINVAL;
+  SPEC_REQ(ctx, M > 0 && n > 0 && K > 0 && K <= 256 && K <= n, SPEC_EINVAL, "bad sizes");
+  SPEC_REQ(ctx, scores && ids_out, SPEC_EINVAL, "null argument");
+  SPEC_HIP(ctx, topk_large(scores, M, n, K, ids_out, nullptr, STREAM(stream)));
+  return SPEC_OK;
+}
+
 spec_status spec_tree_from_topk(spec_ctx* ctx, int32_t B, int32_t n_new, const int32_t* in_tokens,
                                 const int32_t* ctx_len, const int32_t* topk_ids,
                                 const float* topk_logp, spec_tree* out, void* stream) {

@@ -254,16 +254,46 @@ SPEC_DEV uint32_t okey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict__ z, int n,
-                                                         int K, int* __restrict__ ids) {
-  __shared__ int hist[256];
-  __shared__ int sel_cnt, need_s, take_all;
-  __shared__ uint32_t prefix_s, mask_s;
-  __shared__ float cv[256];
-  __shared__ int ci[256];
-  __shared__ int scan[256];
-  const int r = blockIdx.x, t = threadIdx.x;
-  const float* row = z + (int64_t)r * n;
+// In-place bitonic sort of P (a power of two, <= 4096) (value, id) pairs in
+// LDS, best first by (value desc, id asc); 256 threads, barriers included.
+SPEC_DEV void bitonic_desc(float* cv, int* ci, int P) {
+  const int t = threadIdx.x;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int q = t; q < P; q += 256) {
+        const int partner = q ^ stride;
+        if (partner > q) {
+          const bool desc = (q & size) == 0;
+          const bool pb = better(cv[partner], ci[partner], cv[q], ci[q]);
+          if (pb == desc) {
+            const float tv = cv[q];
+            cv[q] = cv[partner];
+            cv[partner] = tv;
+            const int ti = ci[q];
+            ci[q] = ci[partner];
+            ci[partner] = ti;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Full-row radix select of the K best (K <= 256) of one row: four 8-bit
+// histogram passes over the order-preserving keys, then the keys strictly
+// above the threshold and the smallest ids at it, then a bitonic sort of the
+// 256 slots.  LDS: hist[256], cv/ci[256], scan[256].
+SPEC_DEV void radix_topk_row(const float* __restrict__ row, int n, int K, int* __restrict__ out,
+                             int* hist, float* cv, int* ci, int* scan, int* sh /* >= 5 ints */) {
+  const int t = threadIdx.x;
+  int& sel_cnt = sh[0];
+  int& need_s = sh[1];
+  int& take_all = sh[2];
+  uint32_t& prefix_s = *(uint32_t*)&sh[3];
+  uint32_t& mask_s = *(uint32_t*)&sh[4];
+  __syncthreads();
   if (t == 0) {
     prefix_s = 0;
     mask_s = 0;
@@ -339,26 +369,102 @@ __global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict
     }
     __syncthreads();
   }
-  // bitonic sort of 256 (value desc, id asc)
-  for (int size = 2; size <= 256; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int partner = t ^ stride;
-      if (partner > t) {
-        const bool desc = (t & size) == 0;
-        const bool pb = better(cv[partner], ci[partner], cv[t], ci[t]);
-        if (pb == desc) {
-          const float tv = cv[t];
-          cv[t] = cv[partner];
-          cv[partner] = tv;
-          const int ti = ci[t];
-          ci[t] = ci[partner];
-          ci[partner] = ti;
+  bitonic_desc(cv, ci, 256);
+  if (t < K) out[t] = ci[t];
+}
+
+// Candidate retrieval, K best of a row of n <= kLargeGroups * 16 scores.
+// Pass 1 streams the row once (16-byte loads) and keeps the best value of
+// every 16-value batch (group) in LDS.  The K best values of the row lie in
+// the K best groups (a group holding one of them has a maximum at least that
+// good), so a radix select over the group maxima gives a threshold; the
+// groups at or above it (at most kLargeCand of them, else the full-row
+// select runs) are rescanned and their values sorted.
+constexpr int kLargeGroups = 8192, kLargeCand = 256;
+__global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict__ z, int n,
+                                                         int K, int* __restrict__ ids) {
+  __shared__ float gmax[kLargeGroups];
+  __shared__ float cv[kLargeCand * 16];
+  __shared__ int ci[kLargeCand * 16];
+  __shared__ int hist[256], cg[kLargeCand];
+  __shared__ int sh[8];
+  const int r = blockIdx.x, t = threadIdx.x;
+  const float* row = z + (int64_t)r * n;
+  const int G = (n + 4095) / 4096 * 256;  // groups: batch j of thread t is group 256 j + t
+  const bool fast = ((uintptr_t)row & 15) == 0 && G <= kLargeGroups && K <= kLargeCand;
+  if (fast) {
+    for (int g = t; g < G; g += 256) gmax[g] = -INFINITY;
+    __syncthreads();
+    for_row_batches(row, 0, n, [&](const float (&v)[16], int x0) {
+      float bm = v[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) bm = fmaxf(bm, v[e]);
+      gmax[(x0 >> 12) * 256 + t] = bm;
+    });
+    // radix select of the K-th best group maximum (by key)
+    if (t == 0) {
+      sh[3] = 0;  // prefix
+      sh[4] = 0;  // mask
+      sh[1] = K;  // still needed
+    }
+    __syncthreads();
+    for (int p = 24; p >= 0; p -= 8) {
+      hist[t] = 0;
+      __syncthreads();
+      const uint32_t pre = (uint32_t)sh[3], msk = (uint32_t)sh[4];
+      for (int g = t; g < G; g += 256) {
+        const uint32_t key = okey(gmax[g]);
+        if ((key & msk) == pre) atomicAdd(&hist[(key >> p) & 255], 1);
+      }
+      __syncthreads();
+      if (t == 0) {
+        int need = sh[1], above = 0, dd = 0;
+        for (int d = 255; d >= 0; --d) {
+          if (above + hist[d] >= need) {
+            dd = d;
+            break;
+          }
+          above += hist[d];
         }
+        sh[1] = need - above;
+        sh[3] = (int)(pre | ((uint32_t)dd << p));
+        sh[4] = (int)(msk | (255u << p));
       }
       __syncthreads();
     }
+    const uint32_t T = (uint32_t)sh[3];
+    if (t == 0) sh[0] = 0;
+    __syncthreads();
+    for (int g = t; g < G; g += 256)
+      if (okey(gmax[g]) >= T) {
+        const int slot = atomicAdd(&sh[0], 1);
+        if (slot < kLargeCand) cg[slot] = g;
+      }
+    __syncthreads();
+    const int C = sh[0];
+    if (C <= kLargeCand) {
+      int P2 = 16;
+      while (P2 < C * 16) P2 <<= 1;
+      for (int q = t; q < P2; q += 256) {
+        float v = -INFINITY;
+        int id = kIdNone;
+        if (q < C * 16) {
+          const int g = cg[q >> 4], e = q & 15;
+          const int x = (g >> 8) * 4096 + 4 * (g & 255) + 1024 * (e >> 2) + (e & 3);
+          if (x < n) {
+            v = row[x];
+            id = x;
+          }
+        }
+        cv[q] = v;
+        ci[q] = id;
+      }
+      bitonic_desc(cv, ci, P2);
+      for (int q = t; q < K; q += 256) ids[(int64_t)r * K + q] = ci[q];
+      return;
+    }
   }
-  if (t < K) ids[(int64_t)r * K + t] = ci[t];
+  radix_topk_row(row, n, K, ids + (int64_t)r * K, hist, cv, ci, cg, sh);
 }
 
 template <typename T>
@@ -375,6 +481,56 @@ __global__ __launch_bounds__(256) void gather_dot_kernel(const T* __restrict__ x
   for (int i = lane; i < H; i += 64) a += St<T>::load(w, i) * St<T>::load(xr, i);
   a = wave_sum(a);
   if (lane == 0) out[(int64_t)m * K + j] = a;
+}
+
+// Exact rescoring, bf16, H a multiple of 512: one workgroup per row keeps the
+// row's activation in registers (16-byte chunks at 8 lane + 512 i) and each
+// wave walks candidates j = wave, wave + 4, ..., two at a time, with 16-byte
+// weight loads.
+template <int HC>  // H / 512 chunks per lane
+__global__ __launch_bounds__(256) void gather_dot_vec_kernel(const bf16_t* __restrict__ x,
+                                                             const bf16_t* __restrict__ W, int H,
+                                                             int V, const int* __restrict__ ids,
+                                                             int K, float* __restrict__ out) {
+  const int m = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bf16_t* xr = x + (int64_t)m * H + lane * 8;
+  float xf[HC][8];
+#pragma unroll
+  for (int i = 0; i < HC; ++i) {
+    const u32x4_t w = *(const u32x4_t*)(xr + i * 512);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xf[i][2 * e] = __uint_as_float(w[e] << 16);
+      xf[i][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+  auto dot = [&](const u32x4_t (&wv)[HC]) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < HC; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a += xf[i][2 * e] * __uint_as_float(wv[i][e] << 16);
+        a += xf[i][2 * e + 1] * __uint_as_float(wv[i][e] & 0xffff0000u);
+      }
+    return wave_sum(a);
+  };
+  for (int j = wave; j < K; j += 8) {
+    const int j2 = j + 4;
+    const int r1 = clampi(ids[(int64_t)m * K + j], 0, V - 1);
+    const int r2 = clampi(ids[(int64_t)m * K + min(j2, K - 1)], 0, V - 1);
+    u32x4_t w1[HC], w2[HC];
+#pragma unroll
+    for (int i = 0; i < HC; ++i) {
+      w1[i] = *(const u32x4_t*)(W + (int64_t)r1 * H + lane * 8 + i * 512);
+      w2[i] = *(const u32x4_t*)(W + (int64_t)r2 * H + lane * 8 + i * 512);
+    }
+    const float a1 = dot(w1), a2 = dot(w2);
+    if (lane == 0) {
+      out[(int64_t)m * K + j] = a1;
+      if (j2 < K) out[(int64_t)m * K + j2] = a2;
+    }
+  }
 }
 
 template <int KM>
@@ -455,6 +611,17 @@ hipError_t topk_large(const float* z, int M, int n, int K, int* ids, void* part,
 
 hipError_t gather_dot(bool bf16, const void* x, const void* W, int H, int V, const int* ids, int M,
                       int K, float* out, hipStream_t s) {
+  const bool al = ((uintptr_t)x & 15) == 0 && ((uintptr_t)W & 15) == 0;
+  if (bf16 && al && H == 4096) {
+    hipLaunchKernelGGL(gather_dot_vec_kernel<8>, dim3(M), dim3(256), 0, s, (const bf16_t*)x,
+                       (const bf16_t*)W, H, V, ids, K, out);
+    return hipGetLastError();
+  }
+  if (bf16 && al && H == 2048) {
+    hipLaunchKernelGGL(gather_dot_vec_kernel<4>, dim3(M), dim3(256), 0, s, (const bf16_t*)x,
+                       (const bf16_t*)W, H, V, ids, K, out);
+    return hipGetLastError();
+  }
   dim3 grid((K + 3) / 4, M);
   if (bf16) {
     hipLaunchKernelGGL(gather_dot_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,

@@ -165,6 +165,14 @@ def spec_topk_logprobs(ctx: SpecContext, logits: torch.Tensor, k: int, id_map=No
     return ids, logp
 
 
+def spec_retrieve_candidates(ctx: SpecContext, scores: torch.Tensor, K: int):
+    M, n = scores.shape
+    ids = torch.empty(M, K, dtype=torch.int32, device=scores.device)
+    st = ctx.lib.spec_retrieve_candidates(ctx.h, M, n, _p(scores), K, _p(ids), _stream())
+    ctx._check(st)
+    return ids
+
+
 def spec_tree_from_topk(ctx: SpecContext, B, n_new, in_tokens, ctx_len, ids_tab, lp_tab) -> Tree:
     dev = ctx.device
     tree = Tree(B, ctx.cfg["total_tokens"] + 1, dev)

@@ -47,6 +47,11 @@ CASES = {
     # down projection is not a multiple of 64 and takes the streaming kernel
     "tile_rows72_ragged": (configs.get("tiny_chain", **dict(SMALL, batch=9, top_k=8, total_tokens=20,
                                                             intermediate=480)), 2e-2),
+    # EAGLE-4 head at width 2048 and a 70000 vocab: 128 candidates retrieved by
+    # the group-maximum select and rescored with 16-byte weight loads
+    "eagle4_h2048_v70000": (configs.get("tiny_chain", **dict(SMALL, hidden=2048, n_q_heads=16, n_kv_heads=4,
+                                                             head_dim=128, vocab=70000, draft_vocab=70000,
+                                                             cand_rank=128, num_candidates=128)), 2e-2),
     "bigvocab_k8_rows512": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
                                                              top_k=8, total_tokens=20, batch=64, ctx=24)), 2e-2),
 }
@@ -91,7 +96,8 @@ def _run_both(name):
     toks2 = rng.integers(0, cfg["vocab"], size=B * k).astype(np.int32)
     hid2 = o1["h_out"][seq2]
     o2 = od.draft_pass(cfg, W, kc, vc, 1, hid2, toks2, seq2, pos2, slot2, ctx_len, anc2)
-    hid2_dev = g1["h_out"][torch.from_numpy(seq2).to(DEV)].contiguous()
+    # both sides take the same pass-2 input: the oracle's pass-1 state
+    hid2_dev = to_device(np.ascontiguousarray(hid2), cfg["dtype"])
     g2 = S.spec_draft_step(ctx, w, cache, B, k, 1, hid2_dev, toks2, pos2, slot2, ctx_len, anc2, k,
                            want_logits=True, want_candidates=bool(cfg["cand_rank"]))
     torch.cuda.synchronize()

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 from gpu_helpers import DEV, announce, compare_tree
+from oracle import draft as od
 from oracle import tree as ot
 from speculative_decoding_aux_amd import spec as S
 from synth import configs, gen
@@ -64,6 +65,30 @@ def test_topk_adversarial_layouts(n, k):
         top, want_lp = ot.topk_logprobs(z[r], k)
         np.testing.assert_array_equal(ids[r], top, err_msg=f"row {r}")
         np.testing.assert_allclose(lp[r], want_lp, atol=2e-6, rtol=0, err_msg=f"row {r}")
+
+
+@pytest.mark.parametrize("n,K", [(128256, 128), (70000, 128), (2048, 64), (128256, 256), (5001, 100)])
+def test_candidate_retrieval_matches_oracle(n, K):
+    """Retrieval of the K best scores per row (EAGLE-4 head): random rows, a
+    ramp, the K best packed into few 16-value batches, ties at the threshold,
+    and an all-equal row (far more tied batches than the fast path keeps, so
+    the full-row select runs); 5001 is not a multiple of 4 (unaligned rows)."""
+    announce(f"candidate retrieval n={n} K={K}")
+    rng = np.random.default_rng(n * 3 + K)
+    M = 7
+    z = rng.normal(0, 1, (M, n)).astype(np.float32)
+    z[1] = np.linspace(-1, 1, n, dtype=np.float32)
+    z[2, : min(n, 3 * K)] += 8.0                                    # best values contiguous
+    z[3] = np.round(z[3] * 2) / 2                                   # heavy ties everywhere
+    z[4] = 0.5                                                      # all equal
+    z[5, rng.choice(n, size=min(n, 4 * K), replace=False)] = 3.0    # ties at the threshold
+    cfg = configs.get("tiny_chain", vocab=max(n, 4096), draft_vocab=max(n, 4096))
+    ctx = S.SpecContext(cfg, max_batch=M)
+    ids = S.spec_retrieve_candidates(ctx, torch.from_numpy(z).to(DEV), K)
+    torch.cuda.synchronize()
+    ids = ids.cpu().numpy()
+    for r in range(M):
+        np.testing.assert_array_equal(ids[r], od.topk_desc(z[r], K), err_msg=f"row {r}")
 
 
 def _table(cfg, B, seed, quantise):
