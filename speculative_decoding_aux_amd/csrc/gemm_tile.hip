@@ -54,7 +54,25 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wn = wave % WGN, wm = wave / WGN;
   const int g = lane >> 4, c = lane & 15;
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.z * BM;
+  // Block order: workgroups are dealt to the 8 XCDs round-robin, so ids b and
+  // b + 8 share an XCD (and its L2).  The row blocks of one weight strip get
+  // ids 8 apart and run together there, and the strip is read from HBM once.
+  // The grid is (strips x row blocks, splits): blockIdx.x carries both.
+  const int nstrip = (N + BN - 1) / BN, nmb = (M + BM - 1) / BM;
+  int strip = blockIdx.x, mb = 0;
+  if (nmb > 1) {
+    const int b = blockIdx.x;
+    const int grp = b / (8 * nmb), rem = b % (8 * nmb);
+    strip = grp * 8 + rem % 8;
+    mb = rem / 8;
+    if (strip >= nstrip) {  // the last group is short: spread its ids over what is left
+      const int base = (nstrip / 8) * 8, left = nstrip - base;
+      const int q = b - base * nmb;
+      strip = base + q % left;
+      mb = q / left;
+    }
+  }
+  const int n0 = strip * BN, m0 = mb * BM;
   const int k0 = blockIdx.y * kc, k1 = min(K, k0 + kc);
   const int T = max(0, (k1 - k0) / BK);
 
@@ -213,7 +231,7 @@ GemmPlan gemm_tile_plan(int M, int N, int K) {
 hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N, int K,
                      const GemmPlan& plan, hipStream_t s) {
   if (M <= 0 || N <= 0 || K % kTileBK != 0 || plan.kc % kTileBK != 0) return hipErrorInvalidValue;
-  const dim3 grid((N + kTileBN - 1) / kTileBN, plan.nsplit, (M + kTileBM - 1) / kTileBM);
+  const dim3 grid(((N + kTileBN - 1) / kTileBN) * ((M + kTileBM - 1) / kTileBM), plan.nsplit, 1);
   hipLaunchKernelGGL((gemm_dma_kernel<kTileBN, kTileBM, kTileBK, kTileThreads, kTileStages>), grid,
                      dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M,
                      N, K, plan.kc);
