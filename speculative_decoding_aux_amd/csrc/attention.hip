@@ -263,58 +263,59 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
 
 
 // ---- bf16 context attention on MFMA -----------------------------------------
-// Each wave walks blocks of 32 keys (two 16-key tiles), wave w taking blocks
-// w, w + 4, ... of the chunk.  The K and V rows of a block (2 x 32 x HD bf16)
-// are brought into a wave-private LDS stage by global_load_lds_dwordx4, one
-// block ahead (two stages per wave), so the wave never waits on a barrier
-// and the loads stay 16 bytes wide and coalesced.
-// S^T = K . Q^T takes K rows as the A operand (lane: key = lane&15, 8 dims at
-// 8*(lane>>4)) and the query vectors as B, so the score tile lands with key
-// 4*(lane>>4)+i and query column lane&15 - the B-operand layout of
-// O^T = V^T . P^T over the 32 keys (element e<4: tile 0 key 4g+e, e>=4: tile 1
-// key 16+4g+e-4).  The V^T fragments gather those 8 keys at dim lane&15 from
-// LDS with 2-byte reads.  P goes in as two bf16 parts (hi + lo), keeping the
-// float32 softmax weights to about 16 bits.
-// LDS layout: a row of CH = HD/8 16-byte chunks; K row r keeps chunk j at
-// position j ^ fk(r) (fk = r & 15 for 16 chunks, (r >> 1) & 7 for 8), so the
-// 16 rows of an A fragment hit 16 distinct bank groups; V row r keeps chunk j
-// at j ^ 2((r >> 2) & 3), so the four key rows 4g+e of a V^T read do too.
-// Online softmax runs per query column (shuffles across the four lane
-// groups); the four waves are merged pairwise through LDS at the end.
-SPEC_DEV u32x4_t pack8(const float (&v)[8]) {
-  u32x4_t w;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    w[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
-  return w;
+// Each wave walks blocks of 16 keys, wave w taking blocks w, w + 4, ... of the
+// chunk, one block ahead of use: the K rows load straight into registers in
+// MFMA fragment layout, the V rows go into a wave-private LDS stage by
+// global_load_lds_dwordx4 (two stages per wave, 32 KB per workgroup at hd
+// 128), so the key loop has no workgroup barrier, every load is 16 bytes wide
+// and several workgroups share a CU.
+// S^T = K . Q^T (16x16x32 bf16 MFMA) takes K rows as the A operand (lane:
+// key = lane&15, 8 dims at 8*(lane>>4)) and the query vectors as B, so the
+// score tile lands with key 4*(lane>>4)+i and query column lane&15 - exactly
+// the B-operand layout of the 16x16x16 bf16 MFMA of O^T = V^T . P^T over the
+// 16 keys.  The V^T fragment of 16 dims takes keys 4g..4g+3 at dim lane&15
+// from LDS with 2-byte reads; V row r keeps its 16-byte chunk j at position
+// j ^ 2((r >> 2) & 3), so the four key rows of one read hit distinct bank
+// groups.  P goes in as two bf16 parts (hi + lo), keeping the float32 softmax
+// weights to about 16 bits.  The query fragments sit in LDS, shared by the
+// four waves.  Online softmax runs per query column (shuffles across the four
+// lane groups); the four waves are merged pairwise through LDS at the end.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+SPEC_DEV uint2 pack4(const float (&v)[4]) {
+  return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                    (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
 }
 
-template <int CH>
-SPEC_DEV int k_swz(int r) {
-  return CH == 16 ? (r & 15) : ((r >> 1) & 7);
-}
 SPEC_DEV int v_swz(int r) { return 2 * ((r >> 2) & 3); }
 
 template <int HD, int QT>
-__global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_ctx_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     int64_t sseq, int64_t shead, int S, const int* __restrict__ ctx_len, const int* __restrict__ pos,
     int R, int nq, int nkv, int window, int chunk, float* __restrict__ part) {
   constexpr int DS = HD / 32;        // 32-dim steps of S^T
   constexpr int DT = HD / 16;        // 16-dim tiles of O^T
   constexpr int CH = HD / 8;         // 16-byte chunks per row
-  constexpr int BLK = 32 * CH;       // 16-byte units per 32-row block
-  constexpr int NI = BLK / 64;       // DMA instructions per block (K or V)
+  constexpr int BLK = 16 * CH;       // 16-byte units per 16-row V block
+  constexpr int NI = BLK / 64;       // DMA instructions per V block
+  constexpr int NL = DS + NI;        // vector loads per block (K fragments + V DMA)
   static_assert(HD == 64 || HD == 128, "head dim");
-  static_assert(2 * QT * DT * 64 * 16 <= 4 * BLK * 16, "merge buffer fits in a K stage");
-  // two stages, one LDS object each for K and V; a wave owns BLK units of each
-  __shared__ u32x4_t k0s[4 * BLK], k1s[4 * BLK], v0s[4 * BLK], v1s[4 * BLK];
+  // two V stages, one LDS object each; a wave owns BLK units of each
+  __shared__ u32x4_t v0s[4 * BLK], v1s[4 * BLK];
+  // query fragments (B operand of S^T), [t][ds][lane], shared by the waves
+  __shared__ u32x4_t qsh[QT * DS * 64];
+  // merge buffers: [2][QT][DT][64] accumulators, [2][QT][64] max and sum
+  __shared__ f32x4 mo[2 * QT * DT * 64];
+  __shared__ float mm[2 * QT * 64], ml[2 * QT * 64];
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int nch = gridDim.x;
   const int G = nq / nkv, QV = R * G;
   const int lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const float scale = 1.0f / sqrtf((float)HD);
+  // scores in log2 units (x * log2 e / sqrt(hd)), so the softmax uses the
+  // hardware exp2; the records store the running max back in natural units
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);
 
   const int ctx = clampi(ctx_len[b], 0, S);
   int minpos = 0x7fffffff;
@@ -322,22 +323,24 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
   const int start = window > 0 ? max(0, minpos - window + 1) : 0;
   const int k0 = start + c * chunk;
   const int k1 = min(ctx, k0 + chunk);
-  const int first = k0 + wave * 32;
-  const int nblk = first < k1 ? (k1 - first + 127) / 128 : 0;
+  const int first = k0 + wave * 16;
+  const int nblk = first < k1 ? (k1 - first + 63) / 64 : 0;
 
-  u32x4_t qf[QT][DS];
   int loq[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int qv = t * 16 + col;
     const bool ok = qv < QV;
     const int r = ok ? qv / G : 0, h = kvh * G + (ok ? qv % G : 0);
-    const bf16_t* qp = q + ((int64_t)(b * R + r) * nq + h) * HD + g * 8;
+    if (wave == 0) {
+      const bf16_t* qp = q + ((int64_t)(b * R + r) * nq + h) * HD + g * 8;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-      qf[t][ds] = ok ? *(const u32x4_t*)(qp + ds * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      for (int ds = 0; ds < DS; ++ds)
+        qsh[(t * DS + ds) * 64 + lane] = ok ? *(const u32x4_t*)(qp + ds * 32) : u32x4_t{0u, 0u, 0u, 0u};
+    }
     loq[t] = ok ? (window > 0 ? max(0, pos[b * R + r] - window + 1) : 0) : 0x7fffffff;
   }
+  __syncthreads();
   float mrun[QT], lrun[QT];
   f32x4 o[QT][DT];
 #pragma unroll
@@ -350,97 +353,67 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
   const bf16_t* kb = kc + b * sseq + kvh * shead;
   const bf16_t* vb = vc + b * sseq + kvh * shead;
 
-  // DMA sources: unit u of a block is row u / CH at position u % CH
-  int krow[NI], kch[NI], vch[NI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int u = j * 64 + lane, row = u / CH, p = u % CH;
-    krow[j] = row;
-    kch[j] = p ^ k_swz<CH>(row);
-    vch[j] = p ^ v_swz(row);
-  }
-  auto kbuf = [](auto sc) -> SPEC_LDS u32x4_t* {
-    if constexpr (decltype(sc)::value == 0) return (SPEC_LDS u32x4_t*)k0s;
-    else return (SPEC_LDS u32x4_t*)k1s;
-  };
   auto vbuf = [](auto sc) -> SPEC_LDS u32x4_t* {
     if constexpr (decltype(sc)::value == 0) return (SPEC_LDS u32x4_t*)v0s;
     else return (SPEC_LDS u32x4_t*)v1s;
   };
-  // block i of this wave (past the end: the last block again, never read)
+  u32x4_t kf[2][DS];  // K fragments of the block in use and the one in flight
+  // block i of this wave (past the end: the last block again, never used)
   auto issue = [&](auto sc, int i) {
-    const int base = first + min(i, max(nblk - 1, 0)) * 128;
+    constexpr int Q = decltype(sc)::value;
+    const int base = first + min(i, max(nblk - 1, 0)) * 64;
+    const int kmax = max(k1 - 1, 0);
+    const bf16_t* kp = kb + (int64_t)min(base + col, kmax) * HD + g * 8;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) kf[Q][ds] = *(const u32x4_t*)(kp + ds * 32);
+    // V DMA: unit u of a block is row u / CH at position u % CH, holding
+    // chunk (u % CH) ^ v_swz(row)
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int key = min(base + krow[j], max(k1 - 1, 0));
-      dma16(kb + (int64_t)key * HD + kch[j] * 8, kbuf(sc) + wave * BLK + j * 64);
-      dma16(vb + (int64_t)key * HD + vch[j] * 8, vbuf(sc) + wave * BLK + j * 64);
+      const int u = j * 64 + lane, row = u / CH;
+      const int key = min(base + row, kmax);
+      dma16(vb + (int64_t)key * HD + ((u % CH) ^ v_swz(row)) * 8, vbuf(sc) + wave * BLK + j * 64);
     }
   };
 
   auto block = [&](auto sc, auto sn, int i) {
+    constexpr int Q = decltype(sc)::value;
     // refill the other stage (read by this wave's previous block, whose LDS
-    // reads have completed), then wait for this block's DMA only
-    wait_vm_lgkm0<2 * NI>();
+    // reads have completed), then wait for this block's loads only
+    wait_vm_lgkm0<NL>();
     asm volatile("" ::: "memory");
     issue(sn, i + 1);
-    wait_vm_lgkm0<2 * NI>();
+    wait_vm_lgkm0<NL>();
     asm volatile("" ::: "memory");
     if (i >= nblk) return;
-    const int kb0 = first + i * 128;
-    const SPEC_LDS u32x4_t* ks = kbuf(sc) + wave * BLK;
+    const int kb0 = first + i * 64;
     const SPEC_LDS bf16_t* vs = (const SPEC_LDS bf16_t*)(vbuf(sc) + wave * BLK);
-    f32x4 sc4[2][QT];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int row = kt * 16 + col;
-      u32x4_t kf[DS];
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) kf[ds] = ks[row * CH + ((ds * 4 + g) ^ k_swz<CH>(row))];
-#pragma unroll
-      for (int t = 0; t < QT; ++t) {
-        sc4[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-          sc4[kt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[ds]),
-                                                               __builtin_bit_cast(bf16x8, qf[t][ds]),
-                                                               sc4[kt][t], 0, 0, 0);
-      }
-    }
-    // V^T fragments: keys 4g+e (e < 4) and 16+4g+e-4 at dim dt*16 + col
-    u32x4_t vf[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int chn = (dt * 16 + col) >> 3, el = (dt * 16 + col) & 7;
-      uint32_t h16[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
-        h16[e] = vs[(row * CH + (chn ^ v_swz(row))) * 8 + el];
-      }
-      vf[dt] = u32x4_t{h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16), h16[4] | (h16[5] << 16),
-                       h16[6] | (h16[7] << 16)};
-    }
+    uint2 pf[QT], pl[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      float v[8];
+      f32x4 sc4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        sc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, kf[Q][ds]),
+            __builtin_bit_cast(bf16x8, qsh[(t * DS + ds) * 64 + lane]), sc4, 0, 0, 0);
+      float v[4];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = kb0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-        const float x = (e < 4 ? sc4[0][t][e] : sc4[1][t][e - 4]) * scale;
-        v[e] = (key < k1 && key >= loq[t]) ? x : -INFINITY;
+      for (int e = 0; e < 4; ++e) {
+        const int key = kb0 + 4 * g + e;
+        v[e] = (key < k1 && key >= loq[t]) ? sc4[e] * scale : -INFINITY;
         tmax = fmaxf(tmax, v[e]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mnew = fmaxf(mrun[t], tmax);
-      const float alpha =
-          mrun[t] == -INFINITY ? (mnew == -INFINITY ? 1.f : 0.f) : expf(mrun[t] - mnew);
+      const float alpha = mrun[t] == -INFINITY ? (mnew == -INFINITY ? 1.f : 0.f)
+                                               : __builtin_amdgcn_exp2f(mrun[t] - mnew);
       float psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v[e] = v[e] == -INFINITY ? 0.f : expf(v[e] - mnew);
+      for (int e = 0; e < 4; ++e) {
+        v[e] = v[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[e] - mnew);
         psum += v[e];
       }
       psum += __shfl_xor(psum, 16, 64);
@@ -449,23 +422,38 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
       mrun[t] = mnew;
       // P = P_hi + P_lo in two bf16 parts (about 16 significant bits), so the
       // products with V carry the float32 softmax weights, not bf16-rounded ones
-      float vlo[8];
-      const u32x4_t pf = pack8(v);
+      pf[t] = pack4(v);
+      float vlo[4];
+      vlo[0] = v[0] - __uint_as_float(pf[t].x << 16);
+      vlo[1] = v[1] - __uint_as_float(pf[t].x & 0xffff0000u);
+      vlo[2] = v[2] - __uint_as_float(pf[t].y << 16);
+      vlo[3] = v[3] - __uint_as_float(pf[t].y & 0xffff0000u);
+      pl[t] = pack4(vlo);
+      // the accumulators need rescaling only when some query's max moved
+      if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t h = (pf[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-        vlo[e] = v[e] - __uint_as_float(h << 16);
+        for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
       }
-      const u32x4_t pl = pack8(vlo);
+    }
+    // V^T fragment of dims dt*16 + col: keys 4g..4g+3
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        o[t][dt] *= alpha;
-        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
-                                                           __builtin_bit_cast(bf16x8, pf), o[t][dt],
-                                                           0, 0, 0);
-        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
-                                                           __builtin_bit_cast(bf16x8, pl), o[t][dt],
-                                                           0, 0, 0);
+    for (int dt = 0; dt < DT; ++dt) {
+      const int chn = (dt * 16 + col) >> 3, el = (dt * 16 + col) & 7;
+      uint32_t h16[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 4 * g + e;
+        h16[e] = vs[(row * CH + (chn ^ v_swz(row))) * 8 + el];
+      }
+      const uint2 vf = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vf),
+                                                            __builtin_bit_cast(s16x4, pf[t]),
+                                                            o[t][dt], 0, 0, 0);
+        o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vf),
+                                                            __builtin_bit_cast(s16x4, pl[t]),
+                                                            o[t][dt], 0, 0, 0);
       }
     }
   };
@@ -479,12 +467,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
     }
   }
   wait_vm_lgkm0<0>();  // the repeated loads past the end
-  __syncthreads();
 
-  // merge waves pairwise through LDS (the K stages are free now): (2,3) -> (0,1), then 1 -> 0
-  f32x4* mo = (f32x4*)k0s;    // [2][QT][DT][64]
-  float* mm = (float*)v0s;    // [2][QT][64]
-  float* ml = mm + 2 * QT * 64;
+  // merge waves pairwise through LDS: (2,3) -> (0,1), then 1 -> 0
 #pragma unroll
   for (int round = 0; round < 2; ++round) {
     const int half = round == 0 ? 2 : 1;
@@ -504,8 +488,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
       for (int t = 0; t < QT; ++t) {
         const float mb = mm[(wave * QT + t) * 64 + lane], lb = ml[(wave * QT + t) * 64 + lane];
         const float M = fmaxf(mrun[t], mb);
-        const float ea = mrun[t] == -INFINITY ? 0.f : expf(mrun[t] - M);
-        const float eb = mb == -INFINITY ? 0.f : expf(mb - M);
+        const float ea = mrun[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[t] - M);
+        const float eb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - M);
         lrun[t] = lrun[t] * ea + lb * eb;
         mrun[t] = M;
 #pragma unroll
@@ -527,7 +511,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) rec[dt * 16 + 4 * g + i] = o[t][dt][i];
       if (g == 0) {
-        rec[HD] = mrun[t];
+        rec[HD] = mrun[t] * 0.6931471805599453f;  // log2 units -> natural
         rec[HD + 1] = lrun[t];
       }
     }
@@ -571,12 +555,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 void attn_plan(int B, int nkv, int slots, int window, int* nchunks, int* chunk) {
   const int span = window > 0 ? std::min(window, slots) : slots;
   const int units = std::max(1, B * nkv);
-  // about one workgroup per CU (the bf16 kernel holds 128 KB of LDS)
-  int nc = (256 + units - 1) / units;
-  const int max_nc = std::max(1, (span + 127) / 128);  // at least one 32-key block per wave
+  // about two workgroups per CU (the bf16 kernel holds 74 KB of LDS)
+  int nc = (512 + units - 1) / units;
+  const int max_nc = std::max(1, (span + 63) / 64);  // at least one 16-key block per wave
   nc = std::max(1, std::min(nc, max_nc));
   int ch = (span + nc - 1) / nc;
-  ch = (ch + 127) / 128 * 128;  // whole 32-key blocks for each of the 4 waves
+  ch = (ch + 63) / 64 * 64;  // whole 16-key blocks for each of the 4 waves
   *chunk = ch;
   *nchunks = (span + ch - 1) / ch;
 }
