@@ -264,11 +264,12 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
 
 // ---- bf16 context attention on MFMA -----------------------------------------
 // Each wave walks blocks of 16 keys, wave w taking blocks w, w + 4, ... of the
-// chunk, one block ahead of use: the K rows load straight into registers in
-// MFMA fragment layout, the V rows go into a wave-private LDS stage by
-// global_load_lds_dwordx4 (two stages per wave, 32 KB per workgroup at hd
-// 128), so the key loop has no workgroup barrier, every load is 16 bytes wide
-// and several workgroups share a CU.
+// chunk, one block ahead of use: the V rows go into a wave-private LDS stage
+// by global_load_lds_dwordx4 (two stages per wave, 32 KB per workgroup at hd
+// 128) and the K rows load straight into registers in MFMA fragment layout as
+// soon as the previous block's scores are done, so the key loop has no
+// workgroup barrier, every load is 16 bytes wide and several workgroups share
+// a CU.
 // S^T = K . Q^T (16x16x32 bf16 MFMA) takes K rows as the A operand (lane:
 // key = lane&15, 8 dims at 8*(lane>>4)) and the query vectors as B, so the
 // score tile lands with key 4*(lane>>4)+i and query column lane&15 - exactly
@@ -290,7 +291,7 @@ SPEC_DEV uint2 pack4(const float (&v)[4]) {
 SPEC_DEV int v_swz(int r) { return 2 * ((r >> 2) & 3); }
 
 template <int HD, int QT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_ctx_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_ctx_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     int64_t sseq, int64_t shead, int S, const int* __restrict__ ctx_len, const int* __restrict__ pos,
     int R, int nq, int nkv, int window, int chunk, float* __restrict__ part) {
@@ -300,13 +301,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   constexpr int BLK = 16 * CH;       // 16-byte units per 16-row V block
   constexpr int NI = BLK / 64;       // DMA instructions per V block
   constexpr int NL = DS + NI;        // vector loads per block (K fragments + V DMA)
+  static_assert(NL < 64 && NI < 64, "vmcnt range");
   static_assert(HD == 64 || HD == 128, "head dim");
   // two V stages, one LDS object each; a wave owns BLK units of each
   __shared__ u32x4_t v0s[4 * BLK], v1s[4 * BLK];
   // query fragments (B operand of S^T), [t][ds][lane], shared by the waves
   __shared__ u32x4_t qsh[QT * DS * 64];
-  // merge buffers: [2][QT][DT][64] accumulators, [2][QT][64] max and sum
-  __shared__ f32x4 mo[2 * QT * DT * 64];
+  // merge buffers: [QT][DT][64] accumulators per slot (slot 0 in V stage 0,
+  // slot 1 in V stage 1, free after the key loop), [2][QT][64] max and sum
+  static_assert(QT * DT * 64 * 16 <= 4 * BLK * 16, "merge slot fits in a V stage");
   __shared__ float mm[2 * QT * 64], ml[2 * QT * 64];
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int nch = gridDim.x;
@@ -357,17 +360,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if constexpr (decltype(sc)::value == 0) return (SPEC_LDS u32x4_t*)v0s;
     else return (SPEC_LDS u32x4_t*)v1s;
   };
-  u32x4_t kf[2][DS];  // K fragments of the block in use and the one in flight
-  // block i of this wave (past the end: the last block again, never used)
-  auto issue = [&](auto sc, int i) {
-    constexpr int Q = decltype(sc)::value;
+  u32x4_t kf[DS];  // K fragments: loaded for block i + 1 once block i's scores are done
+  auto issue_k = [&](int i) {
+    const int base = first + min(i, max(nblk - 1, 0)) * 64;
+    const bf16_t* kp = kb + (int64_t)min(base + col, max(k1 - 1, 0)) * HD + g * 8;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) kf[ds] = *(const u32x4_t*)(kp + ds * 32);
+  };
+  // V rows of block i (past the end: the last block again, never used)
+  auto issue_v = [&](auto sc, int i) {
     const int base = first + min(i, max(nblk - 1, 0)) * 64;
     const int kmax = max(k1 - 1, 0);
-    const bf16_t* kp = kb + (int64_t)min(base + col, kmax) * HD + g * 8;
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) kf[Q][ds] = *(const u32x4_t*)(kp + ds * 32);
-    // V DMA: unit u of a block is row u / CH at position u % CH, holding
-    // chunk (u % CH) ^ v_swz(row)
+    // unit u of a block is row u / CH at position u % CH, holding chunk
+    // (u % CH) ^ v_swz(row)
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int u = j * 64 + lane, row = u / CH;
@@ -377,32 +382,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   };
 
   auto block = [&](auto sc, auto sn, int i) {
-    constexpr int Q = decltype(sc)::value;
-    // refill the other stage (read by this wave's previous block, whose LDS
-    // reads have completed), then wait for this block's loads only
+    // refill the other V stage (read by this wave's previous block, whose LDS
+    // reads have completed) with block i + 1, then wait for everything issued
+    // before it: this block's V stage and K fragments
     wait_vm_lgkm0<NL>();
     asm volatile("" ::: "memory");
-    issue(sn, i + 1);
-    wait_vm_lgkm0<NL>();
+    issue_v(sn, i + 1);
+    wait_vm_lgkm0<NI>();
     asm volatile("" ::: "memory");
     if (i >= nblk) return;
     const int kb0 = first + i * 64;
     const SPEC_LDS bf16_t* vs = (const SPEC_LDS bf16_t*)(vbuf(sc) + wave * BLK);
+    f32x4 sc4[QT];
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      sc4[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        sc4[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, kf[ds]),
+            __builtin_bit_cast(bf16x8, qsh[(t * DS + ds) * 64 + lane]), sc4[t], 0, 0, 0);
+    }
+    issue_k(i + 1);  // the K fragments are consumed
     uint2 pf[QT], pl[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      f32x4 sc4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        sc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, kf[Q][ds]),
-            __builtin_bit_cast(bf16x8, qsh[(t * DS + ds) * 64 + lane]), sc4, 0, 0, 0);
       float v[4];
       float tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = kb0 + 4 * g + e;
-        v[e] = (key < k1 && key >= loq[t]) ? sc4[e] * scale : -INFINITY;
+        v[e] = (key < k1 && key >= loq[t]) ? sc4[t][e] * scale : -INFINITY;
         tmax = fmaxf(tmax, v[e]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -460,13 +470,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   if (nblk > 0) {
-    issue(S0{}, 0);
+    issue_v(S0{}, 0);
+    issue_k(0);
     for (int i = 0; i < nblk; i += 2) {
       block(S0{}, S1{}, i);
       block(S1{}, S0{}, i + 1);
     }
   }
   wait_vm_lgkm0<0>();  // the repeated loads past the end
+  __syncthreads();      // every wave is done with the V stages
+  f32x4* const mo0 = (f32x4*)v0s;
+  f32x4* const mo1 = (f32x4*)v1s;
 
   // merge waves pairwise through LDS: (2,3) -> (0,1), then 1 -> 0
 #pragma unroll
@@ -478,8 +492,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int t = 0; t < QT; ++t) {
         mm[(slot * QT + t) * 64 + lane] = mrun[t];
         ml[(slot * QT + t) * 64 + lane] = lrun[t];
+        f32x4* mo = slot ? mo1 : mo0;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) mo[((slot * QT + t) * DT + dt) * 64 + lane] = o[t][dt];
+        for (int dt = 0; dt < DT; ++dt) mo[(t * DT + dt) * 64 + lane] = o[t][dt];
       }
     }
     __syncthreads();
@@ -492,9 +507,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         const float eb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - M);
         lrun[t] = lrun[t] * ea + lb * eb;
         mrun[t] = M;
+        const f32x4* mo = wave ? mo1 : mo0;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          o[t][dt] = o[t][dt] * ea + mo[((wave * QT + t) * DT + dt) * 64 + lane] * eb;
+        for (int dt = 0; dt < DT; ++dt) o[t][dt] = o[t][dt] * ea + mo[(t * DT + dt) * 64 + lane] * eb;
       }
     }
     __syncthreads();
@@ -555,9 +570,10 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 void attn_plan(int B, int nkv, int slots, int window, int* nchunks, int* chunk) {
   const int span = window > 0 ? std::min(window, slots) : slots;
   const int units = std::max(1, B * nkv);
-  // about two workgroups per CU (the bf16 kernel holds 74 KB of LDS)
+  // about two workgroups per CU; chunks of at least 128 keys (two 16-key
+  // blocks per wave), so the combine step has few records per row to merge
   int nc = (512 + units - 1) / units;
-  const int max_nc = std::max(1, (span + 63) / 64);  // at least one 16-key block per wave
+  const int max_nc = std::max(1, (span + 127) / 128);
   nc = std::max(1, std::min(nc, max_nc));
   int ch = (span + nc - 1) / nc;
   ch = (ch + 63) / 64 * 64;  // whole 16-key blocks for each of the 4 waves
