@@ -46,7 +46,9 @@ def lm_head_bytes(cfg, M):
     normed rows in; out, the float32 logits, or - when the vocab top-k is fused
     into the launch (bf16 weight streaming at M <= 64, unsplit: Vd >= 65536, or
     column strips filling the grid) - one (top-k list, max, sum) record per row
-    and column strip.  EAGLE-4: the low-rank score GEMM, scores out."""
+    and column strip; beyond 64 rows (tiled head) the logits plus one (max,
+    sum exp) record per row and 128-column strip.  EAGLE-4: the low-rank
+    score GEMM, scores out."""
     H = cfg["hidden"]
     if cfg["cand_rank"]:
         r, V = cfg["cand_rank"], cfg["vocab"]
@@ -58,6 +60,8 @@ def lm_head_bytes(cfg, M):
     unsplit = Vd >= 65536 or strips * -(-M // 64) >= (1024 if cw1 else 2048)
     fused = cfg["dtype"] == "bf16" and k <= 8 and M <= 64 and unsplit
     out = M * strips * (8 * (1 if k == 1 else 8) + 16) if fused else M * Vd * 4
+    if cfg["dtype"] == "bf16" and M > 64 and k <= 8:
+        out += M * -(-Vd // 128) * 8   # per-strip (max, sum) records of the tiled head
     return Vd * H * 2 + M * H * 2 + out
 
 

@@ -5,9 +5,11 @@
 // so each weight tile is read from HBM once for all BM rows, and walks K in
 // BK-wide stages that global_load_lds_dwordx4 brings straight into LDS.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
+#include "topk_common.h"
 
 namespace spec {
 
@@ -23,19 +25,78 @@ namespace {
 // Synchronisation is a raw s_waitcnt vmcnt lgkmcnt(0) + s_barrier (a
 // workgroup fence would drain every stage in flight; lgkmcnt(0) makes the
 // reads of the stage before complete, so the refill after the barrier cannot
-// overtake them), with compiler fences so that no LDS access moves across it.  Each stage lives in its own LDS object
-// and every wave issues the same DMA count per stage, unconditionally (past
-// the end the last stage is loaded again), so the compiler can tell a stage's
-// reads from the other stages' DMA and adds no wait of its own.
+// overtake them), with compiler fences so that no LDS access moves across it.
+// Each stage lives in its own LDS object and every wave issues the same DMA
+// count per stage, unconditionally (past the last step the last stage is
+// loaded again), so the compiler can tell a stage's reads from the other
+// stages' DMA and adds no wait of its own.
 template <int CH>
 SPEC_DEV int chunk_swz(int row) {
   return CH == 4 ? (row >> 2) & 3 : (row >> 1) & 7;
 }
 
-template <int BN, int BM, int BK, int NTH, int NS>
+// s_waitcnt lgkmcnt(0) with no vector-memory wait (vmcnt and expcnt at their
+// maxima).
+SPEC_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+SPEC_DEV void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int... I, class F>
+SPEC_DEV void unroll_seq(std::integer_sequence<int, I...>, F f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// One output tile: weight rows n0.., X rows m0.., K range k0 .. k0 + T * BK.
+struct TileGeo {
+  int n0, m0, k0, T, split, strip;
+};
+
+// Tile t of the launch: t = split * (strips * row blocks) + r.  Workgroups are
+// dealt to the 8 XCDs round-robin, so block ids b and b + 8 share an XCD (and
+// its L2); with a grid that is a multiple of 8 the same holds for the tiles
+// t and t + 8 that a persistent block takes in turn.  The row blocks of one
+// weight strip get r values 8 apart, so they run together on one XCD and the
+// strip is read from HBM once.
+template <int BN, int BM, int BK>
+SPEC_DEV TileGeo tile_geo(int t, int M, int N, int K, int kc) {
+  const int nstrip = (N + BN - 1) / BN, nmb = (M + BM - 1) / BM, per = nstrip * nmb;
+  TileGeo q;
+  q.split = t / per;
+  const int r = t - q.split * per;
+  int strip = r, mb = 0;
+  if (nmb > 1) {
+    const int grp = r / (8 * nmb), rem = r % (8 * nmb);
+    strip = grp * 8 + rem % 8;
+    mb = rem / 8;
+    if (strip >= nstrip) {  // the last group is short: spread its ids over what is left
+      const int base = (nstrip / 8) * 8, left = nstrip - base;
+      const int u = r - base * nmb;
+      strip = base + u % left;
+      mb = u / left;
+    }
+  }
+  q.strip = strip;
+  q.n0 = strip * BN;
+  q.m0 = mb * BM;
+  q.k0 = q.split * kc;
+  q.T = (min(K, q.k0 + kc) - q.k0) / BK;
+  return q;
+}
+
+// PERSIST (more tiles than CUs): block b takes the tiles b, b + G, b + 2G, ...
+// (G = grid size) and runs their K steps as one stream, so the DMA of the next
+// tile's first stages is in flight while a tile's results are written out.
+// Otherwise every block owns one tile.
+// REC (unsplit launches, BN = 128): also write, per row and BN-column strip,
+// the record (max, sum of exp(v - max)) that the vocab top-k merges.
+template <int BN, int BM, int BK, int NTH, int NS, bool REC, bool PERSIST>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
     const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W, int ldw,
-    float* __restrict__ P, int M, int N, int K, int kc) {
+    float* __restrict__ P, int M, int N, int K, int kc, int ntiles, float2* __restrict__ rec) {
   constexpr int NWAVE = NTH / 64;
   constexpr int WGN = BN / 64, WGM = NWAVE / WGN;  // wave grid
   constexpr int WM = BM / WGM;                     // X rows per wave
@@ -47,54 +108,49 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   constexpr int NW = (IW + NWAVE - 1) / NWAVE, NX = (IX + NWAVE - 1) / NWAVE, NI = NW + NX;
   static_assert(FB >= 1 && WGN * WGM == NWAVE && BM % (16 * WGM) == 0, "tile shape");
   static_assert((BK == 32 || BK == 64) && NS >= 2 && NS <= 4, "stages");
+  static_assert(!REC || WGN == 2, "strip records assume two waves across the strip");
   // one LDS object per stage
-  __shared__ u32x4_t w0[BN * CH], w1[BN * CH], w2[NS > 2 ? BN * CH : 1], w3[NS > 3 ? BN * CH : 1];
+  // (with three stages the fourth object holds the records' exchange: the
+  // (max, sum) of the wn = 1 half of each row)
+  static_assert(!REC || NS < 4, "record exchange lives in the unused fourth stage");
+  __shared__ u32x4_t w0[BN * CH], w1[BN * CH], w2[NS > 2 ? BN * CH : 1],
+      w3[NS > 3 ? BN * CH : (REC ? BM / 2 : 1)];
   __shared__ u32x4_t x0[BM * CH], x1[BM * CH], x2[NS > 2 ? BM * CH : 1], x3[NS > 3 ? BM * CH : 1];
+  float2* const xr = (float2*)w3;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wn = wave % WGN, wm = wave / WGN;
   const int g = lane >> 4, c = lane & 15;
-  // Block order: workgroups are dealt to the 8 XCDs round-robin, so ids b and
-  // b + 8 share an XCD (and its L2).  The row blocks of one weight strip get
-  // ids 8 apart and run together there, and the strip is read from HBM once.
-  // The grid is (strips x row blocks, splits): blockIdx.x carries both.
-  const int nstrip = (N + BN - 1) / BN, nmb = (M + BM - 1) / BM;
-  int strip = blockIdx.x, mb = 0;
-  if (nmb > 1) {
-    const int b = blockIdx.x;
-    const int grp = b / (8 * nmb), rem = b % (8 * nmb);
-    strip = grp * 8 + rem % 8;
-    mb = rem / 8;
-    if (strip >= nstrip) {  // the last group is short: spread its ids over what is left
-      const int base = (nstrip / 8) * 8, left = nstrip - base;
-      const int q = b - base * nmb;
-      strip = base + q % left;
-      mb = q / left;
-    }
-  }
-  const int n0 = strip * BN, m0 = mb * BM;
-  const int k0 = blockIdx.y * kc, k1 = min(K, k0 + kc);
-  const int T = max(0, (k1 - k0) / BK);
+  const int G = gridDim.x, b0 = blockIdx.x;
+  // tiles of this block (the grid is <= ntiles; one each unless PERSIST)
+  const int J = PERSIST ? (ntiles - 1 - b0) / G + 1 : 1;
+  const int nstrip = (N + BN - 1) / BN;
 
-  // DMA sources: LDS unit u (row u / CH, position u % CH) holds chunk
-  // (u % CH) ^ swz(row)
-  const bf16_t* gw[NW];
-  const bf16_t* gx[NX];
-  int uw[NW], ux[NX];
+  // DMA slots: LDS unit u (row u / CH, position u % CH) holds chunk
+  // (u % CH) ^ swz(row) of that row
+  int uw[NW], ux[NX], rw[NW], rx[NX], ow[NW], ox[NX];
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
     uw[j] = ((wave * NW + j) % IW) * 64;
-    const int u = uw[j] + lane, row = u / CH;
-    const int ch = (u % CH) ^ chunk_swz<CH>(row);
-    gw[j] = W + (int64_t)min(n0 + row, N - 1) * ldw + k0 + ch * 8;
+    const int u = uw[j] + lane;
+    rw[j] = u / CH;
+    ow[j] = ((u % CH) ^ chunk_swz<CH>(rw[j])) * 8;
   }
 #pragma unroll
   for (int j = 0; j < NX; ++j) {
     ux[j] = ((wave * NX + j) % IX) * 64;
-    const int u = ux[j] + lane, row = u / CH;
-    const int ch = (u % CH) ^ chunk_swz<CH>(row);
-    gx[j] = X + (int64_t)min(m0 + row, M - 1) * ldx + k0 + ch * 8;
+    const int u = ux[j] + lane;
+    rx[j] = u / CH;
+    ox[j] = ((u % CH) ^ chunk_swz<CH>(rx[j])) * 8;
   }
+  const bf16_t* gw[NW];
+  const bf16_t* gx[NX];
+  auto point = [&](const TileGeo& q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) gw[j] = W + (int64_t)min(q.n0 + rw[j], N - 1) * ldw + q.k0 + ow[j];
+#pragma unroll
+    for (int j = 0; j < NX; ++j) gx[j] = X + (int64_t)min(q.m0 + rx[j], M - 1) * ldx + q.k0 + ox[j];
+  };
   auto wbuf = [](auto sc) -> SPEC_LDS u32x4_t* {
     constexpr int S = decltype(sc)::value;
     if constexpr (S == 0) return (SPEC_LDS u32x4_t*)w0;
@@ -109,12 +165,29 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     else if constexpr (S == 2) return (SPEC_LDS u32x4_t*)x2;
     else return (SPEC_LDS u32x4_t*)x3;
   };
-  auto issue = [&](auto sc, int i) {
-    const int k = min(i, T - 1) * BK;
+
+  int S = 0;  // K steps of all the block's tiles
+  for (int j = 0; j < J; ++j) S += tile_geo<BN, BM, BK>(b0 + j * G, M, N, K, kc).T;
+  // issue cursor: tile ij of the block, K step ii; it stays on the last step
+  // once the block's stream is exhausted
+  int ij = 0, ii = 0;
+  TileGeo iq = tile_geo<BN, BM, BK>(b0, M, N, K, kc);
+  const TileGeo q0 = iq;
+  point(iq);
+  auto issue = [&](auto sc) __attribute__((always_inline)) {
+    const int k = ii * BK;
 #pragma unroll
     for (int j = 0; j < NW; ++j) dma16(gw[j] + k, wbuf(sc) + uw[j]);
 #pragma unroll
     for (int j = 0; j < NX; ++j) dma16(gx[j] + k, xbuf(sc) + ux[j]);
+    if (ii + 1 < iq.T) {
+      ++ii;
+    } else if (ij + 1 < J) {
+      ++ij;
+      ii = 0;
+      iq = tile_geo<BN, BM, BK>(b0 + ij * G, M, N, K, kc);
+      point(iq);
+    }
   };
 
   f32x4 acc[FA][FB];
@@ -125,17 +198,97 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   const int sw = chunk_swz<CH>(c);  // rows of a fragment start at multiples of 16
   const int rowa = (wn * 64 + c) * CH, rowb = (wm * WM + c) * CH;
 
-  // stage i: wait for this wave's DMA of stage i (the NS - 2 stages after it
-  // may still be pending), barrier (every wave's DMA of stage i has landed and
-  // every wave is done reading stage i - 1), refill stage i - 1's buffer with
-  // stage i + NS - 1, compute stage i.  Past T only the refill runs.
-  auto step = [&](auto sc, auto sn, int i) {
+  // lane holds Y[m0 + wm*WM + 16b + c][n0 + wn*64 + 16a + 4g + r]
+  auto epilogue = [&](const TileGeo& q) __attribute__((always_inline)) {
+    float* Pb = P + (int64_t)q.split * M * N;
+#pragma unroll
+    for (int b = 0; b < FB; ++b) {
+      const int m = q.m0 + wm * WM + 16 * b + c;
+      if (m >= M) continue;
+#pragma unroll
+      for (int a = 0; a < FA; ++a) {
+        const int n = q.n0 + wn * 64 + 16 * a + 4 * g;
+        float* dst = Pb + (int64_t)m * N + n;
+        if (n + 3 < N && (N & 3) == 0) {
+          *(float4*)dst = make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) dst[r] = acc[a][b][r];
+        }
+      }
+    }
+    if constexpr (REC) {
+      // (max, sum exp) per row over the strip: the lane's 16 values, the four
+      // lane groups of the wave by shuffles, the two waves of a row via LDS
+      constexpr float kL2e = 1.4426950408889634f;
+      const bool full = q.n0 + BN <= N;
+      const int nl = N - (q.n0 + wn * 64 + 4 * g);  // this lane's columns below N: 16a + r < nl
+      float rm[FB], rs[FB];
+#pragma unroll
+      for (int b = 0; b < FB; ++b) {
+        float m = -INFINITY, sum = 0.f;
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (full || 16 * a + r < nl) m = fmaxf(m, acc[a][b][r]);
+        if (m != -INFINITY) {
+          const float mo = m * kL2e;
+#pragma unroll
+          for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (full || 16 * a + r < nl)
+                sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[a][b][r], kL2e, -mo));
+        }
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+          const float om = __shfl_xor(m, o, 64), os = __shfl_xor(sum, o, 64);
+          const float nm = fmaxf(m, om);
+          if (nm != -INFINITY)
+            sum = (m == -INFINITY ? 0.f : sum * __builtin_amdgcn_exp2f((m - nm) * kL2e)) +
+                  (om == -INFINITY ? 0.f : os * __builtin_amdgcn_exp2f((om - nm) * kL2e));
+          m = nm;
+        }
+        rm[b] = m;
+        rs[b] = sum;
+        if (wn == 1 && g == 0) xr[wm * WM + 16 * b + c] = make_float2(m, sum);
+      }
+      wait_lgkm0();
+      block_barrier();
+      if (wn == 0 && g == 0) {
+#pragma unroll
+        for (int b = 0; b < FB; ++b) {
+          const int row = wm * WM + 16 * b + c, m = q.m0 + row;
+          const float2 o = xr[row];
+          const float nm = fmaxf(rm[b], o.x);
+          float sum = 0.f;
+          if (nm != -INFINITY)
+            sum = (rm[b] == -INFINITY ? 0.f : rs[b] * __builtin_amdgcn_exp2f((rm[b] - nm) * kL2e)) +
+                  (o.x == -INFINITY ? 0.f : o.y * __builtin_amdgcn_exp2f((o.x - nm) * kL2e));
+          if (m < M) rec[(int64_t)m * nstrip + q.strip] = make_float2(nm, sum);
+        }
+      }
+    }
+  };
+
+  // K step s of the block's stream: wait for this wave's DMA of step s (the
+  // NS - 2 steps after it may still be pending), barrier (every wave's DMA of
+  // step s has landed and every wave is done reading the previous stage),
+  // refill the previous stage's buffer with step s + NS - 1, compute step s.
+  // After a tile's last step the tile is written out while the next tile's
+  // first stages load; then every access of the wave is waited for (loads and
+  // stores may complete out of order, so no partial count is safe past a
+  // store).  The block's last tile is written out after the stream, when no
+  // loads are left to overlap.
+  int ci = 0, cj = 0;
+  TileGeo cq = q0;
+  auto step = [&](auto sc, auto sn, int s) __attribute__((always_inline)) {
     wait_vm_lgkm0<(NS - 2) * NI>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue(sn, i + NS - 1);
-    if (i < T) {
+    block_barrier();
+    issue(sn);
+    if (s < S) {
 #pragma unroll
       for (int ks = 0; ks < BK / 32; ++ks) {
         const int pos = (ks * 4 + g) ^ sw;
@@ -152,57 +305,28 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
                                                                 __builtin_bit_cast(bf16x8, fb[b]),
                                                                 acc[a][b], 0, 0, 0);
       }
+      if (PERSIST && ++ci == cq.T && cj + 1 < J) {
+        epilogue(cq);
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+          for (int b = 0; b < FB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ci = 0;
+        cq = tile_geo<BN, BM, BK>(b0 + ++cj * G, M, N, K, kc);
+        wait_vm_lgkm0<0>();
+      }
     }
     asm volatile("" ::: "memory");
   };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  if (T > 0) {
-    issue(S0{}, 0);
-    if constexpr (NS == 4) {
-      issue(S1{}, 1);
-      issue(S2{}, 2);
-      for (int i = 0; i < T; i += 4) {
-        step(S0{}, S3{}, i);
-        step(S1{}, S0{}, i + 1);
-        step(S2{}, S1{}, i + 2);
-        step(S3{}, S2{}, i + 3);
-      }
-    } else if constexpr (NS == 3) {
-      issue(S1{}, 1);
-      for (int i = 0; i < T; i += 3) {
-        step(S0{}, S2{}, i);
-        step(S1{}, S0{}, i + 1);
-        step(S2{}, S1{}, i + 2);
-      }
-    } else {
-      for (int i = 0; i < T; i += 2) {
-        step(S0{}, S1{}, i);
-        step(S1{}, S0{}, i + 1);
-      }
-    }
-    wait_vm_lgkm0<0>();  // the repeated loads past the end
+  unroll_seq(std::make_integer_sequence<int, NS - 1>{}, [&](auto sc) { issue(sc); });
+  for (int s = 0; s < S; s += NS) {
+    unroll_seq(std::make_integer_sequence<int, NS>{}, [&](auto sc) {
+      constexpr int i = decltype(sc)::value;
+      step(sc, std::integral_constant<int, (i + NS - 1) % NS>{}, s + i);
+    });
   }
-  // lane holds Y[m0 + wm*WM + 16b + c][n0 + wn*64 + 16a + 4g + r]
-  float* Pb = P + (int64_t)blockIdx.y * M * N;
-#pragma unroll
-  for (int b = 0; b < FB; ++b) {
-    const int m = m0 + wm * WM + 16 * b + c;
-    if (m >= M) continue;
-#pragma unroll
-    for (int a = 0; a < FA; ++a) {
-      const int n = n0 + wn * 64 + 16 * a + 4 * g;
-      float* dst = Pb + (int64_t)m * N + n;
-      if (n + 3 < N && (N & 3) == 0) {
-        *(float4*)dst = make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
-      } else {
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) dst[r] = acc[a][b][r];
-      }
-    }
-  }
+  wait_vm_lgkm0<0>();  // the repeated loads past the end
+  epilogue(cq);        // the block's last tile
 }
 
 }  // namespace
@@ -228,14 +352,56 @@ GemmPlan gemm_tile_plan(int M, int N, int K) {
   return p;
 }
 
+namespace {
+
+// Persistent grid: one block per CU (a block takes 144 KB of LDS), a multiple
+// of 8 so that a block's successive tiles stay on one XCD.
+int tile_grid(int ntiles) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+      n = 8;
+    cus[dev] = n / 8 * 8;
+  }
+  return std::min(ntiles, cus[dev]);
+}
+
+template <bool REC>
+hipError_t launch_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
+                       int K, int kc, int nsplit, float2* rec, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K % kTileBK != 0 || kc % kTileBK != 0 || kc <= 0 || nsplit < 1 ||
+      (int64_t)(nsplit - 1) * kc >= K)
+    return hipErrorInvalidValue;
+  const int ntiles = ((N + kTileBN - 1) / kTileBN) * ((M + kTileBM - 1) / kTileBM) * nsplit;
+  const int grid = tile_grid(ntiles);
+  if (grid < ntiles)
+    hipLaunchKernelGGL(
+        (gemm_dma_kernel<kTileBN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, true>),
+        dim3(grid), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M,
+        N, K, kc, ntiles, rec);
+  else
+    hipLaunchKernelGGL(
+        (gemm_dma_kernel<kTileBN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, false>),
+        dim3(ntiles), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M,
+        N, K, kc, ntiles, rec);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N, int K,
                      const GemmPlan& plan, hipStream_t s) {
-  if (M <= 0 || N <= 0 || K % kTileBK != 0 || plan.kc % kTileBK != 0) return hipErrorInvalidValue;
-  const dim3 grid(((N + kTileBN - 1) / kTileBN) * ((M + kTileBM - 1) / kTileBM), plan.nsplit, 1);
-  hipLaunchKernelGGL((gemm_dma_kernel<kTileBN, kTileBM, kTileBK, kTileThreads, kTileStages>), grid,
-                     dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M,
-                     N, K, plan.kc);
-  return hipGetLastError();
+  return launch_tile<false>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit, nullptr, s);
+}
+
+int gemm_tile_strips(int N) { return (N + kTileBN - 1) / kTileBN; }
+
+hipError_t gemm_tile_records(const void* X, int ldx, const void* W, int ldw, float* z, int M,
+                             int N, int K, void* rec, hipStream_t s) {
+  return launch_tile<true>(X, ldx, W, ldw, z, M, N, K, K, 1, (float2*)rec, s);
 }
 
 }  // namespace spec

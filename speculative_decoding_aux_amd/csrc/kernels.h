@@ -19,6 +19,12 @@ bool gemm_tile_ok(int M, int K);
 GemmPlan gemm_tile_plan(int M, int N, int K);
 hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N, int K,
                      const GemmPlan& plan, hipStream_t s);
+// Unsplit tiled LM head: logits z[M, N] plus one record (max, sum of
+// exp(v - max)) per row and 128-column strip, float2 [M][strips], for the
+// vocab top-k.
+int gemm_tile_strips(int N);
+hipError_t gemm_tile_records(const void* X, int ldx, const void* W, int ldw, float* z, int M,
+                             int N, int K, void* rec, hipStream_t s);
 // tag 1 launches a separately named instance (the LM head and score GEMMs).
 hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
                 int K, const GemmPlan& plan, hipStream_t s, int tag = 0);
@@ -85,6 +91,11 @@ hipError_t topk(const float* z, int M, int n, int ldz, int k, const int* id_map,
 hipError_t topk_rows(const float* z, int M, int n, int ldz, int k, const int* id_map,
                      const int* rowmap, int* ids, int ldi, float* logp, int ldl, void* part,
                      int nch, int chunk, hipStream_t s);
+// Top-k (k <= 8) and log-probs from the strip records of gemm_tile_records
+// (strip width sw = 128 columns of the logits z[M, n]).
+hipError_t topk_merge_strips(const float* z, int M, int n, int k, int nstrip, int sw,
+                             const void* rec, const int* id_map, int* ids, int ldi, float* logp,
+                             int ldl, hipStream_t s);
 // Merge of the per-strip records written by the fused LM-head GEMM (km = 1 or 8
 // entries per record, layout as the topk partials): ids and log-probs per row.
 hipError_t topk_merge_records(int M, int n, int k, int km, int nch, void* part, const int* id_map,

@@ -186,6 +186,9 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
     const GemmPlan lp = gemm_plan(m, c.draft_vocab, H, true);
     if (bf16 && !c.cand_rank && lp.nsplit == 1 && !lp.tile)
       tk = std::max(tk, topk_part_bytes(m, gemm_strips(m, c.draft_vocab), 8));
+    // strip records of the tiled LM head (one per row and 128-column strip)
+    if (bf16 && !c.cand_rank && lp.nsplit == 1 && lp.tile)
+      tk = std::max(tk, (size_t)m * gemm_tile_strips(c.draft_vocab) * 8);
   }
   ctx->topk_bytes = tk;
   {
@@ -435,6 +438,19 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
       return SPEC_OK;
     }
     float* z = io.logits_out ? io.logits_out : ws.logits;
+    if (bf && p.tile && p.nsplit == 1 && io.k_out <= 8) {
+      // tiled LM head writing per-strip (max, sum exp) records; the top-k
+      // rescans only the k best strips of each row
+      {
+        ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
+        SPEC_HIP(ctx, gemm_tile_records(ws.nrm, H, w->lm_head, H, z, M, Vd, H, ws.topk_part, s));
+      }
+      ProfScope ps(ctx, SPEC_PROF_TOPK, s);
+      SPEC_HIP(ctx, topk_merge_strips(z, M, Vd, io.k_out, gemm_tile_strips(Vd), 128,
+                                      ws.topk_part, w->d2t, io.ids, io.ld_out, io.logp, io.ld_out,
+                                      s));
+      return SPEC_OK;
+    }
     if (p.nsplit == 1) {
       ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
       SPEC_HIP(ctx, gemm(bf, ws.nrm, H, w->lm_head, H, z, M, Vd, H, p, s, 1));

@@ -533,6 +533,132 @@ __global__ __launch_bounds__(256) void gather_dot_vec_kernel(const bf16_t* __res
   }
 }
 
+// Vocab top-k from the per-strip records (max, sum exp(v - max)) of the tiled
+// LM head, one 256-thread workgroup per row.  Strip order by (max desc, strip
+// asc) is the order of the strips' best elements by (value desc, id asc), so
+// the k best elements of the row lie in its k best strips: those are picked
+// from the records and only their k * 128 logits are rescanned.  The row
+// logsumexp comes from the records alone (merged across waves in float64).
+constexpr int kStripW = 128;
+
+template <int KM>
+__global__ __launch_bounds__(256) void topk_strip_merge_kernel(int n, int k, int nstrip,
+                                                               const float* __restrict__ z,
+                                                               const float2* __restrict__ rec,
+                                                               const int* __restrict__ id_map,
+                                                               int* __restrict__ ids, int ldi,
+                                                               float* __restrict__ logp, int ldl) {
+  constexpr float kL2e = 1.4426950408889634f;
+  __shared__ float sv[4 * KM];
+  __shared__ int si[4 * KM];
+  __shared__ float smax[4], ssum[4];
+  __shared__ int sel[KM];
+  const int r = blockIdx.x, t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const float2* pr = rec + (int64_t)r * nstrip;
+  const float* row = z + (int64_t)r * n;
+  List<KM> L;
+  L.init();
+  float m = -INFINITY, s = 0.f;
+  for (int j = t; j < nstrip; j += 256) {
+    const float2 p = pr[j];
+    if (p.x == -INFINITY) continue;
+    L.insert(p.x, j);
+    const float nm = fmaxf(m, p.x);
+    s = (m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - nm) * kL2e)) +
+        p.y * __builtin_amdgcn_exp2f((p.x - nm) * kL2e);
+    m = nm;
+  }
+  const float wm = wave_max(m);
+  const float ws = wave_sum(m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - wm) * kL2e));
+  float wv[KM];
+  int wi[KM];
+  wave_merge<KM, KM>(L, k, wv, wi);
+  if (lane == 0) {
+    smax[wave] = wm;
+    ssum[wave] = ws;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      sv[wave * KM + j] = j < k ? wv[j] : -INFINITY;
+      si[wave * KM + j] = j < k ? wi[j] : kIdNone;
+    }
+  }
+  __syncthreads();
+  float bm = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) bm = fmaxf(bm, smax[w]);
+  double bs = 0.0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (smax[w] != -INFINITY) bs += (double)ssum[w] * exp((double)smax[w] - (double)bm);
+  const double lse = (double)bm + log(bs);
+  if (wave == 0) {  // the k best strips
+    List<1> one;
+    one.init();
+    if (lane < 4 * KM) {
+      one.v[0] = sv[lane];
+      one.i[0] = si[lane];
+    }
+    float ov[KM];
+    int oi[KM];
+    wave_merge<1, KM>(one, k, ov, oi);
+    if (lane < KM) {
+      int id = kIdNone;
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+        if (j == lane && j < k) id = oi[j];
+      sel[lane] = id;
+    }
+  }
+  __syncthreads();
+  // candidate q = t + 256 h: column q % 128 of the (q / 128)-th best strip
+  constexpr int CPT = KM * kStripW / 256;
+  List<KM < CPT ? KM : CPT> cand;
+  cand.init();
+#pragma unroll
+  for (int h = 0; h < CPT; ++h) {
+    const int q = t + 256 * h, rank = q / kStripW;
+    const int st = sel[rank];
+    if (rank < k && st != kIdNone) {
+      const int x = st * kStripW + q % kStripW;
+      if (x < n) cand.insert(row[x], x);
+    }
+  }
+  float cv[KM];
+  int cid[KM];
+  wave_merge<KM < CPT ? KM : CPT, KM>(cand, k, cv, cid);
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      sv[wave * KM + j] = j < k ? cv[j] : -INFINITY;
+      si[wave * KM + j] = j < k ? cid[j] : kIdNone;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  List<1> one;
+  one.init();
+  if (lane < 4 * KM) {
+    one.v[0] = sv[lane];
+    one.i[0] = si[lane];
+  }
+  float ov[KM];
+  int oi[KM];
+  wave_merge<1, KM>(one, k, ov, oi);
+  if (lane < k) {
+    float v = 0.f;
+    int id = 0;
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j == lane) {
+        v = ov[j];
+        id = oi[j];
+      }
+    ids[(int64_t)r * ldi + lane] = id_map ? id_map[clampi(id, 0, n - 1)] : id;
+    logp[(int64_t)r * ldl + lane] = (float)((double)v - lse);
+  }
+}
+
 template <int KM>
 hipError_t launch_topk(const float* z, int M, int n, int ldz, int k, const int* id_map,
                        const int* rowmap, int* ids, int ldi, float* logp, int ldl, void* part,
@@ -586,6 +712,16 @@ hipError_t topk_rows(const float* z, int M, int n, int ldz, int k, const int* id
   if (k <= 8)
     return launch_topk<8>(z, M, n, ldz, k, id_map, rowmap, ids, ldi, logp, ldl, part, nch, chunk, s);
   return launch_topk<16>(z, M, n, ldz, k, id_map, rowmap, ids, ldi, logp, ldl, part, nch, chunk, s);
+}
+
+hipError_t topk_merge_strips(const float* z, int M, int n, int k, int nstrip, int sw,
+                             const void* rec, const int* id_map, int* ids, int ldi, float* logp,
+                             int ldl, hipStream_t s) {
+  if (k < 1 || k > 8 || sw != kStripW || nstrip != (n + kStripW - 1) / kStripW)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_strip_merge_kernel<8>, dim3(M), dim3(256), 0, s, n, k, nstrip, z,
+                     (const float2*)rec, id_map, ids, ldi, logp, ldl);
+  return hipGetLastError();
 }
 
 hipError_t topk_merge_records(int M, int n, int k, int km, int nch, void* part, const int* id_map,

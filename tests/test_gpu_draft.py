@@ -54,6 +54,11 @@ CASES = {
                                                              cand_rank=128, num_candidates=128)), 2e-2),
     "bigvocab_k8_rows512": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
                                                              top_k=8, total_tokens=20, batch=64, ctx=24)), 2e-2),
+    # 96 beam rows of an EAGLE-4 head: the low-rank score GEMM has more column
+    # tiles than the chip has CUs and runs with persistent workgroups
+    "eagle4_rows96_v70000": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
+                                                              cand_rank=64, num_candidates=64, top_k=8,
+                                                              total_tokens=20, batch=12, ctx=24)), 2e-2),
 }
 
 
