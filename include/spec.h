@@ -241,13 +241,16 @@ spec_status spec_compact_kv(spec_ctx* ctx, const spec_kv* kv, int32_t B, const i
                             const int32_t* accepted_nodes, const int32_t* accepted_len,
                             int32_t max_accept, void* stream);
 
-/* Kernel timing for measurement tools.  While enabled, every launch of a
- * labelled kernel is bracketed by a pair of hipEvents recorded on the stream
- * it is launched on (at most 4096 launches per label are kept).  Enabling
- * resets the counts and creates the event pool on first use (the only other
- * host-side allocation of the library); spec_profile_read waits for the
- * recorded events and returns the number of timed launches and their summed
- * duration in milliseconds. */
+/* Kernel timing for measurement tools.  While enabled, every labelled launch
+ * sequence is timed by a pair of hipEvents that its kernels record from their
+ * own dispatch packets (hipExtLaunchKernel: start as the first kernel begins,
+ * stop as the last one ends), so timing adds no commands to the stream; at
+ * most 4096 sequences per label are kept.  enable: 1 starts timing and
+ * resets the counts, 2 resumes timing and keeps them, 0 stops timing (what
+ * was recorded stays readable); the event pool is created on first use (the
+ * only other host-side allocation of the library).  spec_profile_read waits
+ * for the recorded events and returns the number of timed sequences and their
+ * summed duration in milliseconds.  Not for use under stream capture. */
 typedef enum {
   SPEC_PROF_LM_HEAD = 0,    /* LM-head GEMM (EAGLE-3) or low-rank score GEMM (EAGLE-4) */
   SPEC_PROF_ATTENTION = 1,  /* context attention + combine */

@@ -540,25 +540,25 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.nchunks, a.nkv, a.B);
   if (std::is_same<T, bf16_t>::value && QV <= 32) {
     if (QV <= 16) {
-      hipLaunchKernelGGL((attn_ctx_mfma_kernel<HD, 1>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
+      SPEC_LAUNCH((attn_ctx_mfma_kernel<HD, 1>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
                          (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq,
                          a.kv.stride_head, a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
                          a.window, a.chunk, a.part);
     } else {
-      hipLaunchKernelGGL((attn_ctx_mfma_kernel<HD, 2>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
+      SPEC_LAUNCH((attn_ctx_mfma_kernel<HD, 2>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
                          (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq,
                          a.kv.stride_head, a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
                          a.window, a.chunk, a.part);
     }
   } else {
     const size_t lds = (size_t)QV * (HD + kTile + 3) * sizeof(float) + QV * sizeof(int);
-    hipLaunchKernelGGL((attn_ctx_kernel<T, HD>), grid, dim3(256), lds, s, (const T*)a.q,
+    SPEC_LAUNCH((attn_ctx_kernel<T, HD>), grid, dim3(256), lds, s, (const T*)a.q,
                        (const T*)a.kv.k, (const T*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
                        a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv, a.window, a.chunk, a.part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(a.B * a.R, a.nq), dim3(64), 0, s,
+  SPEC_LAUNCH((attn_combine_kernel<T, HD>), dim3(a.B * a.R, a.nq), dim3(64), 0, s,
                      (const T*)a.q, (const T*)a.kv.k, (const T*)a.kv.v, a.kv.stride_seq,
                      a.kv.stride_head, a.kv.slots, a.pos, a.anc, a.A, a.R, a.nq, a.nkv, a.window,
                      a.nchunks, a.part, (T*)a.out);

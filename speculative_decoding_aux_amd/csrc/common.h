@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 #define SPEC_DEV __device__ __forceinline__
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits

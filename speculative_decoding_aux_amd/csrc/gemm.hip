@@ -494,13 +494,13 @@ static void launch_stream(const void* X, int ldx, const void* W, int ldw, float*
                           int K, const GemmPlan& plan, hipStream_t s) {
   const int strips = (N + 64 * CW - 1) / (64 * CW);
   if (M <= 16) {
-    hipLaunchKernelGGL((gemm_bf16_stream<1, TAG, CW>), dim3(strips, plan.nsplit, 1), dim3(256), 0,
+    SPEC_LAUNCH((gemm_bf16_stream<1, TAG, CW>), dim3(strips, plan.nsplit, 1), dim3(256), 0,
                        s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc);
   } else if (M <= 32) {
-    hipLaunchKernelGGL((gemm_bf16_stream<2, TAG, CW>), dim3(strips, plan.nsplit, 1), dim3(256), 0,
+    SPEC_LAUNCH((gemm_bf16_stream<2, TAG, CW>), dim3(strips, plan.nsplit, 1), dim3(256), 0,
                        s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc);
   } else {
-    hipLaunchKernelGGL((gemm_bf16_stream<4, TAG, CW>), dim3(strips, plan.nsplit, (M + 63) / 64),
+    SPEC_LAUNCH((gemm_bf16_stream<4, TAG, CW>), dim3(strips, plan.nsplit, (M + 63) / 64),
                        dim3(256), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K,
                        plan.kc);
   }
@@ -510,7 +510,7 @@ hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float
                 int K, const GemmPlan& plan, hipStream_t s, int tag) {
   if (!bf16) {
     dim3 grid((N + 15) / 16, (M + 15) / 16);
-    hipLaunchKernelGGL(gemm_f32_rows, grid, dim3(256), 0, s, (const float*)X, ldx,
+    SPEC_LAUNCH(gemm_f32_rows, grid, dim3(256), 0, s, (const float*)X, ldx,
                        (const float*)W, ldw, P, M, N, K);
     return hipGetLastError();
   }
@@ -536,10 +536,10 @@ static void launch_lmhead(const void* X, int ldx, const void* W, int ldw, float*
                           int K, int km, float* pv, int* pi, topkdev::Part* pp, hipStream_t s) {
   const dim3 grid((N + 64 * CW - 1) / (64 * CW), 1, (M + 16 * MT - 1) / (16 * MT));
   if (km == 1) {
-    hipLaunchKernelGGL((gemm_lmhead_topk_kernel<MT, CW, 1>), grid, dim3(256), 0, s,
+    SPEC_LAUNCH((gemm_lmhead_topk_kernel<MT, CW, 1>), grid, dim3(256), 0, s,
                        (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, z, M, N, K, pv, pi, pp);
   } else {
-    hipLaunchKernelGGL((gemm_lmhead_topk_kernel<MT, CW, 8>), grid, dim3(256), 0, s,
+    SPEC_LAUNCH((gemm_lmhead_topk_kernel<MT, CW, 8>), grid, dim3(256), 0, s,
                        (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, z, M, N, K, pv, pi, pp);
   }
 }
@@ -577,7 +577,7 @@ hipError_t gemm_epilogue(bool bf16, int op, void* Y, const void* R, const float*
       (op != EPI_RESID || al(R, eb))) {
     const dim3 vgrid((unsigned)((total / 4 + 255) / 256));
 #define SPEC_EPIV(T, OPV)                                                                       \
-  hipLaunchKernelGGL((epi_vec_kernel<T, OPV>), vgrid, dim3(256), 0, s, (T*)Y, (const T*)R, P,  \
+  SPEC_LAUNCH((epi_vec_kernel<T, OPV>), vgrid, dim3(256), 0, s, (T*)Y, (const T*)R, P,  \
                      nsplit, M, N)
     if (op == EPI_F32) SPEC_EPIV(float, EPI_STORE);
     else if (bf16 && op == EPI_STORE) SPEC_EPIV(bf16_t, EPI_STORE);
@@ -590,21 +590,21 @@ hipError_t gemm_epilogue(bool bf16, int op, void* Y, const void* R, const float*
     return hipGetLastError();
   }
   if (op == EPI_F32) {
-    hipLaunchKernelGGL(epi_f32, grid, dim3(256), 0, s, (float*)Y, P, nsplit, total);
+    SPEC_LAUNCH(epi_f32, grid, dim3(256), 0, s, (float*)Y, P, nsplit, total);
     return hipGetLastError();
   }
 #define SPEC_EPI(T)                                                                            \
   switch (op) {                                                                                \
     case EPI_STORE:                                                                            \
-      hipLaunchKernelGGL((epi_kernel<T, EPI_STORE>), grid, dim3(256), 0, s, (T*)Y,             \
+      SPEC_LAUNCH((epi_kernel<T, EPI_STORE>), grid, dim3(256), 0, s, (T*)Y,             \
                          (const T*)R, P, nsplit, M, N);                                        \
       break;                                                                                   \
     case EPI_RESID:                                                                            \
-      hipLaunchKernelGGL((epi_kernel<T, EPI_RESID>), grid, dim3(256), 0, s, (T*)Y,             \
+      SPEC_LAUNCH((epi_kernel<T, EPI_RESID>), grid, dim3(256), 0, s, (T*)Y,             \
                          (const T*)R, P, nsplit, M, N);                                        \
       break;                                                                                   \
     default:                                                                                   \
-      hipLaunchKernelGGL((epi_kernel<T, EPI_SWIGLU>), grid, dim3(256), 0, s, (T*)Y,            \
+      SPEC_LAUNCH((epi_kernel<T, EPI_SWIGLU>), grid, dim3(256), 0, s, (T*)Y,            \
                          (const T*)R, P, nsplit, M, N);                                        \
   }
   if (bf16) {
@@ -622,11 +622,11 @@ hipError_t qkv_epilogue(bool bf16, const float* P, int nsplit, int M, int nq, in
   dim3 grid(M, nq + 2 * nkv);
   dim3 block(256);
   if (bf16) {
-    hipLaunchKernelGGL(qkv_epi_kernel<bf16_t>, grid, block, 0, s, P, nsplit, M, nq, nkv, hd, pos,
+    SPEC_LAUNCH(qkv_epi_kernel<bf16_t>, grid, block, 0, s, P, nsplit, M, nq, nkv, hd, pos,
                        slot, rows_per_seq, rope_base, (bf16_t*)qout, (bf16_t*)kv.k,
                        (bf16_t*)kv.v, kv.stride_seq, kv.stride_head, kv.slots);
   } else {
-    hipLaunchKernelGGL(qkv_epi_kernel<float>, grid, block, 0, s, P, nsplit, M, nq, nkv, hd, pos,
+    SPEC_LAUNCH(qkv_epi_kernel<float>, grid, block, 0, s, P, nsplit, M, nq, nkv, hd, pos,
                        slot, rows_per_seq, rope_base, (float*)qout, (float*)kv.k, (float*)kv.v,
                        kv.stride_seq, kv.stride_head, kv.slots);
   }

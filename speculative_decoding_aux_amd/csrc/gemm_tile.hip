@@ -378,12 +378,12 @@ hipError_t launch_tile(const void* X, int ldx, const void* W, int ldw, float* P,
   const int ntiles = ((N + kTileBN - 1) / kTileBN) * ((M + kTileBM - 1) / kTileBM) * nsplit;
   const int grid = tile_grid(ntiles);
   if (grid < ntiles)
-    hipLaunchKernelGGL(
+    SPEC_LAUNCH(
         (gemm_dma_kernel<kTileBN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, true>),
         dim3(grid), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M,
         N, K, kc, ntiles, rec);
   else
-    hipLaunchKernelGGL(
+    SPEC_LAUNCH(
         (gemm_dma_kernel<kTileBN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, false>),
         dim3(ntiles), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M,
         N, K, kc, ntiles, rec);

@@ -137,11 +137,11 @@ hipError_t prologue(bool bf16, const void* embed, int V, const int* tok, const v
                     const int* src, const void* w_in, const void* w_hid, float eps, int M, int H,
                     void* gout, void* cout, hipStream_t s) {
   if (bf16) {
-    hipLaunchKernelGGL(prologue_kernel<bf16_t>, dim3(M), dim3(256), 0, s, (const bf16_t*)embed, V,
+    SPEC_LAUNCH(prologue_kernel<bf16_t>, dim3(M), dim3(256), 0, s, (const bf16_t*)embed, V,
                        tok, (const bf16_t*)hid, src, (const bf16_t*)w_in, (const bf16_t*)w_hid,
                        eps, H, (bf16_t*)gout, (bf16_t*)cout);
   } else {
-    hipLaunchKernelGGL(prologue_kernel<float>, dim3(M), dim3(256), 0, s, (const float*)embed, V,
+    SPEC_LAUNCH(prologue_kernel<float>, dim3(M), dim3(256), 0, s, (const float*)embed, V,
                        tok, (const float*)hid, src, (const float*)w_in, (const float*)w_hid, eps,
                        H, (float*)gout, (float*)cout);
   }
@@ -151,10 +151,10 @@ hipError_t prologue(bool bf16, const void* embed, int V, const int* tok, const v
 hipError_t rmsnorm(bool bf16, const void* x, const void* w, float eps, int M, int H, void* y,
                    hipStream_t s) {
   if (bf16) {
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, s, (const bf16_t*)x,
+    SPEC_LAUNCH(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, s, (const bf16_t*)x,
                        (const bf16_t*)w, eps, H, (bf16_t*)y);
   } else {
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, s, (const float*)x,
+    SPEC_LAUNCH(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, s, (const float*)x,
                        (const float*)w, eps, H, (float*)y);
   }
   return hipGetLastError();

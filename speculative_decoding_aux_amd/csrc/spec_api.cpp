@@ -13,8 +13,13 @@
 
 #include "../../include/spec.h"
 #include "kernels.h"
+#include "launch.h"
 
 using namespace spec;
+
+namespace spec {
+thread_local LaunchTiming* launch_timing = nullptr;
+}  // namespace spec
 
 namespace {
 
@@ -84,20 +89,32 @@ spec_status fail(spec_ctx* c, spec_status st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Records the start/stop events of one labelled launch when profiling is on.
+// Times one labelled launch sequence when profiling is on: the kernels
+// enqueued inside the scope carry the start/stop events in their dispatch
+// packets (SPEC_LAUNCH); a scope that enqueued nothing records both events
+// directly.
 struct ProfScope {
   spec_ctx* c;
   int label;
   int slot = -1;
   hipStream_t s;
+  LaunchTiming lt{nullptr, nullptr};
+  LaunchTiming* prev = nullptr;
   ProfScope(spec_ctx* c_, int label_, hipStream_t s_) : c(c_), label(label_), s(s_) {
     if (c->prof && c->used[label] < spec_ctx::kProfCap) {
       slot = c->used[label]++;
-      (void)hipEventRecord(c->ev[label][0][slot], s);
+      lt = {c->ev[label][0][slot], c->ev[label][1][slot]};
+      prev = launch_timing;
+      launch_timing = &lt;
     }
   }
   ~ProfScope() {
-    if (slot >= 0) (void)hipEventRecord(c->ev[label][1][slot], s);
+    if (slot < 0) return;
+    launch_timing = prev;
+    if (lt.start) {
+      (void)hipEventRecord(lt.start, s);
+      (void)hipEventRecord(lt.stop, s);
+    }
   }
 };
 
@@ -266,7 +283,7 @@ void spec_destroy(spec_ctx* ctx) {
 }
 
 spec_status spec_profile_enable(spec_ctx* ctx, int32_t enable) {
-  if (!ctx) return SPEC_EINVAL;
+  if (!ctx || enable < 0 || enable > 2) return SPEC_EINVAL;
   if (enable && ctx->ev[0][0].empty()) {
     for (auto& lab : ctx->ev)
       for (auto& vec : lab) {
@@ -275,7 +292,8 @@ spec_status spec_profile_enable(spec_ctx* ctx, int32_t enable) {
       }
   }
   ctx->prof = enable != 0;
-  for (int& u : ctx->used) u = 0;
+  if (enable == 1)
+    for (int& u : ctx->used) u = 0;
   return SPEC_OK;
 }
 

@@ -666,11 +666,11 @@ hipError_t launch_topk(const float* z, int M, int n, int ldz, int k, const int* 
   float* pv = (float*)part;
   int* pi = (int*)(pv + (size_t)M * nch * KM);
   Part* pp = (Part*)(pi + (size_t)M * nch * KM);
-  hipLaunchKernelGGL(topk_partial_kernel<KM>, dim3(nch, M), dim3(256), 0, s, z, n, ldz, k, chunk,
+  SPEC_LAUNCH(topk_partial_kernel<KM>, dim3(nch, M), dim3(256), 0, s, z, n, ldz, k, chunk,
                      rowmap, pv, pi, pp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel<KM>, dim3(M), dim3(256), 0, s, n, k, nch, pv, pi, pp,
+  SPEC_LAUNCH(topk_merge_kernel<KM>, dim3(M), dim3(256), 0, s, n, k, nch, pv, pi, pp,
                      id_map, rowmap, ids, ldi, logp, ldl);
   return hipGetLastError();
 }
@@ -719,7 +719,7 @@ hipError_t topk_merge_strips(const float* z, int M, int n, int k, int nstrip, in
                              int ldl, hipStream_t s) {
   if (k < 1 || k > 8 || sw != kStripW || nstrip != (n + kStripW - 1) / kStripW)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_strip_merge_kernel<8>, dim3(M), dim3(256), 0, s, n, k, nstrip, z,
+  SPEC_LAUNCH(topk_strip_merge_kernel<8>, dim3(M), dim3(256), 0, s, n, k, nstrip, z,
                      (const float2*)rec, id_map, ids, ldi, logp, ldl);
   return hipGetLastError();
 }
@@ -730,10 +730,10 @@ hipError_t topk_merge_records(int M, int n, int k, int km, int nch, void* part, 
   int* pi = (int*)(pv + (size_t)M * nch * km);
   Part* pp = (Part*)(pi + (size_t)M * nch * km);
   if (km == 1) {
-    hipLaunchKernelGGL(topk_merge_kernel<1>, dim3(M), dim3(256), 0, s, n, k, nch, pv, pi, pp, id_map,
+    SPEC_LAUNCH(topk_merge_kernel<1>, dim3(M), dim3(256), 0, s, n, k, nch, pv, pi, pp, id_map,
                        nullptr, ids, ldi, logp, ldl);
   } else {
-    hipLaunchKernelGGL(topk_merge_kernel<8>, dim3(M), dim3(256), 0, s, n, k, nch, pv, pi, pp, id_map,
+    SPEC_LAUNCH(topk_merge_kernel<8>, dim3(M), dim3(256), 0, s, n, k, nch, pv, pi, pp, id_map,
                        nullptr, ids, ldi, logp, ldl);
   }
   return hipGetLastError();
@@ -741,7 +741,7 @@ hipError_t topk_merge_records(int M, int n, int k, int km, int nch, void* part, 
 
 hipError_t topk_large(const float* z, int M, int n, int K, int* ids, void* part, hipStream_t s) {
   (void)part;
-  hipLaunchKernelGGL(topk_large_kernel, dim3(M), dim3(256), 0, s, z, n, K, ids);
+  SPEC_LAUNCH(topk_large_kernel, dim3(M), dim3(256), 0, s, z, n, K, ids);
   return hipGetLastError();
 }
 
@@ -749,21 +749,21 @@ hipError_t gather_dot(bool bf16, const void* x, const void* W, int H, int V, con
                       int K, float* out, hipStream_t s) {
   const bool al = ((uintptr_t)x & 15) == 0 && ((uintptr_t)W & 15) == 0;
   if (bf16 && al && H == 4096) {
-    hipLaunchKernelGGL(gather_dot_vec_kernel<8>, dim3(M), dim3(256), 0, s, (const bf16_t*)x,
+    SPEC_LAUNCH(gather_dot_vec_kernel<8>, dim3(M), dim3(256), 0, s, (const bf16_t*)x,
                        (const bf16_t*)W, H, V, ids, K, out);
     return hipGetLastError();
   }
   if (bf16 && al && H == 2048) {
-    hipLaunchKernelGGL(gather_dot_vec_kernel<4>, dim3(M), dim3(256), 0, s, (const bf16_t*)x,
+    SPEC_LAUNCH(gather_dot_vec_kernel<4>, dim3(M), dim3(256), 0, s, (const bf16_t*)x,
                        (const bf16_t*)W, H, V, ids, K, out);
     return hipGetLastError();
   }
   dim3 grid((K + 3) / 4, M);
   if (bf16) {
-    hipLaunchKernelGGL(gather_dot_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,
+    SPEC_LAUNCH(gather_dot_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,
                        (const bf16_t*)W, H, V, ids, K, out);
   } else {
-    hipLaunchKernelGGL(gather_dot_kernel<float>, grid, dim3(256), 0, s, (const float*)x,
+    SPEC_LAUNCH(gather_dot_kernel<float>, grid, dim3(256), 0, s, (const float*)x,
                        (const float*)W, H, V, ids, K, out);
   }
   return hipGetLastError();

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void tree_expand_kernel(
 hipError_t tree_root_setup(int B, int n_new, const int* in_tokens, const int* ctx_len, int k, int D,
                            int cap, TreeState st, PassRows rows, hipStream_t s) {
   const int n = B * n_new;
-  hipLaunchKernelGGL(root_setup_kernel, dim3((n + 255) / 256), dim3(256), 0, s, B, n_new,
+  SPEC_LAUNCH(root_setup_kernel, dim3((n + 255) / 256), dim3(256), 0, s, B, n_new,
                      in_tokens, ctx_len, k, D, cap, st.active, rows.tok, rows.pos, rows.slot,
                      rows.src, rows.anc, rows.A);
   return hipGetLastError();
@@ -218,7 +218,7 @@ hipError_t tree_expand(int d, int B, int n_new, const int* ctx_len, const int* i
                        int D, int N, const int* ids, const float* logp, int ld, int root_stride,
                        int root_off, TreeState st, PassRows next, TreeOut out, hipStream_t s) {
   const size_t lds = (size_t)(2 * st.cmax + 256) * sizeof(int);
-  hipLaunchKernelGGL(tree_expand_kernel, dim3(B), dim3(256), lds, s, d, n_new, ctx_len, in_tokens,
+  SPEC_LAUNCH(tree_expand_kernel, dim3(B), dim3(256), lds, s, d, n_new, ctx_len, in_tokens,
                      k, D, N, ids, logp, ld, root_stride, root_off, st, st.beam, next, out);
   return hipGetLastError();
 }

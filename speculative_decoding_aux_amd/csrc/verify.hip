@@ -416,21 +416,21 @@ hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const in
   GPart* gpart = (GPart*)w;
   w += align256((size_t)B * p.gch * sizeof(GPart));
   int* stop = (int*)w;
-  hipLaunchKernelGGL(verify_stats_kernel, dim3(p.nch, rows), dim3(256), 0, s, N, V, num_nodes,
+  SPEC_LAUNCH(verify_stats_kernel, dim3(p.nch, rows), dim3(256), 0, s, N, V, num_nodes,
                      logits, mode, temperature, p.chunk, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_walk_kernel, dim3(B), dim3(64), 0, s, N, D, k, V, tokens, parent,
+  SPEC_LAUNCH(verify_walk_kernel, dim3(B), dim3(64), 0, s, N, D, k, V, tokens, parent,
                      num_nodes, logits, mode, temperature, accept_u, p.nch, (const VPart*)part,
                      stop, out_tokens, accepted_len, accepted_nodes);
   e = hipGetLastError();
   if (e != hipSuccess || mode == 0) return e;
-  hipLaunchKernelGGL(verify_gumbel_kernel, dim3(p.gch, B), dim3(256), 0, s, N, V, tokens, parent,
+  SPEC_LAUNCH(verify_gumbel_kernel, dim3(p.gch, B), dim3(256), 0, s, N, V, tokens, parent,
                      num_nodes, logits, temperature, (uint32_t)(seed & 0xffffffffu),
                      (uint32_t)(seed >> 32), p.gchunk, (const int*)stop, gpart);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_emit_kernel, dim3(B), dim3(64), 0, s, D, p.gch, (const GPart*)gpart,
+  SPEC_LAUNCH(verify_emit_kernel, dim3(B), dim3(64), 0, s, D, p.gch, (const GPart*)gpart,
                      (const int*)accepted_len, out_tokens);
   return hipGetLastError();
 }
@@ -442,13 +442,13 @@ hipError_t compact(bool bf16, KvFull kv, int B, const int* base, const int* node
   const dim3 grid(B, kv.layers, kv.nkv);
   const int64_t sl = kv.stride_layer * esz, ss = kv.stride_seq * esz, sh = kv.stride_head * esz;
   if (row_bytes == 256) {
-    hipLaunchKernelGGL(compact_kernel<16>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
+    SPEC_LAUNCH(compact_kernel<16>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
                        sh, kv.slots, base, nodes, alen, max_accept);
   } else if (row_bytes == 128) {
-    hipLaunchKernelGGL(compact_kernel<8>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
+    SPEC_LAUNCH(compact_kernel<8>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
                        sh, kv.slots, base, nodes, alen, max_accept);
   } else {
-    hipLaunchKernelGGL(compact_kernel<32>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
+    SPEC_LAUNCH(compact_kernel<32>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
                        sh, kv.slots, base, nodes, alen, max_accept);
   }
   return hipGetLastError();

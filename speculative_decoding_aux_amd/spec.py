@@ -123,8 +123,8 @@ class SpecContext:
     def workspace_bytes(self) -> int:
         return int(self.lib.spec_workspace_bytes(self.h))
 
-    def profile(self, enable: bool):
-        self._check(self.lib.spec_profile_enable(self.h, 1 if enable else 0))
+    def profile(self, enable: bool, reset: bool = True):
+        self._check(self.lib.spec_profile_enable(self.h, (1 if reset else 2) if enable else 0))
 
     def profile_read(self, label: int):
         n, ms = ctypes.c_int32(), ctypes.c_double()
