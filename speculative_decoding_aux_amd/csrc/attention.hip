@@ -32,6 +32,10 @@ template <> SPEC_DEV float unpack<bf16_t>(const u32x4_t& w, int e) {
 // one wave: merge the context-chunk records with the row's extra keys.  Lane j
 // scores extra key j (its own 16-byte key loads, q from LDS); each lane then
 // accumulates its dims over the chunk records and the extra keys' values.
+// Every load that depends on nothing (q, the extra-key slots, the first
+// chunk records) is issued first and the extra keys' K and V rows right after
+// the slots arrive, so the wave waits on two round trips to memory, not one
+// per stage.
 template <typename T, int HD>
 SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restrict__ kc,
                          const T* __restrict__ vc, int64_t sseq, int64_t shead, int S,
@@ -40,62 +44,104 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
                          T* __restrict__ out, float* qs /* LDS, HD floats for this wave */) {
   constexpr int DPL = HD / 64;  // dims per lane
   constexpr int EPV = 16 / sizeof(T);
+  constexpr int PC = 4;         // chunk records prefetched
+  constexpr int PV = 8;         // extra keys whose values are prefetched
   const int lane = threadIdx.x & 63;
   const int G = nq / nkv, kvh = h / G;
   const int b = r / R, qv = (r % R) * G + h % G, QV = R * G;
   const float inv_sqrt = 1.0f / sqrtf((float)HD);
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) qs[lane + 64 * i] = St<T>::load(q, ((int64_t)r * nq + h) * HD + lane + 64 * i);
   const float* pb = part + ((int64_t)(b * nkv + kvh) * nch * QV + qv) * (HD + 2);
   const int64_t cstride = (int64_t)QV * (HD + 2);
-  float m = -INFINITY;
-  for (int c = lane; c < nch; c += 64) m = fmaxf(m, pb[c * cstride + HD]);
-  // extra keys: valid entries hold consecutive positions ending at pos[r]
+  // round trip 1: slots, q, chunk records
   const int sl = lane < A ? anc[(int64_t)r * A + lane] : -1;
+  const int pq = pos[r];
+  float qr[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) qr[i] = St<T>::load(q, ((int64_t)r * nq + h) * HD + lane + 64 * i);
+  float pm = -INFINITY, pl = 0.f;
+  if (lane < nch) {
+    pm = pb[lane * cstride + HD];
+    pl = pb[lane * cstride + HD + 1];
+  }
+  float po[PC][DPL];
+#pragma unroll
+  for (int c = 0; c < PC; ++c)
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) po[c][i] = c < nch ? pb[c * cstride + lane + 64 * i] : 0.f;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) qs[lane + 64 * i] = qr[i];
+  // extra keys: valid entries hold consecutive positions ending at pos[r]
   const unsigned long long vmask = __ballot(sl >= 0);
   const int nvalid = __popcll(vmask);
   const int rank = __popcll(vmask & ((1ull << lane) - 1ull));
-  const int pq = pos[r];
   const T* kb = kc + b * sseq + kvh * shead;
   const T* vb = vc + b * sseq + kvh * shead;
-  float s = -INFINITY;
   const bool vis = sl >= 0 && sl < S && (window <= 0 || pq - (nvalid - 1 - rank) > pq - window);
+  // round trip 2: the extra keys' K rows (lane j) and the first PV value rows
+  u32x4_t kr[HD / EPV];
   if (vis) {
-    const u32x4_t* kr = (const u32x4_t*)(kb + (int64_t)sl * HD);
+    const u32x4_t* kp = (const u32x4_t*)(kb + (int64_t)sl * HD);
+#pragma unroll
+    for (int vq = 0; vq < HD / EPV; ++vq) kr[vq] = kp[vq];
+  }
+  float vv[PV][DPL];
+#pragma unroll
+  for (int u = 0; u < PV; ++u) {
+    const int slj = __shfl(sl, u, 64);
+    const bool visj = __shfl((int)vis, u, 64) != 0;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) vv[u][i] = visj ? St<T>::load(vb, (int64_t)slj * HD + lane + 64 * i) : 0.f;
+  }
+  float s = -INFINITY;
+  if (vis) {
     float a = 0.f;
 #pragma unroll
-    for (int vq = 0; vq < HD / EPV; ++vq) {
-      const u32x4_t w = kr[vq];
+    for (int vq = 0; vq < HD / EPV; ++vq)
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) a += qs[vq * EPV + e] * unpack<T>(w, e);
-    }
+      for (int e = 0; e < EPV; ++e) a += qs[vq * EPV + e] * unpack<T>(kr[vq], e);
     s = a * inv_sqrt;
   }
-  m = wave_max(fmaxf(m, s));
+  float m = fmaxf(pm, s);
+  for (int c = lane + 64; c < nch; c += 64) m = fmaxf(m, pb[c * cstride + HD]);
+  m = wave_max(m);
   float l = 0.f;
   float o[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) o[i] = 0.f;
   if (m != -INFINITY) {
     const float p = s == -INFINITY ? 0.f : expf(s - m);
-    l = wave_sum(p);
-    float lc = 0.f;
-    for (int c = lane; c < nch; c += 64) {
+    float lc = pm == -INFINITY ? 0.f : pl * expf(pm - m);
+    for (int c = lane + 64; c < nch; c += 64) {
       const float mc = pb[c * cstride + HD];
       if (mc != -INFINITY) lc += pb[c * cstride + HD + 1] * expf(mc - m);
     }
-    l += wave_sum(lc);
+    l = wave_sum(p) + wave_sum(lc);
     for (int c = 0; c < nch; ++c) {
-      const float mc = pb[c * cstride + HD];
-      if (mc == -INFINITY) continue;
-      const float w = expf(mc - m);
+      const float mc = __shfl(pm, c & 63, 64);
+      const float mcc = c < 64 ? mc : pb[c * cstride + HD];
+      if (mcc == -INFINITY) continue;
+      const float w = expf(mcc - m);
+      if (c < PC) {
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) o[i] += pb[c * cstride + lane + 64 * i] * w;
+        for (int cc = 0; cc < PC; ++cc)
+          if (cc == c)
+#pragma unroll
+            for (int i = 0; i < DPL; ++i) o[i] += po[cc][i] * w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o[i] += pb[c * cstride + lane + 64 * i] * w;
+      }
     }
-    // extra keys' values, eight keys' loads in flight at a time
-    for (int j0 = 0; j0 < 64; j0 += 8) {
+#pragma unroll
+    for (int u = 0; u < PV; ++u) {
+      const float pj = __shfl(p, u, 64);
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) o[i] += pj * vv[u][i];
+    }
+    // extra keys past the first PV, eight keys' loads in flight at a time
+    for (int j0 = PV; j0 < 64; j0 += 8) {
       if (!(vmask >> j0)) break;
-      float vv[8][DPL], pj[8];
+      float vw[8][DPL], pj[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int j = j0 + u;
@@ -104,13 +150,13 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
         const bool ok = ((vmask >> j) & 1ull) && pj[u] > 0.f;
 #pragma unroll
         for (int i = 0; i < DPL; ++i)
-          vv[u][i] = ok ? St<T>::load(vb, (int64_t)slj * HD + lane + 64 * i) : 0.f;
+          vw[u][i] = ok ? St<T>::load(vb, (int64_t)slj * HD + lane + 64 * i) : 0.f;
         if (!ok) pj[u] = 0.f;
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) o[i] += pj[u] * vv[u][i];
+        for (int i = 0; i < DPL; ++i) o[i] += pj[u] * vw[u][i];
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
