@@ -103,6 +103,97 @@ SPEC_DEV void stream_acc(const bf16_t* __restrict__ X, int ldx, const bf16_t* __
   }
 }
 
+// Block-shared activations for MT >= 2 (K % 512 == 0, 16-byte aligned X rows):
+// the four waves of a block stream different weight rows against the same
+// 16*MT X rows, so X comes into LDS once per block, 256 K at a time, by
+// global_load_lds (two buffers, one LDS object each), instead of every wave
+// reading it from L2.  Chunk j (16 bytes) of X row r of a buffer sits at
+// position j ^ (r & 15), so the 16 rows of a fragment read hit 16 distinct
+// 16-byte bank groups.  Per 256-K iteration a wave issues its weight loads,
+// waits for its own DMA of the iteration (issued before them, at the end of
+// the previous iteration), meets the other waves at a barrier, runs the
+// MFMAs, and then issues the DMA of the next iteration: no MFMA operand wait
+// ever has an LDS DMA behind it.  Past the last iteration the DMA repeats the
+// last one, keeping every wave's load count uniform.
+template <int MT, int CW>
+SPEC_DEV void stream_acc_lds(const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W,
+                             int ldw, int M, int N, int K, int m0, int n0, f32x4 (&acc)[CW][MT],
+                             SPEC_LDS u32x4_t* xs0, SPEC_LDS u32x4_t* xs1) {
+  constexpr int NXI = 2 * MT;  // DMA instructions per wave per iteration (16*MT rows x 32 chunks)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const bf16_t* wp[CW];
+#pragma unroll
+  for (int w = 0; w < CW; ++w) wp[w] = W + (int64_t)min(n0 + 16 * w + c, N - 1) * ldw + g * 8;
+  const bf16_t* xsrc[NXI];
+  int xdst[NXI];
+#pragma unroll
+  for (int j = 0; j < NXI; ++j) {
+    xdst[j] = (wave * NXI + j) * 64;
+    const int u = xdst[j] + lane, row = u >> 5, pos = u & 31;
+    xsrc[j] = X + (int64_t)min(m0 + row, M - 1) * ldx + 8 * (pos ^ (row & 15));
+  }
+#pragma unroll
+  for (int w = 0; w < CW; ++w)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nit = K / 256;
+  auto issue = [&](SPEC_LDS u32x4_t* xs, int it) __attribute__((always_inline)) {
+    const int k = min(it, nit - 1) * 256;
+#pragma unroll
+    for (int j = 0; j < NXI; ++j) dma16(xsrc[j] + k, xs + xdst[j]);
+  };
+  auto body = [&](SPEC_LDS u32x4_t* xs, SPEC_LDS u32x4_t* xn, int it) __attribute__((always_inline)) {
+    const int k = it * 256;
+    u32x4_t wa[CW][4], wb[CW][4];
+#pragma unroll
+    for (int w = 0; w < CW; ++w)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wa[w][j] = *(const u32x4_t*)(wp[w] + k + j * 32);
+        wb[w][j] = *(const u32x4_t*)(wp[w] + k + 128 + j * 32);
+      }
+    // this wave's DMA of iteration it (older than the 8*CW weight loads) has
+    // landed; after the barrier every wave's has, and every wave is done
+    // with iteration it - 1, whose buffer the DMA below refills
+    wait_vm_lgkm0<8 * CW>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        u32x4_t xr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xr[j] = xs[(16 * t + c) * 32 + ((16 * h + 4 * j + g) ^ c)];
+#pragma unroll
+        for (int w = 0; w < CW; ++w)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[w][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, h ? wb[w][j] : wa[w][j]), __builtin_bit_cast(bf16x8, xr[j]),
+                acc[w][t], 0, 0, 0);
+      }
+    }
+    // the MFMAs (and so their weight-register waits) stay ahead of the DMA:
+    // a wait for weights issued behind a pending DMA would have to wait for it
+#pragma unroll
+    for (int w = 0; w < CW; ++w)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) asm volatile("" : "+v"(acc[w][t]) :: "memory");
+    issue(xn, it + 1);
+    asm volatile("" ::: "memory");  // the next weight loads stay behind this DMA
+  };
+  issue(xs0, 0);
+  for (int it = 0; it < nit; it += 2) {
+    body(xs0, xs1, it);
+    body(xs1, xs0, it + 1);
+  }
+  wait_vm_lgkm0<0>();  // the repeated DMA past the end
+}
+
 // lane holds Y[n0 + 16w + 4g + r][m0 + 16t + c], r = 0..3
 template <int MT, int CW>
 SPEC_DEV void store_tiles(const f32x4 (&acc)[CW][MT], float* __restrict__ P, int M, int N, int m0,
@@ -149,12 +240,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict
 // pair, the four lane groups of a wave merge by shuffles, and the four waves
 // through LDS; one record per (row, workgroup) goes to the partial buffer in
 // the layout the record merge reads (pv/pi [M][nch][KM], pp [M][nch]).
-template <int MT, int CW, int KM>
+template <int MT, int CW, int KM, bool XL>
 __global__ __launch_bounds__(256) void gemm_lmhead_topk_kernel(
     const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W, int ldw,
     float* __restrict__ z, int M, int N, int K, float* __restrict__ pv, int* __restrict__ pi,
     topkdev::Part* __restrict__ pp) {
   using topkdev::List;
+  __shared__ u32x4_t xs0[XL ? 16 * MT * 32 : 1], xs1[XL ? 16 * MT * 32 : 1];
   __shared__ float tv[4][16 * MT][KM];
   __shared__ int ti[4][16 * MT][KM];
   __shared__ float tm[4][16 * MT];
@@ -166,7 +258,13 @@ __global__ __launch_bounds__(256) void gemm_lmhead_topk_kernel(
   const int m0 = blockIdx.z * (16 * MT);
   const bool active = n0 < N;  // no early return: the block meets at a barrier
   f32x4 acc[CW][MT];
-  if (active) {
+  if constexpr (XL) {
+    // every wave takes part in the shared X loads (an inactive one streams
+    // the clamped last weight rows and stores nothing)
+    stream_acc_lds<MT, CW>(X, ldx, W, ldw, M, N, K, m0, n0, acc, (SPEC_LDS u32x4_t*)xs0,
+                           (SPEC_LDS u32x4_t*)xs1);
+    if (active && z) store_tiles<MT, CW>(acc, z, M, N, m0, n0);
+  } else if (active) {
     stream_acc<MT, CW>(X, ldx, W, ldw, M, N, 0, K, m0, n0, acc);
     if (z) store_tiles<MT, CW>(acc, z, M, N, m0, n0);
   }
@@ -531,17 +629,28 @@ int gemm_strips(int M, int N) {
   return (N + 64 * cw - 1) / (64 * cw);
 }
 
+template <int MT, int CW, bool XL>
+static void launch_lmhead_x(const void* X, int ldx, const void* W, int ldw, float* z, int M, int N,
+                            int K, int km, float* pv, int* pi, topkdev::Part* pp, hipStream_t s) {
+  const dim3 grid((N + 64 * CW - 1) / (64 * CW), 1, (M + 16 * MT - 1) / (16 * MT));
+  if (km == 1) {
+    SPEC_LAUNCH((gemm_lmhead_topk_kernel<MT, CW, 1, XL>), grid, dim3(256), 0, s,
+                (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, z, M, N, K, pv, pi, pp);
+  } else {
+    SPEC_LAUNCH((gemm_lmhead_topk_kernel<MT, CW, 8, XL>), grid, dim3(256), 0, s,
+                (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, z, M, N, K, pv, pi, pp);
+  }
+}
+
+// X through LDS (see stream_acc_lds) where the block holds two or more
+// 16-row tiles and the shape allows it.
 template <int MT, int CW>
 static void launch_lmhead(const void* X, int ldx, const void* W, int ldw, float* z, int M, int N,
                           int K, int km, float* pv, int* pi, topkdev::Part* pp, hipStream_t s) {
-  const dim3 grid((N + 64 * CW - 1) / (64 * CW), 1, (M + 16 * MT - 1) / (16 * MT));
-  if (km == 1) {
-    SPEC_LAUNCH((gemm_lmhead_topk_kernel<MT, CW, 1>), grid, dim3(256), 0, s,
-                       (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, z, M, N, K, pv, pi, pp);
-  } else {
-    SPEC_LAUNCH((gemm_lmhead_topk_kernel<MT, CW, 8>), grid, dim3(256), 0, s,
-                       (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, z, M, N, K, pv, pi, pp);
-  }
+  if (MT >= 2 && K % 512 == 0 && ldx % 8 == 0 && ((uintptr_t)X & 15) == 0)
+    launch_lmhead_x<MT, CW, MT >= 2>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
+  else
+    launch_lmhead_x<MT, CW, false>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
 }
 
 hipError_t gemm_lmhead_topk(const void* X, int ldx, const void* W, int ldw, float* z, int M, int N,

@@ -54,6 +54,14 @@ CASES = {
                                                              cand_rank=128, num_candidates=128)), 2e-2),
     "bigvocab_k8_rows512": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
                                                              top_k=8, total_tokens=20, batch=64, ctx=24)), 2e-2),
+    # hidden 512 (K % 512 == 0): LM heads over 17..64 rows share their
+    # activations through LDS (32 beam rows here; a 64-row root pass below)
+    "bigvocab_h512_rows32": (configs.get("tiny_chain", **dict(SMALL, hidden=512, vocab=70000,
+                                                              draft_vocab=70000, top_k=8,
+                                                              total_tokens=20, batch=4)), 2e-2),
+    "bigvocab_h512_root64": (configs.get("tiny_chain", **dict(SMALL, hidden=512, vocab=70000,
+                                                              draft_vocab=70000, top_k=2, depth=2,
+                                                              total_tokens=4, batch=64, ctx=24)), 2e-2),
     # 96 beam rows of an EAGLE-4 head: the low-rank score GEMM has more column
     # tiles than the chip has CUs and runs with persistent workgroups
     "eagle4_rows96_v70000": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
