@@ -61,6 +61,14 @@ hipError_t qkv_epilogue(bool bf16, const float* P, int nsplit, int M, int nq, in
 hipError_t prologue(bool bf16, const void* embed, int V, const int* tok, const void* hid,
                     const int* src, const void* w_in, const void* w_hid, float eps, int M, int H,
                     void* gout, void* cout, hipStream_t s);
+// Split-K sum + residual (stored in y) and RMSNorm of the rounded rows (to
+// yn) in one launch, one workgroup per row; resid_norm_ok tells whether the
+// row count, shape and alignment make it the better choice (else
+// gemm_epilogue + rmsnorm).
+bool resid_norm_ok(bool bf16, int M, int H, const void* P, const void* R, const void* y,
+                   const void* w, const void* yn);
+hipError_t resid_norm(bool bf16, const float* P, int nsplit, int M, int H, const void* R, void* y,
+                      const void* w, float eps, void* yn, hipStream_t s);
 hipError_t rmsnorm(bool bf16, const void* x, const void* w, float eps, int M, int H, void* y,
                    hipStream_t s);
 

@@ -131,6 +131,74 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
   scale_store<T>(v, 1.0 / sqrt(tot / H + (double)eps), w, y + (int64_t)r * H, nvec);
 }
 
+// Split-K reduction, residual and RMSNorm of one row in one pass (one 512-thread
+// block per row): y = round(sum_s P[s][r] + resid[r]) is stored, and the row's
+// RMSNorm of the rounded y (sum of squares in float64, as rmsnorm_kernel) goes
+// to yn.  The splits are summed in order s = 0, 1, ... per element.
+constexpr int kResidThreads = 512, kResidVec = 2;  // 512 threads x 2 x 16 B of output
+
+template <typename T>
+__global__ __launch_bounds__(kResidThreads) void resid_norm_kernel(
+    const float* __restrict__ P, int nsplit, int M, int H, const T* __restrict__ R,
+    T* __restrict__ y, const T* __restrict__ w, float eps, T* __restrict__ yn) {
+  constexpr int NV = V16<T>::N;
+  __shared__ double red[kResidThreads / 64];
+  const int r = blockIdx.x;
+  const int nvec = H / NV;
+  const int64_t ss = (int64_t)M * H;
+  u32x4_t v[kResidVec];
+  double sq = 0.0;
+#pragma unroll
+  for (int j = 0; j < kResidVec; ++j) {
+    const int i = threadIdx.x + kResidThreads * j;
+    v[j] = u32x4_t{0u, 0u, 0u, 0u};
+    if (i >= nvec) continue;
+    float a[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) a[e] = 0.f;
+    const float4* p = (const float4*)(P + (int64_t)r * H + (int64_t)i * NV);
+    for (int sp = 0; sp < nsplit; ++sp) {
+#pragma unroll
+      for (int q = 0; q < NV / 4; ++q) {
+        const float4 x = p[sp * (ss / 4) + q];
+        a[4 * q] += x.x;
+        a[4 * q + 1] += x.y;
+        a[4 * q + 2] += x.z;
+        a[4 * q + 3] += x.w;
+      }
+    }
+    const u32x4_t rv = ((const u32x4_t*)(R + (int64_t)r * H))[i];
+    u32x4_t o = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < NV; ++e) V16<T>::set(o, e, a[e] + V16<T>::get(rv, e));
+    ((u32x4_t*)(y + (int64_t)r * H))[i] = o;
+    v[j] = o;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const double x = V16<T>::get(o, e);
+      sq += x * x;
+    }
+  }
+  sq = wave_sum(sq);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < kResidThreads / 64; ++k) tot += red[k];
+  const double sc = 1.0 / sqrt(tot / H + (double)eps);
+#pragma unroll
+  for (int j = 0; j < kResidVec; ++j) {
+    const int i = threadIdx.x + kResidThreads * j;
+    if (i >= nvec) continue;
+    const u32x4_t wv = ((const u32x4_t*)w)[i];
+    u32x4_t o = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < NV; ++e)
+      V16<T>::set(o, e, (float)((double)V16<T>::get(v[j], e) * sc * (double)V16<T>::get(wv, e)));
+    ((u32x4_t*)(yn + (int64_t)r * H))[i] = o;
+  }
+}
+
 }  // namespace
 
 hipError_t prologue(bool bf16, const void* embed, int V, const int* tok, const void* hid,
@@ -156,6 +224,30 @@ hipError_t rmsnorm(bool bf16, const void* x, const void* w, float eps, int M, in
   } else {
     SPEC_LAUNCH(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, s, (const float*)x,
                        (const float*)w, eps, H, (float*)y);
+  }
+  return hipGetLastError();
+}
+
+// One workgroup per row pulls the row's nsplit partials alone: worth it only
+// with enough rows to spread over the chip (below that the column-parallel
+// epilogue plus a separate norm is faster).
+bool resid_norm_ok(bool bf16, int M, int H, const void* P, const void* R, const void* y,
+                   const void* w, const void* yn) {
+  const int nv = bf16 ? 8 : 4;
+  const auto al = [](const void* q) { return ((uintptr_t)q & 15u) == 0; };
+  return M >= 64 && H % nv == 0 && H / nv <= kResidThreads * kResidVec && al(P) && al(R) &&
+         al(y) && al(w) && al(yn);
+}
+
+hipError_t resid_norm(bool bf16, const float* P, int nsplit, int M, int H, const void* R, void* y,
+                      const void* w, float eps, void* yn, hipStream_t s) {
+  if (!resid_norm_ok(bf16, M, H, P, R, y, w, yn) || nsplit < 1) return hipErrorInvalidValue;
+  if (bf16) {
+    SPEC_LAUNCH(resid_norm_kernel<bf16_t>, dim3(M), dim3(kResidThreads), 0, s, P, nsplit, M, H,
+                (const bf16_t*)R, (bf16_t*)y, (const bf16_t*)w, eps, (bf16_t*)yn);
+  } else {
+    SPEC_LAUNCH(resid_norm_kernel<float>, dim3(M), dim3(kResidThreads), 0, s, P, nsplit, M, H,
+                (const float*)R, (float*)y, (const float*)w, eps, (float*)yn);
   }
   return hipGetLastError();
 }

@@ -419,14 +419,18 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
     ProfScope ps(ctx, SPEC_PROF_ATTENTION, s);
     SPEC_HIP(ctx, attention(bf, a, s));
   }
-  // S6: O projection + residual
+  // S6: O projection + residual; S7: post-attention norm, SwiGLU MLP, residual
   {
     const GemmPlan p = gemm_plan(M, H, nqd, bf);
     SPEC_HIP(ctx, gemm(bf, ws.o, nqd, w->wo, nqd, P, M, H, nqd, p, s));
-    SPEC_HIP(ctx, gemm_epilogue(bf, EPI_RESID, ws.h1, ws.g, P, p.nsplit, M, H, s));
+    if (resid_norm_ok(bf, M, H, P, ws.g, ws.h1, w->post_attn_norm, ws.mn)) {
+      SPEC_HIP(ctx, resid_norm(bf, P, p.nsplit, M, H, ws.g, ws.h1, w->post_attn_norm, c.rms_eps,
+                               ws.mn, s));
+    } else {
+      SPEC_HIP(ctx, gemm_epilogue(bf, EPI_RESID, ws.h1, ws.g, P, p.nsplit, M, H, s));
+      SPEC_HIP(ctx, rmsnorm(bf, ws.h1, w->post_attn_norm, c.rms_eps, M, H, ws.mn, s));
+    }
   }
-  // S7: post-attention norm, SwiGLU MLP, residual
-  SPEC_HIP(ctx, rmsnorm(bf, ws.h1, w->post_attn_norm, c.rms_eps, M, H, ws.mn, s));
   {
     const GemmPlan p = gemm_plan(M, 2 * I, H, bf);
     SPEC_HIP(ctx, gemm(bf, ws.mn, H, w->w_gate_up, H, P, M, 2 * I, H, p, s));
@@ -435,10 +439,15 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
   {
     const GemmPlan p = gemm_plan(M, H, I, bf);
     SPEC_HIP(ctx, gemm(bf, ws.s, I, w->w_down, I, P, M, H, I, p, s));
-    SPEC_HIP(ctx, gemm_epilogue(bf, EPI_RESID, io.hidden_out, ws.h1, P, p.nsplit, M, H, s));
+    // S8: final norm (then the LM head; S9: top-k with log-probs)
+    if (resid_norm_ok(bf, M, H, P, ws.h1, io.hidden_out, w->final_norm, ws.nrm)) {
+      SPEC_HIP(ctx, resid_norm(bf, P, p.nsplit, M, H, ws.h1, io.hidden_out, w->final_norm,
+                               c.rms_eps, ws.nrm, s));
+    } else {
+      SPEC_HIP(ctx, gemm_epilogue(bf, EPI_RESID, io.hidden_out, ws.h1, P, p.nsplit, M, H, s));
+      SPEC_HIP(ctx, rmsnorm(bf, io.hidden_out, w->final_norm, c.rms_eps, M, H, ws.nrm, s));
+    }
   }
-  // S8: final norm and LM head; S9: top-k with log-probs
-  SPEC_HIP(ctx, rmsnorm(bf, io.hidden_out, w->final_norm, c.rms_eps, M, H, ws.nrm, s));
   if (!c.cand_rank) {
     const int Vd = c.draft_vocab;
     const GemmPlan p = gemm_plan(M, Vd, H, bf);

@@ -38,6 +38,9 @@ CASES = {
     # several context chunks and key blocks per wave, window start inside the context
     "small_bf16_longctx_window": (configs.get("tiny_chain", **dict(SMALL, ctx=700, sliding_window=300)), 2e-2),
     "small_f32_longctx": (configs.get("tiny_chain", **dict(SMALL, ctx=530, dtype="f32")), 1e-4),
+    # 64 beam rows in float32: split-K sum, residual and RMSNorm in one launch per row
+    "small_f32_rows64": (configs.get("tiny_chain", **dict(SMALL, dtype="f32", batch=8, top_k=8,
+                                                          total_tokens=20)), 1e-4),
     # large draft vocabularies run the LM head unsplit with the top-k fused in its epilogue
     "bigvocab_k1": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000, top_k=1,
                                                      total_tokens=3)), 2e-2),
