@@ -139,6 +139,15 @@ hipError_t tree_root_setup(int B, int n_new, const int* in_tokens, const int* ct
 hipError_t tree_expand(int d, int B, int n_new, const int* ctx_len, const int* in_tokens, int k,
                        int D, int N, const int* ids, const float* logp, int ld, int root_stride,
                        int root_off, TreeState st, PassRows next, TreeOut out, hipStream_t s);
+// Chain passes (top_k 1) whose LM head left per-strip records (km 1) in part:
+// the record merge of each sequence's expanding row (ids/logp, width 1), the
+// tree step, and - before the last pass - the next pass's prologue (embed,
+// hid = this pass's hidden output, norms, into gout/cout), in one launch.
+hipError_t chain_tail(bool bf16, int d, int B, int M, int n_new, const int* ctx_len,
+                      const int* in_tokens, int D, int N, int nvocab, int nch, const void* part,
+                      const int* id_map, int* ids, float* logp, TreeState st, PassRows next,
+                      TreeOut out, const void* embed, int V, const void* hid, const void* w_in,
+                      const void* w_hid, float eps, int H, void* gout, void* cout, hipStream_t s);
 
 // ------------------------------------------------------------- verify
 struct VerifyPlan {

@@ -330,6 +330,11 @@ struct PassIO {
   float* logits_out;     // null: workspace
   int* cand_ids_out;     // null: workspace
   float* cand_logits_out;
+  // chain trees: the caller merges the fused LM head's records itself (then
+  // *merge_deferred is set), and may have built this pass's prologue already
+  bool defer_merge = false;
+  bool* merge_deferred = nullptr;
+  bool skip_prologue = false;
 };
 
 spec_status check_weights(spec_ctx* ctx, const spec_weights* w) {
@@ -385,7 +390,7 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
     SPEC_HIP(ctx, gemm_epilogue(bf, EPI_STORE, ws.g, nullptr, P, p.nsplit, M, H, s));
     SPEC_HIP(ctx, prologue(bf, w->embed, c.vocab, io.tok, ws.g, nullptr, w->input_norm,
                            w->hidden_norm, c.rms_eps, M, H, ws.g, ws.c, s));
-  } else {
+  } else if (!io.skip_prologue) {
     SPEC_HIP(ctx, prologue(bf, w->embed, c.vocab, io.tok, io.hidden, io.src, w->input_norm,
                            w->hidden_norm, c.rms_eps, M, H, ws.g, ws.c, s));
   }
@@ -458,6 +463,10 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
         ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
         SPEC_HIP(ctx, gemm_lmhead_topk(ws.nrm, H, w->lm_head, H, io.logits_out, M, Vd, H, km,
                                        ws.topk_part, s));
+      }
+      if (io.defer_merge && km == 1) {
+        *io.merge_deferred = true;
+        return SPEC_OK;
       }
       ProfScope ps(ctx, SPEC_PROF_TOPK, s);
       SPEC_HIP(ctx, topk_merge_records(M, Vd, io.k_out, km, gemm_strips(M, Vd), ws.topk_part,
@@ -680,8 +689,13 @@ spec_status spec_build_tree(spec_ctx* ctx, const spec_weights* w, const spec_kv*
   PassRows rows{ws.row_tok, ws.row_pos, ws.row_slot, ws.row_src, ws.row_anc, ctx->anc_w};
   TreeState ts = tree_state(ctx);
   SPEC_HIP(ctx, tree_root_setup(B, n_new, in_tokens, ctx_len, k, D, c.kv_capacity, ts, rows, s));
+  bool pro_done = false;  // the previous chain tail built this pass's prologue
   for (int d = 1; d <= D; ++d) {
     PassIO io{};
+    bool deferred = false;
+    io.defer_merge = k == 1;
+    io.merge_deferred = &deferred;
+    io.skip_prologue = pro_done;
     io.B = B;
     io.R = d == 1 ? n_new : k;
     io.mode = d == 1 ? 0 : 1;
@@ -700,8 +714,19 @@ spec_status spec_build_tree(spec_ctx* ctx, const spec_weights* w, const spec_kv*
     io.hidden_out = ws.hout[(d - 1) & 1];
     st = run_pass(ctx, w, draft_kv, io, s);
     if (st) return st;
-    SPEC_HIP(ctx, tree_expand(d, B, n_new, ctx_len, in_tokens, k, D, c.total_tokens, ws.ids,
-                              ws.logp, k, n_new, n_new - 1, ts, rows, tree_out(out), s));
+    if (deferred) {
+      const int M = B * io.R;
+      SPEC_HIP(ctx, chain_tail(ctx->bf16, d, B, M, n_new, ctx_len, in_tokens, D, c.total_tokens,
+                               c.draft_vocab, gemm_strips(M, c.draft_vocab), ws.topk_part, w->d2t,
+                               ws.ids, ws.logp, ts, rows, tree_out(out), w->embed, c.vocab,
+                               io.hidden_out, w->input_norm, w->hidden_norm, c.rms_eps, c.hidden,
+                               ws.g, ws.c, s));
+      pro_done = d < D;
+    } else {
+      SPEC_HIP(ctx, tree_expand(d, B, n_new, ctx_len, in_tokens, k, D, c.total_tokens, ws.ids,
+                                ws.logp, k, n_new, n_new - 1, ts, rows, tree_out(out), s));
+      pro_done = false;
+    }
   }
   return SPEC_OK;
 }

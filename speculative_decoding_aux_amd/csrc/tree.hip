@@ -13,6 +13,8 @@
 // root and writes no KV.
 #include "common.h"
 #include "kernels.h"
+#include "norm_common.h"
+#include "topk_common.h"
 
 namespace spec {
 
@@ -38,13 +40,15 @@ __global__ void root_setup_kernel(int B, int n_new, const int* __restrict__ in_t
   for (int j = 0; j < A; ++j) anc[(int64_t)idx * A + j] = (act && j <= i) ? ctx + j : -1;
 }
 
-__global__ __launch_bounds__(256) void tree_expand_kernel(
-    int d, int n_new, const int* __restrict__ ctx_len, const int* __restrict__ in_tokens, int k,
-    int D, int N, const int* __restrict__ ids, const float* __restrict__ logp, int ld,
-    int root_stride, int root_off, TreeState st, int* __restrict__ beam, PassRows nx,
-    TreeOut out) {
+// Tree step of sequence b after pass d, by a 256-thread block (every thread
+// calls it).  Dynamic LDS: (2 cmax + 256) ints.
+SPEC_DEV void expand_seq(int b, int d, int n_new, const int* __restrict__ ctx_len,
+                         const int* __restrict__ in_tokens, int k, int D, int N,
+                         const int* __restrict__ ids, const float* __restrict__ logp, int ld,
+                         int root_stride, int root_off, TreeState st, int* __restrict__ beam,
+                         PassRows nx, TreeOut out) {
   extern __shared__ int sh[];  // node_of[cmax] | counts[256] | scores[cmax]
-  const int b = blockIdx.x, t = threadIdx.x;
+  const int t = threadIdx.x;
   const int cmax = st.cmax;
   int* ctok = st.tok + (int64_t)b * cmax;
   int* cpar = st.parent + (int64_t)b * cmax;
@@ -203,6 +207,53 @@ __global__ __launch_bounds__(256) void tree_expand_kernel(
   }
 }
 
+__global__ __launch_bounds__(256) void tree_expand_kernel(
+    int d, int n_new, const int* __restrict__ ctx_len, const int* __restrict__ in_tokens, int k,
+    int D, int N, const int* __restrict__ ids, const float* __restrict__ logp, int ld,
+    int root_stride, int root_off, TreeState st, int* __restrict__ beam, PassRows nx,
+    TreeOut out) {
+  expand_seq(blockIdx.x, d, n_new, ctx_len, in_tokens, k, D, N, ids, logp, ld, root_stride,
+             root_off, st, beam, nx, out);
+}
+
+// Row inputs of the next pass (prologue_row arguments besides tokens and
+// source rows, which the tree step writes).
+template <typename T>
+struct ChainPrologue {
+  const T* embed;
+  int V;
+  const T* hid;
+  const T* w_in;
+  const T* w_hid;
+  float eps;
+  int H;
+  T* gout;
+  T* cout;
+};
+
+// Tail of a chain pass (top_k 1), one block per sequence: merge the LM-head
+// records of the sequence's expanding row into its token and log-prob, run
+// the tree step, and, before the last pass, build the next pass's row input
+// (the prologue) - three launches' work in one.
+template <typename T>
+__global__ __launch_bounds__(256) void chain_tail_kernel(
+    int d, int n_new, const int* __restrict__ ctx_len, const int* __restrict__ in_tokens, int D,
+    int N, int nvocab, int nch, const float* __restrict__ pv, const int* __restrict__ pi,
+    const topkdev::Part* __restrict__ pp, const int* __restrict__ id_map, int* __restrict__ ids,
+    float* __restrict__ logp, TreeState st, int* __restrict__ beam, PassRows nx, TreeOut out,
+    ChainPrologue<T> pro) {
+  const int b = blockIdx.x;
+  const int row = d == 1 ? b * n_new + n_new - 1 : b;
+  topkdev::merge_row<1>(row, nvocab, 1, nch, pv, pi, pp, id_map, nullptr, ids, 1, logp, 1);
+  __syncthreads();  // the row's id and log-prob (global, this block) are visible
+  expand_seq(b, d, n_new, ctx_len, in_tokens, 1, D, N, ids, logp, 1, n_new, n_new - 1, st, beam,
+             nx, out);
+  if (d >= D) return;
+  __syncthreads();  // the next pass's row inputs (global, this block) are visible
+  normdev::prologue_row<T>(b, pro.embed, pro.V, nx.tok, pro.hid, nx.src, pro.w_in, pro.w_hid,
+                           pro.eps, pro.H, pro.gout, pro.cout);
+}
+
 }  // namespace
 
 hipError_t tree_root_setup(int B, int n_new, const int* in_tokens, const int* ctx_len, int k, int D,
@@ -220,6 +271,34 @@ hipError_t tree_expand(int d, int B, int n_new, const int* ctx_len, const int* i
   const size_t lds = (size_t)(2 * st.cmax + 256) * sizeof(int);
   SPEC_LAUNCH(tree_expand_kernel, dim3(B), dim3(256), lds, s, d, n_new, ctx_len, in_tokens,
                      k, D, N, ids, logp, ld, root_stride, root_off, st, st.beam, next, out);
+  return hipGetLastError();
+}
+
+hipError_t chain_tail(bool bf16, int d, int B, int M, int n_new, const int* ctx_len,
+                      const int* in_tokens, int D, int N, int nvocab, int nch, const void* part,
+                      const int* id_map, int* ids, float* logp, TreeState st, PassRows next,
+                      TreeOut out, const void* embed, int V, const void* hid, const void* w_in,
+                      const void* w_hid, float eps, int H, void* gout, void* cout, hipStream_t s) {
+  if (M != B * (d == 1 ? n_new : 1)) return hipErrorInvalidValue;
+  // record layout of the fused LM head (one entry per record): pv, pi [M][nch], pp [M][nch]
+  const float* pv = (const float*)part;
+  const int* pi = (const int*)(pv + (size_t)M * nch);
+  const topkdev::Part* pp = (const topkdev::Part*)(pi + (size_t)M * nch);
+  const size_t lds = (size_t)(2 * st.cmax + 256) * sizeof(int);
+  if (bf16) {
+    const ChainPrologue<bf16_t> pro{(const bf16_t*)embed, V, (const bf16_t*)hid,
+                                    (const bf16_t*)w_in, (const bf16_t*)w_hid, eps, H,
+                                    (bf16_t*)gout, (bf16_t*)cout};
+    SPEC_LAUNCH(chain_tail_kernel<bf16_t>, dim3(B), dim3(256), lds, s, d, n_new, ctx_len,
+                in_tokens, D, N, nvocab, nch, pv, pi, pp, id_map, ids, logp, st, st.beam, next,
+                out, pro);
+  } else {
+    const ChainPrologue<float> pro{(const float*)embed, V, (const float*)hid, (const float*)w_in,
+                                   (const float*)w_hid, eps, H, (float*)gout, (float*)cout};
+    SPEC_LAUNCH(chain_tail_kernel<float>, dim3(B), dim3(256), lds, s, d, n_new, ctx_len,
+                in_tokens, D, N, nvocab, nch, pv, pi, pp, id_map, ids, logp, st, st.beam, next,
+                out, pro);
+  }
   return hipGetLastError();
 }
 
