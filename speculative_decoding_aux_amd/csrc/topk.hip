@@ -11,6 +11,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "topk_common.h"
+#include "topk_merge.h"
 
 namespace spec {
 

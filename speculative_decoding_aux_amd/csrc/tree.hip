@@ -15,6 +15,7 @@
 #include "kernels.h"
 #include "norm_common.h"
 #include "topk_common.h"
+#include "topk_merge.h"
 
 namespace spec {
 
