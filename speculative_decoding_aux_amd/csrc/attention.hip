@@ -116,20 +116,31 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
       if (mc != -INFINITY) lc += pb[c * cstride + HD + 1] * expf(mc - m);
     }
     l = wave_sum(p) + wave_sum(lc);
-    for (int c = 0; c < nch; ++c) {
-      const float mc = __shfl(pm, c & 63, 64);
-      const float mcc = c < 64 ? mc : pb[c * cstride + HD];
-      if (mcc == -INFINITY) continue;
-      const float w = expf(mcc - m);
-      if (c < PC) {
 #pragma unroll
-        for (int cc = 0; cc < PC; ++cc)
-          if (cc == c)
+    for (int c = 0; c < PC; ++c) {
+      const float mc = __shfl(pm, c, 64);
+      if (c < nch && mc != -INFINITY) {
+        const float w = expf(mc - m);
 #pragma unroll
-            for (int i = 0; i < DPL; ++i) o[i] += po[cc][i] * w;
-      } else {
+        for (int i = 0; i < DPL; ++i) o[i] += po[c][i] * w;
+      }
+    }
+    // the remaining chunk records, four chunks' loads in flight at a time
+    for (int c0 = PC; c0 < nch; c0 += 4) {
+      float mq[4], oq[4][DPL];
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) o[i] += pb[c * cstride + lane + 64 * i] * w;
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u;
+        mq[u] = c < nch ? pb[c * cstride + HD] : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) oq[u][i] = c < nch ? pb[c * cstride + lane + 64 * i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (mq[u] == -INFINITY) continue;
+        const float w = expf(mq[u] - m);
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) o[i] += oq[u][i] * w;
       }
     }
 #pragma unroll
