@@ -559,7 +559,7 @@ __global__ __launch_bounds__(256) void qkv_epi_kernel(
 static constexpr int kMaxSplit = 32;  // bounds the epilogue's reduction depth
 static int gemm_cw(int M, int N) { return (M <= 16 && N >= 65536) ? 1 : 2; }
 
-GemmPlan gemm_plan(int M, int N, int K, bool bf16) {
+GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split) {
   GemmPlan p;
   if (bf16 && gemm_tile_ok(M, K)) {
     p = gemm_tile_plan(M, N, K);
@@ -577,7 +577,7 @@ GemmPlan gemm_plan(int M, int N, int K, bool bf16) {
   const int target = cw == 1 ? 1024 : 2048;  // workgroups in flight
   int ns = (target + strips * mblocks - 1) / (strips * mblocks);
   const int kblocks = (K + 127) / 128;
-  ns = std::max(1, std::min(std::min(ns, kblocks), kMaxSplit));
+  ns = std::max(1, std::min(std::min(ns, kblocks), std::min(kMaxSplit, std::max(1, max_split))));
   // vocab-wide heads have >= 1024 strips already: no split, so the top-k can
   // be fused into the epilogue and no M x N partials are written
   if (N >= 65536) ns = 1;

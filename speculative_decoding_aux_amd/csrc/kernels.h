@@ -13,7 +13,8 @@ struct GemmPlan {
   int kc = 0;         // K elements per split
   bool tile = false;  // LDS-tiled kernel (beam passes, M > 64) instead of weight streaming
 };
-GemmPlan gemm_plan(int M, int N, int K, bool bf16);
+// max_split caps the split-K depth of the weight-streaming kernel (M <= 64).
+GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split = 32);
 // LDS-tiled GEMM for M > 64 and K % 64 == 0 (gemm_tile.hip).
 bool gemm_tile_ok(int M, int K);
 GemmPlan gemm_tile_plan(int M, int N, int K);
@@ -65,8 +66,10 @@ hipError_t prologue(bool bf16, const void* embed, int V, const int* tok, const v
 // yn) in one launch, one workgroup per row; resid_norm_ok tells whether the
 // row count, shape and alignment make it the better choice (else
 // gemm_epilogue + rmsnorm).
-bool resid_norm_ok(bool bf16, int M, int H, const void* P, const void* R, const void* y,
-                   const void* w, const void* yn);
+bool resid_norm_ok(bool bf16, int M, int H, int nsplit, const void* P, const void* R,
+                   const void* y, const void* w, const void* yn);
+// Split-K depth at which a GEMM feeding resid_norm keeps it worthwhile at few rows.
+constexpr int kResidNormSplit = 8;
 hipError_t resid_norm(bool bf16, const float* P, int nsplit, int M, int H, const void* R, void* y,
                       const void* w, float eps, void* yn, hipStream_t s);
 hipError_t rmsnorm(bool bf16, const void* x, const void* w, float eps, int M, int H, void* y,

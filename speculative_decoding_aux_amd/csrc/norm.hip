@@ -72,15 +72,22 @@ __global__ __launch_bounds__(kResidThreads) void resid_norm_kernel(
 #pragma unroll
     for (int e = 0; e < NV; ++e) a[e] = 0.f;
     const float4* p = (const float4*)(P + (int64_t)r * H + (int64_t)i * NV);
-    for (int sp = 0; sp < nsplit; ++sp) {
+    for (int sp0 = 0; sp0 < nsplit; sp0 += 8) {  // eight splits' loads in flight
+      float4 x[8][NV / 4];
 #pragma unroll
-      for (int q = 0; q < NV / 4; ++q) {
-        const float4 x = p[sp * (ss / 4) + q];
-        a[4 * q] += x.x;
-        a[4 * q + 1] += x.y;
-        a[4 * q + 2] += x.z;
-        a[4 * q + 3] += x.w;
-      }
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int q = 0; q < NV / 4; ++q)
+          x[u][q] = sp0 + u < nsplit ? p[(sp0 + u) * (ss / 4) + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int q = 0; q < NV / 4; ++q) {
+          a[4 * q] += x[u][q].x;
+          a[4 * q + 1] += x[u][q].y;
+          a[4 * q + 2] += x[u][q].z;
+          a[4 * q + 3] += x[u][q].w;
+        }
     }
     const u32x4_t rv = ((const u32x4_t*)(R + (int64_t)r * H))[i];
     u32x4_t o = {0u, 0u, 0u, 0u};
@@ -143,20 +150,22 @@ hipError_t rmsnorm(bool bf16, const void* x, const void* w, float eps, int M, in
   return hipGetLastError();
 }
 
-// One workgroup per row pulls the row's nsplit partials alone: worth it only
-// with enough rows to spread over the chip (below that the column-parallel
-// epilogue plus a separate norm is faster).
-bool resid_norm_ok(bool bf16, int M, int H, const void* P, const void* R, const void* y,
-                   const void* w, const void* yn) {
+// One workgroup per row pulls the row's nsplit partials alone: worth it with
+// enough rows to spread over the chip, or with few partials per row (at most
+// 8 splits of 4096 float32: below that the column-parallel epilogue plus a
+// separate norm is faster).
+bool resid_norm_ok(bool bf16, int M, int H, int nsplit, const void* P, const void* R,
+                   const void* y, const void* w, const void* yn) {
   const int nv = bf16 ? 8 : 4;
   const auto al = [](const void* q) { return ((uintptr_t)q & 15u) == 0; };
-  return M >= 64 && H % nv == 0 && H / nv <= kResidThreads * kResidVec && al(P) && al(R) &&
-         al(y) && al(w) && al(yn);
+  const bool few = (int64_t)nsplit * H * 4 <= (int64_t)kResidNormSplit * 4096 * 4;
+  return (M >= 64 || few) && H % nv == 0 && H / nv <= kResidThreads * kResidVec && al(P) &&
+         al(R) && al(y) && al(w) && al(yn);
 }
 
 hipError_t resid_norm(bool bf16, const float* P, int nsplit, int M, int H, const void* R, void* y,
                       const void* w, float eps, void* yn, hipStream_t s) {
-  if (!resid_norm_ok(bf16, M, H, P, R, y, w, yn) || nsplit < 1) return hipErrorInvalidValue;
+  if (!resid_norm_ok(bf16, M, H, nsplit, P, R, y, w, yn) || nsplit < 1) return hipErrorInvalidValue;
   if (bf16) {
     SPEC_LAUNCH(resid_norm_kernel<bf16_t>, dim3(M), dim3(kResidThreads), 0, s, P, nsplit, M, H,
                 (const bf16_t*)R, (bf16_t*)y, (const bf16_t*)w, eps, (bf16_t*)yn);

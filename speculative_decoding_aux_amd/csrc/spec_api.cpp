@@ -425,10 +425,12 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
     SPEC_HIP(ctx, attention(bf, a, s));
   }
   // S6: O projection + residual; S7: post-attention norm, SwiGLU MLP, residual
+  // (at few rows the O and down GEMMs split K less, so that one launch per row
+  // can sum the splits and take the norm)
   {
-    const GemmPlan p = gemm_plan(M, H, nqd, bf);
+    const GemmPlan p = gemm_plan(M, H, nqd, bf, kResidNormSplit);
     SPEC_HIP(ctx, gemm(bf, ws.o, nqd, w->wo, nqd, P, M, H, nqd, p, s));
-    if (resid_norm_ok(bf, M, H, P, ws.g, ws.h1, w->post_attn_norm, ws.mn)) {
+    if (resid_norm_ok(bf, M, H, p.nsplit, P, ws.g, ws.h1, w->post_attn_norm, ws.mn)) {
       SPEC_HIP(ctx, resid_norm(bf, P, p.nsplit, M, H, ws.g, ws.h1, w->post_attn_norm, c.rms_eps,
                                ws.mn, s));
     } else {
@@ -442,10 +444,10 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
     SPEC_HIP(ctx, gemm_epilogue(bf, EPI_SWIGLU, ws.s, nullptr, P, p.nsplit, M, I, s));
   }
   {
-    const GemmPlan p = gemm_plan(M, H, I, bf);
+    const GemmPlan p = gemm_plan(M, H, I, bf, kResidNormSplit);
     SPEC_HIP(ctx, gemm(bf, ws.s, I, w->w_down, I, P, M, H, I, p, s));
     // S8: final norm (then the LM head; S9: top-k with log-probs)
-    if (resid_norm_ok(bf, M, H, P, ws.h1, io.hidden_out, w->final_norm, ws.nrm)) {
+    if (resid_norm_ok(bf, M, H, p.nsplit, P, ws.h1, io.hidden_out, w->final_norm, ws.nrm)) {
       SPEC_HIP(ctx, resid_norm(bf, P, p.nsplit, M, H, ws.h1, io.hidden_out, w->final_norm,
                                c.rms_eps, ws.nrm, s));
     } else {
