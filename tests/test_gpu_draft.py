@@ -189,6 +189,10 @@ BUILD = {
     "small_trimmed_tree": (configs.get("tiny_chain", **dict(SMALLB, vocab=4096, draft_vocab=512)), 2e-2),
     "small_eagle4_tree": (configs.get("tiny_chain", **dict(SMALLB, cand_rank=32, num_candidates=64)), 2e-2),
     "small_two_new_rows": (configs.get("tiny_chain", **dict(SMALLB, n_new=2)), 2e-2),
+    # deep trees: up to 10 extra keys per row (root rows, ancestors, itself),
+    # more than one batch of the attention combine
+    "deep_tree_two_new": (configs.get("tiny_chain", **dict(SMALLB, depth=8, total_tokens=10, n_new=2)), 2e-2),
+    "deep_chain": (configs.get("tiny_chain", **dict(SMALLB, top_k=1, depth=9, total_tokens=9)), 2e-2),
     # chains over a vocab-wide LM head: its records are merged, the tree step
     # taken and the next pass's inputs built in one launch per pass
     "bigvocab_chain": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000, top_k=1,
