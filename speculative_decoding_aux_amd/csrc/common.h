@@ -67,10 +67,29 @@ SPEC_DEV double wave_sum(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// Lane exchange within rows of 16 lanes by DPP (no LDS round trip):
+// CTRL 0xB1 / 0x4E swap lanes xor 1 / xor 2 within quads, 0x141 mirrors each
+// half-row (lane i <-> 7 - i), 0x140 each row (i <-> 15 - i).  Applied in that
+// order they pair every lane with one lane of each other quad, half-row and
+// row half, so a commutative, associative reduction reaches the whole row.
+template <int CTRL>
+SPEC_DEV int dpp_row(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+SPEC_DEV float dpp_row(float x) {
+  return __int_as_float(dpp_row<CTRL>(__float_as_int(x)));
+}
+SPEC_DEV float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 SPEC_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_row<0xB1>(v));
+  v = fmaxf(v, dpp_row<0x4E>(v));
+  v = fmaxf(v, dpp_row<0x141>(v));
+  v = fmaxf(v, dpp_row<0x140>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // Block-wide sum of one float (blockDim.x a multiple of 64, <= 1024).

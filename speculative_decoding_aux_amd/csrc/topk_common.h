@@ -48,17 +48,36 @@ struct List {
   }
 };
 
-// Wave-wide best (value, id) of each lane's head.
+// Wave-wide best (value, id) of each lane's head: within each row of 16 lanes
+// by DPP exchanges, then the four rows' bests read back as scalars (the order
+// (value desc, id asc) is total, so the combining order does not matter).
+template <int CTRL>
+SPEC_DEV void best_step(float& v, int& id) {
+  const float ov = dpp_row<CTRL>(v);
+  const int oi = dpp_row<CTRL>(id);
+  if (better(ov, oi, v, id)) {
+    v = ov;
+    id = oi;
+  }
+}
 SPEC_DEV void wave_best(float& v, int& id) {
+  best_step<0xB1>(v, id);
+  best_step<0x4E>(v, id);
+  best_step<0x141>(v, id);
+  best_step<0x140>(v, id);
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(id, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(id, o, 64);
-    if (better(ov, oi, v, id)) {
-      v = ov;
-      id = oi;
+  for (int r = 16; r < 64; r += 16) {
+    const float ov = lane_f(v, r);
+    const int oi = __builtin_amdgcn_readlane(id, r);
+    if (better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
     }
   }
+  v = bv;
+  id = bi;
 }
 
 // Merge the lists of the wave: the k best go to (outv, outi) (valid in every lane).
