@@ -551,6 +551,57 @@ __global__ __launch_bounds__(256) void qkv_epi_kernel(
   }
 }
 
+// The same epilogue for many rows (M >= 64): a block covers one row and HPB
+// of its heads, a group of hd/2 threads per head at a time, and each thread
+// takes its rotation pair's angle once for all its heads.  Splits are summed
+// in order s = 0, 1, ...
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_epi_rows_kernel(
+    const float* __restrict__ P, int nsplit, int M, int nq, int nkv, int hd,
+    const int* __restrict__ pos, const int* __restrict__ slot, int rows_per_seq, float rope_base,
+    T* __restrict__ qout, T* __restrict__ kc, T* __restrict__ vc, int64_t stride_seq,
+    int64_t stride_head, int slots, int hpb) {
+  const int m = blockIdx.x, half = hd >> 1;
+  const int par = blockDim.x / half;  // heads in flight per block
+  const int i = threadIdx.x % half, hs = threadIdx.x / half;
+  const int NH = nq + 2 * nkv, N = NH * hd;
+  const int64_t ss = (int64_t)M * N;
+  const double inv = pow((double)rope_base, -2.0 * i / hd);
+  double sn, cs;
+  sincos((double)pos[m] * inv, &sn, &cs);
+  const float c = (float)cs, sf = (float)sn;
+  const int seq = m / rows_per_seq;
+  const int sl = slot ? slot[m] : -1;
+  const int h1 = min(NH, (blockIdx.y + 1) * hpb);
+  for (int h = blockIdx.y * hpb + hs; h < h1; h += par) {
+    const float* p = P + (int64_t)m * N + h * hd;
+    float x1 = 0.f, x2 = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      x1 += p[sp * ss + i];
+      x2 += p[sp * ss + i + half];
+    }
+    x1 = St<T>::round(x1);
+    x2 = St<T>::round(x2);
+    if (h < nq + nkv) {
+      const float y1 = x1 * c - x2 * sf;
+      const float y2 = x2 * c + x1 * sf;
+      if (h < nq) {
+        T* q = qout + ((int64_t)m * nq + h) * hd;
+        St<T>::store(q, i, y1);
+        St<T>::store(q, i + half, y2);
+      } else if (sl >= 0 && sl < slots) {
+        T* k = kc + seq * stride_seq + (int64_t)(h - nq) * stride_head + (int64_t)sl * hd;
+        St<T>::store(k, i, y1);
+        St<T>::store(k, i + half, y2);
+      }
+    } else if (sl >= 0 && sl < slots) {
+      T* v = vc + seq * stride_seq + (int64_t)(h - nq - nkv) * stride_head + (int64_t)sl * hd;
+      St<T>::store(v, i, x1);
+      St<T>::store(v, i + half, x2);
+    }
+  }
+}
+
 }  // namespace
 
 // Columns per wave: 16 for the very wide LM head at M <= 16 (one long K sweep
@@ -728,7 +779,23 @@ hipError_t gemm_epilogue(bool bf16, int op, void* Y, const void* R, const float*
 hipError_t qkv_epilogue(bool bf16, const float* P, int nsplit, int M, int nq, int nkv, int hd,
                         const int* pos, const int* slot, int rows_per_seq, float rope_base,
                         void* qout, KvView kv, hipStream_t s) {
-  dim3 grid(M, nq + 2 * nkv);
+  const int NH = nq + 2 * nkv;
+  if (M >= 64 && hd % 2 == 0 && hd <= 256 && 256 % (hd / 2) == 0) {
+    // four blocks per row (about a dozen heads each)
+    const int hpb = (NH + 3) / 4;
+    const dim3 grid(M, (NH + hpb - 1) / hpb);
+    if (bf16) {
+      SPEC_LAUNCH(qkv_epi_rows_kernel<bf16_t>, grid, dim3(256), 0, s, P, nsplit, M, nq, nkv, hd,
+                  pos, slot, rows_per_seq, rope_base, (bf16_t*)qout, (bf16_t*)kv.k,
+                  (bf16_t*)kv.v, kv.stride_seq, kv.stride_head, kv.slots, hpb);
+    } else {
+      SPEC_LAUNCH(qkv_epi_rows_kernel<float>, grid, dim3(256), 0, s, P, nsplit, M, nq, nkv, hd,
+                  pos, slot, rows_per_seq, rope_base, (float*)qout, (float*)kv.k, (float*)kv.v,
+                  kv.stride_seq, kv.stride_head, kv.slots, hpb);
+    }
+    return hipGetLastError();
+  }
+  dim3 grid(M, NH);
   dim3 block(256);
   if (bf16) {
     SPEC_LAUNCH(qkv_epi_kernel<bf16_t>, grid, block, 0, s, P, nsplit, M, nq, nkv, hd, pos,

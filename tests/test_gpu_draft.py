@@ -50,6 +50,9 @@ CASES = {
     # down projection is not a multiple of 64 and takes the streaming kernel
     "tile_rows72_ragged": (configs.get("tiny_chain", **dict(SMALL, batch=9, top_k=8, total_tokens=20,
                                                             intermediate=480)), 2e-2),
+    # 72 beam rows with 128-wide heads (the many-row QKV epilogue, 4 heads in flight)
+    "tile_rows72_hd128": (configs.get("tiny_chain", **dict(SMALL, batch=9, top_k=8, total_tokens=20,
+                                                           head_dim=128)), 2e-2),
     # EAGLE-4 head at width 2048 and a 70000 vocab: 128 candidates retrieved by
     # the group-maximum select and rescored with 16-byte weight loads
     "eagle4_h2048_v70000": (configs.get("tiny_chain", **dict(SMALL, hidden=2048, n_q_heads=16, n_kv_heads=4,
