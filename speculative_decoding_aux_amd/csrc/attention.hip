@@ -472,8 +472,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         v[e] = (key < k1 && key >= loq[t]) ? sc4[t][e] * scale : -INFINITY;
         tmax = fmaxf(tmax, v[e]);
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      {
+        float a, bb;
+        swap16(tmax, a, bb);
+        tmax = fmaxf(a, bb);
+        swap32(tmax, a, bb);
+        tmax = fmaxf(a, bb);
+      }
       const float mnew = fmaxf(mrun[t], tmax);
       const float alpha = mrun[t] == -INFINITY ? (mnew == -INFINITY ? 1.f : 0.f)
                                                : __builtin_amdgcn_exp2f(mrun[t] - mnew);
@@ -483,8 +488,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         v[e] = v[e] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(v[e] - mnew);
         psum += v[e];
       }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
+      {
+        float a, bb;
+        swap16(psum, a, bb);
+        psum = a + bb;
+        swap32(psum, a, bb);
+        psum = a + bb;
+      }
       lrun[t] = lrun[t] * alpha + psum;
       mrun[t] = mnew;
       // P = P_hi + P_lo in two bf16 parts (about 16 significant bits), so the

@@ -84,6 +84,40 @@ SPEC_DEV float lane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// Row-pair and half-wave exchanges (gfx950 permlane swaps, no LDS round
+// trip): with both operands x, permlane16_swap returns rows (x0, x0, x2, x2)
+// and (x1, x1, x3, x3) of 16 lanes, permlane32_swap the halves (xlo, xlo) and
+// (xhi, xhi).  Combining the two results commutatively equals combining each
+// lane with lane ^ 16 (^ 32); the partner value itself is picked by row parity.
+SPEC_DEV void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+SPEC_DEV void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+// x of lane ^ 16 and lane ^ 32
+SPEC_DEV float xor16(float x) {
+  float a, b;
+  swap16(x, a, b);
+  return ((threadIdx.x >> 4) & 1) ? a : b;
+}
+SPEC_DEV float xor32(float x) {
+  float a, b;
+  swap32(x, a, b);
+  return ((threadIdx.x >> 5) & 1) ? a : b;
+}
+SPEC_DEV int xor16(int x) { return __float_as_int(xor16(__int_as_float(x))); }
+SPEC_DEV int xor32(int x) { return __float_as_int(xor32(__int_as_float(x))); }
+// lane ^ o for o = 16 or 32 (uniform)
+template <typename V>
+SPEC_DEV V xor_hi(V x, int o) {
+  return o == 16 ? xor16(x) : xor32(x);
+}
+
 SPEC_DEV float wave_max(float v) {
   v = fmaxf(v, dpp_row<0xB1>(v));
   v = fmaxf(v, dpp_row<0x4E>(v));

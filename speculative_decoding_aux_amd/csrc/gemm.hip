@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void gemm_lmhead_topk_kernel(
     // merge the four lane groups holding the same row
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
-      const float om = __shfl_xor(lm, o, 64), os = __shfl_xor(ls, o, 64);
+      const float om = xor_hi(lm, o), os = xor_hi(ls, o);
       const float mx = fmaxf(lm, om);
       ls = (lm == -INFINITY ? 0.f : ls * expf(lm - mx)) + (om == -INFINITY ? 0.f : os * expf(om - mx));
       lm = mx;
@@ -301,8 +301,8 @@ __global__ __launch_bounds__(256) void gemm_lmhead_topk_kernel(
       int pii[KM];
 #pragma unroll
       for (int j = 0; j < KM; ++j) {
-        pvv[j] = __shfl_xor(L.v[j], o, 64);
-        pii[j] = __shfl_xor(L.i[j], o, 64);
+        pvv[j] = xor_hi(L.v[j], o);
+        pii[j] = xor_hi(L.i[j], o);
       }
 #pragma unroll
       for (int j = 0; j < KM; ++j) L.insert(pvv[j], pii[j]);

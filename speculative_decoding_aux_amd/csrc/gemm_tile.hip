@@ -244,7 +244,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
         }
 #pragma unroll
         for (int o = 16; o <= 32; o <<= 1) {
-          const float om = __shfl_xor(m, o, 64), os = __shfl_xor(sum, o, 64);
+          const float om = xor_hi(m, o), os = xor_hi(sum, o);
           const float nm = fmaxf(m, om);
           if (nm != -INFINITY)
             sum = (m == -INFINITY ? 0.f : sum * __builtin_amdgcn_exp2f((m - nm) * kL2e)) +
