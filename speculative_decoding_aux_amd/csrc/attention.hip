@@ -512,17 +512,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         for (int dt = 0; dt < DT; ++dt) o[t][dt] *= alpha;
       }
     }
-    // V^T fragment of dims dt*16 + col: keys 4g..4g+3
+    // V^T fragment of dims dt*16 + col, keys 4g..4g+3, by one transposed LDS
+    // read (ds_read_b64_tr_b16): within each 16-lane group, lane s points at
+    // key 4g + s/4, dims dt*16 + 4(s%4) .. +3, and lane t receives dim
+    // dt*16 + t of the group's four keys
+    const int trow = 4 * g + (col >> 2);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const int chn = (dt * 16 + col) >> 3, el = (dt * 16 + col) & 7;
-      uint32_t h16[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 4 * g + e;
-        h16[e] = vs[(row * CH + (chn ^ v_swz(row))) * 8 + el];
-      }
-      const uint2 vf = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
+      const int d0 = dt * 16 + 4 * (col & 3);
+      SPEC_LDS s16x4* ap =
+          (SPEC_LDS s16x4*)(vs + (trow * CH + ((d0 >> 3) ^ v_swz(trow))) * 8 + (d0 & 7));
+      const uint2 vf = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(ap));
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
         o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vf),
