@@ -28,7 +28,7 @@ HBM_PEAK_GBS = 8000.0
 # PROF_EVERY-th timed step: it still costs the stream a few microseconds per
 # timed launch, so the other steps run untimed.
 PROF_EVERY = 5
-BF16_PEAK_TFLOPS = 2500.0
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 
 
 def parse():
@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--config", default="llama8b_chain")
     ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the attainable-peak probes run after the timed steps")
     ap.add_argument("--cpu-steps", type=int, default=2)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
@@ -84,6 +86,39 @@ def measured_traffic(workload):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["kernel_source_sha256"] else None
 
 
+def kernel_figures(cfg, rows, lm, att, ver):
+    """Per-label launch figures of the sampled steps: average launch time,
+    algorithmic bytes (and, for the LM head, GEMM flops) per launch, achieved
+    rates and their fractions of the published peaks.  Attention: the visible
+    context K and V of every (sequence, kv head) once per pass (the window at
+    most); verify: every node row's target logits once."""
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    B, nkv, hd = cfg["batch"], cfg["n_kv_heads"], cfg["head_dim"]
+    ctx = min(cfg["ctx"], cfg["sliding_window"]) if cfg["sliding_window"] else cfg["ctx"]
+    out = {}
+
+    def rate(name, nl, ms, byts, flops=None):
+        if nl <= 0:
+            return
+        us = ms / nl * 1e3
+        e = {"avg_launch_us": round(us, 2), "launches": nl, "algorithmic_bytes_per_launch": int(byts),
+             "achieved_gbs": round(byts / (us * 1e-6) / 1e9, 1)}
+        e["frac"] = round(e["achieved_gbs"] / HBM_PEAK_GBS, 4)
+        if flops:
+            e["flops_per_launch"] = int(flops)
+            e["mfma_tflops"] = round(flops / (us * 1e-6) / 1e12, 1)
+            e["mfma_frac"] = round(e["mfma_tflops"] / BF16_PEAK_TFLOPS, 4)
+        out[name] = e
+
+    if cfg["dtype"] == "bf16" and not cfg["cand_rank"]:
+        byts = sum(lm_head_bytes(cfg, m) for m in rows) / len(rows)
+        flops = sum(2.0 * m * cfg["draft_vocab"] * cfg["hidden"] for m in rows) / len(rows)
+        rate("lm_head", lm[0], lm[1], byts, flops)
+    rate("attention", att[0], att[1], B * nkv * ctx * hd * 2 * es)
+    rate("verify", ver[0], ver[1], B * (cfg["total_tokens"] + 1) * cfg["vocab"] * 4)
+    return out
+
+
 def pass_rows(cfg):
     B, k, D, n_new = cfg["batch"], cfg["top_k"], cfg["depth"], cfg["n_new"]
     return [B * n_new] + [B * k] * (D - 1)
@@ -121,9 +156,23 @@ def cpu_baseline(cfg, W, inp, seed, steps):
         t3 = time.perf_counter()
         times.append((t1 - t0) + (t3 - t2))  # input planting excluded
     med = float(np.median(times))
-    return {"value": 1.0 / med, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} whole steps of the same workload (batch {cfg['batch']}); "
-                      f"median {med:.3f} s per step; compaction on a 1-layer cache"}
+    res = {"value": 1.0 / med, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{steps} whole steps of the same workload (batch {cfg['batch']}); "
+                     f"median {med:.3f} s per step; compaction on a 1-layer cache"}
+    if med < 2.0:  # the same step on one BLAS thread, where that stays within seconds
+        try:
+            from threadpoolctl import threadpool_limits
+        except Exception:  # pragma: no cover
+            return res
+        with threadpool_limits(limits=1):
+            t1 = []
+            for _ in range(steps):
+                kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
+                t0 = time.perf_counter()
+                ot.build_tree(cfg, W, kc, vc, inp["aux"], inp["in_tokens"], inp["ctx_len"])
+                t1.append(time.perf_counter() - t0)
+        res["value_1thread_build"] = round(1.0 / float(np.median(t1)), 4)
+    return res
 
 
 def main():
@@ -243,6 +292,7 @@ def main():
                 "kernel": "LM head (gemm_lmhead_topk_kernel / gemm_bf16_stream<*,1,*>)" if cfg["dtype"] == "bf16" else "gemm_f32_rows",
                 "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n, "timed_every_nth_step": PROF_EVERY,
                 "algorithmic_bytes_per_launch": int(byts)}
+        kern = kernel_figures(cfg, rows, (n, ms), (na, msa), (nv, msv))
         print(f"[bench] lm_head {n} launches avg {avg_ms*1e3:.1f} us; attention avg "
               f"{msa / max(na, 1) * 1e3:.1f} us; verify avg {msv / max(nv, 1) * 1e3:.1f} us",
               file=sys.stderr, flush=True)
@@ -264,6 +314,21 @@ def main():
                    "graph": bool(graph is not None), "wall_s": round(wall, 3)},
         "roofline": roof,
     }
+    if roof is not None:
+        res["kernels"] = kern
+        if not args.no_peaks:
+            from speculative_decoding_aux_amd import peaks as PK
+
+            print("[bench] measuring attainable peaks (read/copy stream, MFMA loop)", file=sys.stderr, flush=True)
+            pk = PK.measure()
+            res["peaks_measured"] = pk
+            roof["measured_peak"] = pk["hbm_read_gbs"]
+            roof["frac_of_measured"] = round(roof["achieved"] / pk["hbm_read_gbs"], 4)
+            for v in kern.values():
+                if "achieved_gbs" in v:
+                    v["frac_of_measured"] = round(v["achieved_gbs"] / pk["hbm_read_gbs"], 4)
+                if "mfma_tflops" in v:
+                    v["mfma_frac_of_measured"] = round(v["mfma_tflops"] / pk["mfma_bf16_tflops"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, W, inp, seed, args.cpu_steps)

@@ -28,24 +28,49 @@ template <> SPEC_DEV float unpack<bf16_t>(const u32x4_t& w, int e) {
   return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
 }
 
+// N consecutive values (N = 1 or 2) as floats, by one load or store.
+template <typename T, int N>
+SPEC_DEV void load_dims(const T* p, float (&x)[N]) {
+  if constexpr (N == 1) {
+    x[0] = St<T>::load(p, 0);
+  } else if constexpr (std::is_same<T, float>::value) {
+    const float2 v = *(const float2*)p;
+    x[0] = v.x;
+    x[1] = v.y;
+  } else {
+    const uint32_t v = *(const uint32_t*)p;
+    x[0] = __uint_as_float(v << 16);
+    x[1] = __uint_as_float(v & 0xffff0000u);
+  }
+}
+template <typename T, int N>
+SPEC_DEV void store_dims(T* p, const float (&x)[N]) {
+  if constexpr (N == 1) {
+    St<T>::store(p, 0, x[0]);
+  } else if constexpr (std::is_same<T, float>::value) {
+    *(float2*)p = make_float2(x[0], x[1]);
+  } else {
+    *(uint32_t*)p = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+  }
+}
+
 // Final attention output of one query vector (row r, q-head h), computed by
-// one wave: merge the context-chunk records with the row's extra keys.  Lane j
-// scores extra key j (its own 16-byte key loads, q from LDS); each lane then
-// accumulates its dims over the chunk records and the extra keys' values.
-// Every load that depends on nothing (q, the extra-key slots, the first
-// chunk records) is issued first and the extra keys' K and V rows right after
-// the slots arrive, so the wave waits on two round trips to memory, not one
-// per stage.
+// one wave: merge the context-chunk records with the row's extra keys.  Lane l
+// holds dims DPL*l .. DPL*l + DPL - 1 (DPL = HD / 64) of q, of the output and
+// of every K and V row it reads, so an extra key's score is a wave-wide sum
+// and a row is one coalesced load of DPL consecutive values per lane.  Extra keys go in batches of eight (their K and V rows
+// loaded together); the loads that depend on nothing (q, the extra-key
+// slots, the first chunk records) are issued first and the first batch's rows
+// as soon as the slots arrive, so the wave waits on two round trips to memory.
 template <typename T, int HD>
 SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restrict__ kc,
                          const T* __restrict__ vc, int64_t sseq, int64_t shead, int S,
                          const int* __restrict__ pos, const int* __restrict__ anc, int A, int R,
                          int nq, int nkv, int window, int nch, const float* __restrict__ part,
-                         T* __restrict__ out, float* qs /* LDS, HD floats for this wave */) {
+                         T* __restrict__ out) {
   constexpr int DPL = HD / 64;  // dims per lane
-  constexpr int EPV = 16 / sizeof(T);
   constexpr int PC = 4;         // chunk records prefetched
-  constexpr int PV = 8;         // extra keys whose values are prefetched
+  constexpr int KB = 8;         // extra keys per batch
   const int lane = threadIdx.x & 63;
   const int G = nq / nkv, kvh = h / G;
   const int b = r / R, qv = (r % R) * G + h % G, QV = R * G;
@@ -56,8 +81,7 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
   const int sl = lane < A ? anc[(int64_t)r * A + lane] : -1;
   const int pq = pos[r];
   float qr[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) qr[i] = St<T>::load(q, ((int64_t)r * nq + h) * HD + lane + 64 * i);
+  load_dims<T, DPL>(q + ((int64_t)r * nq + h) * HD + DPL * lane, qr);
   float pm = -INFINITY, pl = 0.f;
   if (lane < nch) {
     pm = pb[lane * cstride + HD];
@@ -65,43 +89,42 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
   }
   float po[PC][DPL];
 #pragma unroll
-  for (int c = 0; c < PC; ++c)
+  for (int c = 0; c < PC; ++c) {
+    if (c < nch) {
+      load_dims<float, DPL>(pb + c * cstride + DPL * lane, po[c]);
+    } else {
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) po[c][i] = c < nch ? pb[c * cstride + lane + 64 * i] : 0.f;
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) qs[lane + 64 * i] = qr[i];
+      for (int i = 0; i < DPL; ++i) po[c][i] = 0.f;
+    }
+  }
   // extra keys: valid entries hold consecutive positions ending at pos[r]
   const unsigned long long vmask = __ballot(sl >= 0);
   const int nvalid = __popcll(vmask);
   const int rank = __popcll(vmask & ((1ull << lane) - 1ull));
+  const bool vis = sl >= 0 && sl < S && (window <= 0 || pq - (nvalid - 1 - rank) > pq - window);
+  const unsigned long long kmask = __ballot(vis);
   const T* kb = kc + b * sseq + kvh * shead;
   const T* vb = vc + b * sseq + kvh * shead;
-  const bool vis = sl >= 0 && sl < S && (window <= 0 || pq - (nvalid - 1 - rank) > pq - window);
-  // round trip 2: the extra keys' K rows (lane j) and the first PV value rows
-  u32x4_t kr[HD / EPV];
-  if (vis) {
-    const u32x4_t* kp = (const u32x4_t*)(kb + (int64_t)sl * HD);
+  float kv[KB][DPL], vv[KB][DPL];
+  auto load_batch = [&](int j0) {
 #pragma unroll
-    for (int vq = 0; vq < HD / EPV; ++vq) kr[vq] = kp[vq];
-  }
-  float vv[PV][DPL];
+    for (int u = 0; u < KB; ++u) {
+      const int j = j0 + u;
+      const bool ok = j < 64 && ((kmask >> j) & 1ull);
+      const int64_t row = (int64_t)__shfl(sl, j & 63, 64) * HD + DPL * lane;
+      if (ok) {
+        load_dims<T, DPL>(kb + row, kv[u]);
+        load_dims<T, DPL>(vb + row, vv[u]);
+      } else {
 #pragma unroll
-  for (int u = 0; u < PV; ++u) {
-    const int slj = __shfl(sl, u, 64);
-    const bool visj = __shfl((int)vis, u, 64) != 0;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) vv[u][i] = visj ? St<T>::load(vb, (int64_t)slj * HD + lane + 64 * i) : 0.f;
-  }
-  float s = -INFINITY;
-  if (vis) {
-    float a = 0.f;
-#pragma unroll
-    for (int vq = 0; vq < HD / EPV; ++vq)
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) a += qs[vq * EPV + e] * unpack<T>(kr[vq], e);
-    s = a * inv_sqrt;
-  }
-  float m = fmaxf(pm, s);
+        for (int i = 0; i < DPL; ++i) kv[u][i] = vv[u][i] = 0.f;
+      }
+    }
+  };
+  // round trip 2: the first batch of extra keys
+  load_batch(0);
+  // context chunks: their maximum, then the rescaled sums
+  float m = pm;
   for (int c = lane + 64; c < nch; c += 64) m = fmaxf(m, pb[c * cstride + HD]);
   m = wave_max(m);
   float l = 0.f;
@@ -109,13 +132,12 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
 #pragma unroll
   for (int i = 0; i < DPL; ++i) o[i] = 0.f;
   if (m != -INFINITY) {
-    const float p = s == -INFINITY ? 0.f : expf(s - m);
     float lc = pm == -INFINITY ? 0.f : pl * expf(pm - m);
     for (int c = lane + 64; c < nch; c += 64) {
       const float mc = pb[c * cstride + HD];
       if (mc != -INFINITY) lc += pb[c * cstride + HD + 1] * expf(mc - m);
     }
-    l = wave_sum(p) + wave_sum(lc);
+    l = wave_sum_uniform(lc);
 #pragma unroll
     for (int c = 0; c < PC; ++c) {
       const float mc = __shfl(pm, c, 64);
@@ -132,8 +154,12 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
       for (int u = 0; u < 4; ++u) {
         const int c = c0 + u;
         mq[u] = c < nch ? pb[c * cstride + HD] : -INFINITY;
+        if (c < nch) {
+          load_dims<float, DPL>(pb + c * cstride + DPL * lane, oq[u]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) oq[u][i] = c < nch ? pb[c * cstride + lane + 64 * i] : 0.f;
+          for (int i = 0; i < DPL; ++i) oq[u][i] = 0.f;
+        }
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -143,36 +169,45 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
         for (int i = 0; i < DPL; ++i) o[i] += oq[u][i] * w;
       }
     }
+  }
+  // extra keys, batch by batch: scores, running max, rescale, accumulate
+#pragma unroll 1
+  for (int j0 = 0; j0 < 64 && (kmask >> j0); j0 += KB) {
+    if (j0 > 0) load_batch(j0);
+    float s[KB];
 #pragma unroll
-    for (int u = 0; u < PV; ++u) {
-      const float pj = __shfl(p, u, 64);
+    for (int u = 0; u < KB; ++u) {
+      float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) o[i] += pj * vv[u][i];
+      for (int i = 0; i < DPL; ++i) a += qr[i] * kv[u][i];
+      s[u] = wave_sum_uniform(a) * inv_sqrt;
     }
-    // extra keys past the first PV, eight keys' loads in flight at a time
-    for (int j0 = PV; j0 < 64; j0 += 8) {
-      if (!(vmask >> j0)) break;
-      float vw[8][DPL], pj[8];
+    float bm = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u;
-        const int slj = __shfl(sl, j, 64);
-        pj[u] = __shfl(p, j, 64);
-        const bool ok = ((vmask >> j) & 1ull) && pj[u] > 0.f;
+    for (int u = 0; u < KB; ++u)
+      if (j0 + u < 64 && ((kmask >> (j0 + u)) & 1ull)) bm = fmaxf(bm, s[u]);
+    const float mn = fmaxf(m, bm);
+    if (mn == -INFINITY) continue;
+    if (mn != m) {
+      const float alpha = m == -INFINITY ? 0.f : expf(m - mn);
+      l *= alpha;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i)
-          vw[u][i] = ok ? St<T>::load(vb, (int64_t)slj * HD + lane + 64 * i) : 0.f;
-        if (!ok) pj[u] = 0.f;
-      }
+      for (int i = 0; i < DPL; ++i) o[i] *= alpha;
+      m = mn;
+    }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < KB; ++u) {
+      if (!(j0 + u < 64 && ((kmask >> (j0 + u)) & 1ull))) continue;
+      const float p = expf(s[u] - m);
+      l += p;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) o[i] += pj[u] * vw[u][i];
+      for (int i = 0; i < DPL; ++i) o[i] += p * vv[u][i];
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) St<T>::store(out, ((int64_t)r * nq + h) * HD + lane + 64 * i, o[i] * inv);
+  for (int i = 0; i < DPL; ++i) o[i] *= inv;
+  store_dims<T, DPL>(out + ((int64_t)r * nq + h) * HD + DPL * lane, o);
 }
 
 // One wave per (row, q-head).
@@ -186,9 +221,8 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const T* __restrict__ 
                                                           int R, int nq, int nkv, int window,
                                                           int nch, const float* __restrict__ part,
                                                           T* __restrict__ out) {
-  __shared__ float qs[HD];
   combine_qv<T, HD>(blockIdx.x, blockIdx.y, q, kc, vc, sseq, shead, S, pos, anc, A, R, nq, nkv,
-                    window, nch, part, out, qs);
+                    window, nch, part, out);
 }
 
 template <typename T, int HD>

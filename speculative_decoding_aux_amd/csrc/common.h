@@ -126,6 +126,16 @@ SPEC_DEV float wave_max(float v) {
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// Wave-wide sum by DPP row reductions and four lane reads: the same value in
+// every lane (the row sums are added in the order of rows 0..3).
+SPEC_DEV float wave_sum_uniform(float v) {
+  v += dpp_row<0xB1>(v);
+  v += dpp_row<0x4E>(v);
+  v += dpp_row<0x141>(v);
+  v += dpp_row<0x140>(v);
+  return ((lane_f(v, 0) + lane_f(v, 16)) + lane_f(v, 32)) + lane_f(v, 48);
+}
+
 // Block-wide sum of one float (blockDim.x a multiple of 64, <= 1024).
 SPEC_DEV float block_sum(float v, float* red /* >= 16 floats of LDS */) {
   v = wave_sum(v);

@@ -1,5 +1,7 @@
-"""The C-ABI library loads on the CPU, exports every function include/spec.h
-declares, and rejects bad configurations before touching the GPU."""
+"""The C-ABI libraries load on the CPU and export every function their headers
+declare (include/spec.h: the speculation library; include/spec_peaks.h: the
+peak probes), and the speculation library rejects bad configurations before
+touching the GPU."""
 
 import ctypes
 import os
@@ -19,8 +21,8 @@ def lib():
     return L.load()
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "spec.h")).read()
+def _declared(header="spec.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", src)))
 
 
@@ -30,6 +32,28 @@ def test_every_declared_symbol_is_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
+
+
+def test_every_include_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["spec.h", "spec_peaks.h"]
+
+
+def test_peak_probes_export_their_header():
+    from speculative_decoding_aux_amd import peaks as PK
+
+    if not os.path.exists(PK.LIB_PATH):
+        from speculative_decoding_aux_amd import build
+        build.build()
+    plib = PK.load()
+    names = _declared("spec_peaks.h")
+    assert set(names) == set(PK.EXPORTS)
+    for n in names:
+        assert hasattr(plib, n), n
+    assert plib.spec_peak_mfma_flops(10, 4) == 4 * 4 * 10 * 8 * 16 * 16 * 32 * 2
+    # argument checks return before any launch
+    assert plib.spec_peak_read(None, 16, None, 1, None) == -1
+    assert plib.spec_peak_copy(ctypes.c_void_p(16), ctypes.c_void_p(16), 16, 1, None) == -1
+    assert plib.spec_peak_mfma(0, ctypes.c_void_p(16), 1, None) == -1
 
 
 def test_version_string(lib):
