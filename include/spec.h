@@ -11,6 +11,10 @@
  * Stage-level entry points expose single steps of the same path:
  *   spec_draft_step, spec_topk_logprobs, spec_retrieve_candidates,
  *   spec_tree_from_topk.
+ * Flat batches of variable-length draft chains with per-request sampling
+ * parameters: spec_decode_metadata (index bookkeeping) and
+ * spec_rejection_sample (greedy / random acceptance with temperature, top-k
+ * and top-p).
  *
  * Sources: "Speculative Decoding (EAGLE3) in the vLLM Neuron Framework"
  * (sections "What is EAGLE3?", "Eagle3 Draft Model Architecture", "The
@@ -231,6 +235,56 @@ spec_status spec_verify_tree(spec_ctx* ctx, int32_t B, const spec_tree* tree,
                              const float* target_logits, int32_t mode, float temperature,
                              const float* accept_u, uint64_t seed, int32_t* out_tokens,
                              int32_t* accepted_len, int32_t* accepted_nodes, void* stream);
+
+/* Index bookkeeping of a flat batch of variable-length draft chains (vLLM
+ * Neuron page, "SpecDecodeMetadata: Index Bookkeeping"): request r has
+ * n_r = num_draft_tokens[r] drafts (negative counts read as 0) and logits at
+ * its last n_r + 1 scheduled positions, cu_num_scheduled_tokens[r] - n_r - 1
+ * + j for j = 0..n_r.  Outputs (device, caller-owned, T = sum of n_r):
+ *   cu_num_draft_tokens[B]   inclusive prefix sums of n_r;
+ *   logits_indices[T + B]    those positions, request by request;
+ *   target_logits_indices[T] entries of logits_indices at draft positions;
+ *   bonus_logits_indices[B]  the entry of each request's last position.
+ * One workgroup; no host synchronisation. */
+spec_status spec_decode_metadata(spec_ctx* ctx, int32_t B, const int32_t* cu_num_scheduled_tokens,
+                                 const int32_t* num_draft_tokens, int32_t* cu_num_draft_tokens,
+                                 int32_t* logits_indices, int32_t* target_logits_indices,
+                                 int32_t* bonus_logits_indices, void* stream);
+
+/* Rejection sampling of a flat batch (vLLM Neuron page, "Rejection
+ * Sampling", CPU rejection sampler: mixed greedy / random requests with
+ * per-request temperature, top-k and top-p, draft_prob = 1).
+ *   cu_num_draft_tokens[B]: inclusive prefix sums of the per-request draft
+ *     counts n_r (0 <= n_r <= max_spec_len <= total_tokens);
+ *   draft_token_ids[T]: drafts of request r at [cu[r] - n_r, cu[r]), ids in
+ *     [0, vocab) (an id outside is never accepted by a random request);
+ *   logits[num_logits_rows, vocab] float32: draft j of request r is verified
+ *     against row target_logits_indices[cu[r] - n_r + j], the bonus position
+ *     is row bonus_logits_indices[r] (indices clamped to the rows);
+ *   temperature[B]: 0 = greedy (argmax, first index on ties; top-k/top-p
+ *     ignored); top_k[B] (<= 0 or >= vocab: off) and top_p[B] (>= 1: off)
+ *     may be NULL (off for every request);
+ *   uniform[T]: the acceptance draws; NULL makes every request greedy.
+ * A random request ranks tokens by (logit desc, id asc), keeps the first
+ * top_k, then the shortest prefix of those whose mass (renormalised over the
+ * top-k set) reaches top_p, and samples from p_f = softmax(l / T) over the
+ * kept tokens: draft j is accepted iff uniform <= p_f(draft); at the first
+ * rejection the emitted token is argmax over kept v != draft of
+ * l/T - log(-log U), after n_r acceptances the bonus is the same argmax at
+ * the bonus row without exclusion; U from Philox4x32-10 keyed by seed with
+ * counter (v >> 2, j, r, 0) (j = n_r at the bonus row), word v & 3,
+ * U = ((x >> 8) + 0.5) * 2^-24.  Masses are exp(l/T - max) in float32
+ * summed in float64.
+ * Outputs: out_tokens[B, max_spec_len + 1] (accepted drafts, the emitted
+ * token, -1 padding) and num_accepted[B].  vocab <= 2^18. */
+spec_status spec_rejection_sample(spec_ctx* ctx, int32_t B, int32_t max_spec_len,
+                                  const int32_t* cu_num_draft_tokens,
+                                  const int32_t* draft_token_ids, const float* logits,
+                                  int32_t num_logits_rows, const int32_t* target_logits_indices,
+                                  const int32_t* bonus_logits_indices, const float* temperature,
+                                  const int32_t* top_k, const float* top_p, const float* uniform,
+                                  uint64_t seed, int32_t* out_tokens, int32_t* num_accepted,
+                                  void* stream);
 
 /* KV compaction of the accepted path, every layer of `kv`: for each
  * sequence b and j < accepted_len[b], the row at slot tree_base[b] +

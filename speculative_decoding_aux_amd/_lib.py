@@ -45,7 +45,8 @@ class SpecTree(ctypes.Structure):
 
 EXPORTS = ["spec_create", "spec_destroy", "spec_last_error", "spec_workspace_bytes", "spec_version",
            "spec_draft_step", "spec_topk_logprobs", "spec_retrieve_candidates", "spec_tree_from_topk", "spec_build_tree",
-           "spec_verify_tree", "spec_compact_kv", "spec_profile_enable", "spec_profile_read"]
+           "spec_verify_tree", "spec_compact_kv", "spec_decode_metadata", "spec_rejection_sample",
+           "spec_profile_enable", "spec_profile_read"]
 SPEC_PROF_LM_HEAD, SPEC_PROF_ATTENTION, SPEC_PROF_VERIFY, SPEC_PROF_TOPK = 0, 1, 2, 3
 
 _lib = None
@@ -89,6 +90,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_tree.restype = c_i32
     lib.spec_compact_kv.argtypes = [c_vp, P(SpecKV), c_i32, c_vp, c_vp, c_vp, c_i32, c_vp]
     lib.spec_compact_kv.restype = c_i32
+    lib.spec_decode_metadata.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.spec_decode_metadata.restype = c_i32
+    lib.spec_rejection_sample.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp,
+                                          c_vp, c_vp, c_vp, c_vp, ctypes.c_uint64, c_vp, c_vp, c_vp]
+    lib.spec_rejection_sample.restype = c_i32
     lib.spec_profile_enable.argtypes = [c_vp, c_i32]
     lib.spec_profile_enable.restype = c_i32
     lib.spec_profile_read.argtypes = [c_vp, c_i32, P(c_i32), P(ctypes.c_double)]

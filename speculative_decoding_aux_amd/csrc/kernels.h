@@ -164,6 +164,20 @@ hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const in
                   const float* accept_u, uint64_t seed, int* out_tokens, int* accepted_len,
                   int* accepted_nodes, void* ws, const VerifyPlan& p, hipStream_t s);
 
+// ------------------------------------------------------------ flat-batch sampling
+struct SamplePlan {
+  int gch, gchunk;   // Gumbel pass: vocab chunks per request's stop row
+};
+SamplePlan sample_plan(int B, int V);
+size_t sample_ws_bytes(const SamplePlan& p, int B, int L);
+hipError_t sample_metadata(int B, const int* cu_sched, const int* nd, int* cu_nd, int* logits_idx,
+                           int* tgt_idx, int* bonus_idx, hipStream_t s);
+hipError_t rejection_sample(int B, int L, int V, int nrows, const int* cu_nd, const int* drafts,
+                            const float* logits, const int* tgt_idx, const int* bonus_idx,
+                            const float* temperature, const int* top_k, const float* top_p,
+                            const float* uniform, uint64_t seed, int* out_tokens,
+                            int* num_accepted, void* ws, const SamplePlan& p, hipStream_t s);
+
 // ------------------------------------------------------------ compact
 struct KvFull {
   void* k; void* v; int layers; int batch; int nkv; int slots; int hd;

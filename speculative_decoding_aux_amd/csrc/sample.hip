@@ -1,0 +1,552 @@
+// Rejection sampling of flat batches of variable-length draft chains with
+// per-request temperature, top-k and top-p: the CPU rejection sampler of the
+// vLLM Neuron design page ("Rejection Sampling"), on the flat index layout of
+// its "SpecDecodeMetadata: Index Bookkeeping" section.
+//
+// Order and keys.  Tokens rank by (logit desc, id asc).  The 50-bit key
+// (monotone(l) << 18) | (2^18 - 1 - id) is larger for a better token, so the
+// kept set of a filter is {v : key(v) >= kstar} for the key kstar of its last
+// kept token, and one 64-bit value per row describes it.
+//
+// Stage 1, one workgroup per (request, position j <= n_r): greedy rows keep
+// the argmax (first index on ties) and whether draft j equals it.  Random
+// rows find kstar of top-k (by count) and then of top-p (by mass, over the
+// top-k set) by radix selection over key intervals: each level histograms the
+// candidate interval into at most 2048 power-of-two-wide bins in LDS, keeps
+// the bin where the running count or mass from the top crosses the target,
+// and stops when that bin holds one token.  Masses are exp(l/T - max) in
+// float32 summed in float64.  A draft is accepted iff u <= p_f(x).
+// Stage 2, vocabulary chunks of each request's stop row (first rejection, or
+// the bonus row): the Gumbel-max over the kept tokens with the rejected draft
+// excluded, U from the Philox4x32-10 stream of the tree verifier with
+// counter (v >> 2, j, r, 0).
+// Stage 3, one wave per request: merge the chunk records and write the
+// accepted drafts, the emitted token and -1 padding.
+#include "common.h"
+#include "kernels.h"
+
+namespace spec {
+
+namespace {
+
+constexpr int kSelBins = 2048;
+constexpr int kRowThreads = 256;
+
+struct SRow {                  // per (request, position)
+  unsigned long long kstar;    // kept iff key >= kstar (0: every token)
+  double skept;                // sum over kept tokens of exp(l/T - zmax)
+  float zmax;                  // max of l/T
+  int arg;                     // argmax of l (greedy)
+  int acc;                     // draft at this position accepted
+  int pad;
+};
+
+struct SPart {  // Gumbel record per (request, vocab chunk)
+  float gs;
+  int gid;
+};
+
+SPEC_DEV unsigned long long tok_key(float l, int v) {
+  uint32_t b = l == 0.f ? 0u : __float_as_uint(l);  // -0 ranks with +0
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)b << 18) | (unsigned long long)(0x3FFFF - v);
+}
+
+// f(l, v) for every token of the row owned by this thread; 16-byte loads when
+// the row is 16-byte aligned and V a multiple of 4.
+template <typename F>
+SPEC_DEV void for_row(const float* __restrict__ row, int V, F&& f) {
+  if ((V & 3) == 0 && ((uintptr_t)row & 15) == 0) {
+    const float4* r4 = (const float4*)row;
+    for (int q = threadIdx.x; q < (V >> 2); q += blockDim.x) {
+      const float4 w = r4[q];
+      f(w.x, 4 * q);
+      f(w.y, 4 * q + 1);
+      f(w.z, 4 * q + 2);
+      f(w.w, 4 * q + 3);
+    }
+  } else {
+    for (int v = threadIdx.x; v < V; v += blockDim.x) f(row[v], v);
+  }
+}
+
+SPEC_DEV unsigned long long wave_max_u64(unsigned long long x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long y = __shfl_xor(x, o, 64);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+SPEC_DEV unsigned long long wave_min_u64(unsigned long long x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long y = __shfl_xor(x, o, 64);
+    x = y < x ? y : x;
+  }
+  return x;
+}
+
+struct SelLds {
+  unsigned int cnt[kSelBins];
+  double mass[kSelBins];
+  unsigned long long red_u[kRowThreads / 64];
+  double red_d[kRowThreads / 64];
+  float red_f[kRowThreads / 64];
+  int red_i[kRowThreads / 64];
+  int sel_bin;
+  unsigned int sel_above_cnt;
+  double sel_above_mass;
+};
+
+// Block-wide maximum of keys in [lo, hi] (the one token left in a bin).
+SPEC_DEV unsigned long long max_key_in(const float* row, int V, unsigned long long lo,
+                                       unsigned long long hi, SelLds& s) {
+  unsigned long long best = 0;
+  for_row(row, V, [&](float l, int v) {
+    const unsigned long long k = tok_key(l, v);
+    if (k >= lo && k <= hi && k > best) best = k;
+  });
+  best = wave_max_u64(best);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.red_u[w] = best;
+  __syncthreads();
+  unsigned long long b = 0;
+  for (int i = 0; i < kRowThreads / 64; ++i) b = s.red_u[i] > b ? s.red_u[i] : b;
+  return b;
+}
+
+// Sum of exp(l * invT - zmax) over tokens with key >= kfloor.
+SPEC_DEV double mass_from(const float* row, int V, float invT, float zmax,
+                          unsigned long long kfloor, SelLds& s) {
+  double acc = 0.0;
+  for_row(row, V, [&](float l, int v) {
+    if (kfloor == 0 || tok_key(l, v) >= kfloor) acc += (double)expf(l * invT - zmax);
+  });
+  acc = wave_sum(acc);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.red_d[w] = acc;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < kRowThreads / 64; ++i) t += s.red_d[i];
+  return t;
+}
+
+// Radix selection over the key interval [lo, hi] (every token there is a
+// candidate; better tokens have larger keys).  BY_MASS = false: the key of
+// the need_cnt-th best candidate.  BY_MASS = true: the key of the first
+// candidate, best first, at which the running mass reaches need_mass (the
+// last candidate when it never does); *mass_upto gets the mass of the
+// candidates up to and including it.
+template <bool BY_MASS>
+SPEC_DEV unsigned long long radix_select(const float* row, int V, float invT, float zmax,
+                                         unsigned long long lo, unsigned long long hi,
+                                         unsigned int need_cnt, double need_mass,
+                                         double* mass_upto, SelLds& s) {
+  const int t = threadIdx.x;
+  double above_mass = 0.0;
+  while (true) {
+    const unsigned long long span = hi - lo;
+    int sh = 0;
+    while ((span >> sh) >= (unsigned long long)kSelBins) ++sh;
+    const int nb = (int)(span >> sh) + 1;
+    for (int i = t; i < nb; i += kRowThreads) {
+      s.cnt[i] = 0;
+      if (BY_MASS) s.mass[i] = 0.0;
+    }
+    __syncthreads();
+    for_row(row, V, [&](float l, int v) {
+      const unsigned long long k = tok_key(l, v);
+      if (k >= lo && k <= hi) {
+        const int bin = (int)((k - lo) >> sh);
+        atomicAdd(&s.cnt[bin], 1u);
+        if (BY_MASS) atomicAdd(&s.mass[bin], (double)expf(l * invT - zmax));
+      }
+    });
+    __syncthreads();
+    // wave 0 walks the bins from the top: each lane sums a run of bins, the
+    // lanes' runs are scanned from the top, the crossing lane walks its run
+    if (t < 64) {
+      const int per = (nb + 63) / 64;
+      const int b1 = nb - 1 - t * per;         // this lane's run: b1 down to b0
+      const int b0 = max(0, b1 - per + 1);
+      unsigned int c = 0;
+      double m = 0.0;
+      for (int b = b1; b >= b0; --b) {
+        c += s.cnt[b];
+        if (BY_MASS) m += s.mass[b];
+      }
+      // exclusive prefix over lanes 0..t-1 (lane 0 holds the top run)
+      unsigned int cx = c;
+      double mx = m;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned int oc = __shfl_up(cx, o, 64);
+        const double om = __shfl_up(mx, o, 64);
+        if (t >= o) {
+          cx += oc;
+          mx += om;
+        }
+      }
+      cx -= c;
+      mx -= m;
+      // crossing lane: first lane whose inclusive total reaches the target
+      // (bins with no candidate never count as reaching it)
+      const bool reach = c > 0 && (BY_MASS ? (mx + m >= need_mass) : (cx + c >= need_cnt));
+      const unsigned long long bal = __ballot(reach);
+      // the lowest non-empty run when the target is never reached
+      const unsigned long long nz = __ballot(c > 0);
+      const int lane = bal ? __ffsll((long long)bal) - 1 : (nz ? 63 - __clzll((long long)nz) : 0);
+      if (t == lane) {
+        unsigned int ca = cx;
+        double ma = mx;
+        int pick = -1, last = -1;
+        for (int b = b1; b >= b0; --b) {
+          const unsigned int cb = s.cnt[b];
+          if (!cb) continue;
+          const double mb = BY_MASS ? s.mass[b] : 0.0;
+          last = b;
+          if (bal && (BY_MASS ? (ma + mb >= need_mass) : (ca + cb >= need_cnt))) {
+            pick = b;
+            break;
+          }
+          ca += cb;
+          ma += mb;
+        }
+        if (pick < 0 && last >= 0) {  // target not reached: the lowest non-empty bin
+          pick = last;
+          ca -= s.cnt[last];
+          if (BY_MASS) ma -= s.mass[last];
+        }
+        if (pick < 0) pick = 0;  // no candidate left (not reached: the interval holds a token)
+        s.sel_bin = pick;
+        s.sel_above_cnt = ca;
+        s.sel_above_mass = ma;
+      }
+    }
+    __syncthreads();
+    const int pick = s.sel_bin;
+    const unsigned int cb = s.cnt[pick];
+    const double mb = BY_MASS ? s.mass[pick] : 0.0;
+    need_cnt -= s.sel_above_cnt;
+    need_mass -= s.sel_above_mass;
+    above_mass += s.sel_above_mass;
+    const unsigned long long nlo = lo + ((unsigned long long)pick << sh);
+    const unsigned long long nhi_full = nlo + ((1ull << sh) - 1);
+    const unsigned long long nhi = nhi_full < hi ? nhi_full : hi;
+    __syncthreads();  // everyone has read the selection before LDS is reused
+    if (sh == 0) {
+      if (BY_MASS) *mass_upto = above_mass + mb;
+      return nlo;
+    }
+    if (cb == 1) {
+      if (BY_MASS) *mass_upto = above_mass + mb;
+      return max_key_in(row, V, nlo, nhi, s);
+    }
+    lo = nlo;
+    hi = nhi;
+  }
+}
+
+__global__ __launch_bounds__(256) void sample_meta_kernel(int B, const int* __restrict__ cu_sched,
+                                                          const int* __restrict__ nd,
+                                                          int* __restrict__ cu_nd,
+                                                          int* __restrict__ logits_idx,
+                                                          int* __restrict__ tgt_idx,
+                                                          int* __restrict__ bonus_idx) {
+  __shared__ int part[4];
+  __shared__ int carry_s;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  if (t == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += 256) {
+    const int r = base + t;
+    const int n = r < B ? max(0, nd[r]) : 0;
+    int x = n;  // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) part[w] = x;
+    __syncthreads();
+    int off = carry_s;
+    for (int i = 0; i < w; ++i) off += part[i];
+    const int incl = off + x;  // drafts of requests 0..r
+    if (r < B) {
+      cu_nd[r] = incl;
+      const int d0 = incl - n;    // first draft entry of request r
+      const int o = d0 + r;       // first logits row of request r
+      const int first = cu_sched[r] - (n + 1);
+      for (int j = 0; j <= n; ++j) {
+        logits_idx[o + j] = first + j;
+        if (j < n) tgt_idx[d0 + j] = o + j;
+      }
+      bonus_idx[r] = o + n;
+    }
+    __syncthreads();
+    if (t == 255) carry_s = incl;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kRowThreads) void sample_row_kernel(
+    int L, int V, int nrows, const int* __restrict__ cu_nd, const int* __restrict__ drafts,
+    const float* __restrict__ logits, const int* __restrict__ tgt_idx,
+    const int* __restrict__ bonus_idx, const float* __restrict__ temperature,
+    const int* __restrict__ top_k, const float* __restrict__ top_p,
+    const float* __restrict__ uniform, SRow* __restrict__ srow) {
+  __shared__ SelLds s;
+  const int r = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
+  const int start = r ? cu_nd[r - 1] : 0;
+  const int n = min(max(cu_nd[r] - start, 0), L);
+  if (j > n) return;
+  const int rid = clampi(j < n ? tgt_idx[start + j] : bonus_idx[r], 0, nrows - 1);
+  const float* row = logits + (int64_t)rid * V;
+  const float T = temperature[r];
+  const bool greedy = !(T > 0.f) || uniform == nullptr;
+  const int x = j < n ? drafts[start + j] : -1;
+  // pass 1: max / argmax and the smallest key
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  unsigned long long kmin = ~0ull;
+  for_row(row, V, [&](float l, int v) {
+    if (better(l, v, bv, bi)) {
+      bv = l;
+      bi = v;
+    }
+    const unsigned long long k = tok_key(l, v);
+    kmin = k < kmin ? k : kmin;
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  kmin = wave_min_u64(kmin);
+  const int w = t >> 6;
+  if ((t & 63) == 0) {
+    s.red_f[w] = bv;
+    s.red_i[w] = bi;
+    s.red_u[w] = kmin;
+  }
+  __syncthreads();
+  for (int i = 0; i < kRowThreads / 64; ++i) {
+    if (better(s.red_f[i], s.red_i[i], bv, bi)) {
+      bv = s.red_f[i];
+      bi = s.red_i[i];
+    }
+    kmin = s.red_u[i] < kmin ? s.red_u[i] : kmin;
+  }
+  SRow out;
+  out.arg = bi;
+  out.pad = 0;
+  if (greedy) {
+    out.kstar = 0;
+    out.skept = 0.0;
+    out.zmax = 0.f;
+    out.acc = j < n && x == bi;
+    if (t == 0) srow[r * (L + 1) + j] = out;
+    return;
+  }
+  const float invT = 1.0f / T;
+  const float zmax = bv * invT;
+  const unsigned long long kmax = tok_key(bv, bi);
+  const int k = top_k ? top_k[r] : 0;
+  const float p = top_p ? top_p[r] : 1.0f;
+  unsigned long long kstar = 0;
+  double S;
+  if (k > 0 && k < V) {
+    double unused;
+    kstar = radix_select<false>(row, V, invT, zmax, kmin, kmax, (unsigned int)k, 0.0, &unused, s);
+  }
+  S = mass_from(row, V, invT, zmax, kstar, s);
+  if (p < 1.0f) {
+    double upto = S;
+    kstar = radix_select<true>(row, V, invT, zmax, kstar ? kstar : kmin, kmax, 0u,
+                               (double)p * S, &upto, s);
+    S = upto;
+  }
+  out.kstar = kstar;
+  out.skept = S;
+  out.zmax = zmax;
+  out.acc = 0;
+  if (j < n) {
+    const int xc = clampi(x, 0, V - 1);
+    const float lx = row[xc];
+    const bool kept = x == xc && (kstar == 0 || tok_key(lx, xc) >= kstar);
+    const double px = kept ? (double)expf(lx * invT - zmax) / S : 0.0;
+    out.acc = (double)uniform[start + j] <= px;
+  }
+  if (t == 0) srow[r * (L + 1) + j] = out;
+}
+
+// First position of request r whose draft was rejected, n when none was.
+SPEC_DEV int stop_position(const SRow* srow, int r, int L, int n) {
+  int js = n;
+  for (int j = 0; j < n; ++j)
+    if (!srow[r * (L + 1) + j].acc) {
+      js = j;
+      break;
+    }
+  return js;
+}
+
+__global__ __launch_bounds__(256) void sample_gumbel_kernel(
+    int L, int V, int nrows, const int* __restrict__ cu_nd, const int* __restrict__ drafts,
+    const float* __restrict__ logits, const int* __restrict__ tgt_idx,
+    const int* __restrict__ bonus_idx, const float* __restrict__ temperature,
+    const float* __restrict__ uniform, uint32_t seed_lo, uint32_t seed_hi, int chunk,
+    const SRow* __restrict__ srow, SPart* __restrict__ gpart) {
+  __shared__ float rg[4];
+  __shared__ int rgi[4];
+  const int c = blockIdx.x, r = blockIdx.y, nch = gridDim.x;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const float T = temperature[r];
+  if (!(T > 0.f) || uniform == nullptr) return;  // greedy: the emit stage takes the argmax
+  const int start = r ? cu_nd[r - 1] : 0;
+  const int n = min(max(cu_nd[r] - start, 0), L);
+  const int js = stop_position(srow, r, L, n);
+  const int rid = clampi(js < n ? tgt_idx[start + js] : bonus_idx[r], 0, nrows - 1);
+  const int x = js < n ? drafts[start + js] : -1;
+  const unsigned long long kstar = srow[r * (L + 1) + js].kstar;
+  const float* row = logits + (int64_t)rid * V;
+  const float invT = 1.0f / T;
+  const int lo = c * chunk, hi = min(V, lo + chunk);
+  float gs = -INFINITY;
+  int gi = 0x7fffffff;
+  const int q0 = lo >> 2, q1 = (hi + 3) >> 2;
+  for (int qd = q0 + t; qd < q1; qd += 256) {
+    const u32x4 rnd = philox4x32_10(u32x4{(uint32_t)qd, (uint32_t)js, (uint32_t)r, 0u}, seed_lo,
+                                    seed_hi);
+    const uint32_t wd[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = qd * 4 + e;
+      if (v < lo || v >= hi || v == x) continue;
+      const float l = row[v];
+      if (kstar != 0 && tok_key(l, v) < kstar) continue;
+      const float sc = l * invT + gumbel_from_bits(wd[e]);
+      if (better(sc, v, gs, gi)) {
+        gs = sc;
+        gi = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float og = __shfl_xor(gs, o, 64);
+    const int oi = __shfl_xor(gi, o, 64);
+    if (better(og, oi, gs, gi)) {
+      gs = og;
+      gi = oi;
+    }
+  }
+  if (lane == 0) {
+    rg[wave] = gs;
+    rgi[wave] = gi;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int w2 = 1; w2 < 4; ++w2)
+      if (better(rg[w2], rgi[w2], rg[0], rgi[0])) {
+        rg[0] = rg[w2];
+        rgi[0] = rgi[w2];
+      }
+    gpart[(int64_t)r * nch + c] = SPart{rg[0], rgi[0]};
+  }
+}
+
+__global__ __launch_bounds__(64) void sample_emit_kernel(
+    int L, int nch, const int* __restrict__ cu_nd, const int* __restrict__ drafts,
+    const float* __restrict__ temperature, const float* __restrict__ uniform,
+    const SRow* __restrict__ srow, const SPart* __restrict__ gpart, int* __restrict__ out_tokens,
+    int* __restrict__ num_accepted) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const int start = r ? cu_nd[r - 1] : 0;
+  const int n = min(max(cu_nd[r] - start, 0), L);
+  const int js = stop_position(srow, r, L, n);
+  int tok;
+  const float T = temperature[r];
+  if (!(T > 0.f) || uniform == nullptr) {
+    tok = srow[r * (L + 1) + js].arg;
+  } else {
+    float gs = -INFINITY;
+    int gi = 0x7fffffff;
+    for (int c = lane; c < nch; c += 64) {
+      const SPart q = gpart[(int64_t)r * nch + c];
+      if (better(q.gs, q.gid, gs, gi)) {
+        gs = q.gs;
+        gi = q.gid;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float og = __shfl_xor(gs, o, 64);
+      const int oi = __shfl_xor(gi, o, 64);
+      if (better(og, oi, gs, gi)) {
+        gs = og;
+        gi = oi;
+      }
+    }
+    tok = gi == 0x7fffffff ? -1 : gi;
+  }
+  for (int jj = lane; jj <= L; jj += 64)
+    out_tokens[(int64_t)r * (L + 1) + jj] = jj < js ? drafts[start + jj] : (jj == js ? tok : -1);
+  if (lane == 0) num_accepted[r] = js;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+SamplePlan sample_plan(int B, int V) {
+  SamplePlan p;
+  int g = (1024 + B - 1) / std::max(1, B);
+  g = std::max(1, std::min(g, std::max(1, (V + 2047) / 2048)));
+  p.gchunk = ((V + g - 1) / g + 1023) / 1024 * 1024;
+  p.gch = (V + p.gchunk - 1) / p.gchunk;
+  return p;
+}
+
+size_t sample_ws_bytes(const SamplePlan& p, int B, int L) {
+  return align256((size_t)B * (L + 1) * sizeof(SRow)) + align256((size_t)B * p.gch * sizeof(SPart));
+}
+
+hipError_t sample_metadata(int B, const int* cu_sched, const int* nd, int* cu_nd, int* logits_idx,
+                           int* tgt_idx, int* bonus_idx, hipStream_t s) {
+  SPEC_LAUNCH(sample_meta_kernel, dim3(1), dim3(256), 0, s, B, cu_sched, nd, cu_nd, logits_idx,
+              tgt_idx, bonus_idx);
+  return hipGetLastError();
+}
+
+hipError_t rejection_sample(int B, int L, int V, int nrows, const int* cu_nd, const int* drafts,
+                            const float* logits, const int* tgt_idx, const int* bonus_idx,
+                            const float* temperature, const int* top_k, const float* top_p,
+                            const float* uniform, uint64_t seed, int* out_tokens,
+                            int* num_accepted, void* ws, const SamplePlan& p, hipStream_t s) {
+  char* w = (char*)ws;
+  SRow* srow = (SRow*)w;
+  w += align256((size_t)B * (L + 1) * sizeof(SRow));
+  SPart* gpart = (SPart*)w;
+  SPEC_LAUNCH(sample_row_kernel, dim3(B, L + 1), dim3(kRowThreads), 0, s, L, V, nrows, cu_nd,
+              drafts, logits, tgt_idx, bonus_idx, temperature, top_k, top_p, uniform, srow);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SPEC_LAUNCH(sample_gumbel_kernel, dim3(p.gch, B), dim3(256), 0, s, L, V, nrows, cu_nd, drafts,
+              logits, tgt_idx, bonus_idx, temperature, uniform, (uint32_t)(seed & 0xffffffffu),
+              (uint32_t)(seed >> 32), p.gchunk, (const SRow*)srow, gpart);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SPEC_LAUNCH(sample_emit_kernel, dim3(B), dim3(64), 0, s, L, p.gch, cu_nd, drafts, temperature,
+              uniform, (const SRow*)srow, (const SPart*)gpart, out_tokens, num_accepted);
+  return hipGetLastError();
+}
+
+}  // namespace spec

@@ -211,8 +211,9 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
   {
     size_t vb = 0;
     for (int b = 1; b <= c.max_batch; ++b)
-      vb = std::max(vb, verify_ws_bytes(verify_plan(b, c.total_tokens, c.vocab), b,
-                                        c.total_tokens));
+      vb = std::max({vb, verify_ws_bytes(verify_plan(b, c.total_tokens, c.vocab), b,
+                                         c.total_tokens),
+                     sample_ws_bytes(sample_plan(b, c.vocab), b, c.total_tokens)});
     ctx->verify_bytes = vb;
   }
   const int nc = c.cand_rank ? c.num_candidates : 1;
@@ -757,6 +758,53 @@ spec_status spec_verify_tree(spec_ctx* ctx, int32_t B, const spec_tree* tree,
                        tree->num_nodes, target_logits, mode, temperature, accept_u, seed,
                        out_tokens, accepted_len, accepted_nodes, ctx->ws.verify_part, vp,
                        STREAM(stream)));
+  return SPEC_OK;
+}
+
+spec_status spec_decode_metadata(spec_ctx* ctx, int32_t B, const int32_t* cu_num_scheduled_tokens,
+                                 const int32_t* num_draft_tokens, int32_t* cu_num_draft_tokens,
+                                 int32_t* logits_indices, int32_t* target_logits_indices,
+                                 int32_t* bonus_logits_indices, void* stream) {
+  if (!ctx) return SPEC_EINVAL;
+  SPEC_REQ(ctx, B > 0, SPEC_EINVAL, "bad B");
+  SPEC_REQ(ctx, cu_num_scheduled_tokens && num_draft_tokens && cu_num_draft_tokens &&
+                    logits_indices && target_logits_indices && bonus_logits_indices,
+           SPEC_EINVAL, "null argument");
+  SPEC_HIP(ctx, sample_metadata(B, cu_num_scheduled_tokens, num_draft_tokens, cu_num_draft_tokens,
+                                logits_indices, target_logits_indices, bonus_logits_indices,
+                                STREAM(stream)));
+  return SPEC_OK;
+}
+
+spec_status spec_rejection_sample(spec_ctx* ctx, int32_t B, int32_t max_spec_len,
+                                  const int32_t* cu_num_draft_tokens,
+                                  const int32_t* draft_token_ids, const float* logits,
+                                  int32_t num_logits_rows, const int32_t* target_logits_indices,
+                                  const int32_t* bonus_logits_indices, const float* temperature,
+                                  const int32_t* top_k, const float* top_p, const float* uniform,
+                                  uint64_t seed, int32_t* out_tokens, int32_t* num_accepted,
+                                  void* stream) {
+  if (!ctx) return SPEC_EINVAL;
+  const spec_config& c = ctx->cfg;
+  SPEC_REQ(ctx, B > 0 && B <= c.max_batch, SPEC_EINVAL, "bad B");
+  SPEC_REQ(ctx, max_spec_len >= 0 && max_spec_len <= c.total_tokens, SPEC_EUNSUPPORTED,
+           "max_spec_len=%d outside [0, total_tokens]", max_spec_len);
+  SPEC_REQ(ctx, num_logits_rows > 0, SPEC_EINVAL, "num_logits_rows must be positive");
+  SPEC_REQ(ctx, c.vocab <= (1 << 18), SPEC_EUNSUPPORTED, "vocab above 2^18");
+  SPEC_REQ(ctx, cu_num_draft_tokens && logits && bonus_logits_indices && temperature &&
+                    out_tokens && num_accepted,
+           SPEC_EINVAL, "null argument");
+  SPEC_REQ(ctx, max_spec_len == 0 || (draft_token_ids && target_logits_indices), SPEC_EINVAL,
+           "null draft arrays");
+  const SamplePlan sp = sample_plan(B, c.vocab);
+  SPEC_REQ(ctx, sample_ws_bytes(sp, B, max_spec_len) <= ctx->verify_bytes, SPEC_EUNSUPPORTED,
+           "workspace too small");
+  ProfScope ps(ctx, SPEC_PROF_VERIFY, STREAM(stream));
+  SPEC_HIP(ctx, rejection_sample(B, max_spec_len, c.vocab, num_logits_rows, cu_num_draft_tokens,
+                                 draft_token_ids, logits, target_logits_indices,
+                                 bonus_logits_indices, temperature, top_k, top_p, uniform, seed,
+                                 out_tokens, num_accepted, ctx->ws.verify_part, sp,
+                                 STREAM(stream)));
   return SPEC_OK;
 }
 

@@ -219,3 +219,49 @@ def spec_compact_kv(ctx: SpecContext, kv: KVCache, tree_base, accepted_nodes, ac
     st = ctx.lib.spec_compact_kv(ctx.h, ctypes.byref(kv.struct), B, _p(tree_base), _p(accepted_nodes),
                                  _p(accepted_len), max_accept, _stream())
     ctx._check(st)
+
+
+def spec_decode_metadata(ctx: SpecContext, cu_num_scheduled_tokens, num_draft_tokens, total_drafts: int):
+    """Index bookkeeping of a flat batch; ``total_drafts`` (the sum of the
+    draft counts) sizes the outputs.  Returns (cu_num_draft_tokens,
+    logits_indices, target_logits_indices, bonus_logits_indices)."""
+    dev = ctx.device
+    cu_s = _i32(cu_num_scheduled_tokens, dev)
+    nd = _i32(num_draft_tokens, dev)
+    B = nd.shape[0]
+    out = (torch.empty(B, dtype=torch.int32, device=dev),
+           torch.empty(total_drafts + B, dtype=torch.int32, device=dev),
+           torch.empty(max(total_drafts, 1), dtype=torch.int32, device=dev),
+           torch.empty(B, dtype=torch.int32, device=dev))
+    st = ctx.lib.spec_decode_metadata(ctx.h, B, _p(cu_s), _p(nd), _p(out[0]), _p(out[1]), _p(out[2]),
+                                      _p(out[3]), _stream())
+    ctx._check(st)
+    return out[0], out[1], out[2][:total_drafts], out[3]
+
+
+def spec_rejection_sample(ctx: SpecContext, cu_num_draft_tokens, draft_token_ids, logits,
+                          target_logits_indices, bonus_logits_indices, temperature, top_k=None, top_p=None,
+                          uniform=None, seed=0, max_spec_len=None, out=None):
+    """Flat-batch rejection sampling; returns (out_tokens [B, L+1], num_accepted [B])."""
+    dev = logits.device
+    cu = _i32(cu_num_draft_tokens, dev)
+    B = cu.shape[0]
+    L = ctx.cfg["total_tokens"] if max_spec_len is None else int(max_spec_len)
+    drafts = _i32(draft_token_ids, dev)
+    tgt = _i32(target_logits_indices, dev)
+    if drafts.numel() == 0:  # no drafts in the batch: any valid pointer will do
+        drafts = torch.zeros(1, dtype=torch.int32, device=dev)
+        tgt = torch.zeros(1, dtype=torch.int32, device=dev)
+    bonus = _i32(bonus_logits_indices, dev)
+    temp = torch.as_tensor(temperature, dtype=torch.float32).to(dev)
+    tk = None if top_k is None else _i32(top_k, dev)
+    tp = None if top_p is None else torch.as_tensor(top_p, dtype=torch.float32).to(dev)
+    u = None if uniform is None else torch.as_tensor(uniform, dtype=torch.float32).to(dev)
+    if out is None:
+        out = (torch.empty(B, L + 1, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    st = ctx.lib.spec_rejection_sample(ctx.h, B, L, _p(cu), _p(drafts), _p(logits), logits.shape[0], _p(tgt),
+                                       _p(bonus), _p(temp), _p(tk), _p(tp), _p(u), int(seed) & (2**64 - 1),
+                                       _p(out[0]), _p(out[1]), _stream())
+    ctx._check(st)
+    return out

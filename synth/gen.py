@@ -223,3 +223,43 @@ def random_tree(cfg: dict, seed: int, batch: int | None = None) -> dict:
             frontier = nxt
         num_nodes[b] = nodes - 1
     return {"tokens": tokens, "parent": parent, "depth": depth, "num_nodes": num_nodes}
+
+
+def flat_batch(seed: int, B: int, max_spec_len: int, V: int, *, plant=(6.0, 14.0), p_right=0.8,
+               greedy_frac=0.25, ties=False) -> dict:
+    """A flat batch of variable-length draft chains with per-request sampling
+    parameters.  Draft counts are uniform in [0, max_spec_len]; request r
+    schedules 1 + its drafts + a random number of earlier tokens, so
+    ``cu_num_scheduled_tokens`` is increasing.  The logits rows (one per draft
+    and one bonus row per request, in request order) are N(0, 2) with one
+    planted token per row raised by U(plant) (integer-valued draws from
+    [-4, 4] when ``ties``); the draft at a row is the planted token with
+    probability ``p_right``, else a uniform id.  A fraction of the requests is
+    greedy (temperature 0); the others draw T from [0.3, 1.5], top-k from
+    {0, 1, 5, 50, 1000} and top-p from {1.0, 0.5, 0.9, 0.97}.  Uniforms ~ U(0, 1)."""
+    rng = _rng(seed, "flat_batch")
+    nd = rng.integers(0, max_spec_len + 1, B).astype(np.int32)
+    sched = nd + 1 + rng.integers(0, 5, B)
+    cu_sched = np.cumsum(sched).astype(np.int32)
+    rows = int(nd.sum()) + B
+    if ties:
+        logits = rng.integers(-4, 5, (rows, V)).astype(np.float32)
+    else:
+        logits = _normal(seed, "flat_logits", (rows, V), 2.0, "f32")
+    planted = rng.integers(0, V, rows)
+    logits[np.arange(rows), planted] += rng.uniform(*plant, rows).astype(np.float32)
+    drafts = []
+    row = 0
+    for r in range(B):
+        for j in range(nd[r]):
+            drafts.append(int(planted[row]) if rng.random() < p_right else int(rng.integers(0, V)))
+            row += 1
+        row += 1
+    greedy = rng.random(B) < greedy_frac
+    temp = np.where(greedy, 0.0, rng.uniform(0.3, 1.5, B)).astype(np.float32)
+    top_k = rng.choice(np.array([0, 1, 5, 50, 1000], np.int32), B).astype(np.int32)
+    top_p = rng.choice(np.array([1.0, 0.5, 0.9, 0.97], np.float32), B).astype(np.float32)
+    u = rng.random(int(nd.sum()), dtype=np.float32)
+    return {"num_draft_tokens": nd, "cu_num_scheduled_tokens": cu_sched, "logits": logits,
+            "draft_token_ids": np.array(drafts, np.int32), "temperature": temp, "top_k": top_k,
+            "top_p": top_p, "uniform": u, "seed": philox_seed(seed)}
