@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the attainable-peak probes run after the timed steps")
     ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--flat-sampling", type=int, default=0, metavar="B",
+                    help="instead of the step, time rejection sampling of a flat batch of B "
+                         "variable-length chains with per-request temperature/top-k/top-p "
+                         "(the workload's vocabulary and draft length)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
@@ -193,6 +197,10 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 3}))
         return
 
+    if args.flat_sampling:
+        bench_flat_sampling(args)
+        return
+
     from speculative_decoding_aux_amd import spec as S
     from speculative_decoding_aux_amd import _lib as L
     from speculative_decoding_aux_amd.tensors import to_device, upload_kv, upload_weights
@@ -332,6 +340,86 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, W, inp, seed, args.cpu_steps)
+    print(json.dumps(res), flush=True)
+
+
+def bench_flat_sampling(args):
+    """Rejection sampling of one flat batch per call (spec_rejection_sample):
+    B requests with 0..K drafts each over the workload's target vocabulary,
+    mixed greedy / random requests with per-request temperature, top-k and
+    top-p (synth.gen.flat_batch).  Algorithmic bytes: every logits row (each
+    draft row and each bonus row) read once."""
+    import torch
+
+    from oracle import sampling as osm
+    from speculative_decoding_aux_amd import spec as S
+    from speculative_decoding_aux_amd import _lib as L
+    from synth import configs, gen
+
+    cfg0 = configs.get(args.config)
+    B, K, V = args.flat_sampling, cfg0["total_tokens"], cfg0["vocab"]
+    cfg = configs.get(args.config, batch=B)
+    seed = configs.SEEDS[args.config] + 500
+    d = gen.flat_batch(seed, B, K, V)
+    nd = d["num_draft_tokens"]
+    T = int(nd.sum())
+    ctx = S.SpecContext(cfg, max_batch=B, max_new=cfg["n_new"])
+    dev = "cuda"
+    meta = S.spec_decode_metadata(ctx, d["cu_num_scheduled_tokens"], nd, T)
+    cu, _, tgt, bonus = meta
+    lg = torch.from_numpy(d["logits"]).to(dev)
+    drafts = torch.from_numpy(d["draft_token_ids"]).to(dev)
+    temp = torch.from_numpy(d["temperature"]).to(dev)
+    tk = torch.from_numpy(d["top_k"]).to(dev)
+    tp = torch.from_numpy(d["top_p"]).to(dev)
+    u = torch.from_numpy(d["uniform"]).to(dev)
+    out = (torch.empty(B, K + 1, dtype=torch.int32, device=dev), torch.empty(B, dtype=torch.int32, device=dev))
+
+    def call():
+        S.spec_rejection_sample(ctx, cu, drafts, lg, tgt, bonus, temp, tk, tp, u, d["seed"], K, out=out)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} flat-sampling calls (B={B}, rows={T + B}, V={V})",
+          file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ctx.profile(True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    n, ms = ctx.profile_read(L.SPEC_PROF_VERIFY)
+    ctx.profile(False)
+    ms_call = e0.elapsed_time(e1) / args.steps
+    avg_ms = ms / max(n, 1)
+    byts = (T + B) * V * 4
+    achieved = byts / (avg_ms * 1e-3) / 1e9
+    res = {"metric": "flat-batch rejection sampling calls/sec at 1 GPU", "value": round(1000.0 / ms_call, 2),
+           "unit": "calls/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_call, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"flat_sampling_{args.config}", "requests": B, "max_spec_len": K,
+                      "drafts": T, "logits_rows": T + B, "vocab": V,
+                      "greedy_requests": int((d["temperature"] == 0).sum())},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "sample_row_kernel + sample_gumbel_kernel + sample_emit_kernel",
+                        "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n,
+                        "algorithmic_bytes_per_launch": byts}}
+    if not args.no_cpu_baseline:
+        wall = []
+        for _ in range(max(1, args.cpu_steps)):
+            t0 = time.perf_counter()
+            m = osm.spec_decode_metadata(d["cu_num_scheduled_tokens"], nd)
+            osm.rejection_sample(m[0], d["draft_token_ids"], d["logits"], m[2], m[3], d["temperature"],
+                                 d["top_k"], d["top_p"], d["uniform"], d["seed"], K)
+            wall.append(time.perf_counter() - t0)
+        med = float(np.median(wall))
+        res["cpu_baseline"] = {"value": round(1.0 / med, 3), "unit": "calls/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{len(wall)} whole calls of the same batch; median {med:.3f} s"}
     print(json.dumps(res), flush=True)
 
 

@@ -30,7 +30,7 @@ namespace spec {
 namespace {
 
 constexpr int kSelBins = 2048;
-constexpr int kRowThreads = 256;
+constexpr int kRowThreads = 1024;
 
 struct SRow {                  // per (request, position)
   unsigned long long kstar;    // kept iff key >= kstar (0: every token)
@@ -52,21 +52,45 @@ SPEC_DEV unsigned long long tok_key(float l, int v) {
   return ((unsigned long long)b << 18) | (unsigned long long)(0x3FFFF - v);
 }
 
-// f(l, v) for every token of the row owned by this thread; 16-byte loads when
-// the row is 16-byte aligned and V a multiple of 4.
+// f(l, v) for every token of the row owned by this thread, four loads in
+// flight per thread (16-byte loads when the row is 16-byte aligned and V a
+// multiple of 4).
 template <typename F>
 SPEC_DEV void for_row(const float* __restrict__ row, int V, F&& f) {
+  const int nt = blockDim.x;
   if ((V & 3) == 0 && ((uintptr_t)row & 15) == 0) {
     const float4* r4 = (const float4*)row;
-    for (int q = threadIdx.x; q < (V >> 2); q += blockDim.x) {
-      const float4 w = r4[q];
-      f(w.x, 4 * q);
-      f(w.y, 4 * q + 1);
-      f(w.z, 4 * q + 2);
-      f(w.w, 4 * q + 3);
+    const int n4 = V >> 2;
+    for (int q0 = threadIdx.x; q0 < n4; q0 += 4 * nt) {
+      float4 w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = q0 + i * nt;
+        w[i] = q < n4 ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = q0 + i * nt;
+        if (q < n4) {
+          f(w[i].x, 4 * q);
+          f(w[i].y, 4 * q + 1);
+          f(w[i].z, 4 * q + 2);
+          f(w[i].w, 4 * q + 3);
+        }
+      }
     }
   } else {
-    for (int v = threadIdx.x; v < V; v += blockDim.x) f(row[v], v);
+    for (int v0 = threadIdx.x; v0 < V; v0 += 4 * nt) {
+      float w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = v0 + i * nt;
+        w[i] = v < V ? row[v] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (v0 + i * nt < V) f(w[i], v0 + i * nt);
+    }
   }
 }
 
@@ -87,23 +111,130 @@ SPEC_DEV unsigned long long wave_min_u64(unsigned long long x) {
   return x;
 }
 
+SPEC_DEV float float_of_mono(uint32_t m) {
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+}
+// logit and id of a key
+SPEC_DEV void key_parts(unsigned long long k, float& l, int& v) {
+  v = 0x3FFFF - (int)(k & 0x3FFFFull);
+  l = float_of_mono((uint32_t)(k >> 18));
+}
+
+constexpr int kL0Bits = 12;            // static first level: top 12 bits of monotone(l)
+constexpr int kL0Bins = 1 << kL0Bits;
+constexpr int kL0Shift = 18 + 32 - kL0Bits;  // key >> kL0Shift = first-level bin
+constexpr int kCap = 8192;             // candidates of one first-level bin kept in LDS
+
 struct SelLds {
-  unsigned int cnt[kSelBins];
+  unsigned int l0_cnt[kL0Bins];        // first level over the whole row
+  double l0_mass[kL0Bins];
+  unsigned int cnt[kSelBins];          // refinement levels
   double mass[kSelBins];
+  unsigned long long cand[kCap];       // keys of one first-level bin
   unsigned long long red_u[kRowThreads / 64];
   double red_d[kRowThreads / 64];
   float red_f[kRowThreads / 64];
   int red_i[kRowThreads / 64];
+  int ncand;
   int sel_bin;
   unsigned int sel_above_cnt;
   double sel_above_mass;
 };
 
-// Block-wide maximum of keys in [lo, hi] (the one token left in a bin).
-SPEC_DEV unsigned long long max_key_in(const float* row, int V, unsigned long long lo,
+// Candidate sources: f(l, v) for every token of the row, or of the LDS list.
+struct RowSrc {
+  const float* row;
+  int V;
+  template <typename F>
+  SPEC_DEV void operator()(F&& f) const { for_row(row, V, f); }
+};
+struct CandSrc {
+  const unsigned long long* cand;
+  int n;
+  template <typename F>
+  SPEC_DEV void operator()(F&& f) const {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      float l;
+      int v;
+      key_parts(cand[i], l, v);
+      f(l, v);
+    }
+  }
+};
+
+// Wave 0 walks nb bins from the top (bin nb-1 first): each lane sums a run
+// of bins, the runs are scanned from the top, the crossing lane walks its
+// run.  The picked bin is the first non-empty one at which the running count
+// (or mass) reaches the target, the lowest non-empty bin when none does;
+// s.sel_bin / sel_above_cnt / sel_above_mass get the bin and the totals of
+// the bins above it.  Called by the whole block (ends with a barrier).
+template <bool BY_MASS>
+SPEC_DEV void scan_pick(const unsigned int* cnt, const double* mass, int nb, unsigned int need_cnt,
+                        double need_mass, SelLds& s) {
+  const int t = threadIdx.x;
+  if (t < 64) {
+    const int per = (nb + 63) / 64;
+    const int b1 = nb - 1 - t * per;  // this lane's run: b1 down to b0
+    const int b0 = max(0, b1 - per + 1);
+    unsigned int c = 0;
+    double m = 0.0;
+    for (int b = b1; b >= b0; --b) {
+      c += cnt[b];
+      if (BY_MASS) m += mass[b];
+    }
+    unsigned int cx = c;
+    double mx = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned int oc = __shfl_up(cx, o, 64);
+      const double om = __shfl_up(mx, o, 64);
+      if (t >= o) {
+        cx += oc;
+        mx += om;
+      }
+    }
+    cx -= c;
+    mx -= m;
+    const bool reach = c > 0 && (BY_MASS ? (mx + m >= need_mass) : (cx + c >= need_cnt));
+    const unsigned long long bal = __ballot(reach);
+    const unsigned long long nz = __ballot(c > 0);
+    const int lane = bal ? __ffsll((long long)bal) - 1 : (nz ? 63 - __clzll((long long)nz) : 0);
+    if (t == lane) {
+      unsigned int ca = cx;
+      double ma = mx;
+      int pick = -1, last = -1;
+      for (int b = b1; b >= b0; --b) {
+        const unsigned int cb = cnt[b];
+        if (!cb) continue;
+        const double mb = BY_MASS ? mass[b] : 0.0;
+        last = b;
+        if (bal && (BY_MASS ? (ma + mb >= need_mass) : (ca + cb >= need_cnt))) {
+          pick = b;
+          break;
+        }
+        ca += cb;
+        ma += mb;
+      }
+      if (pick < 0 && last >= 0) {  // target not reached: the lowest non-empty bin
+        pick = last;
+        ca -= cnt[last];
+        if (BY_MASS) ma -= mass[last];
+      }
+      if (pick < 0) pick = 0;  // no candidate at all (callers never ask for that)
+      s.sel_bin = pick;
+      s.sel_above_cnt = ca;
+      s.sel_above_mass = ma;
+    }
+  }
+  __syncthreads();
+}
+
+// Block-wide maximum of keys in [lo, hi] over a source.
+template <typename Src>
+SPEC_DEV unsigned long long max_key_in(const Src& src, unsigned long long lo,
                                        unsigned long long hi, SelLds& s) {
   unsigned long long best = 0;
-  for_row(row, V, [&](float l, int v) {
+  src([&](float l, int v) {
     const unsigned long long k = tok_key(l, v);
     if (k >= lo && k <= hi && k > best) best = k;
   });
@@ -117,31 +248,25 @@ SPEC_DEV unsigned long long max_key_in(const float* row, int V, unsigned long lo
   return b;
 }
 
-// Sum of exp(l * invT - zmax) over tokens with key >= kfloor.
-SPEC_DEV double mass_from(const float* row, int V, float invT, float zmax,
-                          unsigned long long kfloor, SelLds& s) {
+// Sum of exp(l * invT - zmax) over a source's tokens with key in [lo, hi].
+template <typename Src>
+SPEC_DEV double mass_in(const Src& src, float invT, float zmax, unsigned long long lo,
+                        unsigned long long hi, SelLds& s) {
   double acc = 0.0;
-  for_row(row, V, [&](float l, int v) {
-    if (kfloor == 0 || tok_key(l, v) >= kfloor) acc += (double)expf(l * invT - zmax);
+  src([&](float l, int v) {
+    const unsigned long long k = tok_key(l, v);
+    if (k >= lo && k <= hi && l != -INFINITY) acc += (double)expf(l * invT - zmax);
   });
-  acc = wave_sum(acc);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) s.red_d[w] = acc;
-  __syncthreads();
-  double t = 0.0;
-  for (int i = 0; i < kRowThreads / 64; ++i) t += s.red_d[i];
-  return t;
+  return block_sum(acc, s.red_d);
 }
 
-// Radix selection over the key interval [lo, hi] (every token there is a
-// candidate; better tokens have larger keys).  BY_MASS = false: the key of
-// the need_cnt-th best candidate.  BY_MASS = true: the key of the first
-// candidate, best first, at which the running mass reaches need_mass (the
-// last candidate when it never does); *mass_upto gets the mass of the
-// candidates up to and including it.
-template <bool BY_MASS>
-SPEC_DEV unsigned long long radix_select(const float* row, int V, float invT, float zmax,
+// Radix selection over the key interval [lo, hi] of a source (better tokens
+// have larger keys).  BY_MASS = false: the key of the need_cnt-th best
+// candidate.  BY_MASS = true: the key of the first candidate, best first, at
+// which the running mass reaches need_mass (the last candidate when it never
+// does); *mass_upto gets the mass up to and including it.
+template <bool BY_MASS, typename Src>
+SPEC_DEV unsigned long long radix_select(const Src& src, float invT, float zmax,
                                          unsigned long long lo, unsigned long long hi,
                                          unsigned int need_cnt, double need_mass,
                                          double* mass_upto, SelLds& s) {
@@ -157,76 +282,16 @@ SPEC_DEV unsigned long long radix_select(const float* row, int V, float invT, fl
       if (BY_MASS) s.mass[i] = 0.0;
     }
     __syncthreads();
-    for_row(row, V, [&](float l, int v) {
+    src([&](float l, int v) {
       const unsigned long long k = tok_key(l, v);
       if (k >= lo && k <= hi) {
         const int bin = (int)((k - lo) >> sh);
         atomicAdd(&s.cnt[bin], 1u);
-        if (BY_MASS) atomicAdd(&s.mass[bin], (double)expf(l * invT - zmax));
+        if (BY_MASS && l != -INFINITY) atomicAdd(&s.mass[bin], (double)expf(l * invT - zmax));
       }
     });
     __syncthreads();
-    // wave 0 walks the bins from the top: each lane sums a run of bins, the
-    // lanes' runs are scanned from the top, the crossing lane walks its run
-    if (t < 64) {
-      const int per = (nb + 63) / 64;
-      const int b1 = nb - 1 - t * per;         // this lane's run: b1 down to b0
-      const int b0 = max(0, b1 - per + 1);
-      unsigned int c = 0;
-      double m = 0.0;
-      for (int b = b1; b >= b0; --b) {
-        c += s.cnt[b];
-        if (BY_MASS) m += s.mass[b];
-      }
-      // exclusive prefix over lanes 0..t-1 (lane 0 holds the top run)
-      unsigned int cx = c;
-      double mx = m;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned int oc = __shfl_up(cx, o, 64);
-        const double om = __shfl_up(mx, o, 64);
-        if (t >= o) {
-          cx += oc;
-          mx += om;
-        }
-      }
-      cx -= c;
-      mx -= m;
-      // crossing lane: first lane whose inclusive total reaches the target
-      // (bins with no candidate never count as reaching it)
-      const bool reach = c > 0 && (BY_MASS ? (mx + m >= need_mass) : (cx + c >= need_cnt));
-      const unsigned long long bal = __ballot(reach);
-      // the lowest non-empty run when the target is never reached
-      const unsigned long long nz = __ballot(c > 0);
-      const int lane = bal ? __ffsll((long long)bal) - 1 : (nz ? 63 - __clzll((long long)nz) : 0);
-      if (t == lane) {
-        unsigned int ca = cx;
-        double ma = mx;
-        int pick = -1, last = -1;
-        for (int b = b1; b >= b0; --b) {
-          const unsigned int cb = s.cnt[b];
-          if (!cb) continue;
-          const double mb = BY_MASS ? s.mass[b] : 0.0;
-          last = b;
-          if (bal && (BY_MASS ? (ma + mb >= need_mass) : (ca + cb >= need_cnt))) {
-            pick = b;
-            break;
-          }
-          ca += cb;
-          ma += mb;
-        }
-        if (pick < 0 && last >= 0) {  // target not reached: the lowest non-empty bin
-          pick = last;
-          ca -= s.cnt[last];
-          if (BY_MASS) ma -= s.mass[last];
-        }
-        if (pick < 0) pick = 0;  // no candidate left (not reached: the interval holds a token)
-        s.sel_bin = pick;
-        s.sel_above_cnt = ca;
-        s.sel_above_mass = ma;
-      }
-    }
-    __syncthreads();
+    scan_pick<BY_MASS>(s.cnt, s.mass, nb, need_cnt, need_mass, s);
     const int pick = s.sel_bin;
     const unsigned int cb = s.cnt[pick];
     const double mb = BY_MASS ? s.mass[pick] : 0.0;
@@ -243,12 +308,40 @@ SPEC_DEV unsigned long long radix_select(const float* row, int V, float invT, fl
     }
     if (cb == 1) {
       if (BY_MASS) *mass_upto = above_mass + mb;
-      return max_key_in(row, V, nlo, nhi, s);
+      return max_key_in(src, nlo, nhi, s);
     }
     lo = nlo;
     hi = nhi;
   }
 }
+
+// Keys of the row's tokens in first-level bin b into s.cand (the bin holds
+// at most kCap tokens); returns their number.
+SPEC_DEV int collect_bin(const float* row, int V, int b, SelLds& s) {
+  if (threadIdx.x == 0) s.ncand = 0;
+  __syncthreads();
+  for_row(row, V, [&](float l, int v) {
+    const unsigned long long k = tok_key(l, v);
+    const bool in = (int)(k >> kL0Shift) == b;
+    const unsigned long long act = __ballot(true);
+    const unsigned long long m = __ballot(in);
+    if (m) {
+      const int lane = threadIdx.x & 63;
+      const int leader = __ffsll((long long)act) - 1;
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&s.ncand, __popcll(m));
+      base = __shfl(base, leader, 64);
+      const int pos = base + __popcll(m & ((1ull << lane) - 1));
+      if (in && pos < kCap) s.cand[pos] = k;
+    }
+  });
+  __syncthreads();
+  return min(s.ncand, kCap);
+}
+
+// Key interval of first-level bin b.
+SPEC_DEV unsigned long long bin_lo(int b) { return (unsigned long long)b << kL0Shift; }
+SPEC_DEV unsigned long long bin_hi(int b) { return (((unsigned long long)b + 1) << kL0Shift) - 1; }
 
 __global__ __launch_bounds__(256) void sample_meta_kernel(int B, const int* __restrict__ cu_sched,
                                                           const int* __restrict__ nd,
@@ -308,17 +401,14 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(
   const float T = temperature[r];
   const bool greedy = !(T > 0.f) || uniform == nullptr;
   const int x = j < n ? drafts[start + j] : -1;
-  // pass 1: max / argmax and the smallest key
+  // pass 1: max / argmax
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  unsigned long long kmin = ~0ull;
   for_row(row, V, [&](float l, int v) {
     if (better(l, v, bv, bi)) {
       bv = l;
       bi = v;
     }
-    const unsigned long long k = tok_key(l, v);
-    kmin = k < kmin ? k : kmin;
   });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -329,21 +419,21 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(
       bi = oi;
     }
   }
-  kmin = wave_min_u64(kmin);
   const int w = t >> 6;
   if ((t & 63) == 0) {
     s.red_f[w] = bv;
     s.red_i[w] = bi;
-    s.red_u[w] = kmin;
+  }
+  for (int i = t; i < kL0Bins; i += kRowThreads) {
+    s.l0_cnt[i] = 0;
+    s.l0_mass[i] = 0.0;
   }
   __syncthreads();
-  for (int i = 0; i < kRowThreads / 64; ++i) {
+  for (int i = 0; i < kRowThreads / 64; ++i)
     if (better(s.red_f[i], s.red_i[i], bv, bi)) {
       bv = s.red_f[i];
       bi = s.red_i[i];
     }
-    kmin = s.red_u[i] < kmin ? s.red_u[i] : kmin;
-  }
   SRow out;
   out.arg = bi;
   out.pad = 0;
@@ -357,21 +447,86 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(
   }
   const float invT = 1.0f / T;
   const float zmax = bv * invT;
-  const unsigned long long kmax = tok_key(bv, bi);
   const int k = top_k ? top_k[r] : 0;
   const float p = top_p ? top_p[r] : 1.0f;
-  unsigned long long kstar = 0;
-  double S;
-  if (k > 0 && k < V) {
+  const bool use_k = k > 0 && k < V, use_p = p < 1.0f;
+  // pass 2: first-level histogram (count and mass) over the whole row
+  double sum = 0.0;
+  for_row(row, V, [&](float l, int v) {
+    const int b = (int)(tok_key(l, v) >> kL0Shift);
+    const double e = l == -INFINITY ? 0.0 : (double)expf(l * invT - zmax);
+    sum += e;
+    if (use_k || use_p) {
+      atomicAdd(&s.l0_cnt[b], 1u);
+      if (e != 0.0) atomicAdd(&s.l0_mass[b], e);
+    }
+  });
+  double S = block_sum(sum, s.red_d);  // also orders the histogram before its use
+  unsigned long long kstar = 0;        // kept iff key >= kstar
+  int cbin = -1;                       // first-level bin whose keys are in s.cand
+  int ncand = 0;
+  int bk = -1;                         // first-level bin of the k-th best token
+  if (use_k) {
+    // the first-level bin holding the k-th best token, then the token itself
+    scan_pick<false>(s.l0_cnt, s.l0_mass, kL0Bins, (unsigned int)k, 0.0, s);
+    bk = s.sel_bin;
+    const unsigned int above = s.sel_above_cnt;
+    const unsigned int cbk = s.l0_cnt[bk];
+    double above_mass = 0.0;
+    for (int b = kL0Bins - 1 - t; b > bk; b -= kRowThreads) above_mass += s.l0_mass[b];
+    above_mass = block_sum(above_mass, s.red_d);
     double unused;
-    kstar = radix_select<false>(row, V, invT, zmax, kmin, kmax, (unsigned int)k, 0.0, &unused, s);
+    if (cbk <= (unsigned int)kCap) {
+      ncand = collect_bin(row, V, bk, s);
+      cbin = bk;
+      const CandSrc cs{s.cand, ncand};
+      kstar = radix_select<false>(cs, invT, zmax, bin_lo(bk), bin_hi(bk), (unsigned int)k - above,
+                                  0.0, &unused, s);
+      S = above_mass + mass_in(cs, invT, zmax, kstar, bin_hi(bk), s);
+    } else {
+      const RowSrc rs{row, V};
+      kstar = radix_select<false>(rs, invT, zmax, bin_lo(bk), bin_hi(bk), (unsigned int)k - above,
+                                  0.0, &unused, s);
+      S = above_mass + mass_in(rs, invT, zmax, kstar, bin_hi(bk), s);
+    }
+    // the top-k set as a first-level histogram: bins below bk emptied, bin
+    // bk reduced to its kept part
+    const int bkeep = bk;
+    for (int b = t; b < bkeep; b += kRowThreads) {
+      s.l0_cnt[b] = 0;
+      s.l0_mass[b] = 0.0;
+    }
+    __syncthreads();
+    if (t == 0) {
+      s.l0_cnt[bkeep] = (unsigned int)k - above;
+      s.l0_mass[bkeep] = S - above_mass;
+    }
+    __syncthreads();
   }
-  S = mass_from(row, V, invT, zmax, kstar, s);
-  if (p < 1.0f) {
-    double upto = S;
-    kstar = radix_select<true>(row, V, invT, zmax, kstar ? kstar : kmin, kmax, 0u,
-                               (double)p * S, &upto, s);
-    S = upto;
+  if (use_p) {
+    const double target = (double)p * S;
+    scan_pick<true>(s.l0_cnt, s.l0_mass, kL0Bins, 0u, target, s);
+    const int bp = s.sel_bin;
+    const double above_mass = s.sel_above_mass;
+    const unsigned int cbp = s.l0_cnt[bp];
+    __syncthreads();
+    // in the top-k cut's bin only its kept part counts; its tokens are in
+    // LDS when the top-k selection collected them, else the row is scanned
+    const unsigned long long lo = bp == bk ? kstar : bin_lo(bp);
+    const bool have = bp == cbin;
+    double upto = 0.0;
+    if (have || (bp != bk && cbp <= (unsigned int)kCap)) {
+      if (!have) {
+        ncand = collect_bin(row, V, bp, s);
+        cbin = bp;
+      }
+      const CandSrc cs{s.cand, ncand};
+      kstar = radix_select<true>(cs, invT, zmax, lo, bin_hi(bp), 0u, target - above_mass, &upto, s);
+    } else {
+      const RowSrc rs{row, V};
+      kstar = radix_select<true>(rs, invT, zmax, lo, bin_hi(bp), 0u, target - above_mass, &upto, s);
+    }
+    S = above_mass + upto;
   }
   out.kstar = kstar;
   out.skept = S;
@@ -381,7 +536,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(
     const int xc = clampi(x, 0, V - 1);
     const float lx = row[xc];
     const bool kept = x == xc && (kstar == 0 || tok_key(lx, xc) >= kstar);
-    const double px = kept ? (double)expf(lx * invT - zmax) / S : 0.0;
+    const double px = kept && lx != -INFINITY ? (double)expf(lx * invT - zmax) / S : 0.0;
     out.acc = (double)uniform[start + j] <= px;
   }
   if (t == 0) srow[r * (L + 1) + j] = out;

@@ -226,14 +226,15 @@ def random_tree(cfg: dict, seed: int, batch: int | None = None) -> dict:
 
 
 def flat_batch(seed: int, B: int, max_spec_len: int, V: int, *, plant=(6.0, 14.0), p_right=0.8,
-               greedy_frac=0.25, ties=False) -> dict:
+               greedy_frac=0.25, ties=False, crowded=False) -> dict:
     """A flat batch of variable-length draft chains with per-request sampling
     parameters.  Draft counts are uniform in [0, max_spec_len]; request r
     schedules 1 + its drafts + a random number of earlier tokens, so
     ``cu_num_scheduled_tokens`` is increasing.  The logits rows (one per draft
     and one bonus row per request, in request order) are N(0, 2) with one
     planted token per row raised by U(plant) (integer-valued draws from
-    [-4, 4] when ``ties``); the draft at a row is the planted token with
+    [-4, 4] when ``ties``; U(1, 1.1) when ``crowded``, so that almost every
+    logit shares its sign, exponent and leading mantissa bits); the draft at a row is the planted token with
     probability ``p_right``, else a uniform id.  A fraction of the requests is
     greedy (temperature 0); the others draw T from [0.3, 1.5], top-k from
     {0, 1, 5, 50, 1000} and top-p from {1.0, 0.5, 0.9, 0.97}.  Uniforms ~ U(0, 1)."""
@@ -244,6 +245,8 @@ def flat_batch(seed: int, B: int, max_spec_len: int, V: int, *, plant=(6.0, 14.0
     rows = int(nd.sum()) + B
     if ties:
         logits = rng.integers(-4, 5, (rows, V)).astype(np.float32)
+    elif crowded:
+        logits = rng.uniform(1.0, 1.1, (rows, V)).astype(np.float32)
     else:
         logits = _normal(seed, "flat_logits", (rows, V), 2.0, "f32")
     planted = rng.integers(0, V, rows)

@@ -69,26 +69,27 @@ def _margins_ok(d, meta):
 
 
 CASES = [
-    # V, B, L, ties, greedy fraction
-    (151936, 8, 5, False, 0.25),
-    (128256, 6, 7, False, 0.0),
-    (4099, 16, 4, True, 0.3),     # ragged vocabulary (scalar loads), tied logits
-    (1000, 32, 6, False, 0.5),
+    # V, B, L, ties, greedy fraction, crowded
+    (151936, 8, 5, False, 0.25, False),
+    (128256, 6, 7, False, 0.0, False),
+    (4099, 16, 4, True, 0.3, False),     # ragged vocabulary (scalar loads), tied logits
+    (1000, 32, 6, False, 0.5, False),
+    (100000, 8, 4, False, 0.0, True),    # one first-level bin holds almost every token
 ]
 
 
-@pytest.mark.parametrize("V,B,L,ties,gf", CASES)
-def test_rejection_sample_matches_oracle(V, B, L, ties, gf):
+@pytest.mark.parametrize("V,B,L,ties,gf,crowded", CASES)
+def test_rejection_sample_matches_oracle(V, B, L, ties, gf, crowded):
     chosen = None
     for s in range(40):
-        d = gen.flat_batch(9000 + 31 * s + V % 97, B, L, V, ties=ties, greedy_frac=gf)
+        d = gen.flat_batch(9000 + 31 * s + V % 97, B, L, V, ties=ties, greedy_frac=gf, crowded=crowded)
         meta = osm.spec_decode_metadata(d["cu_num_scheduled_tokens"], d["num_draft_tokens"])
         if _margins_ok(d, meta):
             chosen = (s, d, meta)
             break
     assert chosen is not None, "no seed with clear decision margins"
     s, d, meta = chosen
-    announce(f"rejection sample V={V} B={B} L={L} ties={ties} seed-index={s}")
+    announce(f"rejection sample V={V} B={B} L={L} ties={ties} crowded={crowded} seed-index={s}")
     cu, _, tgt, bonus = meta
     want_out, want_acc = osm.rejection_sample(cu, d["draft_token_ids"], d["logits"], tgt, bonus,
                                               d["temperature"], d["top_k"], d["top_p"], d["uniform"],
