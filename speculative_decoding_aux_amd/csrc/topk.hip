@@ -302,12 +302,32 @@ __global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict
   if (fast) {
     for (int g = t; g < G; g += 256) gmax[g] = -INFINITY;
     __syncthreads();
-    for_row_batches(row, 0, n, [&](const float (&v)[16], int x0) {
-      float bm = v[0];
+    // two batches per thread per step (eight 16-byte loads in flight); the
+    // batch at x0 = 4096 j + 4 t holds row[x0 + 1024 i + e] and is group 256 j + t
+    for (int x0 = 4 * t; x0 < n; x0 += 8192) {
+      float4 w[8];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) bm = fmaxf(bm, v[e]);
-      gmax[(x0 >> 12) * 256 + t] = bm;
-    });
+      for (int i = 0; i < 8; ++i) {
+        const int x = x0 + 1024 * i;
+        if (x + 3 < n) {
+          w[i] = *(const float4*)(row + x);
+        } else {
+          w[i].x = x < n ? row[x] : -INFINITY;
+          w[i].y = x + 1 < n ? row[x + 1] : -INFINITY;
+          w[i].z = x + 2 < n ? row[x + 2] : -INFINITY;
+          w[i].w = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float bm = -INFINITY;
+#pragma unroll
+        for (int i = 4 * h; i < 4 * h + 4; ++i)
+          bm = fmaxf(fmaxf(bm, fmaxf(w[i].x, w[i].y)), fmaxf(w[i].z, w[i].w));
+        const int xb = x0 + 4096 * h;
+        if (xb < n) gmax[(xb >> 12) * 256 + t] = bm;
+      }
+    }
     // radix select of the K-th best group maximum (by key)
     if (t == 0) {
       sh[3] = 0;  // prefix
@@ -324,18 +344,37 @@ __global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict
         if ((key & msk) == pre) atomicAdd(&hist[(key >> p) & 255], 1);
       }
       __syncthreads();
-      if (t == 0) {
-        int need = sh[1], above = 0, dd = 0;
-        for (int d = 255; d >= 0; --d) {
-          if (above + hist[d] >= need) {
-            dd = d;
-            break;
-          }
-          above += hist[d];
+      // wave 0 finds the digit where the count from the top reaches `need`:
+      // lane l sums digits 255 - 4 l down to 252 - 4 l, the lane sums are
+      // scanned from the top and the crossing lane walks its four digits
+      if (t < 64) {
+        const int need = sh[1];
+        const int d1 = 255 - 4 * t;
+        const int c0 = hist[d1], c1 = hist[d1 - 1], c2 = hist[d1 - 2], c3 = hist[d1 - 3];
+        const int c = c0 + c1 + c2 + c3;
+        int cx = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(cx, o, 64);
+          if (t >= o) cx += y;
         }
-        sh[1] = need - above;
-        sh[3] = (int)(pre | ((uint32_t)dd << p));
-        sh[4] = (int)(msk | (255u << p));
+        cx -= c;  // count of the digits above this lane's
+        const unsigned long long bal = __ballot(cx < need && cx + c >= need);
+        if (bal && t == __ffsll((long long)bal) - 1) {
+          int above = cx, dd = d1 - 3;
+          const int cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (above + cs[q] >= need) {
+              dd = d1 - q;
+              break;
+            }
+            above += cs[q];
+          }
+          sh[1] = need - above;
+          sh[3] = (int)(pre | ((uint32_t)dd << p));
+          sh[4] = (int)(msk | (255u << p));
+        }
       }
       __syncthreads();
     }
@@ -350,24 +389,91 @@ __global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict
     __syncthreads();
     const int C = sh[0];
     if (C <= kLargeCand) {
-      int P2 = 16;
-      while (P2 < C * 16) P2 <<= 1;
-      for (int q = t; q < P2; q += 256) {
+      const int nc = C * 16;
+      for (int q = t; q < nc; q += 256) {
         float v = -INFINITY;
         int id = kIdNone;
-        if (q < C * 16) {
-          const int g = cg[q >> 4], e = q & 15;
-          const int x = (g >> 8) * 4096 + 4 * (g & 255) + 1024 * (e >> 2) + (e & 3);
-          if (x < n) {
-            v = row[x];
-            id = x;
-          }
+        const int g = cg[q >> 4], e = q & 15;
+        const int x = (g >> 8) * 4096 + 4 * (g & 255) + 1024 * (e >> 2) + (e & 3);
+        if (x < n) {
+          v = row[x];
+          id = x;
         }
         cv[q] = v;
         ci[q] = id;
       }
-      bitonic_desc(cv, ci, P2);
-      for (int q = t; q < K; q += 256) ids[(int64_t)r * K + q] = ci[q];
+      // radix select of the K-th best candidate by the unique key
+      // (okey(value) << 32) | ~id, 8 bits at a time from the top; it stops
+      // once the picked digit holds exactly the number still needed, and the
+      // K best are then the candidates whose key prefix is >= the picked one
+      auto ckey = [&](int q) -> unsigned long long {
+        return ((unsigned long long)okey(cv[q]) << 32) | (unsigned long long)(~(uint32_t)ci[q]);
+      };
+      if (t == 0) {
+        sh[1] = K;  // still needed
+        sh[5] = 0;  // done
+      }
+      unsigned long long pre = 0;  // picked digits so far (bits above p)
+      int p = 56;
+      for (;; p -= 8) {
+        hist[t] = 0;
+        __syncthreads();
+        for (int q = t; q < nc; q += 256) {
+          const unsigned long long k = ckey(q);
+          if (p == 56 || (k >> (p + 8)) == pre) atomicAdd(&hist[(int)((k >> p) & 255)], 1);
+        }
+        __syncthreads();
+        if (t < 64) {
+          const int need = sh[1];
+          const int d1 = 255 - 4 * t;
+          const int c0 = hist[d1], c1 = hist[d1 - 1], c2 = hist[d1 - 2], c3 = hist[d1 - 3];
+          const int c = c0 + c1 + c2 + c3;
+          int cx = c;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(cx, o, 64);
+            if (t >= o) cx += y;
+          }
+          cx -= c;
+          const unsigned long long bal = __ballot(cx < need && cx + c >= need);
+          if (bal && t == __ffsll((long long)bal) - 1) {
+            int above = cx, dd = d1 - 3;
+            const int cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (above + cs[q] >= need) {
+                dd = d1 - q;
+                break;
+              }
+              above += cs[q];
+            }
+            sh[1] = need - above;
+            sh[6] = dd;
+            sh[5] = (hist[dd] == need - above) ? 1 : 0;
+          }
+        }
+        __syncthreads();
+        pre = (pre << 8) | (unsigned long long)sh[6];
+        if (sh[5] || p == 0) break;
+        __syncthreads();  // sh read by everyone before the next level writes it
+      }
+      // the K best: key prefix (bits >= p) >= pre; sort them (at most 256)
+      __shared__ float sv[256];
+      __shared__ int si[256];
+      if (t == 0) sh[0] = 0;
+      sv[t] = -INFINITY;
+      si[t] = kIdNone;
+      __syncthreads();
+      for (int q = t; q < nc; q += 256)
+        if ((ckey(q) >> p) >= pre) {
+          const int slot = atomicAdd(&sh[0], 1);
+          if (slot < 256) {
+            sv[slot] = cv[q];
+            si[slot] = ci[q];
+          }
+        }
+      bitonic_desc(sv, si, 256);
+      for (int q = t; q < K; q += 256) ids[(int64_t)r * K + q] = si[q];
       return;
     }
   }
