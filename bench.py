@@ -322,6 +322,13 @@ def main():
                    "graph": bool(graph is not None), "wall_s": round(wall, 3)},
         "roofline": roof,
     }
+    # acceptance of the last timed step on the synthetic target logits: mean
+    # accepted drafts per sequence and mean emitted tokens (accepted + the
+    # correction or bonus token)
+    alen = vout[1].cpu().numpy()
+    res["acceptance"] = {"mean_accepted": round(float(alen.mean()), 4),
+                         "mean_emitted": round(float(alen.mean()) + 1.0, 4), "sequences": int(B),
+                         "target_logits": cfg["target_logits"]}
     if roof is not None:
         res["kernels"] = kern
         if not args.no_peaks:
