@@ -48,7 +48,33 @@ def round_bf16_inplace(a: np.ndarray) -> np.ndarray:
     return a
 
 
-def _normal(seed, tag, shape, std, dtype):
+# Tensors of at least this many values may be drawn in independently seeded
+# chunks on several threads (their values then differ from one sequential
+# draw, but are as deterministic).
+_PAR_MIN = 1 << 26
+_PAR_CHUNK = 1 << 24
+
+
+def _normal(seed, tag, shape, std, dtype, parallel=False):
+    n = int(np.prod(shape))
+    if parallel and n >= _PAR_MIN:
+        import concurrent.futures as cf
+        import os
+
+        a = np.empty(n, dtype=np.float32)
+
+        def fill(i):
+            c = a[i * _PAR_CHUNK:(i + 1) * _PAR_CHUNK]
+            np.random.default_rng([int(seed), zlib.crc32(tag.encode()), 0x5EED, i]).standard_normal(
+                size=c.shape[0], dtype=np.float32, out=c)
+            if std != 1.0:
+                c *= np.float32(std)
+            if dtype == "bf16":
+                round_bf16_inplace(c)
+
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range((n + _PAR_CHUNK - 1) // _PAR_CHUNK)))
+        return a.reshape(shape)
     a = _rng(seed, tag).standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
         a *= np.float32(std)
@@ -86,7 +112,7 @@ def make_weights(cfg: dict, seed: int) -> dict:
     dt = cfg["dtype"]
     w = {}
     for name, shape in weight_shapes(cfg).items():
-        w[name] = _normal(seed, "w/" + name, shape, WEIGHT_STD, dt)
+        w[name] = _normal(seed, "w/" + name, shape, WEIGHT_STD, dt, parallel=True)
     H = cfg["hidden"]
     for name in ("input_norm", "hidden_norm", "post_attn_norm", "final_norm"):
         w[name] = np.ones(H, dtype=np.float32)
@@ -119,7 +145,7 @@ def make_step_inputs(cfg: dict, seed: int, ctx_len=None) -> dict:
     }
     for name in ("k", "v"):
         cache = np.zeros((B, nkv, S, hd), dtype=np.float32)
-        cache[:, :, :L, :] = _normal(seed, "kv/" + name, (B, nkv, L, hd), 1.0, dt)
+        cache[:, :, :L, :] = _normal(seed, "kv/" + name, (B, nkv, L, hd), 1.0, dt, parallel=True)
         out[name + "_cache"] = cache
     return out
 
@@ -187,6 +213,11 @@ def philox_seed(seed: int) -> int:
 
 def random_logits(seed: int, tag: str, shape, std: float = 2.0) -> np.ndarray:
     return _normal(seed, tag, shape, std, "f32")
+
+
+def random_states(seed: int, tag: str, shape, dtype: str) -> np.ndarray:
+    """N(0, 1) rows in the workload's storage type (synthetic recurrent states)."""
+    return _normal(seed, tag, shape, 1.0, dtype)
 
 
 def random_tree(cfg: dict, seed: int, batch: int | None = None) -> dict:
