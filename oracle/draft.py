@@ -26,6 +26,14 @@ MLP is SwiGLU with the gate rows first in w_gate_up; the low-rank product
 n @ cand_down^T is rounded to storage precision and there is no nonlinearity
 between the two factors.
 
+EAGLE-3.1 flags (the AMD Quark "EAGLE-3" page, "Background: EAGLE-3 and
+EAGLE-3.1": extra normalisation inside the draft head, named fc_norm and
+norm_output; where it sits is not stated).  Readings: fc_norm is an RMSNorm
+with its own gain (W["fc_norm"]) on the FC output, so the initial pass's layer
+input g (and residual) is the normalised fusion; norm_output makes the
+recurrent output the final-normed row n (the LM head's input) instead of the
+pre-norm state.  Both are off unless the configuration sets them.
+
 Rounding points (storage precision = bf16 or f32 by workload):
   g, c, qkv, rotated q/k, attention output, h1, post-attention norm, the SwiGLU
   product, h_out and the final-normed n are rounded; logits stay float32.
@@ -109,6 +117,8 @@ def draft_pass(cfg, W, kcache, vcache, mode, hidden_in, tokens, seq, pos, slot, 
 
     # S1: FC fusion of the aux states, or the recurrent state as given
     g = to_storage(x @ W["fc"].T, dt) if mode == 0 else to_storage(x, dt)
+    if mode == 0 and cfg.get("fc_norm"):
+        g = to_storage(rmsnorm(g, W["fc_norm"], eps), dt)
     # S2: normalised token embedding | normalised hidden -> [M, 2H]
     e = W["embed"][tokens]
     a = to_storage(rmsnorm(e, W["input_norm"], eps), dt)
@@ -140,7 +150,7 @@ def draft_pass(cfg, W, kcache, vcache, mode, hidden_in, tokens, seq, pos, slot, 
     h_out = to_storage(h1.astype(np.float64) + (s @ W["w_down"].T).astype(np.float64), dt)
     # S8: final norm and LM head
     n = to_storage(rmsnorm(h_out, W["final_norm"], eps), dt)
-    out = {"h_out": h_out, "normed": n}
+    out = {"h_out": n if cfg.get("norm_output") else h_out, "normed": n}
     if not cfg["cand_rank"]:
         out["logits"] = (n @ W["lm_head"].T).astype(np.float32)
         return out

@@ -37,6 +37,8 @@ _BASE = dict(
     target_logits="planted",  # or "draft_plus_noise"
     plant_p=0.7,
     target_layers=1,          # layers of the target-shaped KV compacted after verify
+    fc_norm=0,                # EAGLE-3.1 normalisation flags (off)
+    norm_output=0,
 )
 
 CONFIGS = {

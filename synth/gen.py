@@ -116,6 +116,8 @@ def make_weights(cfg: dict, seed: int) -> dict:
     H = cfg["hidden"]
     for name in ("input_norm", "hidden_norm", "post_attn_norm", "final_norm"):
         w[name] = np.ones(H, dtype=np.float32)
+    if cfg.get("fc_norm"):
+        w["fc_norm"] = np.ones(H, dtype=np.float32)
     w["d2t"] = make_d2t(cfg, seed)
     return w
 

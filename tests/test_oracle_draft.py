@@ -177,3 +177,42 @@ def test_wide_window_equals_full_attention():
     a = od.draft_pass(cfg0, W, inp["k_cache"].copy(), inp["v_cache"].copy(), *args)
     b = od.draft_pass(cfgw, W, inp["k_cache"].copy(), inp["v_cache"].copy(), *args)
     np.testing.assert_array_equal(a["logits"], b["logits"])
+
+
+# ------------------------------------------------ EAGLE-3.1 normalisation flags
+def test_fc_norm_makes_the_pass_invariant_to_the_fc_scale():
+    """With fc_norm the layer input is RMSNorm(FC(a)): scaling the FC weights
+    by 8 (exact in bf16) leaves the pass unchanged (eps = 0); without it the
+    scale changes the logits."""
+    for flag in (1, 0):
+        cfg = _cfg("bf16", fc_norm=flag, rms_eps=0.0)
+        W = gen.make_weights(cfg, 23)
+        inp = gen.make_step_inputs(cfg, 23)
+        W8 = dict(W, fc=W["fc"] * np.float32(8.0))
+        args = (0, inp["aux"][:, 0], inp["in_tokens"][:, 0], [0, 1], [12, 12], [12, 12], inp["ctx_len"],
+                [[12], [12]])
+        a = od.draft_pass(cfg, W, inp["k_cache"].copy(), inp["v_cache"].copy(), *args)
+        b = od.draft_pass(cfg, W8, inp["k_cache"].copy(), inp["v_cache"].copy(), *args)
+        if flag:
+            np.testing.assert_allclose(a["logits"], b["logits"], rtol=0, atol=1e-6)
+            np.testing.assert_array_equal(a["h_out"], b["h_out"])
+        else:
+            assert np.abs(a["logits"] - b["logits"]).max() > 1e-2
+
+
+def test_norm_output_returns_the_normed_row():
+    """With norm_output the recurrent output is the final-normed row: it
+    equals the LM head's input and has unit RMS (gain 1), while the logits do
+    not change."""
+    cfg0 = _cfg("f32")
+    cfg1 = _cfg("f32", norm_output=1)
+    W = gen.make_weights(cfg0, 24)
+    inp = gen.make_step_inputs(cfg0, 24)
+    args = (0, inp["aux"][:, 0], inp["in_tokens"][:, 0], [0, 1], [12, 12], [12, 12], inp["ctx_len"],
+            [[12], [12]])
+    a = od.draft_pass(cfg0, W, inp["k_cache"].copy(), inp["v_cache"].copy(), *args)
+    b = od.draft_pass(cfg1, W, inp["k_cache"].copy(), inp["v_cache"].copy(), *args)
+    np.testing.assert_array_equal(a["logits"], b["logits"])
+    np.testing.assert_array_equal(b["h_out"], b["normed"])
+    np.testing.assert_allclose(np.sqrt((b["h_out"].astype(np.float64) ** 2).mean(axis=1)), 1.0, rtol=1e-5)
+    assert not np.allclose(a["h_out"], b["h_out"])
