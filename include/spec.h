@@ -90,6 +90,14 @@ typedef struct spec_config {
   int32_t max_new;         /* largest n_new (rows per sequence in the root pass) */
   int32_t kv_capacity;     /* S: draft-KV slots per sequence */
   int32_t dtype;           /* spec_dtype: storage type of weights/activations/KV */
+  /* EAGLE-3.1 normalisation (AMD Quark "EAGLE-3" page, "Background: EAGLE-3
+   * and EAGLE-3.1": fc_norm, norm_output; placement not stated there).
+   * fc_norm != 0: the FC output of the initial pass is RMS-normalised with
+   * spec_weights.fc_norm before it enters the layer (input and residual).
+   * norm_output != 0: the recurrent output hidden_out is the final-normed
+   * row (the LM head's input) instead of the pre-norm state. */
+  int32_t fc_norm;
+  int32_t norm_output;
 } spec_config;
 
 /* Draft weights (device, storage type unless stated).  The QKV rows are
@@ -110,6 +118,7 @@ typedef struct spec_weights {
   const int32_t* d2t;         /* [Vd] draft id -> target id, or NULL when Vd == V */
   const void* cand_down;      /* [r, H]  efficient_lm_head_down_proj, or NULL */
   const void* cand_up;        /* [V, r]  efficient_lm_head, or NULL */
+  const void* fc_norm;        /* [H]     RMSNorm gain on the FC output (config fc_norm), or NULL */
 } spec_weights;
 
 /* A KV cache laid out [layers][batch][n_kv_heads][slots][head_dim] in the

@@ -23,13 +23,13 @@ class SpecConfig(ctypes.Structure):
                                      "sliding_window")] + \
                [("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float)] + \
                [(n, c_i32) for n in ("top_k", "depth", "total_tokens", "max_batch", "max_new",
-                                     "kv_capacity", "dtype")]
+                                     "kv_capacity", "dtype", "fc_norm", "norm_output")]
 
 
 class SpecWeights(ctypes.Structure):
     _fields_ = [(n, c_vp) for n in ("fc", "embed", "input_norm", "hidden_norm", "post_attn_norm",
                                     "final_norm", "wqkv", "wo", "w_gate_up", "w_down", "lm_head",
-                                    "d2t", "cand_down", "cand_up")]
+                                    "d2t", "cand_down", "cand_up", "fc_norm")]
 
 
 class SpecKV(ctypes.Structure):

@@ -348,6 +348,9 @@ spec_status check_weights(spec_ctx* ctx, const spec_weights* w) {
   }
   if (ctx->cfg.draft_vocab < ctx->cfg.vocab && !ctx->cfg.cand_rank)
     SPEC_REQ(ctx, w->d2t, SPEC_EINVAL, "a trimmed draft vocabulary needs d2t");
+  if (ctx->cfg.fc_norm)
+    SPEC_REQ(ctx, w->fc_norm && aligned16(w->fc_norm), SPEC_EINVAL,
+             "fc_norm needs a 16-byte aligned fc_norm gain");
   if (ctx->cfg.cand_rank) {
     SPEC_REQ(ctx, w->cand_down && w->cand_up, SPEC_EINVAL, "candidate head factors are null");
     SPEC_REQ(ctx, aligned16(w->cand_down) && aligned16(w->cand_up), SPEC_EINVAL,
@@ -388,7 +391,12 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
   if (io.mode == 0) {
     const GemmPlan p = gemm_plan(M, H, 3 * H, bf);
     SPEC_HIP(ctx, gemm(bf, io.hidden, 3 * H, w->fc, 3 * H, P, M, H, 3 * H, p, s));
-    SPEC_HIP(ctx, gemm_epilogue(bf, EPI_STORE, ws.g, nullptr, P, p.nsplit, M, H, s));
+    if (c.fc_norm) {  // EAGLE-3.1: the layer input is the normalised fusion
+      SPEC_HIP(ctx, gemm_epilogue(bf, EPI_STORE, ws.h1, nullptr, P, p.nsplit, M, H, s));
+      SPEC_HIP(ctx, rmsnorm(bf, ws.h1, w->fc_norm, c.rms_eps, M, H, ws.g, s));
+    } else {
+      SPEC_HIP(ctx, gemm_epilogue(bf, EPI_STORE, ws.g, nullptr, P, p.nsplit, M, H, s));
+    }
     SPEC_HIP(ctx, prologue(bf, w->embed, c.vocab, io.tok, ws.g, nullptr, w->input_norm,
                            w->hidden_norm, c.rms_eps, M, H, ws.g, ws.c, s));
   } else if (!io.skip_prologue) {
@@ -455,6 +463,9 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
       SPEC_HIP(ctx, gemm_epilogue(bf, EPI_RESID, io.hidden_out, ws.h1, P, p.nsplit, M, H, s));
       SPEC_HIP(ctx, rmsnorm(bf, io.hidden_out, w->final_norm, c.rms_eps, M, H, ws.nrm, s));
     }
+    if (c.norm_output)  // EAGLE-3.1: the recurrent output is the normed row
+      SPEC_HIP(ctx, hipMemcpyAsync(io.hidden_out, ws.nrm, (size_t)M * H * ctx->esz,
+                                   hipMemcpyDeviceToDevice, s));
   }
   if (!c.cand_rank) {
     const int Vd = c.draft_vocab;

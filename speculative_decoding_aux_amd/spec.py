@@ -42,7 +42,7 @@ class Weights:
     """Draft weights resident on the GPU, in the workload's storage type."""
 
     NAMES = ("fc", "embed", "input_norm", "hidden_norm", "post_attn_norm", "final_norm", "wqkv", "wo",
-             "w_gate_up", "w_down", "lm_head", "cand_down", "cand_up")
+             "w_gate_up", "w_down", "lm_head", "cand_down", "cand_up", "fc_norm")
 
     def __init__(self, tensors: dict):
         self.t = tensors
@@ -100,7 +100,8 @@ class SpecContext:
                          sliding_window=cfg.get("sliding_window", 0), rope_base=cfg["rope_base"],
                          rms_eps=cfg["rms_eps"], top_k=cfg["top_k"], depth=cfg["depth"],
                          total_tokens=cfg["total_tokens"], max_batch=max_batch, max_new=max_new,
-                         kv_capacity=cfg["kv_capacity"], dtype=code)
+                         kv_capacity=cfg["kv_capacity"], dtype=code, fc_norm=int(cfg.get("fc_norm", 0)),
+                         norm_output=int(cfg.get("norm_output", 0)))
         h = ctypes.c_void_p()
         st = self.lib.spec_create(ctypes.byref(c), ctypes.byref(h))
         if st != L.SPEC_OK:

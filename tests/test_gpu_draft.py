@@ -73,6 +73,11 @@ CASES = {
     "eagle4_rows96_v70000": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
                                                               cand_rank=64, num_candidates=64, top_k=8,
                                                               total_tokens=20, batch=12, ctx=24)), 2e-2),
+    # EAGLE-3.1 flags: normalised FC output, normed recurrent output
+    "small_bf16_eagle31": (configs.get("tiny_chain", **dict(SMALL, fc_norm=1, norm_output=1)), 2e-2),
+    "small_f32_eagle31_rows64": (configs.get("tiny_chain", **dict(SMALL, dtype="f32", batch=8, top_k=8,
+                                                                  total_tokens=20, fc_norm=1,
+                                                                  norm_output=1)), 1e-4),
 }
 
 
@@ -196,6 +201,7 @@ BUILD = {
     # more than one batch of the attention combine
     "deep_tree_two_new": (configs.get("tiny_chain", **dict(SMALLB, depth=8, total_tokens=10, n_new=2)), 2e-2),
     "deep_chain": (configs.get("tiny_chain", **dict(SMALLB, top_k=1, depth=9, total_tokens=9)), 2e-2),
+    "eagle31_tree": (configs.get("tiny_chain", **dict(SMALLB, fc_norm=1, norm_output=1)), 2e-2),
     # chains over a vocab-wide LM head: its records are merged, the tree step
     # taken and the next pass's inputs built in one launch per pass
     "bigvocab_chain": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000, top_k=1,
@@ -203,6 +209,10 @@ BUILD = {
     "bigvocab_chain_two_new": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
                                                                 top_k=1, depth=3, total_tokens=3,
                                                                 n_new=2)), 2e-2),
+    # the chain's one-launch tail builds the next pass from the normed output
+    "bigvocab_chain_eagle31": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
+                                                                top_k=1, depth=3, total_tokens=3,
+                                                                fc_norm=1, norm_output=1)), 2e-2),
 }
 
 
