@@ -329,6 +329,8 @@ def main():
     res["acceptance"] = {"mean_accepted": round(float(alen.mean()), 4),
                          "mean_emitted": round(float(alen.mean()) + 1.0, 4), "sequences": int(B),
                          "target_logits": cfg["target_logits"]}
+    if cfg["cand_rank"]:
+        res["candidate_recall"] = candidate_recall(cfg, ctx, w, draft_kv, aux, inp)
     if roof is not None:
         res["kernels"] = kern
         if not args.no_peaks:
@@ -348,6 +350,38 @@ def main():
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, W, inp, seed, args.cpu_steps)
     print(json.dumps(res), flush=True)
+
+
+def candidate_recall(cfg, ctx4, w, draft_kv, aux, inp):
+    """EAGLE-4 candidate recall on the root pass: the share of the full LM
+    head's top-k (an EAGLE-3 head over the same lm_head, the same rows and
+    inputs) that the low-rank head's retrieved candidates contain; at 1 and
+    at top_k, averaged over the sequences.  Both passes run in the library;
+    they write the root rows' K/V into a copy of the draft cache."""
+    import torch
+
+    from speculative_decoding_aux_amd import spec as S
+
+    B, k = cfg["batch"], cfg["top_k"]
+    cfg3 = dict(cfg, cand_rank=0, num_candidates=0)
+    ctx3 = S.SpecContext(cfg3, max_batch=B, max_new=cfg["n_new"])
+    kv = S.KVCache(draft_kv.k.clone(), draft_kv.v.clone())
+    pos = inp["ctx_len"].astype(np.int32)
+    toks = inp["in_tokens"][:, 0]
+    anc = pos[:, None]
+    g4 = S.spec_draft_step(ctx4, w, kv, B, 1, 0, aux[:, 0].contiguous(), toks, pos, pos, inp["ctx_len"], anc,
+                           k, want_candidates=True)
+    g3 = S.spec_draft_step(ctx3, w, kv, B, 1, 0, aux[:, 0].contiguous(), toks, pos, pos, inp["ctx_len"], anc,
+                           k)
+    torch.cuda.synchronize()
+    full = g3["ids"].cpu().numpy()
+    cands = g4["cand_ids"].cpu().numpy()
+    at1 = np.mean([full[r, 0] in set(cands[r].tolist()) for r in range(B)])
+    atk = np.mean([len(set(full[r].tolist()) & set(cands[r].tolist())) / k for r in range(B)])
+    del kv
+    ctx3.close()
+    return {"at_1": round(float(at1), 4), f"at_{k}": round(float(atk), 4), "rows": int(B),
+            "candidates": int(cfg["num_candidates"]), "note": "random synthetic factors: recall near K/V"}
 
 
 def bench_flat_sampling(args):
