@@ -136,6 +136,19 @@ typedef struct spec_kv {
   int64_t stride_layer;
   int64_t stride_seq;
   int64_t stride_head;
+  /* Paged caches (vLLM Neuron page, "KV Cache Sharing": physical slot =
+   * block_table[pos / block_size] * block_size + pos % block_size).  NULL
+   * block_table: the contiguous layout above.  Otherwise k and v are pools
+   * [layers][num_blocks][n_kv_heads][block_size][head_dim]; stride_seq is the
+   * stride of one block, stride_head the stride of a head inside a block;
+   * block_table is [batch][max_blocks] int32 on the device; slots must equal
+   * max_blocks * block_size (the logical slots of a sequence).  Block ids
+   * outside [0, num_blocks) are clamped.  The blocks a call writes (new
+   * rows, compaction) must not be shared between sequences. */
+  const int32_t* block_table;
+  int32_t block_size;
+  int32_t max_blocks;
+  int32_t num_blocks;
 } spec_kv;
 
 /* The draft tree of each sequence, N+1 nodes; node 0 is the root (the last

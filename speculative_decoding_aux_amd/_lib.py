@@ -35,7 +35,9 @@ class SpecWeights(ctypes.Structure):
 class SpecKV(ctypes.Structure):
     _fields_ = [("k", c_vp), ("v", c_vp)] + \
                [(n, c_i32) for n in ("num_layers", "batch", "n_kv_heads", "slots", "head_dim")] + \
-               [(n, ctypes.c_int64) for n in ("stride_layer", "stride_seq", "stride_head")]
+               [(n, ctypes.c_int64) for n in ("stride_layer", "stride_seq", "stride_head")] + \
+               [("block_table", c_vp)] + \
+               [(n, c_i32) for n in ("block_size", "max_blocks", "num_blocks")]
 
 
 class SpecTree(ctypes.Structure):

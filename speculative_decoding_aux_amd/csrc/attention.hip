@@ -64,7 +64,7 @@ SPEC_DEV void store_dims(T* p, const float (&x)[N]) {
 // as soon as the slots arrive, so the wave waits on two round trips to memory.
 template <typename T, int HD>
 SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restrict__ kc,
-                         const T* __restrict__ vc, int64_t sseq, int64_t shead, int S,
+                         const T* __restrict__ vc, int64_t sseq, int64_t shead, int S, KvPages pg,
                          const int* __restrict__ pos, const int* __restrict__ anc, int A, int R,
                          int nq, int nkv, int window, int nch, const float* __restrict__ part,
                          T* __restrict__ out) {
@@ -103,15 +103,17 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
   const int rank = __popcll(vmask & ((1ull << lane) - 1ull));
   const bool vis = sl >= 0 && sl < S && (window <= 0 || pq - (nvalid - 1 - rank) > pq - window);
   const unsigned long long kmask = __ballot(vis);
-  const T* kb = kc + b * sseq + kvh * shead;
-  const T* vb = vc + b * sseq + kvh * shead;
+  // each lane's own extra slot as an element offset (a page lookup when paged)
+  const long long soff = vis ? (long long)kv_slot_off(pg, b, sl, sseq, HD) : 0ll;
+  const T* kb = kc + kvh * shead;
+  const T* vb = vc + kvh * shead;
   float kv[KB][DPL], vv[KB][DPL];
   auto load_batch = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int j = j0 + u;
       const bool ok = j < 64 && ((kmask >> j) & 1ull);
-      const int64_t row = (int64_t)__shfl(sl, j & 63, 64) * HD + DPL * lane;
+      const int64_t row = (int64_t)__shfl(soff, j & 63, 64) + DPL * lane;
       if (ok) {
         load_dims<T, DPL>(kb + row, kv[u]);
         load_dims<T, DPL>(vb + row, vv[u]);
@@ -215,13 +217,13 @@ template <typename T, int HD>
 __global__ __launch_bounds__(64) void attn_combine_kernel(const T* __restrict__ q,
                                                           const T* __restrict__ kc,
                                                           const T* __restrict__ vc, int64_t sseq,
-                                                          int64_t shead, int S,
+                                                          int64_t shead, int S, KvPages pg,
                                                           const int* __restrict__ pos,
                                                           const int* __restrict__ anc, int A,
                                                           int R, int nq, int nkv, int window,
                                                           int nch, const float* __restrict__ part,
                                                           T* __restrict__ out) {
-  combine_qv<T, HD>(blockIdx.x, blockIdx.y, q, kc, vc, sseq, shead, S, pos, anc, A, R, nq, nkv,
+  combine_qv<T, HD>(blockIdx.x, blockIdx.y, q, kc, vc, sseq, shead, S, pg, pos, anc, A, R, nq, nkv,
                     window, nch, part, out);
 }
 
@@ -229,7 +231,7 @@ template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ kc,
                                                        const T* __restrict__ vc, int64_t sseq,
-                                                       int64_t shead, int S,
+                                                       int64_t shead, int S, KvPages pg,
                                                        const int* __restrict__ ctx_len,
                                                        const int* __restrict__ pos, int R, int nq,
                                                        int nkv, int window, int chunk,
@@ -267,8 +269,8 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
   }
   __syncthreads();
 
-  const T* kb = kc + b * sseq + kvh * shead;
-  const T* vb = vc + b * sseq + kvh * shead;
+  const T* kb = kc + kvh * shead;  // rows at kv_slot_off(pg, b, key, ...)
+  const T* vb = vc + kvh * shead;
   constexpr int NG = 256 / HD;          // PV thread groups
   const int d = threadIdx.x % HD, grp = threadIdx.x / HD;
   float acc[(64 + NG - 1) / NG];
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
     float kv[HD];
     if (kok) {
       // 16-byte loads of the key row
-      const u32x4_t* kr = (const u32x4_t*)(kb + (int64_t)key * HD);
+      const u32x4_t* kr = (const u32x4_t*)(kb + kv_slot_off(pg, b, key, sseq, HD));
       constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
 #pragma unroll
       for (int vq = 0; vq < HD / EPV; ++vq) {
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
       float v8[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        v8[u] = kk0 + u < nk ? St<T>::load(vb, (int64_t)(t0 + kk0 + u) * HD + d) : 0.f;
+        v8[u] = kk0 + u < nk ? St<T>::load(vb, kv_slot_off(pg, b, t0 + kk0 + u, sseq, HD) + d) : 0.f;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (kk0 + u >= nk) break;
@@ -384,8 +386,9 @@ SPEC_DEV int v_swz(int r) { return 2 * ((r >> 2) & 3); }
 template <int HD, int QT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_ctx_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
-    int64_t sseq, int64_t shead, int S, const int* __restrict__ ctx_len, const int* __restrict__ pos,
-    int R, int nq, int nkv, int window, int chunk, float* __restrict__ part) {
+    int64_t sseq, int64_t shead, int S, KvPages pg, const int* __restrict__ ctx_len,
+    const int* __restrict__ pos, int R, int nq, int nkv, int window, int chunk,
+    float* __restrict__ part) {
   constexpr int DS = HD / 32;        // 32-dim steps of S^T
   constexpr int DT = HD / 16;        // 16-dim tiles of O^T
   constexpr int CH = HD / 8;         // 16-byte chunks per row
@@ -402,6 +405,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   // slot 1 in V stage 1, free after the key loop), [2][QT][64] max and sum
   static_assert(QT * DT * 64 * 16 <= 4 * BLK * 16, "merge slot fits in a V stage");
   __shared__ float mm[2 * QT * 64], ml[2 * QT * 64];
+  // paged caches: the blocks of the pages this chunk touches, read once
+  __shared__ int ptab[kAttnMaxChunkPages];
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int nch = gridDim.x;
   const int G = nq / nkv, QV = R * G;
@@ -419,6 +424,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const int k1 = min(ctx, k0 + chunk);
   const int first = k0 + wave * 16;
   const int nblk = first < k1 ? (k1 - first + 63) / 64 : 0;
+
+  // every key the kernel touches lies in [kmin, kmax] (clamped reads past
+  // the end included)
+  const int kmax = max(k1 - 1, 0), kmin = min(k0, kmax);
+  const int pg0 = pg.tbl ? kmin / pg.bs : 0;
+  const int npg = pg.tbl ? min(kmax / pg.bs - pg0 + 1, kAttnMaxChunkPages) : 0;
+  for (int i = threadIdx.x; i < npg; i += 256) {
+    const int page = min(pg0 + i, pg.mb - 1);
+    const int blk = pg.tbl[(int64_t)b * pg.mb + page];
+    ptab[i] = blk < 0 ? 0 : (blk >= pg.nblk ? pg.nblk - 1 : blk);
+  }
+  // element offset of key row `key` of this sequence (head 0)
+  auto koff = [&](int key) -> int64_t {
+    if (!pg.tbl) return (int64_t)b * sseq + (int64_t)key * HD;
+    const int page = key / pg.bs;
+    const int i = min(max(page - pg0, 0), npg - 1);
+    return (int64_t)ptab[i] * sseq + (int64_t)(key - page * pg.bs) * HD;
+  };
 
   int loq[QT];
 #pragma unroll
@@ -444,8 +467,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const bf16_t* kb = kc + b * sseq + kvh * shead;
-  const bf16_t* vb = vc + b * sseq + kvh * shead;
+  const bf16_t* kb = kc + kvh * shead;  // key rows at koff(key)
+  const bf16_t* vb = vc + kvh * shead;
 
   auto vbuf = [](auto sc) -> SPEC_LDS u32x4_t* {
     if constexpr (decltype(sc)::value == 0) return (SPEC_LDS u32x4_t*)v0s;
@@ -454,21 +477,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   u32x4_t kf[DS];  // K fragments: loaded for block i + 1 once block i's scores are done
   auto issue_k = [&](int i) {
     const int base = first + min(i, max(nblk - 1, 0)) * 64;
-    const bf16_t* kp = kb + (int64_t)min(base + col, max(k1 - 1, 0)) * HD + g * 8;
+    const bf16_t* kp = kb + koff(min(base + col, max(k1 - 1, 0))) + g * 8;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) kf[ds] = *(const u32x4_t*)(kp + ds * 32);
   };
   // V rows of block i (past the end: the last block again, never used)
   auto issue_v = [&](auto sc, int i) {
     const int base = first + min(i, max(nblk - 1, 0)) * 64;
-    const int kmax = max(k1 - 1, 0);
     // unit u of a block is row u / CH at position u % CH, holding chunk
     // (u % CH) ^ v_swz(row)
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       const int u = j * 64 + lane, row = u / CH;
       const int key = min(base + row, kmax);
-      dma16(vb + (int64_t)key * HD + ((u % CH) ^ v_swz(row)) * 8, vbuf(sc) + wave * BLK + j * 64);
+      dma16(vb + koff(key) + ((u % CH) ^ v_swz(row)) * 8, vbuf(sc) + wave * BLK + j * 64);
     }
   };
 
@@ -643,25 +665,27 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     if (QV <= 16) {
       SPEC_LAUNCH((attn_ctx_mfma_kernel<HD, 1>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
                          (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq,
-                         a.kv.stride_head, a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
+                         a.kv.stride_head, a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
                          a.window, a.chunk, a.part);
     } else {
       SPEC_LAUNCH((attn_ctx_mfma_kernel<HD, 2>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
                          (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq,
-                         a.kv.stride_head, a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
+                         a.kv.stride_head, a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
                          a.window, a.chunk, a.part);
     }
   } else {
     const size_t lds = (size_t)QV * (HD + kTile + 3) * sizeof(float) + QV * sizeof(int);
     SPEC_LAUNCH((attn_ctx_kernel<T, HD>), grid, dim3(256), lds, s, (const T*)a.q,
                        (const T*)a.kv.k, (const T*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
-                       a.kv.slots, a.ctx_len, a.pos, a.R, a.nq, a.nkv, a.window, a.chunk, a.part);
+                       a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, a.nq, a.nkv, a.window, a.chunk,
+                       a.part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SPEC_LAUNCH((attn_combine_kernel<T, HD>), dim3(a.B * a.R, a.nq), dim3(64), 0, s,
                      (const T*)a.q, (const T*)a.kv.k, (const T*)a.kv.v, a.kv.stride_seq,
-                     a.kv.stride_head, a.kv.slots, a.pos, a.anc, a.A, a.R, a.nq, a.nkv, a.window,
+                     a.kv.stride_head, a.kv.slots, a.kv.pg, a.pos, a.anc, a.A, a.R, a.nq, a.nkv,
+                     a.window,
                      a.nchunks, a.part, (T*)a.out);
   return hipGetLastError();
 }

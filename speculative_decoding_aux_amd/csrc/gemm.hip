@@ -504,7 +504,7 @@ __global__ __launch_bounds__(256) void qkv_epi_kernel(
     const float* __restrict__ P, int nsplit, int M, int nq, int nkv, int hd,
     const int* __restrict__ pos, const int* __restrict__ slot, int rows_per_seq, float rope_base,
     T* __restrict__ qout, T* __restrict__ kc, T* __restrict__ vc, int64_t stride_seq,
-    int64_t stride_head, int slots) {
+    int64_t stride_head, int slots, KvPages pg) {
   __shared__ float red[2][4][64];
   const int m = blockIdx.x, h = blockIdx.y, i = threadIdx.x & 63, sg = threadIdx.x >> 6;
   const int half = hd >> 1;
@@ -540,12 +540,12 @@ __global__ __launch_bounds__(256) void qkv_epi_kernel(
       St<T>::store(q, i, y1);
       St<T>::store(q, i + half, y2);
     } else if (sl >= 0 && sl < slots) {
-      T* k = kc + seq * stride_seq + (int64_t)(h - nq) * stride_head + (int64_t)sl * hd;
+      T* k = kc + kv_slot_off(pg, seq, sl, stride_seq, hd) + (int64_t)(h - nq) * stride_head;
       St<T>::store(k, i, y1);
       St<T>::store(k, i + half, y2);
     }
   } else if (sl >= 0 && sl < slots) {
-    T* v = vc + seq * stride_seq + (int64_t)(h - nq - nkv) * stride_head + (int64_t)sl * hd;
+    T* v = vc + kv_slot_off(pg, seq, sl, stride_seq, hd) + (int64_t)(h - nq - nkv) * stride_head;
     St<T>::store(v, i, x1);
     St<T>::store(v, i + half, x2);
   }
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(256) void qkv_epi_rows_kernel(
     const float* __restrict__ P, int nsplit, int M, int nq, int nkv, int hd,
     const int* __restrict__ pos, const int* __restrict__ slot, int rows_per_seq, float rope_base,
     T* __restrict__ qout, T* __restrict__ kc, T* __restrict__ vc, int64_t stride_seq,
-    int64_t stride_head, int slots, int hpb) {
+    int64_t stride_head, int slots, KvPages pg, int hpb) {
   const int m = blockIdx.x, half = hd >> 1;
   const int par = blockDim.x / half;  // heads in flight per block
   const int i = threadIdx.x % half, hs = threadIdx.x / half;
@@ -590,12 +590,12 @@ __global__ __launch_bounds__(256) void qkv_epi_rows_kernel(
         St<T>::store(q, i, y1);
         St<T>::store(q, i + half, y2);
       } else if (sl >= 0 && sl < slots) {
-        T* k = kc + seq * stride_seq + (int64_t)(h - nq) * stride_head + (int64_t)sl * hd;
+        T* k = kc + kv_slot_off(pg, seq, sl, stride_seq, hd) + (int64_t)(h - nq) * stride_head;
         St<T>::store(k, i, y1);
         St<T>::store(k, i + half, y2);
       }
     } else if (sl >= 0 && sl < slots) {
-      T* v = vc + seq * stride_seq + (int64_t)(h - nq - nkv) * stride_head + (int64_t)sl * hd;
+      T* v = vc + kv_slot_off(pg, seq, sl, stride_seq, hd) + (int64_t)(h - nq - nkv) * stride_head;
       St<T>::store(v, i, x1);
       St<T>::store(v, i + half, x2);
     }
@@ -787,11 +787,11 @@ hipError_t qkv_epilogue(bool bf16, const float* P, int nsplit, int M, int nq, in
     if (bf16) {
       SPEC_LAUNCH(qkv_epi_rows_kernel<bf16_t>, grid, dim3(256), 0, s, P, nsplit, M, nq, nkv, hd,
                   pos, slot, rows_per_seq, rope_base, (bf16_t*)qout, (bf16_t*)kv.k,
-                  (bf16_t*)kv.v, kv.stride_seq, kv.stride_head, kv.slots, hpb);
+                  (bf16_t*)kv.v, kv.stride_seq, kv.stride_head, kv.slots, kv.pg, hpb);
     } else {
       SPEC_LAUNCH(qkv_epi_rows_kernel<float>, grid, dim3(256), 0, s, P, nsplit, M, nq, nkv, hd,
                   pos, slot, rows_per_seq, rope_base, (float*)qout, (float*)kv.k, (float*)kv.v,
-                  kv.stride_seq, kv.stride_head, kv.slots, hpb);
+                  kv.stride_seq, kv.stride_head, kv.slots, kv.pg, hpb);
     }
     return hipGetLastError();
   }
@@ -800,11 +800,11 @@ hipError_t qkv_epilogue(bool bf16, const float* P, int nsplit, int M, int nq, in
   if (bf16) {
     SPEC_LAUNCH(qkv_epi_kernel<bf16_t>, grid, block, 0, s, P, nsplit, M, nq, nkv, hd, pos,
                        slot, rows_per_seq, rope_base, (bf16_t*)qout, (bf16_t*)kv.k,
-                       (bf16_t*)kv.v, kv.stride_seq, kv.stride_head, kv.slots);
+                       (bf16_t*)kv.v, kv.stride_seq, kv.stride_head, kv.slots, kv.pg);
   } else {
     SPEC_LAUNCH(qkv_epi_kernel<float>, grid, block, 0, s, P, nsplit, M, nq, nkv, hd, pos,
                        slot, rows_per_seq, rope_base, (float*)qout, (float*)kv.k, (float*)kv.v,
-                       kv.stride_seq, kv.stride_head, kv.slots);
+                       kv.stride_seq, kv.stride_head, kv.slots, kv.pg);
   }
   return hipGetLastError();
 }

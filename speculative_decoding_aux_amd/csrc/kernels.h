@@ -44,11 +44,38 @@ enum EpiOp { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_F32 = 3 };
 hipError_t gemm_epilogue(bool bf16, int op, void* Y, const void* R, const float* P, int nsplit,
                          int M, int N, hipStream_t s);
 
+// Paged KV (vLLM Neuron page, "KV Cache Sharing": the physical slot of a
+// logical position is block_table[pos / block_size] * block_size + pos %
+// block_size).  tbl == nullptr: contiguous caches, slot s of sequence b at
+// b * stride_seq + s * hd.  Otherwise the pool holds nblk blocks of bs slots,
+// stride_seq apart, and slot s of sequence b lies in block tbl[b * mb + s / bs]
+// at offset s % bs; slots and block ids are clamped into the table and the
+// pool, so no value in them addresses memory outside the caches.
+struct KvPages {
+  const int* tbl = nullptr;
+  int bs = 0, mb = 0, nblk = 0;
+};
+__device__ __forceinline__ int64_t kv_slot_off(const KvPages& pg, int b, int s, int64_t sseq,
+                                               int hd) {
+  if (!pg.tbl) return (int64_t)b * sseq + (int64_t)s * hd;
+  const int cap = pg.mb * pg.bs;
+  s = s < 0 ? 0 : (s >= cap ? cap - 1 : s);
+  const int page = s / pg.bs;
+  int blk = pg.tbl[(int64_t)b * pg.mb + page];
+  blk = blk < 0 ? 0 : (blk >= pg.nblk ? pg.nblk - 1 : blk);
+  return (int64_t)blk * sseq + (int64_t)(s - page * pg.bs) * hd;
+}
+
+// Pages one attention chunk may touch (paged caches need att_chunk / block_size + 2
+// at most this many).
+constexpr int kAttnMaxChunkPages = 512;
+
 struct KvView {
   void* k;
   void* v;
-  int64_t stride_seq, stride_head;  // elements
+  int64_t stride_seq, stride_head;  // elements (paged: block stride, head stride in a block)
   int slots;
+  KvPages pg;
 };
 // QKV epilogue: sum partials, round, RoPE on q and k at pos[m], store q to
 // qout[M, nq, hd], k/v to the cache at (m / rows_per_seq, head, slot[m]).
@@ -182,6 +209,7 @@ hipError_t rejection_sample(int B, int L, int V, int nrows, const int* cu_nd, co
 struct KvFull {
   void* k; void* v; int layers; int batch; int nkv; int slots; int hd;
   int64_t stride_layer, stride_seq, stride_head;
+  KvPages pg;
 };
 hipError_t compact(bool bf16, KvFull kv, int B, const int* base, const int* nodes,
                    const int* alen, int max_accept, hipStream_t s);

@@ -371,9 +371,32 @@ spec_status check_kv(spec_ctx* ctx, const spec_kv* kv, int B, int layers_min) {
   SPEC_REQ(ctx, (kv->stride_head * e) % 16 == 0 && (kv->stride_seq * e) % 16 == 0 &&
                     (kv->stride_layer * e) % 16 == 0,
            SPEC_EINVAL, "KV strides must keep 16-byte alignment");
-  SPEC_REQ(ctx, kv->stride_head >= (int64_t)kv->slots * kv->head_dim, SPEC_EINVAL,
-           "KV head stride smaller than slots * head_dim");
+  if (!kv->block_table) {
+    SPEC_REQ(ctx, kv->stride_head >= (int64_t)kv->slots * kv->head_dim, SPEC_EINVAL,
+             "KV head stride smaller than slots * head_dim");
+    return SPEC_OK;
+  }
+  SPEC_REQ(ctx, kv->block_size > 0 && kv->max_blocks > 0 && kv->num_blocks > 0 &&
+                    (int64_t)kv->max_blocks * kv->block_size == kv->slots,
+           SPEC_EINVAL, "paged KV: slots must equal max_blocks * block_size");
+  SPEC_REQ(ctx, kv->stride_head >= (int64_t)kv->block_size * kv->head_dim &&
+                    kv->stride_seq >= (int64_t)kv->n_kv_heads * kv->stride_head,
+           SPEC_EINVAL, "paged KV: block strides smaller than a block");
+  SPEC_REQ(ctx, ctx->att_chunk / kv->block_size + 2 <= kAttnMaxChunkPages, SPEC_EUNSUPPORTED,
+           "paged KV: block_size %d too small for attention chunks of %d keys", kv->block_size,
+           ctx->att_chunk);
   return SPEC_OK;
+}
+
+KvPages kv_pages(const spec_kv* kv) {
+  KvPages pg;
+  if (kv->block_table) {
+    pg.tbl = kv->block_table;
+    pg.bs = kv->block_size;
+    pg.mb = kv->max_blocks;
+    pg.nblk = kv->num_blocks;
+  }
+  return pg;
 }
 
 spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, const PassIO& io,
@@ -404,7 +427,7 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
                            w->hidden_norm, c.rms_eps, M, H, ws.g, ws.c, s));
   }
   // S3 + S4: QKV, RoPE, K/V store
-  KvView kvv{kv->k, kv->v, kv->stride_seq, kv->stride_head, kv->slots};
+  KvView kvv{kv->k, kv->v, kv->stride_seq, kv->stride_head, kv->slots, kv_pages(kv)};
   {
     const GemmPlan p = gemm_plan(M, qkvN, 2 * H, bf);
     SPEC_HIP(ctx, gemm(bf, ws.c, 2 * H, w->wqkv, 2 * H, P, M, qkvN, 2 * H, p, s));
@@ -829,7 +852,7 @@ spec_status spec_compact_kv(spec_ctx* ctx, const spec_kv* kv, int32_t B, const i
            "null argument");
   SPEC_REQ(ctx, max_accept > 0 && max_accept <= 64, SPEC_EUNSUPPORTED, "max_accept outside [1, 64]");
   KvFull f{kv->k, kv->v, kv->num_layers, kv->batch, kv->n_kv_heads, kv->slots, kv->head_dim,
-           kv->stride_layer, kv->stride_seq, kv->stride_head};
+           kv->stride_layer, kv->stride_seq, kv->stride_head, kv_pages(kv)};
   SPEC_HIP(ctx, compact(ctx->bf16, f, B, tree_base, accepted_nodes, accepted_len, max_accept,
                         STREAM(stream)));
   return SPEC_OK;

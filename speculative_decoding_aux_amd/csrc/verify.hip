@@ -339,14 +339,15 @@ __global__ __launch_bounds__(64) void verify_emit_kernel(int D, int nch,
 template <int VEC_PER_ROW>
 __global__ __launch_bounds__(256) void compact_kernel(char* __restrict__ kb, char* __restrict__ vb,
                                                       int64_t sl_bytes, int64_t ss_bytes,
-                                                      int64_t sh_bytes, int slots,
+                                                      int64_t sh_bytes, int slots, KvPages pg,
                                                       const int* __restrict__ base,
                                                       const int* __restrict__ nodes,
                                                       const int* __restrict__ alen, int max_accept) {
   const int b = blockIdx.x, layer = blockIdx.y, h = blockIdx.z, t = threadIdx.x;
   const int a = clampi(alen[b], 0, max_accept);
   const int bs = base[b];
-  const int64_t off = layer * sl_bytes + b * ss_bytes + h * sh_bytes;
+  const int64_t off = layer * sl_bytes + h * sh_bytes;  // + the row of (b, slot)
+  constexpr int kRow = VEC_PER_ROW * 16;
   constexpr int kPer = (2 * 64 * VEC_PER_ROW + 255) / 256;  // up to 64 rows of K and V
   u32x4_t buf[kPer];
   const int total = 2 * a * VEC_PER_ROW;
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(256) void compact_kernel(char* __restrict__ kb, cha
       const int j = rem / VEC_PER_ROW, q = rem % VEC_PER_ROW;
       const int src = bs + nodes[(int64_t)b * max_accept + j];
       if (src >= 0 && src < slots) {
-        const char* p = (kv ? vb : kb) + off + (int64_t)src * VEC_PER_ROW * 16 + q * 16;
+        const char* p = (kv ? vb : kb) + off + kv_slot_off(pg, b, src, ss_bytes, kRow) + q * 16;
         buf[i] = *(const u32x4_t*)p;
       }
     }
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(256) void compact_kernel(char* __restrict__ kb, cha
       const int src = bs + nodes[(int64_t)b * max_accept + j];
       const int dst = bs + 1 + j;
       if (src >= 0 && src < slots && dst >= 0 && dst < slots) {
-        char* p = (kv ? vb : kb) + off + (int64_t)dst * VEC_PER_ROW * 16 + q * 16;
+        char* p = (kv ? vb : kb) + off + kv_slot_off(pg, b, dst, ss_bytes, kRow) + q * 16;
         *(u32x4_t*)p = buf[i];
       }
     }
@@ -443,13 +444,13 @@ hipError_t compact(bool bf16, KvFull kv, int B, const int* base, const int* node
   const int64_t sl = kv.stride_layer * esz, ss = kv.stride_seq * esz, sh = kv.stride_head * esz;
   if (row_bytes == 256) {
     SPEC_LAUNCH(compact_kernel<16>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
-                       sh, kv.slots, base, nodes, alen, max_accept);
+                       sh, kv.slots, kv.pg, base, nodes, alen, max_accept);
   } else if (row_bytes == 128) {
     SPEC_LAUNCH(compact_kernel<8>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
-                       sh, kv.slots, base, nodes, alen, max_accept);
+                       sh, kv.slots, kv.pg, base, nodes, alen, max_accept);
   } else {
     SPEC_LAUNCH(compact_kernel<32>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
-                       sh, kv.slots, base, nodes, alen, max_accept);
+                       sh, kv.slots, kv.pg, base, nodes, alen, max_accept);
   }
   return hipGetLastError();
 }

@@ -61,7 +61,23 @@ class KVCache:
         self.k, self.v = k, v
         Lr, B, H, S, D = k.shape
         self.struct = L.SpecKV(k.data_ptr(), v.data_ptr(), Lr, B, H, S, D,
-                               k.stride(0), k.stride(1), k.stride(2))
+                               k.stride(0), k.stride(1), k.stride(2), None, 0, 0, 0)
+
+
+class PagedKVCache:
+    """K and V block pools [layers, num_blocks, n_kv, block_size, head_dim]
+    (contiguous) and a block table [B, max_blocks] int32: logical slot s of
+    sequence b lives in block block_table[b, s // block_size] at offset
+    s % block_size."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, block_table: torch.Tensor):
+        assert k.shape == v.shape and k.dim() == 5 and k.is_contiguous() and v.is_contiguous()
+        assert block_table.dtype == torch.int32 and block_table.is_contiguous() and block_table.dim() == 2
+        self.k, self.v, self.block_table = k, v, block_table
+        Lr, NB, H, BS, D = k.shape
+        B, MB = block_table.shape
+        self.struct = L.SpecKV(k.data_ptr(), v.data_ptr(), Lr, B, H, MB * BS, D,
+                               k.stride(0), k.stride(1), k.stride(2), block_table.data_ptr(), BS, MB, NB)
 
 
 class Tree:
