@@ -19,10 +19,12 @@ Modules
   verify    greedy and stochastic acceptance, Philox4x32-10
   sampling  flat (variable-length chain) batches: metadata bookkeeping,
             per-request temperature / top-k / top-p rejection sampling
+  target    the target's verification forward over the tree (logits and
+            aux states)
   compact   KV compaction of the accepted path
 
 Parity status of each function is stated in its docstring; every function is
 pinned by a CPU test except where a docstring says "parity unpinned".
 """
 
-from . import numerics, draft, tree, verify, compact, sampling  # noqa: F401
+from . import numerics, draft, tree, verify, compact, sampling, target  # noqa: F401

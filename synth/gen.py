@@ -299,3 +299,39 @@ def flat_batch(seed: int, B: int, max_spec_len: int, V: int, *, plant=(6.0, 14.0
     return {"num_draft_tokens": nd, "cu_num_scheduled_tokens": cu_sched, "logits": logits,
             "draft_token_ids": np.array(drafts, np.int32), "temperature": temp, "top_k": top_k,
             "top_p": top_p, "uniform": u, "seed": philox_seed(seed)}
+
+
+def make_target_weights(cfg: dict, seed: int, layers: int) -> dict:
+    """Synthetic weights of an L-layer Llama-style target with the draft's
+    shapes: embed, lm_head [V, H]; per layer wqkv [(nq+2nkv)hd, H], wo, the
+    SwiGLU pair and down; matrices N(0, 0.02), norm gains 1."""
+    dt, H, I = cfg["dtype"], cfg["hidden"], cfg["intermediate"]
+    V, nqd = cfg["vocab"], cfg["n_q_heads"] * cfg["head_dim"]
+    w = {"embed": _normal(seed, "t/embed", (V, H), WEIGHT_STD, dt, parallel=True),
+         "lm_head": _normal(seed, "t/lm_head", (V, H), WEIGHT_STD, dt, parallel=True),
+         "final_norm": np.ones(H, dtype=np.float32), "layers": []}
+    for l in range(layers):
+        w["layers"].append({
+            "attn_norm": np.ones(H, dtype=np.float32),
+            "wqkv": _normal(seed, f"t/{l}/wqkv", (qkv_rows(cfg), H), WEIGHT_STD, dt, parallel=True),
+            "wo": _normal(seed, f"t/{l}/wo", (H, nqd), WEIGHT_STD, dt, parallel=True),
+            "mlp_norm": np.ones(H, dtype=np.float32),
+            "w_gate_up": _normal(seed, f"t/{l}/w_gate_up", (2 * I, H), WEIGHT_STD, dt, parallel=True),
+            "w_down": _normal(seed, f"t/{l}/w_down", (H, I), WEIGHT_STD, dt, parallel=True),
+        })
+    return w
+
+
+def chain_tree(B: int, K: int, V: int, ctx_len, seed: int) -> dict:
+    """A chain of K random draft tokens per sequence in the tree layout
+    (node n at depth n, parent n - 1, position ctx + n, ancestors 0..n)."""
+    rng = _rng(seed, "chain_tree")
+    n1 = K + 1
+    ctx = np.asarray(ctx_len, dtype=np.int64)
+    tokens = rng.integers(0, V, size=(B, n1)).astype(np.int32)
+    parent = np.tile(np.arange(-1, K, dtype=np.int32), (B, 1))
+    depth = np.tile(np.arange(n1, dtype=np.int32), (B, 1))
+    position = (ctx[:, None] + np.arange(n1)[None, :]).astype(np.int32)
+    anc = np.array([(1 << (n + 1)) - 1 for n in range(n1)], dtype=np.uint64)
+    return {"tokens": tokens, "parent": parent, "depth": depth, "position": position,
+            "num_nodes": np.full(B, K, np.int32), "anc_mask": np.tile(anc, (B, 1))}
