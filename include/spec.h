@@ -11,6 +11,8 @@
  * Stage-level entry points expose single steps of the same path:
  *   spec_draft_step, spec_topk_logprobs, spec_retrieve_candidates,
  *   spec_tree_from_topk.
+ * Target side: spec_target_forward (tree-masked target layers, logits and
+ * aux states of every tree node).
  * Flat batches of variable-length draft chains with per-request sampling
  * parameters: spec_decode_metadata (index bookkeeping) and
  * spec_rejection_sample (greedy / random acceptance with temperature, top-k
@@ -307,6 +309,46 @@ spec_status spec_rejection_sample(spec_ctx* ctx, int32_t B, int32_t max_spec_len
                                   const int32_t* top_k, const float* top_p, const float* uniform,
                                   uint64_t seed, int32_t* out_tokens, int32_t* num_accepted,
                                   void* stream);
+
+/* Weights of one decoder layer of a Llama-style target (device pointers,
+ * storage type). */
+typedef struct spec_target_layer {
+  const void* attn_norm;   /* [H]  RMSNorm gain before attention */
+  const void* wqkv;        /* [(nq+2nkv)*hd, H] */
+  const void* wo;          /* [H, nq*hd] */
+  const void* mlp_norm;    /* [H]  RMSNorm gain before the MLP */
+  const void* w_gate_up;   /* [2I, H] gate rows first */
+  const void* w_down;      /* [H, I] */
+} spec_target_layer;
+
+typedef struct spec_target_weights {
+  const void* embed;                /* [V, H] */
+  const void* final_norm;           /* [H] */
+  const void* lm_head;              /* [V, H] */
+  int32_t num_layers;               /* L >= 7 */
+  const spec_target_layer* layers;  /* host array of L layers */
+} spec_target_weights;
+
+/* The target's verification forward over the draft trees (vLLM Neuron page:
+ * "What is Speculative Decoding?" - one target pass over the original token
+ * and every draft; "Auxiliary Hidden State Extraction" - the hidden states
+ * entering layers (2, L/2, L-3) are captured for the draft; "KV Cache
+ * Sharing").  Every node n of sequence b is one row at its tree position; it
+ * writes its K/V at slot ctx_len[b] + n of every target_kv layer and attends
+ * to the context slots [0, ctx_len[b]) and to the slots of its ancestors and
+ * itself (anc_mask); nodes past num_nodes see the context only and write no
+ * K/V.  Each layer: RMSNorm, QKV of the H-wide state, RoPE, GQA attention,
+ * O projection + residual, RMSNorm, SwiGLU MLP + residual; then the final
+ * norm and the LM head.
+ * The context's config gives the target's shapes (vocab = draft_vocab = V,
+ * sliding_window 0) and the tree (total_tokens N, depth); it must be created
+ * with max_new >= N + 1 (rows per sequence of the forward).
+ * Outputs: logits [B, N+1, V] float32 (the verify step's target logits) and
+ * aux_hidden [B, N+1, 3H] in the storage type (low | mid | high). */
+spec_status spec_target_forward(spec_ctx* ctx, const spec_target_weights* w,
+                                const spec_kv* target_kv, int32_t B, const spec_tree* tree,
+                                const int32_t* ctx_len, float* logits, void* aux_hidden,
+                                void* stream);
 
 /* KV compaction of the accepted path, every layer of `kv`: for each
  * sequence b and j < accepted_len[b], the row at slot tree_base[b] +

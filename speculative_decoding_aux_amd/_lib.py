@@ -45,9 +45,19 @@ class SpecTree(ctypes.Structure):
                                     "num_nodes", "score", "anc_mask")]
 
 
+class SpecTargetLayer(ctypes.Structure):
+    _fields_ = [(n, c_vp) for n in ("attn_norm", "wqkv", "wo", "mlp_norm", "w_gate_up", "w_down")]
+
+
+class SpecTargetWeights(ctypes.Structure):
+    _fields_ = [("embed", c_vp), ("final_norm", c_vp), ("lm_head", c_vp), ("num_layers", c_i32),
+                ("layers", ctypes.POINTER(SpecTargetLayer))]
+
+
 EXPORTS = ["spec_create", "spec_destroy", "spec_last_error", "spec_workspace_bytes", "spec_version",
            "spec_draft_step", "spec_topk_logprobs", "spec_retrieve_candidates", "spec_tree_from_topk", "spec_build_tree",
            "spec_verify_tree", "spec_compact_kv", "spec_decode_metadata", "spec_rejection_sample",
+           "spec_target_forward",
            "spec_profile_enable", "spec_profile_read"]
 SPEC_PROF_LM_HEAD, SPEC_PROF_ATTENTION, SPEC_PROF_VERIFY, SPEC_PROF_TOPK = 0, 1, 2, 3
 
@@ -97,6 +107,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_rejection_sample.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp,
                                           c_vp, c_vp, c_vp, c_vp, ctypes.c_uint64, c_vp, c_vp, c_vp]
     lib.spec_rejection_sample.restype = c_i32
+    lib.spec_target_forward.argtypes = [c_vp, P(SpecTargetWeights), P(SpecKV), c_i32, P(SpecTree), c_vp,
+                                        c_vp, c_vp, c_vp]
+    lib.spec_target_forward.restype = c_i32
     lib.spec_profile_enable.argtypes = [c_vp, c_i32]
     lib.spec_profile_enable.restype = c_i32
     lib.spec_profile_read.argtypes = [c_vp, c_i32, P(c_i32), P(ctypes.c_double)]

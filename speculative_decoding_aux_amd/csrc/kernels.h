@@ -191,6 +191,17 @@ hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const in
                   const float* accept_u, uint64_t seed, int* out_tokens, int* accepted_len,
                   int* accepted_nodes, void* ws, const VerifyPlan& p, hipStream_t s);
 
+// ------------------------------------------------------------ target forward
+// Rows of the target's verification forward: token, position, KV slot and
+// the A-wide list of visible tree slots of every node (target.hip).
+hipError_t target_rows(int B, int N1, int A, const int* tokens, const int* position,
+                       const int* num_nodes, const unsigned long long* anc_mask,
+                       const int* ctx_len, int V, int S, int* tok, int* pos, int* slot, int* anc,
+                       hipStream_t s);
+// h[m] = embed[tok[m]] (row_bytes a multiple of 16).
+hipError_t gather_rows(const void* embed, const int* tok, int M, int row_bytes, void* h,
+                       hipStream_t s);
+
 // ------------------------------------------------------------ flat-batch sampling
 struct SamplePlan {
   int gch, gchunk;   // Gumbel pass: vocab chunks per request's stop row

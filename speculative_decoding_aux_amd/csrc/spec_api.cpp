@@ -126,7 +126,7 @@ struct GemmShape {
 size_t max_partials(const spec_config& c, bool bf16, int m_max, int m_root) {
   const int H = c.hidden, I = c.intermediate, nqd = c.n_q_heads * c.head_dim;
   const int qkvN = (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
-  GemmShape shapes[] = {{H, 3 * H}, {qkvN, 2 * H}, {H, nqd}, {2 * I, H}, {H, I},
+  GemmShape shapes[] = {{H, 3 * H}, {qkvN, 2 * H}, {qkvN, H}, {H, nqd}, {2 * I, H}, {H, I},
                         {c.cand_rank ? c.cand_rank : 1, H}, {c.cand_rank ? c.vocab : c.draft_vocab, H}};
   size_t best = 0;
   for (int M = 1; M <= std::max(m_max, m_root); ++M) {
@@ -839,6 +839,122 @@ spec_status spec_rejection_sample(spec_ctx* ctx, int32_t B, int32_t max_spec_len
                                  bonus_logits_indices, temperature, top_k, top_p, uniform, seed,
                                  out_tokens, num_accepted, ctx->ws.verify_part, sp,
                                  STREAM(stream)));
+  return SPEC_OK;
+}
+
+spec_status spec_target_forward(spec_ctx* ctx, const spec_target_weights* tw,
+                                const spec_kv* kv, int32_t B, const spec_tree* tree,
+                                const int32_t* ctx_len, float* logits, void* aux_hidden,
+                                void* stream) {
+  if (!ctx) return SPEC_EINVAL;
+  const spec_config& c = ctx->cfg;
+  const bool bf = ctx->bf16;
+  const int N1 = c.total_tokens + 1, L = tw ? tw->num_layers : 0;
+  SPEC_REQ(ctx, tw && tw->embed && tw->final_norm && tw->lm_head && tw->layers, SPEC_EINVAL,
+           "null target weights");
+  SPEC_REQ(ctx, L >= 7, SPEC_EUNSUPPORTED, "the aux layers (2, L/2, L-3) need L >= 7 (L=%d)", L);
+  for (int l = 0; l < L; ++l) {
+    const spec_target_layer& y = tw->layers[l];
+    const void* req[] = {y.attn_norm, y.wqkv, y.wo, y.mlp_norm, y.w_gate_up, y.w_down};
+    for (const void* p : req)
+      SPEC_REQ(ctx, p && aligned16(p), SPEC_EINVAL, "target layer %d: null or unaligned weight", l);
+  }
+  SPEC_REQ(ctx, B > 0 && B <= c.max_batch, SPEC_EINVAL, "bad B");
+  SPEC_REQ(ctx, c.max_new >= N1 && c.sliding_window == 0 && c.draft_vocab == c.vocab &&
+                    !c.cand_rank,
+           SPEC_EUNSUPPORTED,
+           "target forward needs max_new >= total_tokens + 1, no window, a full LM head");
+  SPEC_REQ(ctx, logits && aux_hidden && ctx_len, SPEC_EINVAL, "null argument");
+  spec_status st = check_tree(ctx, tree, false);
+  if (st) return st;
+  st = check_kv(ctx, kv, B, L);
+  if (st) return st;
+  SPEC_REQ(ctx, (int64_t)ctx->att_nch * ctx->att_chunk >= kv->slots, SPEC_EUNSUPPORTED,
+           "target KV slots (%d) beyond the attention plan: create the context with kv_capacity "
+           ">= the slots", kv->slots);
+  hipStream_t s = STREAM(stream);
+  Workspace& ws = ctx->ws;
+  const int M = B * N1, A = c.depth + 1;
+  const int H = c.hidden, I = c.intermediate, nq = c.n_q_heads, nkv = c.n_kv_heads,
+            hd = c.head_dim, nqd = nq * hd, V = c.vocab;
+  const int qkvN = (nq + 2 * nkv) * hd;
+  const size_t esz = ctx->esz;
+  float* P = ws.P;
+  SPEC_HIP(ctx, target_rows(B, N1, A, tree->tokens, tree->position, tree->num_nodes,
+                            (const unsigned long long*)tree->anc_mask, ctx_len, V, kv->slots,
+                            ws.row_tok, ws.row_pos, ws.row_slot, ws.row_anc, s));
+  void* h = ws.hout[0];
+  void* h_next = ws.hout[1];
+  SPEC_HIP(ctx, gather_rows(tw->embed, ws.row_tok, M, H * (int)esz, h, s));
+  const int aux_ids[3] = {2, L / 2, L - 3};
+  for (int l = 0; l < L; ++l) {
+    const spec_target_layer& y = tw->layers[l];
+    for (int a = 0; a < 3; ++a)  // the state entering an aux layer
+      if (aux_ids[a] == l)
+        SPEC_HIP(ctx, hipMemcpy2DAsync((char*)aux_hidden + (size_t)a * H * esz, 3 * H * esz, h,
+                                       H * esz, H * esz, M, hipMemcpyDeviceToDevice, s));
+    SPEC_HIP(ctx, rmsnorm(bf, h, y.attn_norm, c.rms_eps, M, H, ws.nrm, s));
+    KvView kvv{(char*)kv->k + (size_t)l * kv->stride_layer * esz,
+               (char*)kv->v + (size_t)l * kv->stride_layer * esz, kv->stride_seq, kv->stride_head,
+               kv->slots, kv_pages(kv)};
+    {
+      const GemmPlan p = gemm_plan(M, qkvN, H, bf);
+      SPEC_HIP(ctx, gemm(bf, ws.nrm, H, y.wqkv, H, P, M, qkvN, H, p, s));
+      SPEC_HIP(ctx, qkv_epilogue(bf, P, p.nsplit, M, nq, nkv, hd, ws.row_pos, ws.row_slot, N1,
+                                 c.rope_base, ws.q, kvv, s));
+    }
+    {
+      AttnArgs a;
+      a.q = ws.q;
+      a.kv = kvv;
+      a.ctx_len = ctx_len;
+      a.pos = ws.row_pos;
+      a.anc = ws.row_anc;
+      a.A = A;
+      a.B = B;
+      a.R = N1;
+      a.nq = nq;
+      a.nkv = nkv;
+      a.hd = hd;
+      a.window = 0;
+      a.out = ws.o;
+      a.part = ws.attn_part;
+      a.nchunks = ctx->att_nch;
+      a.chunk = ctx->att_chunk;
+      ProfScope ps(ctx, SPEC_PROF_ATTENTION, s);
+      SPEC_HIP(ctx, attention(bf, a, s));
+    }
+    {
+      const GemmPlan p = gemm_plan(M, H, nqd, bf, kResidNormSplit);
+      SPEC_HIP(ctx, gemm(bf, ws.o, nqd, y.wo, nqd, P, M, H, nqd, p, s));
+      if (resid_norm_ok(bf, M, H, p.nsplit, P, h, ws.h1, y.mlp_norm, ws.mn)) {
+        SPEC_HIP(ctx, resid_norm(bf, P, p.nsplit, M, H, h, ws.h1, y.mlp_norm, c.rms_eps, ws.mn, s));
+      } else {
+        SPEC_HIP(ctx, gemm_epilogue(bf, EPI_RESID, ws.h1, h, P, p.nsplit, M, H, s));
+        SPEC_HIP(ctx, rmsnorm(bf, ws.h1, y.mlp_norm, c.rms_eps, M, H, ws.mn, s));
+      }
+    }
+    {
+      const GemmPlan p = gemm_plan(M, 2 * I, H, bf);
+      SPEC_HIP(ctx, gemm(bf, ws.mn, H, y.w_gate_up, H, P, M, 2 * I, H, p, s));
+      SPEC_HIP(ctx, gemm_epilogue(bf, EPI_SWIGLU, ws.s, nullptr, P, p.nsplit, M, I, s));
+    }
+    {
+      const GemmPlan p = gemm_plan(M, H, I, bf);
+      SPEC_HIP(ctx, gemm(bf, ws.s, I, y.w_down, I, P, M, H, I, p, s));
+      SPEC_HIP(ctx, gemm_epilogue(bf, EPI_RESID, h_next, ws.h1, P, p.nsplit, M, H, s));
+    }
+    std::swap(h, h_next);
+  }
+  SPEC_HIP(ctx, rmsnorm(bf, h, tw->final_norm, c.rms_eps, M, H, ws.nrm, s));
+  const GemmPlan p = gemm_plan(M, V, H, bf);
+  ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
+  if (p.nsplit == 1) {
+    SPEC_HIP(ctx, gemm(bf, ws.nrm, H, tw->lm_head, H, logits, M, V, H, p, s, 1));
+  } else {
+    SPEC_HIP(ctx, gemm(bf, ws.nrm, H, tw->lm_head, H, P, M, V, H, p, s, 1));
+    SPEC_HIP(ctx, gemm_epilogue(bf, EPI_F32, logits, nullptr, P, p.nsplit, M, V, s));
+  }
   return SPEC_OK;
 }
 

@@ -282,3 +282,35 @@ def spec_rejection_sample(ctx: SpecContext, cu_num_draft_tokens, draft_token_ids
                                        _p(out[0]), _p(out[1]), _stream())
     ctx._check(st)
     return out
+
+
+class TargetWeights:
+    """Weights of a Llama-style target on the GPU: embed, final_norm, lm_head
+    and a list of per-layer dicts (attn_norm, wqkv, wo, mlp_norm, w_gate_up,
+    w_down) of device tensors."""
+
+    LAYER = ("attn_norm", "wqkv", "wo", "mlp_norm", "w_gate_up", "w_down")
+
+    def __init__(self, tensors: dict):
+        self.t = tensors
+        L_ = len(tensors["layers"])
+        self._layers = (L.SpecTargetLayer * L_)()
+        for i, lw in enumerate(tensors["layers"]):
+            for n in self.LAYER:
+                setattr(self._layers[i], n, lw[n].data_ptr())
+        self.struct = L.SpecTargetWeights(tensors["embed"].data_ptr(), tensors["final_norm"].data_ptr(),
+                                          tensors["lm_head"].data_ptr(), L_, self._layers)
+
+
+def spec_target_forward(ctx: SpecContext, tw: TargetWeights, kv, tree: Tree, ctx_len):
+    """The target's forward over the trees: (logits [B, N+1, V] float32,
+    aux_hidden [B, N+1, 3H])."""
+    cfg, dev = ctx.cfg, ctx.device
+    B, n1 = tree.tokens.shape
+    ctx_len = _i32(ctx_len, dev)
+    logits = torch.empty(B, n1, cfg["vocab"], dtype=torch.float32, device=dev)
+    aux = torch.empty(B, n1, 3 * cfg["hidden"], dtype=ctx.tdtype, device=dev)
+    st = ctx.lib.spec_target_forward(ctx.h, ctypes.byref(tw.struct), ctypes.byref(kv.struct), B,
+                                     ctypes.byref(tree.struct), _p(ctx_len), _p(logits), _p(aux), _stream())
+    ctx._check(st)
+    return logits, aux

@@ -7,7 +7,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .spec import KVCache, Weights
+from .spec import KVCache, TargetWeights, Weights
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -43,3 +43,10 @@ def from_device(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.float().cpu().numpy()
     return t.cpu().numpy()
+
+
+def upload_target_weights(cfg: dict, W: dict, device="cuda") -> TargetWeights:
+    t = {n: to_device(W[n], cfg["dtype"], device) for n in ("embed", "final_norm", "lm_head")}
+    t["layers"] = [{n: to_device(lw[n], cfg["dtype"], device) for n in TargetWeights.LAYER}
+                   for lw in W["layers"]]
+    return TargetWeights(t)

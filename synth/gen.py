@@ -335,3 +335,21 @@ def chain_tree(B: int, K: int, V: int, ctx_len, seed: int) -> dict:
     anc = np.array([(1 << (n + 1)) - 1 for n in range(n1)], dtype=np.uint64)
     return {"tokens": tokens, "parent": parent, "depth": depth, "position": position,
             "num_nodes": np.full(B, K, np.int32), "anc_mask": np.tile(anc, (B, 1))}
+
+
+def with_positions(tree: dict, ctx_len) -> dict:
+    """Fill a tree's position (ctx + depth) and ancestor mask (bit j set for
+    every node j on the path from the root to the node, itself included)."""
+    B, n1 = tree["tokens"].shape
+    ctx = np.asarray(ctx_len, dtype=np.int64)
+    pos = np.full((B, n1), -1, np.int32)
+    anc = np.zeros((B, n1), np.uint64)
+    for b in range(B):
+        for n in range(int(tree["num_nodes"][b]) + 1):
+            pos[b, n] = ctx[b] + tree["depth"][b, n]
+            m, j = 0, n
+            while j >= 0:
+                m |= 1 << j
+                j = int(tree["parent"][b, j])
+            anc[b, n] = np.uint64(m)
+    return dict(tree, position=pos, anc_mask=anc)
