@@ -46,6 +46,9 @@ def parse():
                     help="instead of the step, time rejection sampling of a flat batch of B "
                          "variable-length chains with per-request temperature/top-k/top-p "
                          "(the workload's vocabulary and draft length)")
+    ap.add_argument("--target-forward", type=int, default=0, metavar="L",
+                    help="instead of the step, time the target's verification forward over the "
+                         "workload's trees with L synthetic layers of the workload's shapes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
@@ -199,6 +202,9 @@ def main():
 
     if args.flat_sampling:
         bench_flat_sampling(args)
+        return
+    if args.target_forward:
+        bench_target_forward(args)
         return
 
     from speculative_decoding_aux_amd import spec as S
@@ -461,6 +467,88 @@ def bench_flat_sampling(args):
         med = float(np.median(wall))
         res["cpu_baseline"] = {"value": round(1.0 / med, 3), "unit": "calls/s", "cores": 1, "kind": "oracle",
                                "sample": f"{len(wall)} whole calls of the same batch; median {med:.3f} s"}
+    print(json.dumps(res), flush=True)
+
+
+def bench_target_forward(args):
+    """spec_target_forward over the workload's tree shape (chain trees of K
+    drafts for chain workloads, random trees otherwise) with L synthetic
+    target layers of the workload's dimensions.  Algorithmic bytes per
+    forward: every layer's weights and the final LM head once, the context
+    K/V of every layer once per sequence, the logits written once."""
+    import torch
+
+    from speculative_decoding_aux_amd import spec as S
+    from speculative_decoding_aux_amd import _lib as L
+    from speculative_decoding_aux_amd.tensors import to_device, upload_target_weights
+    from synth import configs, gen
+
+    cfg = configs.get(args.config)
+    Lr, B, N, dt = args.target_forward, cfg["batch"], cfg["total_tokens"], cfg["dtype"]
+    n1 = N + 1
+    seed = configs.SEEDS[args.config] + 600
+    H, I, V = cfg["hidden"], cfg["intermediate"], cfg["vocab"]
+    nkv, hd = cfg["n_kv_heads"], cfg["head_dim"]
+    print(f"[bench] generating a {Lr}-layer target for {args.config}", file=sys.stderr, flush=True)
+    W = gen.make_target_weights(cfg, seed, Lr)
+    ctx_len = np.full(B, cfg["ctx"], np.int64)
+    slots = cfg["kv_capacity"]
+    if cfg["top_k"] == 1:
+        tree = gen.chain_tree(B, N, V, ctx_len, seed)
+    else:
+        tree = gen.with_positions(gen.random_tree(cfg, seed, batch=B), ctx_len)
+    dev = "cuda"
+    tw = upload_target_weights(cfg, W)
+    del W
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(seed)
+    shape = (Lr, B, nkv, slots, hd)
+    kv = S.KVCache(torch.randn(shape, generator=g, device=dev).to(tdt),
+                   torch.randn(shape, generator=g, device=dev).to(tdt))
+    ctx = S.SpecContext(cfg, max_batch=B, max_new=n1)
+    tr = S.Tree(B, n1, dev)
+    for f in ("tokens", "parent", "depth", "position", "num_nodes"):
+        getattr(tr, f).copy_(torch.from_numpy(np.ascontiguousarray(tree[f], dtype=np.int32)))
+    tr.anc_mask.copy_(torch.from_numpy(np.ascontiguousarray(tree["anc_mask"]).view(np.int64)))
+    cl = torch.from_numpy(ctx_len.astype(np.int32)).to(dev)
+    for _ in range(args.warmup):
+        S.spec_target_forward(ctx, tw, kv, tr, cl)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} target forwards ({Lr} layers, {B * n1} rows)", file=sys.stderr,
+          flush=True)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ctx.profile(True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        S.spec_target_forward(ctx, tw, kv, tr, cl)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    nl, msl = ctx.profile_read(L.SPEC_PROF_LM_HEAD)
+    na, msa = ctx.profile_read(L.SPEC_PROF_ATTENTION)
+    ctx.profile(False)
+    ms = e0.elapsed_time(e1) / args.steps
+    es = 2 if dt == "bf16" else 4
+    qkvN = (cfg["n_q_heads"] + 2 * nkv) * hd
+    layer_w = (qkvN * H + H * cfg["n_q_heads"] * hd + 2 * I * H + H * I) * es
+    kv_bytes = Lr * B * nkv * cfg["ctx"] * hd * es * 2
+    byts = Lr * layer_w + V * H * es + kv_bytes + B * n1 * V * 4
+    achieved = byts / (ms * 1e-3) / 1e9
+    M = B * n1
+    flops = 2.0 * M * (Lr * (qkvN * H + H * cfg["n_q_heads"] * hd + 2 * I * H + H * I) + V * H)
+    res = {"metric": "target verification forwards/sec at 1 GPU", "value": round(1000.0 / ms, 2),
+           "unit": "forwards/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": dt, "data": "synthetic",
+           "config": {"workload": f"target_forward_{args.config}", "layers": Lr, "batch": B, "tree_rows": M,
+                      "ctx": cfg["ctx"]},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                        "kernel": "whole forward (weights, context K/V, logits)",
+                        "algorithmic_bytes_per_launch": int(byts),
+                        "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+           "kernels": {"lm_head": {"avg_launch_us": round(msl / max(nl, 1) * 1e3, 2), "launches": nl},
+                       "attention": {"avg_launch_us": round(msa / max(na, 1) * 1e3, 2), "launches": na}}}
     print(json.dumps(res), flush=True)
 
 
