@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--target-forward", type=int, default=0, metavar="L",
                     help="instead of the step, time the target's verification forward over the "
                          "workload's trees with L synthetic layers of the workload's shapes")
+    ap.add_argument("--paged", type=int, default=0, metavar="BS",
+                    help="keep the draft KV cache in a paged pool of BS-slot blocks (shuffled)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
@@ -221,6 +223,8 @@ def main():
     dev = "cuda"
     w = upload_weights(cfg, W)
     draft_kv = upload_kv(cfg, inp["k_cache"], inp["v_cache"])
+    if args.paged:
+        draft_kv = paged_copy(draft_kv, args.paged, seed)
     aux = to_device(inp["aux"], cfg["dtype"])
     in_tok = torch.from_numpy(inp["in_tokens"]).to(dev)
     ctx_len = torch.from_numpy(inp["ctx_len"]).to(dev)
@@ -325,7 +329,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "batch": B, "ctx": cfg["ctx"], "top_k": cfg["top_k"],
                    "depth": cfg["depth"], "total_tokens": cfg["total_tokens"], "verify": cfg["verify"],
-                   "graph": bool(graph is not None), "wall_s": round(wall, 3)},
+                   "graph": bool(graph is not None), "paged_block": args.paged or None,
+                   "wall_s": round(wall, 3)},
         "roofline": roof,
     }
     # acceptance of the last timed step on the synthetic target logits: mean
@@ -356,6 +361,29 @@ def main():
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, W, inp, seed, args.cpu_steps)
     print(json.dumps(res), flush=True)
+
+
+def paged_copy(kv, bs, seed):
+    """The same caches as a pool of bs-slot blocks in a shuffled order (plus
+    spare blocks) with a block table: [layers, blocks, n_kv, bs, hd]."""
+    import torch
+
+    from speculative_decoding_aux_amd import spec as S
+
+    Lr, B, nkv, Sl, hd = kv.k.shape
+    mb = -(-Sl // bs)
+    nb = B * mb + 8
+    g = torch.Generator().manual_seed(seed)
+    table = torch.randperm(nb, generator=g)[: B * mb].reshape(B, mb).to(torch.int32)
+    pools = []
+    for a in (kv.k, kv.v):
+        pad = torch.zeros(Lr, B, nkv, mb * bs, hd, dtype=a.dtype, device=a.device)
+        pad[:, :, :, :Sl] = a
+        pool = torch.zeros(Lr, nb, nkv, bs, hd, dtype=a.dtype, device=a.device)
+        blocks = pad.reshape(Lr, B, nkv, mb, bs, hd).permute(0, 1, 3, 2, 4, 5).reshape(Lr, B * mb, nkv, bs, hd)
+        pool[:, table.reshape(-1).long().to(a.device)] = blocks
+        pools.append(pool.contiguous())
+    return S.PagedKVCache(pools[0], pools[1], table.to(kv.k.device).contiguous())
 
 
 def candidate_recall(cfg, ctx4, w, draft_kv, aux, inp):
