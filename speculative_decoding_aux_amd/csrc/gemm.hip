@@ -625,7 +625,7 @@ GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split) {
   const int cw = gemm_cw(M, N);
   const int strips = (N + 64 * cw - 1) / (64 * cw);
   const int mblocks = (M + 63) / 64;
-  const int target = cw == 1 ? 1024 : 2048;  // workgroups in flight
+  const int target = (cw == 1 || M > 16) ? 1024 : 2048;  // workgroups in flight
   int ns = (target + strips * mblocks - 1) / (strips * mblocks);
   const int kblocks = (K + 127) / 128;
   ns = std::max(1, std::min(std::min(ns, kblocks), std::min(kMaxSplit, std::max(1, max_split))));
