@@ -6,7 +6,7 @@ Llama-3.1-8B-shaped EAGLE-3 chain (batch 4, context 256, 5 draft tokens,
 greedy), on synthetic seeded inputs.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
-                    [--graph] [--no-cpu-baseline]
+                    [--graph] [--no-cpu-baseline] [--n-new N] [--paged BS]
 """
 
 from __future__ import annotations
@@ -51,6 +51,9 @@ def parse():
                          "workload's trees with L synthetic layers of the workload's shapes")
     ap.add_argument("--paged", type=int, default=0, metavar="BS",
                     help="keep the draft KV cache in a paged pool of BS-slot blocks (shuffled)")
+    ap.add_argument("--n-new", type=int, default=0, metavar="N",
+                    help="new aux rows per sequence on the root pass (default: the workload's, 1); "
+                         "a sensitivity run, e.g. depth + 1 after a fully accepted chain")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
@@ -214,7 +217,7 @@ def main():
     from speculative_decoding_aux_amd.tensors import to_device, upload_kv, upload_weights
     from synth import configs, gen
 
-    cfg = configs.get(args.config)
+    cfg = configs.get(args.config, **({"n_new": args.n_new} if args.n_new else {}))
     seed = configs.SEEDS[args.config]
     B = cfg["batch"]
     print(f"[bench] generating inputs for {args.config}", file=sys.stderr, flush=True)
@@ -306,7 +309,7 @@ def main():
         avg_ms = ms / max(n, 1)
         achieved = byts / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if args.n_new else measured_traffic(args.config),
                 "kernel": "LM head (gemm_lmhead_topk_kernel / gemm_bf16_stream<*,1,*>)" if cfg["dtype"] == "bf16" else "gemm_f32_rows",
                 "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n, "timed_every_nth_step": PROF_EVERY,
                 "algorithmic_bytes_per_launch": int(byts)}
@@ -329,7 +332,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "batch": B, "ctx": cfg["ctx"], "top_k": cfg["top_k"],
                    "depth": cfg["depth"], "total_tokens": cfg["total_tokens"], "verify": cfg["verify"],
-                   "graph": bool(graph is not None), "paged_block": args.paged or None,
+                   "n_new": cfg["n_new"], "graph": bool(graph is not None), "paged_block": args.paged or None,
                    "wall_s": round(wall, 3)},
         "roofline": roof,
     }
