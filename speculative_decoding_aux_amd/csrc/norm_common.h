@@ -66,6 +66,22 @@ SPEC_DEV void scale_store(const u32x4_t (&v)[kVecPerThread], double sc, const T*
   }
 }
 
+// The same with the weight vectors already in registers (loaded by load_row).
+template <typename T>
+SPEC_DEV void scale_store(const u32x4_t (&v)[kVecPerThread], double sc, const u32x4_t (&wv)[kVecPerThread],
+                          T* y, int nvec) {
+#pragma unroll
+  for (int j = 0; j < kVecPerThread; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    if (i >= nvec) continue;
+    u32x4_t o = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < V16<T>::N; ++e)
+      V16<T>::set(o, e, (float)((double)V16<T>::get(v[j], e) * sc * (double)V16<T>::get(wv[j], e)));
+    ((u32x4_t*)y)[i] = o;
+  }
+}
+
 // Prologue of row r by a 256-thread block (every thread calls it: it meets at
 // a barrier).
 template <typename T>

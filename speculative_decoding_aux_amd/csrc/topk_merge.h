@@ -8,15 +8,17 @@ namespace spec {
 namespace topkdev {
 
 // Merge of per-chunk records (top-KM lists with ids, and (sum exp, max)) of
-// row r by a 256-thread block, four records per thread per round: ids
-// (through id_map, unless rowmap ids are already output ids) and log-probs of
-// the row's k best.  Every thread of the block must call it (it meets at a
-// barrier); on return the row's outputs are written by wave 0.
+// row r by a 256-thread block: ids (through id_map, unless rowmap ids are
+// already output ids) and log-probs of the row's k best.  Every thread of the
+// block must call it (it meets at a barrier); on return the row's outputs are
+// written by wave 0, and, given an LDS pair bcast, the best id and its
+// log-prob (float bits) are stored there too (visible after a barrier).
 template <int KM>
 SPEC_DEV void merge_row(int r, int n, int k, int nch, const float* __restrict__ pv,
                         const int* __restrict__ pi, const Part* __restrict__ pp,
                         const int* __restrict__ id_map, const int* __restrict__ rowmap,
-                        int* __restrict__ ids, int ldi, float* __restrict__ logp, int ldl) {
+                        int* __restrict__ ids, int ldi, float* __restrict__ logp, int ldl,
+                        int* bcast = nullptr) {
   __shared__ float sv[4 * KM];
   __shared__ int si[4 * KM];
   __shared__ float smax[4];
@@ -27,30 +29,33 @@ SPEC_DEV void merge_row(int r, int n, int k, int nch, const float* __restrict__ 
   const int* ri = pi + (int64_t)r * total;
   List<KM> L;
   L.init();
-  for (int x0 = t; x0 < total; x0 += 1024) {
-    float v[4];
-    int id[4];
+  float m = -INFINITY;
+  double s = 0.0;
+  // rounds of U list entries and U chunk records per thread, every load of a
+  // round issued before any is used (thread t takes entries t, t + 256, ...)
+  constexpr int U = 8;
+  const int rounds = (max(total, nch) + 256 * U - 1) / (256 * U);
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int x0 = rd * 256 * U + t;
+    float v[U];
+    int id[U];
+    Part q[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int x = x0 + 256 * u;
       const bool ok = x < total && (x % KM) < k;
       v[u] = ok ? rv[x] : -INFINITY;
       id[u] = ok ? ri[x] : kIdNone;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) L.insert(v[u], id[u]);
-  }
-  float m = -INFINITY;
-  double s = 0.0;
-  for (int c0 = t; c0 < nch; c0 += 1024) {
-    Part q[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = c0 + 256 * u;
+    for (int u = 0; u < U; ++u) {
+      const int c = x0 + 256 * u;
       q[u] = c < nch ? pp[(int64_t)r * nch + c] : Part{0.0, -INFINITY, 0};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) L.insert(v[u], id[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const Part p = q[u];
       if (p.m == -INFINITY) continue;
       if (p.m > m) {
@@ -110,6 +115,10 @@ SPEC_DEV void merge_row(int r, int n, int k, int nch, const float* __restrict__ 
     const int out = rowmap ? id : (id_map ? id_map[clampi(id, 0, n - 1)] : id);
     ids[(int64_t)r * ldi + lane] = out;
     logp[(int64_t)r * ldl + lane] = v - lse;
+    if (bcast && lane == 0) {
+      bcast[0] = out;
+      bcast[1] = __float_as_int(v - lse);
+    }
   }
 }
 

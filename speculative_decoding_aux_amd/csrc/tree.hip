@@ -255,6 +255,85 @@ __global__ __launch_bounds__(256) void chain_tail_kernel(
                            pro.eps, pro.H, pro.gout, pro.cout);
 }
 
+// Chain pass d < D (top_k 1), one block per sequence.  In a chain the
+// depth-d candidate is index d - 1 and the only beam node, its slot is
+// ctx + n_new + d - 1, and the slots of its ancestors follow the root rows',
+// so the next row's visible slots are ctx .. ctx + n_new + d - 1: the tree
+// step needs nothing back from the candidate arrays but the previous score.
+// That score, the sequence state, the next row's hidden state and both norm
+// weights are requested before the record merge, so they arrive with the
+// records; the merged token comes through LDS.  Writes exactly what
+// chain_tail_kernel writes for d < D.
+template <typename T>
+__global__ __launch_bounds__(256) void chain_step_kernel(
+    int d, int n_new, const int* __restrict__ ctx_len, int nvocab, int nch,
+    const float* __restrict__ pv, const int* __restrict__ pi, const topkdev::Part* __restrict__ pp,
+    const int* __restrict__ id_map, int* __restrict__ ids, float* __restrict__ logp, TreeState st,
+    int* __restrict__ beam, PassRows nx, ChainPrologue<T> pro) {
+  __shared__ int bc[2];
+  __shared__ double red[2][4];
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int row = d == 1 ? b * n_new + n_new - 1 : b;
+  const int act = st.active[b];
+  const int ctx = ctx_len[b];
+  const int c = d - 1;
+  const int64_t cb = (int64_t)b * st.cmax;
+  const float prev = (d > 1 && t == 0) ? st.score[cb + c - 1] : 0.f;
+  const int src = act ? row : (d == 1 ? b * n_new : b);
+  const int nvec = pro.H / normdev::V16<T>::N;
+  u32x4_t gv[normdev::kVecPerThread], wi[normdev::kVecPerThread], wh[normdev::kVecPerThread];
+  normdev::load_row<T>(pro.hid + (int64_t)src * pro.H, nvec, gv);
+  normdev::load_row<T>(pro.w_in, nvec, wi);
+  normdev::load_row<T>(pro.w_hid, nvec, wh);
+  topkdev::merge_row<1>(row, nvocab, 1, nch, pv, pi, pp, id_map, nullptr, ids, 1, logp, 1, bc);
+  __syncthreads();  // bc holds the row's token and log-prob
+  const int tok = bc[0];
+  const float lp = __int_as_float(bc[1]);
+  const int sl = ctx + n_new + d - 1;
+  if (t == 0) {
+    if (act) {
+      st.tok[cb + c] = tok;
+      st.parent[cb + c] = d == 1 ? -1 : c - 1;
+      st.slot[cb + c] = sl;
+      st.src[cb + c] = row;
+      st.score[cb + c] = d == 1 ? lp : prev + lp;
+      beam[b] = c;
+    }
+    nx.pos[b] = ctx + n_new - 1 + d;
+    nx.tok[b] = act ? tok : 0;
+    nx.slot[b] = act ? sl : -1;
+    nx.src[b] = src;
+  }
+  for (int i = t; i < nx.A; i += 256) nx.anc[(int64_t)b * nx.A + i] = (act && i < n_new + d) ? ctx + i : -1;
+  // prologue of the next pass's row b (prologue_row with the hidden state and
+  // weights already in registers)
+  const int te = clampi(act ? tok : 0, 0, pro.V - 1);
+  u32x4_t ev[normdev::kVecPerThread];
+  normdev::load_row<T>(pro.embed + (int64_t)te * pro.H, nvec, ev);
+  double se = wave_sum(normdev::sumsq<T>(ev)), sg = wave_sum(normdev::sumsq<T>(gv));
+  const int w = t >> 6;
+  if ((t & 63) == 0) {
+    red[0][w] = se;
+    red[1][w] = sg;
+  }
+  __syncthreads();
+  se = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  sg = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const double ce = 1.0 / sqrt(se / pro.H + (double)pro.eps);
+  const double cg = 1.0 / sqrt(sg / pro.H + (double)pro.eps);
+  T* co = pro.cout + (int64_t)b * 2 * pro.H;
+  normdev::scale_store<T>(ev, ce, wi, co, nvec);
+  normdev::scale_store<T>(gv, cg, wh, co + pro.H, nvec);
+  T* go = pro.gout + (int64_t)b * pro.H;
+  if (go != pro.hid + (int64_t)src * pro.H) {
+#pragma unroll
+    for (int j = 0; j < normdev::kVecPerThread; ++j) {
+      const int i = t + 256 * j;
+      if (i < nvec) ((u32x4_t*)go)[i] = gv[j];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t tree_root_setup(int B, int n_new, const int* in_tokens, const int* ctx_len, int k, int D,
@@ -290,12 +369,22 @@ hipError_t chain_tail(bool bf16, int d, int B, int M, int n_new, const int* ctx_
     const ChainPrologue<bf16_t> pro{(const bf16_t*)embed, V, (const bf16_t*)hid,
                                     (const bf16_t*)w_in, (const bf16_t*)w_hid, eps, H,
                                     (bf16_t*)gout, (bf16_t*)cout};
+    if (d < D) {
+      SPEC_LAUNCH(chain_step_kernel<bf16_t>, dim3(B), dim3(256), 0, s, d, n_new, ctx_len, nvocab,
+                  nch, pv, pi, pp, id_map, ids, logp, st, st.beam, next, pro);
+      return hipGetLastError();
+    }
     SPEC_LAUNCH(chain_tail_kernel<bf16_t>, dim3(B), dim3(256), lds, s, d, n_new, ctx_len,
                 in_tokens, D, N, nvocab, nch, pv, pi, pp, id_map, ids, logp, st, st.beam, next,
                 out, pro);
   } else {
     const ChainPrologue<float> pro{(const float*)embed, V, (const float*)hid, (const float*)w_in,
                                    (const float*)w_hid, eps, H, (float*)gout, (float*)cout};
+    if (d < D) {
+      SPEC_LAUNCH(chain_step_kernel<float>, dim3(B), dim3(256), 0, s, d, n_new, ctx_len, nvocab,
+                  nch, pv, pi, pp, id_map, ids, logp, st, st.beam, next, pro);
+      return hipGetLastError();
+    }
     SPEC_LAUNCH(chain_tail_kernel<float>, dim3(B), dim3(256), lds, s, d, n_new, ctx_len,
                 in_tokens, D, N, nvocab, nch, pv, pi, pp, id_map, ids, logp, st, st.beam, next,
                 out, pro);
