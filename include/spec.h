@@ -336,8 +336,9 @@ typedef struct spec_target_weights {
  * Sharing").  Every node n of sequence b is one row at its tree position; it
  * writes its K/V at slot ctx_len[b] + n of every target_kv layer and attends
  * to the context slots [0, ctx_len[b]) and to the slots of its ancestors and
- * itself (anc_mask); nodes past num_nodes see the context only and write no
- * K/V.  Each layer: RMSNorm, QKV of the H-wide state, RoPE, GQA attention,
+ * itself (anc_mask, any of its N+1 bits: the tree may be deeper than the
+ * config's depth, e.g. a chain of N+1 prompt tokens); nodes past num_nodes
+ * see the context only and write no K/V.  Each layer: RMSNorm, QKV of the H-wide state, RoPE, GQA attention,
  * O projection + residual, RMSNorm, SwiGLU MLP + residual; then the final
  * norm and the LM head.
  * The context's config gives the target's shapes (vocab = draft_vocab = V,

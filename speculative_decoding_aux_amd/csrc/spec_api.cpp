@@ -874,7 +874,10 @@ spec_status spec_target_forward(spec_ctx* ctx, const spec_target_weights* tw,
            ">= the slots", kv->slots);
   hipStream_t s = STREAM(stream);
   Workspace& ws = ctx->ws;
-  const int M = B * N1, A = c.depth + 1;
+  // a node's extra keys are its ancestors and itself: at most N1 of them for
+  // any tree (a chain of N1 tokens, a prompt's prefill, is deeper than the
+  // draft's trees); M * N1 fits the row_anc workspace since N1 <= max_new
+  const int M = B * N1, A = N1;
   const int H = c.hidden, I = c.intermediate, nq = c.n_q_heads, nkv = c.n_kv_heads,
             hd = c.head_dim, nqd = nq * hd, V = c.vocab;
   const int qkvN = (nq + 2 * nkv) * hd;

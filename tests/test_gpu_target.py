@@ -4,8 +4,9 @@ seeded weights, caches and trees: logits within 1e-4 (float32) / 2e-2
 (bf16) absolute, aux states and the K/V rows written at the nodes' slots
 within the activation tolerance of the draft tests, greedy verification
 with the GPU's logits equal to verification with the oracle's wherever the
-oracle's argmax gaps exceed the tolerance.  Chains and random trees, float32
-and bf16, 8 layers (aux layers 2, 4, 5)."""
+oracle's argmax gaps exceed the tolerance.  Chains (also deeper than the
+config's draft depth) and random trees, float32 and bf16, 8 layers (aux
+layers 2, 4, 5)."""
 
 import numpy as np
 import pytest
@@ -27,6 +28,9 @@ CASES = {
     "chain_f32": (dict(BASE, dtype="f32", top_k=1, depth=5, total_tokens=5), "chain", 1e-4),
     "chain_bf16": (dict(BASE, dtype="bf16", top_k=1, depth=5, total_tokens=5), "chain", 2e-2),
     "tree_bf16": (dict(BASE, dtype="bf16", top_k=3, depth=3, total_tokens=9), "tree", 2e-2),
+    # a chain of 17 tokens (a prompt's prefill) under a config whose draft
+    # trees are 3 deep: every node sees all the chain before it
+    "deep_chain_f32": (dict(BASE, dtype="f32", top_k=4, depth=3, total_tokens=16), "chain", 1e-4),
     "tree_bf16_hd128": (dict(BASE, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128, top_k=2,
                              depth=4, total_tokens=7), "tree", 2e-2),
 }
