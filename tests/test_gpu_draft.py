@@ -209,6 +209,11 @@ BUILD = {
     "bigvocab_chain_two_new": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
                                                                 top_k=1, depth=3, total_tokens=3,
                                                                 n_new=2)), 2e-2),
+    # the first sequence has an empty context (its rows see only the root
+    # rows and their ancestors)
+    "small_tree_empty_ctx": (configs.get("tiny_chain", **SMALLB), 2e-2),
+    "bigvocab_chain_empty_ctx": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
+                                                                  top_k=1, depth=3, total_tokens=3)), 2e-2),
     # a chain whose second sequence is past the capacity cutoff (root only, no
     # KV writes) while the others draft
     "bigvocab_chain_cutoff": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
@@ -233,6 +238,8 @@ def test_build_tree_matches_oracle(name):
         ctx_len = [cfg["ctx"] - 3 * i for i in range(B)]
         if name.endswith("_cutoff"):
             ctx_len[1] = cfg["kv_capacity"] - 2
+        if name.endswith("_empty_ctx"):
+            ctx_len[0] = 0
         inp = gen.make_step_inputs(cfg, seed, ctx_len=ctx_len)
         kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
         rec = []
