@@ -46,6 +46,12 @@ CASES = {
                                                      total_tokens=3)), 2e-2),
     "bigvocab_trimmed_k8": (configs.get("tiny_chain", **dict(SMALL, vocab=90000, draft_vocab=70000,
                                                              top_k=8, total_tokens=20)), 2e-2),
+    # mid-size draft vocabularies at <= 16 rows: the split-K head, its
+    # reduction and the two-stage top-k (a ragged last chunk at 32040)
+    "midvocab_trimmed_k8": (configs.get("tiny_chain", **dict(SMALL, vocab=40000, draft_vocab=32000,
+                                                             top_k=8, total_tokens=20)), 2e-2),
+    "midvocab_k1_ragged": (configs.get("tiny_chain", **dict(SMALL, vocab=32040, draft_vocab=32040, top_k=1,
+                                                            total_tokens=3)), 2e-2),
     # 72 beam rows: the LDS-tiled GEMM with ragged row and column tiles; K = 480 of the
     # down projection is not a multiple of 64 and takes the streaming kernel
     "tile_rows72_ragged": (configs.get("tiny_chain", **dict(SMALL, batch=9, top_k=8, total_tokens=20,
@@ -214,6 +220,9 @@ BUILD = {
     "small_tree_empty_ctx": (configs.get("tiny_chain", **SMALLB), 2e-2),
     "bigvocab_chain_empty_ctx": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
                                                                   top_k=1, depth=3, total_tokens=3)), 2e-2),
+    # a chain over a mid-size vocabulary (split head, separate top-k and tree step)
+    "midvocab_chain": (configs.get("tiny_chain", **dict(SMALL, vocab=32000, draft_vocab=32000, top_k=1,
+                                                        depth=3, total_tokens=3)), 2e-2),
     # a chain whose second sequence is past the capacity cutoff (root only, no
     # KV writes) while the others draft
     "bigvocab_chain_cutoff": (configs.get("tiny_chain", **dict(SMALL, vocab=70000, draft_vocab=70000,
