@@ -155,6 +155,9 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
   int cur = 0, depth = 0, emit = -1;
   for (int j = lane; j <= D; j += 64) out_tokens[(int64_t)b * (D + 1) + j] = -1;
   for (int j = lane; j < D; j += 64) accepted_nodes[(int64_t)b * D + j] = -1;
+  // node lane + 1's token and parent, read once (nn <= 63: one node per lane)
+  const int xl = lane + 1;
+  const int tkl = xl <= nn ? tk[xl] : -1, prl = xl <= nn ? pr[xl] : -2;
   while (true) {
     const VPart* pb = part + (int64_t)(b * n1 + cur) * nch;
     // merge the chunk records of node cur
@@ -187,12 +190,8 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
     int next = -1;
     if (mode == 0) {
       // child whose token is the argmax (first in node order)
-      for (int x0 = 1; x0 <= nn && next < 0; x0 += 64) {
-        const int x = x0 + lane;
-        const bool hit = x <= nn && pr[x] == cur && tk[x] == arg;
-        const unsigned long long bal = __ballot(hit);
-        if (bal) next = x0 + __ffsll((long long)bal) - 1;
-      }
+      const unsigned long long bal = __ballot(xl <= nn && prl == cur && tkl == arg);
+      if (bal) next = __ffsll((long long)bal);  // node lane + 1 of the lowest hit
       emit = arg;
     } else {
       double z = 0.0;
