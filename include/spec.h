@@ -186,6 +186,9 @@ const char* spec_version(void);
  *   anc_slots[M, anc_width]: further visible slots, -1 padded; the valid
  *     entries of a row hold consecutive positions ending at the row's own
  *     position, in order (root rows, ancestors, the row itself);
+ *   with sliding_window > 0 every row's position must be >= ctx_len - 1 of
+ *     its sequence (the context span of a window is planned from the
+ *     context's end; tree rows always satisfy this);
  *   k_out <= top_k: outputs topk_ids[M, k_out] (target ids, d2t applied) and
  *     topk_logp[M, k_out] (float32 log-probs), ordered by (logit desc, id asc);
  *   hidden_out[M, H]: pre-norm output state (storage type);
@@ -247,7 +250,9 @@ spec_status spec_build_tree(spec_ctx* ctx, const spec_weights* w, const spec_kv*
  *     the current node's argmax (first index on ties); emit the accepted
  *     tokens, then the argmax at the last accepted node.
  *   mode SPEC_VERIFY_STOCHASTIC: at the current node test the children in
- *     node order with Z = 1: accept child c_i iff accept_u[b, cur, i] <=
+ *     node order with Z = 1 (a node may have at most top_k children, as
+ *     every tree spec_build_tree makes; accept_u has one draw per child
+ *     ordinal): accept child c_i iff accept_u[b, cur, i] <=
  *     p(c_i) / Z, else Z -= p(c_i), with p = softmax(logits / temperature);
  *     if none is accepted emit argmax over non-children of
  *     l/T - log(-log U) with U from Philox4x32-10 keyed by seed and counter
@@ -351,7 +356,10 @@ spec_status spec_target_forward(spec_ctx* ctx, const spec_target_weights* w,
                                 const int32_t* ctx_len, float* logits, void* aux_hidden,
                                 void* stream);
 
-/* KV compaction of the accepted path, every layer of `kv`: for each
+/* KV compaction of the accepted path (vLLM Neuron page, "KV Cache Sharing":
+ * the draft and target layers share one cache addressed by slot, so the
+ * accepted tokens' rows must sit at the slots that follow the root before
+ * the next step), every layer of `kv`: for each
  * sequence b and j < accepted_len[b], the row at slot tree_base[b] +
  * accepted_nodes[b, j] moves to slot tree_base[b] + 1 + j.  All rows of a
  * sequence are read before any is written, so overlapping source and

@@ -56,8 +56,3 @@ def silu(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     return x / (1.0 + np.exp(-x))
 
-
-def softmax(x) -> np.ndarray:
-    x = np.asarray(x, dtype=np.float64)
-    e = np.exp(x - np.max(x, axis=-1, keepdims=True))
-    return e / np.sum(e, axis=-1, keepdims=True)

@@ -24,7 +24,9 @@ chain tree is the causal forward of the token sequence (each position sees
 the context and the previous chain tokens), checked against an independent
 torch formulation with F.scaled_dot_product_attention and a causal mask;
 sibling nodes do not see each other (a node's output is unchanged when a
-sibling's token changes); the aux states at layer 0 are the embeddings.
+sibling's token changes); the aux states at layer 0 are the embeddings; rows
+past num_nodes equal an independent one-token forward (token 0 at position
+ctx) that sees the context alone, and leave the cache untouched.
 """
 
 from __future__ import annotations

@@ -35,7 +35,11 @@ float32 once, then the subtraction in float32.
 Pinned by tests/test_oracle_tree.py: brute-force enumeration of every token
 sequence on tiny vocabularies, the structural invariants (ancestor closure,
 scores non-increasing along paths, depth and position of every node), the
-D = 1 and k = 1 reductions, and numpy sorting of the log-probs.
+D = 1 and k = 1 reductions, numpy sorting of the log-probs; the trimmed
+vocabulary (d2t) against the full head's logits restricted to the subset,
+ranked by a stable sort in draft-id order (sorted and unsorted maps, exact
+ties); a root pass over several new rows against one-row passes run in order,
+with the beam's positions and slots.
 """
 
 from __future__ import annotations

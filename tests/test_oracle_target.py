@@ -32,9 +32,10 @@ def _rope_c(x, pos, base):
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def _torch_causal(cfg, W, kc, vc, toks, ctx):
+def _torch_causal(cfg, W, kc, vc, toks, ctx, ctx_only=False):
     """One sequence: context keys [0, ctx) already in the cache (positions =
-    slots), then the token run at positions ctx.. with causal attention."""
+    slots), then the token run at positions ctx.. with causal attention (with
+    ``ctx_only`` every token sees the context alone, not even itself)."""
     dt = cfg["dtype"]
     rnd = (lambda a: torch.from_numpy(gen.round_bf16_inplace(a.float().numpy().copy())).double()) \
         if dt == "bf16" else (lambda a: a.float().double())
@@ -57,7 +58,7 @@ def _torch_causal(cfg, W, kc, vc, toks, ctx):
         K = torch.cat([t(kc[l, :, :ctx]).permute(1, 0, 2), k], 0)  # [ctx+T, nkv, hd]
         Vv = torch.cat([t(vc[l, :, :ctx]).permute(1, 0, 2), v], 0)
         mask = torch.ones(T, ctx + T, dtype=torch.bool)
-        mask[:, ctx:] = torch.tril(torch.ones(T, T, dtype=torch.bool))
+        mask[:, ctx:] = False if ctx_only else torch.tril(torch.ones(T, T, dtype=torch.bool))
         g = nq // nkv
         Kh = K.permute(1, 0, 2).repeat_interleave(g, 0)[None]
         Vh = Vv.permute(1, 0, 2).repeat_interleave(g, 0)[None]
@@ -116,3 +117,32 @@ def test_siblings_do_not_see_each_other():
     b, _ = ot.target_forward(cfg, W, kc.copy(), vc.copy(), tree2, ctx)
     np.testing.assert_array_equal(a[0, [0, 1, 3]], b[0, [0, 1, 3]])
     assert not np.array_equal(a[0, 2], b[0, 2])
+
+
+def test_nodes_past_num_nodes_see_the_context_only():
+    """Rows of a tree past num_nodes (unused nodes) are computed as a token 0
+    at position ctx that attends to the context alone and writes no K/V; the
+    live nodes are the causal forward of their own chain."""
+    cfg = _cfg("f32")
+    W = gen.make_target_weights(cfg, 43, L)
+    ctx = np.array([9])
+    S = 20
+    kc = np.stack([gen.random_states(43, f"tk{l}", (1, 2, S, 32), "f32") for l in range(L)])
+    vc = np.stack([gen.random_states(43, f"tv{l}", (1, 2, S, 32), "f32") for l in range(L)])
+    tree = gen.chain_tree(1, 5, cfg["vocab"], ctx, 43)
+    live = 2  # nodes 0..2 live, 3..5 unused
+    for key in ("tokens", "parent", "depth", "position"):
+        tree[key][0, live + 1:] = -1
+    tree["anc_mask"][0, live + 1:] = 0
+    tree["num_nodes"][:] = live
+    k1, v1 = kc.copy(), vc.copy()
+    logits, aux = ot.target_forward(cfg, W, k1, v1, tree, ctx)
+    z_live, a_live = _torch_causal(cfg, W, kc[:, 0], vc[:, 0], tree["tokens"][0, :live + 1], 9)
+    np.testing.assert_allclose(logits[0, :live + 1], z_live, atol=1e-5, rtol=1e-5)
+    z_dead, a_dead = _torch_causal(cfg, W, kc[:, 0], vc[:, 0], [0], 9, ctx_only=True)
+    for n in range(live + 1, 6):
+        np.testing.assert_allclose(logits[0, n], z_dead[0], atol=1e-5, rtol=1e-5)
+        np.testing.assert_allclose(aux[0, n], a_dead[0], atol=1e-5, rtol=1e-5)
+    # no K/V written at the unused nodes' slots (or anywhere past the live ones)
+    np.testing.assert_array_equal(k1[:, :, :, 9 + live + 1:], kc[:, :, :, 9 + live + 1:])
+    np.testing.assert_array_equal(v1[:, :, :, 9 + live + 1:], vc[:, :, :, 9 + live + 1:])

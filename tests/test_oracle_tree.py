@@ -204,3 +204,142 @@ def test_tree_from_table_equals_model_build():
     t2 = ot.build_tree_from_topk(cfg, inp["ctx_len"], inp["in_tokens"], ids, lps)
     for key in ("tokens", "parent", "depth", "position", "draft_slot", "score", "anc_mask", "num_nodes"):
         np.testing.assert_array_equal(t2[key], tree[key])
+
+
+# ------------------------------------------------ trimmed draft vocabulary
+def _masked_full_head_pass(cfg_full, W_full, kc, vc, aux, ctx_len, d2t, k, seen):
+    """Reference draft for the trimmed-vocabulary pin: the full head's logits
+    restricted to the subset (the normed row against the full head's rows at
+    the subset's target ids, gathered so that the float32 product has the
+    trimmed head's shape and rounds alike); ranking by a stable sort of
+    the subset's logits in draft-id order (so equal logits keep the smaller
+    draft id first), log-probs against scipy's logsumexp over the subset, then
+    the draft ids mapped to target ids.  ``seen`` receives the subset logits
+    of every row."""
+    state = {}
+
+    def fn(d, rows):
+        hidden = (np.stack([aux[r["b"], r["i"]] for r in rows]) if d == 1
+                  else state["h"][[r["src"] for r in rows]])
+        A = max(len(r["anc"]) for r in rows)
+        anc = np.full((len(rows), A), -1, np.int64)
+        for i, r in enumerate(rows):
+            anc[i, :len(r["anc"])] = r["anc"]
+        out = od.draft_pass(cfg_full, W_full, kc, vc, 0 if d == 1 else 1, hidden,
+                            [r["token"] for r in rows], [r["b"] for r in rows],
+                            [r["pos"] for r in rows], [r["slot"] for r in rows], ctx_len, anc)
+        state["h"] = out["h_out"]
+        res = []
+        zs = (out["normed"] @ W_full["lm_head"][d2t].T).astype(np.float32)
+        for i in range(len(rows)):
+            z = zs[i]
+            seen.append(z)
+            order = np.argsort(-z.astype(np.float64), kind="stable")[:k]
+            lp = (z[order] - np.float32(logsumexp(z.astype(np.float64)))).astype(np.float32)
+            res.append((d2t[order].astype(np.int64), lp))
+        return res
+
+    return fn
+
+
+@pytest.mark.parametrize("sorted_map", [True, False])
+def test_trimmed_vocabulary_equals_the_masked_full_head(sorted_map):
+    """A trimmed head whose rows are the full head's rows at the d2t ids must
+    give the tree chosen from the full head's logits restricted to that subset
+    ("Eaglet", "Approach 1: YAML Recipe": trimmed draft vocabulary with an id
+    map).  With an unsorted map the tie-break runs in draft-id order: two
+    trimmed rows are made identical so their logits tie exactly."""
+    V, Vd = 512, 96
+    cfg_t = _tiny_tree_cfg(vocab=V, draft_vocab=Vd, top_k=3, depth=3, total_tokens=9, batch=2)
+    cfg_f = _tiny_tree_cfg(vocab=V, draft_vocab=V, top_k=3, depth=3, total_tokens=9, batch=2)
+    W = gen.make_weights(cfg_f, 31)
+    rng = np.random.default_rng(31)
+    d2t = np.sort(rng.choice(V, Vd, replace=False)) if sorted_map else rng.choice(V, Vd, replace=False)
+    d2t = d2t.astype(np.int32)
+    if not sorted_map:
+        # draft ids 5 and 6 tie everywhere (identical rows, scaled up so that
+        # both often reach the top 3); their target ids run the other way
+        lo, hi = sorted(d2t[5:7])
+        d2t[5], d2t[6] = hi, lo
+        W["lm_head"][d2t[5]] *= np.float32(32.0)
+        W["lm_head"][d2t[6]] = W["lm_head"][d2t[5]]
+    Wt = dict(W, lm_head=np.ascontiguousarray(W["lm_head"][d2t]), d2t=d2t)
+    inp = gen.make_step_inputs(cfg_f, 31)
+    rec = []
+    got = ot.build_tree(cfg_t, Wt, inp["k_cache"].copy(), inp["v_cache"].copy(), inp["aux"],
+                        inp["in_tokens"], inp["ctx_len"], record=rec)
+    seen = []
+    fn = _masked_full_head_pass(cfg_f, W, inp["k_cache"].copy(), inp["v_cache"].copy(), inp["aux"],
+                                inp["ctx_len"], d2t, cfg_f["top_k"], seen)
+    want = ot.build_tree_core(cfg_f, 2, 1, inp["ctx_len"], inp["in_tokens"], fn)
+    # precondition: the two heads computed bit-identical logits on the subset
+    trimmed = np.concatenate([out["logits"] for _, out in rec])
+    np.testing.assert_array_equal(trimmed, np.stack(seen))
+    for key in ("tokens", "parent", "depth", "position", "draft_slot", "anc_mask", "num_nodes"):
+        np.testing.assert_array_equal(got[key], want[key], err_msg=key)
+    np.testing.assert_allclose(got["score"], want["score"], rtol=0, atol=1e-6)
+    assert set(got["tokens"][:, 1:].ravel().tolist()) - {-1} <= set(d2t.tolist())
+    if not sorted_map:
+        # the tie between draft ids 5 and 6: the smaller draft id (the larger
+        # target id) is the earlier child wherever both were drafted
+        assert all(z[5] == z[6] for z in seen)
+        hits = 0
+        for b in range(2):
+            toks = got["tokens"][b].tolist()
+            par = got["parent"][b].tolist()
+            nodes = range(1, int(got["num_nodes"][b]) + 1)
+            for n in nodes:
+                if toks[n] != d2t[6]:
+                    continue
+                twin = [m for m in nodes if par[m] == par[n] and toks[m] == d2t[5]]
+                if twin:
+                    assert twin[0] < n
+                    hits += 1
+        assert hits > 0, "no node drafted both tied ids"
+
+
+# ------------------------------------------- root pass over several new rows
+def test_root_pass_over_new_rows_equals_sequential_single_rows():
+    """n_new > 1 ("The propose() Method": the prefill runs the shifted ids of
+    the new tokens): the root pass over n rows equals n one-row passes run in
+    order, row i at position and slot ctx + i seeing the context and rows
+    0..i; the last row seeds depth 1; a beam node of depth 1 at rank j runs at
+    position ctx + n - 1 + 1 and slot ctx + n + j and sees every root row.
+    Every candidate is selected (N = k + k*k), so the whole tree is checked."""
+    n_new, k = 3, 2
+    cfg = _tiny_tree_cfg(top_k=k, depth=2, total_tokens=k + k * k, batch=2, n_new=n_new, dtype="bf16")
+    W = gen.make_weights(cfg, 33)
+    inp = gen.make_step_inputs(cfg, 33, ctx_len=[20, 11])
+    tree = ot.build_tree(cfg, W, inp["k_cache"].copy(), inp["v_cache"].copy(), inp["aux"],
+                         inp["in_tokens"], inp["ctx_len"])
+    kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
+    for b in range(2):
+        c = int(inp["ctx_len"][b])
+        for i in range(n_new):  # one row at a time, in order
+            out = od.draft_pass(cfg, W, kc, vc, 0, inp["aux"][b, i:i + 1], [int(inp["in_tokens"][b, i])],
+                                [b], [c + i], [c + i], inp["ctx_len"], [list(range(c, c + i + 1))])
+        z = out["logits"][0].astype(np.float64)
+        top = np.argsort(-z, kind="stable")[:k]
+        assert z[top[-1]] - np.sort(z)[::-1][k] > 1e-3  # no near-tie at the cut
+        lse = logsumexp(z)
+        assert tree["tokens"][b, 0] == inp["in_tokens"][b, n_new - 1]
+        assert tree["position"][b, 0] == c + n_new - 1 and tree["draft_slot"][b, 0] == c + n_new - 1
+        d1 = [n for n in range(1, k + k * k + 1) if tree["depth"][b, n] == 1]
+        assert [int(tree["tokens"][b, n]) for n in d1] == top.tolist()
+        np.testing.assert_allclose([tree["score"][b, n] for n in d1], z[top] - lse, atol=2e-5)
+        # depth 1 is the beam (k nodes); rank j by score runs at slot c + n + j
+        ranked = sorted(d1, key=lambda n: (-float(tree["score"][b, n]), n))
+        h_root = out["h_out"]
+        for j, n in enumerate(ranked):
+            slot = c + n_new + j
+            assert tree["draft_slot"][b, n] == slot and tree["position"][b, n] == c + n_new
+            o2 = od.draft_pass(cfg, W, kc, vc, 1, h_root, [int(tree["tokens"][b, n])], [b], [c + n_new],
+                               [slot], inp["ctx_len"], [list(range(c, c + n_new)) + [slot]])
+            z2 = o2["logits"][0].astype(np.float64)
+            top2 = np.argsort(-z2, kind="stable")[:k]
+            kids = [m for m in range(1, k + k * k + 1) if tree["parent"][b, m] == n]
+            assert [int(tree["tokens"][b, m]) for m in kids] == top2.tolist()
+            np.testing.assert_allclose([tree["score"][b, m] for m in kids],
+                                       tree["score"][b, n] + (z2[top2] - logsumexp(z2)), atol=3e-5)
+            for m in kids:
+                assert tree["position"][b, m] == c + n_new + 1 and tree["draft_slot"][b, m] == -1
