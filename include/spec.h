@@ -171,7 +171,7 @@ typedef struct spec_tree {
 /* Allocate a context and its workspace (the only allocation of the library). */
 spec_status spec_create(const spec_config* cfg, spec_ctx** out);
 void spec_destroy(spec_ctx* ctx);
-const char* spec_last_error(const spec_ctx* ctx);
+const char* spec_last_error(const spec_ctx* ctx);  /* NULL: last context-free call's error */
 int64_t spec_workspace_bytes(const spec_ctx* ctx);
 const char* spec_version(void);
 
@@ -264,6 +264,27 @@ spec_status spec_verify_tree(spec_ctx* ctx, int32_t B, const spec_tree* tree,
                              const float* target_logits, int32_t mode, float temperature,
                              const float* accept_u, uint64_t seed, int32_t* out_tokens,
                              int32_t* accepted_len, int32_t* accepted_nodes, void* stream);
+
+/* Allocation-free variant of spec_verify_tree, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It takes no context: the tree shape
+ * (total_tokens N, depth, top_k, vocab) is passed in, and the arguments,
+ * modes, outputs and results are those of spec_verify_tree.  The call
+ * allocates nothing: its scratch (statistics records per node and
+ * vocabulary chunk, Gumbel records, stop nodes) lives in one fixed device
+ * array of 1 MiB per GPU, held until the process ends; shapes that need more
+ * (about B * (N + 1) * 16 bytes plus a little, at least 32 KiB) are rejected
+ * with SPEC_EUNSUPPORTED.  Every call on one GPU shares that array and may
+ * overwrite what the previous call left there: calls that overlap on one
+ * GPU (concurrent streams, several host threads) race and must be
+ * serialised by the caller.  Errors: SPEC_EINVAL / SPEC_EUNSUPPORTED before
+ * any launch, SPEC_EHIP if a launch failed; spec_last_error(NULL) returns the
+ * message of the last failed context-free call on the calling thread. */
+spec_status spec_verify_tree_static(int32_t B, int32_t total_tokens, int32_t depth, int32_t top_k,
+                                    int32_t vocab, const spec_tree* tree, const float* target_logits,
+                                    int32_t mode, float temperature, const float* accept_u,
+                                    uint64_t seed, int32_t* out_tokens, int32_t* accepted_len,
+                                    int32_t* accepted_nodes, void* stream);
 
 /* Index bookkeeping of a flat batch of variable-length draft chains (vLLM
  * Neuron page, "SpecDecodeMetadata: Index Bookkeeping"): request r has

@@ -56,7 +56,7 @@ class SpecTargetWeights(ctypes.Structure):
 
 EXPORTS = ["spec_create", "spec_destroy", "spec_last_error", "spec_workspace_bytes", "spec_version",
            "spec_draft_step", "spec_topk_logprobs", "spec_retrieve_candidates", "spec_tree_from_topk", "spec_build_tree",
-           "spec_verify_tree", "spec_compact_kv", "spec_decode_metadata", "spec_rejection_sample",
+           "spec_verify_tree", "spec_verify_tree_static", "spec_compact_kv", "spec_decode_metadata", "spec_rejection_sample",
            "spec_target_forward",
            "spec_profile_enable", "spec_profile_read"]
 SPEC_PROF_LM_HEAD, SPEC_PROF_ATTENTION, SPEC_PROF_VERIFY, SPEC_PROF_TOPK = 0, 1, 2, 3
@@ -100,6 +100,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_tree.argtypes = [c_vp, c_i32, P(SpecTree), c_vp, c_i32, ctypes.c_float, c_vp,
                                      ctypes.c_uint64, c_vp, c_vp, c_vp, c_vp]
     lib.spec_verify_tree.restype = c_i32
+    lib.spec_verify_tree_static.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32, P(SpecTree), c_vp, c_i32,
+                                            ctypes.c_float, c_vp, ctypes.c_uint64, c_vp, c_vp, c_vp, c_vp]
+    lib.spec_verify_tree_static.restype = c_i32
     lib.spec_compact_kv.argtypes = [c_vp, P(SpecKV), c_i32, c_vp, c_vp, c_vp, c_i32, c_vp]
     lib.spec_compact_kv.restype = c_i32
     lib.spec_decode_metadata.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]

@@ -190,6 +190,10 @@ hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const in
                   const int* num_nodes, const float* logits, int mode, float temperature,
                   const float* accept_u, uint64_t seed, int* out_tokens, int* accepted_len,
                   int* accepted_nodes, void* ws, const VerifyPlan& p, hipStream_t s);
+// Fixed device scratch of the allocation-free verification entry point (one
+// copy per GPU) and its device address on the current device.
+constexpr size_t kStaticVerifyScratchBytes = size_t(1) << 20;
+hipError_t static_verify_scratch(void** out);
 
 // ------------------------------------------------------------ target forward
 // Rows of the target's verification forward: token, position, KV slot and

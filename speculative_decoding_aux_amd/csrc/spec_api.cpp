@@ -144,7 +144,10 @@ extern "C" {
 
 const char* spec_version(void) { return "spec_mi355x 0.1 (gfx950)"; }
 
-const char* spec_last_error(const spec_ctx* ctx) { return ctx ? ctx->err.c_str() : "null context"; }
+// Message of the last failed context-free call on this thread.
+static thread_local std::string g_static_err = "no error";
+
+const char* spec_last_error(const spec_ctx* ctx) { return ctx ? ctx->err.c_str() : g_static_err.c_str(); }
 
 int64_t spec_workspace_bytes(const spec_ctx* ctx) { return ctx ? (int64_t)ctx->bytes : 0; }
 
@@ -792,6 +795,51 @@ spec_status spec_verify_tree(spec_ctx* ctx, int32_t B, const spec_tree* tree,
                        tree->num_nodes, target_logits, mode, temperature, accept_u, seed,
                        out_tokens, accepted_len, accepted_nodes, ctx->ws.verify_part, vp,
                        STREAM(stream)));
+  return SPEC_OK;
+}
+
+spec_status spec_verify_tree_static(int32_t B, int32_t total_tokens, int32_t depth, int32_t top_k,
+                                    int32_t vocab, const spec_tree* tree, const float* target_logits,
+                                    int32_t mode, float temperature, const float* accept_u,
+                                    uint64_t seed, int32_t* out_tokens, int32_t* accepted_len,
+                                    int32_t* accepted_nodes, void* stream) {
+  auto bad = [](spec_status st, const char* msg) {
+    g_static_err = msg;
+    return st;
+  };
+  if (B <= 0 || total_tokens <= 0 || depth <= 0 || depth > total_tokens || top_k <= 0 ||
+      vocab <= 0)
+    return bad(SPEC_EINVAL, "spec_verify_tree_static: sizes must be positive, depth <= total_tokens");
+  if (total_tokens + 1 > 64 || top_k > 64)
+    return bad(SPEC_EUNSUPPORTED, "spec_verify_tree_static: total_tokens + 1 and top_k must be <= 64");
+  if (!tree || !tree->tokens || !tree->parent || !tree->num_nodes || !target_logits ||
+      !out_tokens || !accepted_len || !accepted_nodes)
+    return bad(SPEC_EINVAL, "spec_verify_tree_static: null argument");
+  if (mode != SPEC_VERIFY_GREEDY && mode != SPEC_VERIFY_STOCHASTIC)
+    return bad(SPEC_EINVAL, "spec_verify_tree_static: bad mode");
+  if (mode == SPEC_VERIFY_STOCHASTIC && (!accept_u || !(temperature > 0.f)))
+    return bad(SPEC_EINVAL,
+               "spec_verify_tree_static: stochastic verification needs accept_u and temperature > 0");
+  const VerifyPlan vp = verify_plan(B, total_tokens, vocab);
+  if (verify_ws_bytes(vp, B, total_tokens) > kStaticVerifyScratchBytes) {
+    char buf[160];
+    snprintf(buf, sizeof buf,
+             "spec_verify_tree_static: B=%d, total_tokens=%d, vocab=%d need %zu scratch bytes "
+             "(at most %zu)",
+             B, total_tokens, vocab, verify_ws_bytes(vp, B, total_tokens),
+             kStaticVerifyScratchBytes);
+    return bad(SPEC_EUNSUPPORTED, buf);
+  }
+  void* ws = nullptr;
+  hipError_t e = static_verify_scratch(&ws);
+  if (e == hipSuccess)
+    e = verify(B, total_tokens, depth, top_k, vocab, tree->tokens, tree->parent, tree->num_nodes,
+               target_logits, mode, temperature, accept_u, seed, out_tokens, accepted_len,
+               accepted_nodes, ws, vp, STREAM(stream));
+  if (e != hipSuccess) {
+    g_static_err = std::string("spec_verify_tree_static: ") + hipGetErrorString(e);
+    return SPEC_EHIP;
+  }
   return SPEC_OK;
 }
 

@@ -13,10 +13,19 @@
 // distribution when it has no children).  U is drawn in-kernel from
 // Philox4x32-10 (key = seed, counter = (v >> 2, node, b, 0), word v & 3), so
 // the noise costs no memory traffic and is drawn for B rows, not B (N + 1).
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace spec {
+
+// Scratch of the allocation-free verification entry point: the per (node,
+// vocabulary chunk) statistics records, the Gumbel records and the stop
+// nodes.  Each GPU holds its own copy for the life of the process; host code
+// never passes this name to a kernel, only the device address that
+// hipGetSymbolAddress returns for it (static_verify_scratch).
+static __device__ __align__(256) unsigned char scratch[kStaticVerifyScratchBytes];
 
 namespace {
 
@@ -433,6 +442,27 @@ hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const in
   SPEC_LAUNCH(verify_emit_kernel, dim3(B), dim3(64), 0, s, D, p.gch, (const GPart*)gpart,
                      (const int*)accepted_len, out_tokens);
   return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t static_verify_scratch(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::once_flag once[kMaxDev];
+  static void* ptr[kMaxDev];
+  static hipError_t err[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [&] {
+    void* p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    ptr[dev] = err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (err[dev] != hipSuccess) return err[dev];
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t compact(bool bf16, KvFull kv, int B, const int* base, const int* nodes,

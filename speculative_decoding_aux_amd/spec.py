@@ -229,6 +229,27 @@ def spec_verify_tree(ctx: SpecContext, tree: Tree, target_logits, mode, temperat
     return out
 
 
+def spec_verify_tree_static(tree: Tree, target_logits, mode, total_tokens, depth, top_k, temperature=1.0,
+                            accept_u=None, seed=0, out=None):
+    """spec_verify_tree without a context: its scratch is the library's fixed
+    per-GPU array, so the call allocates no device memory (``out`` may be
+    passed preallocated as well)."""
+    lib = L.load()
+    B = tree.tokens.shape[0]
+    V = target_logits.shape[-1]
+    dev = target_logits.device
+    if out is None:
+        out = (torch.empty(B, depth + 1, dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev),
+               torch.empty(B, depth, dtype=torch.int32, device=dev))
+    st = lib.spec_verify_tree_static(B, total_tokens, depth, top_k, V, ctypes.byref(tree.struct),
+                                     _p(target_logits), mode, float(temperature), _p(accept_u),
+                                     int(seed) & (2**64 - 1), _p(out[0]), _p(out[1]), _p(out[2]), _stream())
+    if st != L.SPEC_OK:
+        raise SpecError(st, lib.spec_last_error(None).decode())
+    return out
+
+
 def spec_compact_kv(ctx: SpecContext, kv: KVCache, tree_base, accepted_nodes, accepted_len):
     B, max_accept = accepted_nodes.shape
     dev = ctx.device

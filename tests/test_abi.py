@@ -89,4 +89,21 @@ def test_create_rejects_bad_configs_before_any_gpu_call(lib, kw, code):
 
 def test_null_context_is_rejected(lib):
     assert lib.spec_verify_tree(None, 1, None, None, 0, 1.0, None, 0, None, None, None, None) == L.SPEC_EINVAL
-    assert lib.spec_last_error(None) == b"null context"
+
+
+
+def test_static_verify_rejects_bad_arguments_before_any_launch(lib):
+    """The context-free verification refuses null arrays and shapes beyond
+    its fixed scratch on the host (no GPU needed) and reports why through
+    spec_last_error(NULL)."""
+    tree = L.SpecTree()
+    assert lib.spec_verify_tree_static(4, 63, 7, 8, 1000, ctypes.byref(tree), None, 0, 1.0, None, 0,
+                                       None, None, None, None) == L.SPEC_EINVAL
+    assert b"null argument" in lib.spec_last_error(None)
+    assert lib.spec_verify_tree_static(4, 64, 7, 8, 1000, None, None, 0, 1.0, None, 0,
+                                       None, None, None, None) == L.SPEC_EUNSUPPORTED
+    p = ctypes.c_void_p(16)  # never dereferenced: the call is refused first
+    big = L.SpecTree(p, p, p, p, p, p, p, p)
+    assert lib.spec_verify_tree_static(40000, 63, 7, 8, 1000, ctypes.byref(big), p, 0, 1.0, None, 0,
+                                       p, p, p, None) == L.SPEC_EUNSUPPORTED
+    assert b"scratch bytes" in lib.spec_last_error(None)
