@@ -2,8 +2,12 @@
 
 A step is spec_build_tree + spec_verify_tree + spec_compact_kv for the whole
 batch, on inputs already resident in HBM.  Default workload: the
-Llama-3.1-8B-shaped EAGLE-3 chain (batch 4, context 256, 5 draft tokens,
-greedy), on synthetic seeded inputs.  Prints one JSON line.
+Qwen3-8B-shaped tree (batch 32, context 2048, top_k 8 / depth 7 / 63 draft
+tokens, stochastic verification at T = 1 against target logits made of the
+oracle's draft logits of every node plus N(0, 1) noise), on synthetic seeded
+inputs.  The oracle leg (cpu_baseline) runs first: it times whole oracle
+steps on the host cores and prepares those target logits, which both legs
+then verify.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                     [--graph] [--no-cpu-baseline] [--n-new N] [--paged BS]
@@ -36,12 +40,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="llama8b_chain")
+    ap.add_argument("--config", default="qwen8b_tree")
     ap.add_argument("--graph", action="store_true", help="replay the step as one captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the attainable-peak probes run after the timed steps")
-    ap.add_argument("--cpu-steps", type=int, default=2)
+    ap.add_argument("--cpu-steps", type=int, default=3)
     ap.add_argument("--flat-sampling", type=int, default=0, metavar="B",
                     help="instead of the step, time rejection sampling of a flat batch of B "
                          "variable-length chains with per-request temperature/top-k/top-p "
@@ -60,35 +64,36 @@ def parse():
 
 
 def lm_head_bytes(cfg, M):
-    """Algorithmic bytes of one LM-head launch: the weight stream and the
-    normed rows in; out, the float32 logits, or - when the vocab top-k is fused
-    into the launch (bf16 weight streaming at M <= 64, unsplit: Vd >= 65536, or
-    column strips filling the grid) - one (top-k list, max, sum) record per row
-    and column strip; beyond 64 rows (tiled head) the logits plus one (max,
-    sum exp) record per row and 128-column strip.  EAGLE-4: the low-rank
-    score GEMM, scores out."""
+    """Algorithmic bytes of one LM-head launch over M rows: the weight stream
+    and the normed rows in; out, the float32 logits, or - when the vocab
+    top-k is fused into the launch (bf16 weight streaming at M <= 64,
+    unsplit: Vd >= 65536, or column strips filling the grid) - one (top-k
+    list, max, sum) record per row and column strip; beyond 64 rows (tiled
+    head) one (max, sum exp) record per row and 128-column strip (the logits
+    it also writes are a round trip the method does not need and are not
+    counted).  EAGLE-4: the low-rank score GEMM, scores out."""
     H = cfg["hidden"]
     if cfg["cand_rank"]:
         r, V = cfg["cand_rank"], cfg["vocab"]
         return V * r * 2 + M * r * 2 + M * V * 4
     Vd, k = cfg["draft_vocab"], cfg["top_k"]
+    if cfg["dtype"] == "bf16" and M > 64 and k <= 8:
+        return Vd * H * 2 + M * H * 2 + M * -(-Vd // 128) * 8
     cw1 = M <= 16 and Vd >= 65536
     cols = 64 if cw1 else 128
     strips = -(-Vd // cols)
     unsplit = Vd >= 65536 or strips * -(-M // 64) >= (1024 if cw1 else 2048)
     fused = cfg["dtype"] == "bf16" and k <= 8 and M <= 64 and unsplit
     out = M * strips * (8 * (1 if k == 1 else 8) + 16) if fused else M * Vd * 4
-    if cfg["dtype"] == "bf16" and M > 64 and k <= 8:
-        out += M * -(-Vd // 128) * 8   # per-strip (max, sum) records of the tiled head
     return Vd * H * 2 + M * H * 2 + out
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the LM head from the committed counter profile
-    (FETCH_SIZE and WRITE_SIZE scaled by a copy of known size), or None when
-    the kernel sources changed since the counters were taken."""
+def measured_traffic(workload, kernel="lm_head"):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    profile (FETCH_SIZE and WRITE_SIZE scaled by a copy of known size), or
+    None when the kernel sources changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{workload}_lm_head_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{workload}_{kernel}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -98,12 +103,14 @@ def measured_traffic(workload):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["kernel_source_sha256"] else None
 
 
-def kernel_figures(cfg, rows, lm, att, ver):
+def kernel_figures(cfg, rows, lm, lmt, att, ver):
     """Per-label launch figures of the sampled steps: average launch time,
     algorithmic bytes (and, for the LM head, GEMM flops) per launch, achieved
-    rates and their fractions of the published peaks.  Attention: the visible
-    context K and V of every (sequence, kv head) once per pass (the window at
-    most); verify: every node row's target logits once."""
+    rates and their fractions of the published peaks.  LM head: the launches
+    up to 64 rows (root pass, chains) and the tiled launches of the beam
+    passes apart; attention: the visible context K and V of every (sequence,
+    kv head) once per pass (the window at most); verify: every node row's
+    target logits once."""
     es = 2 if cfg["dtype"] == "bf16" else 4
     B, nkv, hd = cfg["batch"], cfg["n_kv_heads"], cfg["head_dim"]
     ctx = min(cfg["ctx"], cfg["sliding_window"]) if cfg["sliding_window"] else cfg["ctx"]
@@ -123,9 +130,13 @@ def kernel_figures(cfg, rows, lm, att, ver):
         out[name] = e
 
     if cfg["dtype"] == "bf16" and not cfg["cand_rank"]:
-        byts = sum(lm_head_bytes(cfg, m) for m in rows) / len(rows)
-        flops = sum(2.0 * m * cfg["draft_vocab"] * cfg["hidden"] for m in rows) / len(rows)
-        rate("lm_head", lm[0], lm[1], byts, flops)
+        small = [m for m in rows if m <= 64]
+        big = [m for m in rows if m > 64]
+        for name, rs, (nl, ms) in (("lm_head", small, lm), ("lm_head_tiled", big, lmt)):
+            if rs:
+                byts = sum(lm_head_bytes(cfg, m) for m in rs) / len(rs)
+                flops = sum(2.0 * m * cfg["draft_vocab"] * cfg["hidden"] for m in rs) / len(rs)
+                rate(name, nl, ms, byts, flops)
     rate("attention", att[0], att[1], B * nkv * ctx * hd * 2 * es)
     rate("verify", ver[0], ver[1], B * (cfg["total_tokens"] + 1) * cfg["vocab"] * 4)
     return out
@@ -136,55 +147,100 @@ def pass_rows(cfg):
     return [B * n_new] + [B * k] * (D - 1)
 
 
-def cpu_baseline(cfg, W, inp, seed, steps):
-    """The oracle, as it stands, on a bounded sample: whole steps of the same
-    workload (same weights and inputs), timed on the host cores."""
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        return os.cpu_count()
+
+
+def _oracle_step(cfg, W, inp, seed, make_logits, sl=slice(None)):
+    """One whole step of the oracle over the sequences ``sl``: tree build,
+    verification, compaction (of a 1-layer target-shaped cache).  The target
+    logits come from ``make_logits(tree, sub_cfg, record, caches)`` between
+    the build and the verification; that preparation is not timed.  Returns
+    (seconds, accepted lengths, logits)."""
     from oracle import compact as oc
     from oracle import tree as ot
     from oracle import verify as ov
     from synth import gen
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+
+    B = len(range(*sl.indices(cfg["batch"])))
+    c = dict(cfg, batch=B)
+    kc, vc = inp["k_cache"][sl].copy(), inp["v_cache"][sl].copy()
+    ctx_len = inp["ctx_len"][sl]
+    rec = []
+    t0 = time.perf_counter()
+    tree = ot.build_tree(c, W, kc, vc, inp["aux"][sl], inp["in_tokens"][sl], ctx_len, record=rec)
+    t1 = time.perf_counter()
+    logits = make_logits(tree, c, rec, (kc, vc), sl)
+    del rec
+    t2 = time.perf_counter()
+    if cfg["verify"] == "greedy":
+        out, alen, nodes = ov.verify_greedy(tree, logits, cfg["depth"])
+    else:
+        u = gen.make_accept_u(cfg, seed)[sl]
+        out, alen, nodes = ov.verify_stochastic(tree, logits, cfg["depth"], cfg["temperature"], u,
+                                                gen.philox_seed(seed))
+    base = ctx_len + cfg["n_new"] - 1
+    tk = np.zeros((1, B, cfg["n_kv_heads"], cfg["kv_capacity"], cfg["head_dim"]), np.float32)
+    oc.compact_kv(tk, tk.copy(), base, nodes, alen)
+    t3 = time.perf_counter()
+    return (t1 - t0) + (t3 - t2), alen, logits
+
+
+def oracle_leg(cfg, W, inp, seed, steps):
+    """The oracle, as it stands, timed on the host cores, on whole steps of
+    the same workload (same weights and inputs).  For the workload whose
+    target logits are the draft's own logits plus N(0, 1) noise, the first
+    step's tree gives those logits (the draft logits of every node, with one
+    extra pass for the nodes it never expanded; not timed) and every step,
+    and the GPU leg, verifies them.  Returns (cpu_baseline, target logits of
+    the whole batch or None)."""
+    from oracle import tree as ot
+    from synth import gen
+
+    threads = _blas_threads()
+    noisy = cfg["target_logits"] == "draft_plus_noise"
+    held = {}
+
+    def make_logits(tree, c, rec, caches, sl):
+        if not noisy:
+            return gen.plant_target_logits(c, tree, seed)
+        if "tl" not in held:
+            t0 = time.perf_counter()
+            dl = ot.node_draft_logits(c, W, caches[0], caches[1], inp["ctx_len"][sl], tree, rec)
+            held["tl"] = gen.add_noise_logits(dl, seed)
+            print(f"[bench] oracle draft logits of every node: {time.perf_counter() - t0:.1f} s",
+                  file=sys.stderr, flush=True)
+        return held["tl"][sl]
+
     times = []
     for s in range(steps):
-        kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
-        t0 = time.perf_counter()
-        tree = ot.build_tree(cfg, W, kc, vc, inp["aux"], inp["in_tokens"], inp["ctx_len"])
-        t1 = time.perf_counter()
-        logits = gen.plant_target_logits(cfg, tree, seed)
-        t2 = time.perf_counter()
-        if cfg["verify"] == "greedy":
-            out, alen, nodes = ov.verify_greedy(tree, logits, cfg["depth"])
-        else:
-            u = gen.make_accept_u(cfg, seed)
-            out, alen, nodes = ov.verify_stochastic(tree, logits, cfg["depth"], cfg["temperature"], u,
-                                                    gen.philox_seed(seed))
-        base = inp["ctx_len"] + cfg["n_new"] - 1
-        tk = np.zeros((1, cfg["batch"], cfg["n_kv_heads"], cfg["kv_capacity"], cfg["head_dim"]), np.float32)
-        oc.compact_kv(tk, tk.copy(), base, nodes, alen)
-        t3 = time.perf_counter()
-        times.append((t1 - t0) + (t3 - t2))  # input planting excluded
+        sec, _, _ = _oracle_step(cfg, W, inp, seed, make_logits)
+        times.append(sec)
+        print(f"[bench] oracle step {s + 1}/{steps}: {sec:.2f} s", file=sys.stderr, flush=True)
     med = float(np.median(times))
-    res = {"value": 1.0 / med, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-           "sample": f"{steps} whole steps of the same workload (batch {cfg['batch']}); "
-                     f"median {med:.3f} s per step; compaction on a 1-layer cache"}
-    if med < 2.0:  # the same step on one BLAS thread, where that stays within seconds
-        try:
-            from threadpoolctl import threadpool_limits
-        except Exception:  # pragma: no cover
-            return res
-        with threadpool_limits(limits=1):
-            t1 = []
-            for _ in range(steps):
-                kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
-                t0 = time.perf_counter()
-                ot.build_tree(cfg, W, kc, vc, inp["aux"], inp["in_tokens"], inp["ctx_len"])
-                t1.append(time.perf_counter() - t0)
-        res["value_1thread_build"] = round(1.0 / float(np.median(t1)), 4)
-    return res
+    B = cfg["batch"]
+    res = {"value": round(1.0 / med, 5), "unit": "steps/s", "cores": int(threads),
+           "host_cpus": os.cpu_count(), "kind": "oracle",
+           "sample": f"{steps} whole steps of the same workload (batch {B}); median {med:.3f} s per step "
+                     f"(all: {', '.join(f'{t:.2f}' for t in times)} s); numpy with {threads} BLAS threads; "
+                     f"compaction on a 1-layer cache; target-logit preparation not timed"}
+    # the same step on one thread, over a bounded sample of the sequences
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        return res, held.get("tl")
+    bs = max(1, B // 8)
+    with threadpool_limits(limits=1):
+        sec1 = _oracle_step(cfg, W, inp, seed, make_logits, sl=slice(0, bs))[0]
+    res["value_1thread"] = round(1.0 / (sec1 * B / bs), 5)
+    res["sample_1thread"] = (f"1 whole step over {bs} of the {B} sequences on 1 thread: {sec1:.2f} s, "
+                             f"scaled by {B}/{bs} to the batch")
+    print(f"[bench] oracle on 1 thread, {bs} sequences: {sec1:.2f} s", file=sys.stderr, flush=True)
+    return res, held.get("tl")
 
 
 def main():
@@ -223,6 +279,10 @@ def main():
     print(f"[bench] generating inputs for {args.config}", file=sys.stderr, flush=True)
     W = gen.make_weights(cfg, seed)
     inp = gen.make_step_inputs(cfg, seed)
+    cpu_res, tl_oracle = None, None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu_res, tl_oracle = oracle_leg(cfg, W, inp, seed, args.cpu_steps)
     dev = "cuda"
     w = upload_weights(cfg, W)
     draft_kv = upload_kv(cfg, inp["k_cache"], inp["v_cache"])
@@ -249,10 +309,12 @@ def main():
     torch.cuda.synchronize()
     tnp = tree.numpy()
     if cfg["target_logits"] == "planted":
-        tl = gen.plant_target_logits(cfg, tnp, seed)
-    else:
-        base = gen.random_logits(seed, "bench_draft_like", (B, cfg["total_tokens"] + 1, cfg["vocab"]))
-        tl = gen.add_noise_logits(base, seed)
+        tl, tl_kind = gen.plant_target_logits(cfg, tnp, seed), "planted"
+    elif tl_oracle is not None:  # the oracle's draft logits of every node + N(0, 1), as the oracle leg
+        tl, tl_kind = tl_oracle, "oracle_draft_logits_plus_noise"
+    else:  # oracle leg skipped: random logits of the draft's scale + N(0, 1)
+        base = gen.random_logits(seed, "bench_draft_like", (B, cfg["total_tokens"] + 1, cfg["vocab"]), std=1.28)
+        tl, tl_kind = gen.add_noise_logits(base, seed), "random_plus_noise"
     target_logits = torch.from_numpy(tl).to(dev)
     mode = 0 if cfg["verify"] == "greedy" else 1
     accept_u = torch.from_numpy(gen.make_accept_u(cfg, seed)).to(dev) if mode else None
@@ -301,22 +363,43 @@ def main():
     roof = None
     if graph is None:
         n, ms = ctx.profile_read(L.SPEC_PROF_LM_HEAD)
+        nt, mst = ctx.profile_read(L.SPEC_PROF_LM_HEAD_TILED)
         na, msa = ctx.profile_read(L.SPEC_PROF_ATTENTION)
         nv, msv = ctx.profile_read(L.SPEC_PROF_VERIFY)
         ctx.profile(False)
         rows = pass_rows(cfg)
-        byts = sum(lm_head_bytes(cfg, m) for m in rows) / len(rows)
-        avg_ms = ms / max(n, 1)
+        kern = kernel_figures(cfg, rows, (n, ms), (nt, mst), (na, msa), (nv, msv))
+        # the roofline kernel: the LM head launch that takes the most time per
+        # step (the tiled beam-pass head of tree workloads beyond 64 rows)
+        tiled = "lm_head_tiled" in kern and nt * mst >= n * ms
+        if tiled:
+            big = [m for m in rows if m > 64]
+            byts = sum(lm_head_bytes(cfg, m) for m in big) / len(big)
+            nl, avg_ms = nt, mst / max(nt, 1)
+            kname = "tiled beam-pass LM head (gemm_dma_kernel<128,256,64,512,3,REC,PERSIST>)"
+        else:
+            small = [m for m in rows if m <= 64] or rows
+            byts = sum(lm_head_bytes(cfg, m) for m in small) / len(small)
+            nl, avg_ms = n, ms / max(n, 1)
+            kname = ("LM head (gemm_lmhead_topk_kernel / gemm_bf16_stream<*,1,*>)" if cfg["dtype"] == "bf16"
+                     else "gemm_f32_rows")
         achieved = byts / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if args.n_new else measured_traffic(args.config),
-                "kernel": "LM head (gemm_lmhead_topk_kernel / gemm_bf16_stream<*,1,*>)" if cfg["dtype"] == "bf16" else "gemm_f32_rows",
-                "avg_launch_us": round(avg_ms * 1e3, 2), "launches": n, "timed_every_nth_step": PROF_EVERY,
-                "algorithmic_bytes_per_launch": int(byts)}
-        kern = kernel_figures(cfg, rows, (n, ms), (na, msa), (nv, msv))
-        print(f"[bench] lm_head {n} launches avg {avg_ms*1e3:.1f} us; attention avg "
-              f"{msa / max(na, 1) * 1e3:.1f} us; verify avg {msv / max(nv, 1) * 1e3:.1f} us",
-              file=sys.stderr, flush=True)
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if args.n_new else measured_traffic(args.config, "lm_head_tiled" if tiled else "lm_head"),
+                "kernel": kname, "avg_launch_us": round(avg_ms * 1e3, 2), "launches": nl,
+                "timed_every_nth_step": PROF_EVERY, "algorithmic_bytes_per_launch": int(byts)}
+        if tiled:
+            e = kern["lm_head_tiled"]
+            M = rows[-1]
+            roof.update(mfma_tflops=e["mfma_tflops"], mfma_frac=e["mfma_frac"],
+                        arithmetic_intensity=round(e["flops_per_launch"] / byts, 1),
+                        attainable_mfma_frac=round(min(1.0, HBM_PEAK_GBS * 1e9 * e["flops_per_launch"] / byts
+                                                       / (BF16_PEAK_TFLOPS * 1e12)), 4),
+                        rows=M)
+        print(f"[bench] lm_head {n} launches avg {ms / max(n, 1) * 1e3:.1f} us; tiled lm_head {nt} launches avg "
+              f"{mst / max(nt, 1) * 1e3:.1f} us; attention avg {msa / max(na, 1) * 1e3:.1f} us; verify avg "
+              f"{msv / max(nv, 1) * 1e3:.1f} us", file=sys.stderr, flush=True)
     res = {
         "metric": METRIC,
         "value": round(1000.0 / ms_step, 2),
@@ -342,7 +425,7 @@ def main():
     alen = vout[1].cpu().numpy()
     res["acceptance"] = {"mean_accepted": round(float(alen.mean()), 4),
                          "mean_emitted": round(float(alen.mean()) + 1.0, 4), "sequences": int(B),
-                         "target_logits": cfg["target_logits"]}
+                         "target_logits": tl_kind}
     if cfg["cand_rank"]:
         res["candidate_recall"] = candidate_recall(cfg, ctx, w, draft_kv, aux, inp)
     if roof is not None:
@@ -360,9 +443,8 @@ def main():
                     v["frac_of_measured"] = round(v["achieved_gbs"] / pk["hbm_read_gbs"], 4)
                 if "mfma_tflops" in v:
                     v["mfma_frac_of_measured"] = round(v["mfma_tflops"] / pk["mfma_bf16_tflops"], 4)
-    if not args.no_cpu_baseline:
-        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, W, inp, seed, args.cpu_steps)
+    if cpu_res is not None:
+        res["cpu_baseline"] = cpu_res
     print(json.dumps(res), flush=True)
 
 

@@ -400,11 +400,12 @@ spec_status spec_compact_kv(spec_ctx* ctx, const spec_kv* kv, int32_t B, const i
  * for the recorded events and returns the number of timed sequences and their
  * summed duration in milliseconds.  Not for use under stream capture. */
 typedef enum {
-  SPEC_PROF_LM_HEAD = 0,    /* LM-head GEMM (EAGLE-3) or low-rank score GEMM (EAGLE-4) */
+  SPEC_PROF_LM_HEAD = 0,    /* LM-head GEMM up to 64 rows (EAGLE-3) or low-rank score GEMM (EAGLE-4) */
   SPEC_PROF_ATTENTION = 1,  /* context attention + combine */
   SPEC_PROF_VERIFY = 2,     /* verify statistics + walk */
   SPEC_PROF_TOPK = 3,       /* vocab top-k + log-probs */
-  SPEC_PROF_NLABELS = 4
+  SPEC_PROF_LM_HEAD_TILED = 4, /* LM-head GEMM of passes above 64 rows (tree beam passes) */
+  SPEC_PROF_NLABELS = 5
 } spec_prof_label;
 spec_status spec_profile_enable(spec_ctx* ctx, int32_t enable);
 spec_status spec_profile_read(spec_ctx* ctx, int32_t label, int32_t* launches, double* total_ms);

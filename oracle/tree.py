@@ -132,6 +132,7 @@ def build_tree_core(cfg, B, n_new, ctx_len, in_tokens, pass_fn):
         "score": np.zeros((B, n1), np.float32),
         "anc_mask": np.zeros((B, n1), np.uint64),
         "num_nodes": np.zeros(B, np.int32),
+        "node_cand": np.full((B, n1), -1, np.int64),  # candidate index of each draft node
         "cands": cands,
     }
     for b in range(B):
@@ -159,6 +160,7 @@ def build_tree_core(cfg, B, n_new, ctx_len, in_tokens, pass_fn):
             tree["draft_slot"][b, n] = c["slot"]
             tree["score"][b, n] = c["score"]
             tree["anc_mask"][b, n] = tree["anc_mask"][b, par] | np.uint64(1 << n)
+            tree["node_cand"][b, n] = ci
     return tree
 
 
@@ -223,3 +225,72 @@ def build_tree_from_topk(cfg, ctx_len, in_tokens, ids_tab, lp_tab):
     in_tokens = np.asarray(in_tokens)
     B, n_new = in_tokens.shape
     return build_tree_core(cfg, B, n_new, ctx_len, in_tokens, table_pass_fn(ids_tab, lp_tab))
+
+
+def node_draft_logits(cfg, W, kcache, vcache, ctx_len, tree, record):
+    """The draft's logits at every node of the trees: row n of sequence b is
+    the distribution node n's children are ranked by (used to make target
+    logits that resemble the draft's).  ``record`` is the pass record of the
+    build_tree call that made ``tree``; kcache/vcache are the caches it left.
+
+    The root takes the logits of its sequence's last new row; an expanded
+    node those of the pass that expanded it.  Selected nodes that were never
+    expanded run one more recurrent pass here, each on its parent's pre-norm
+    state and its own token at its tree position, seeing the context, the
+    root rows, its ancestors' slots and itself; their own K/V go to scratch
+    slots past the cache (the caches are not changed).  EAGLE-3 heads only.
+    Unused nodes get zero rows.  Returns [B, N+1, Vd] float32."""
+    assert not cfg["cand_rank"]
+    B, n1 = tree["tokens"].shape
+    Vd = cfg["draft_vocab"]
+    S = kcache.shape[2]
+    out = np.zeros((B, n1, Vd), np.float32)
+    # where each candidate's row sits in the recorded passes
+    h_of, z_of = {}, {}
+    rows0, out0 = record[0]
+    n_new = max(r["i"] for r in rows0) + 1
+    for idx, r in enumerate(rows0):
+        if r["i"] == n_new - 1:
+            h_of[(r["b"], -1)] = out0["h_out"][idx]
+            z_of[(r["b"], -1)] = out0["logits"][idx]
+    for rows, o in record[1:]:
+        for idx, r in enumerate(rows):
+            h_of[(r["b"], r["cand"])] = o["h_out"][idx]
+            z_of[(r["b"], r["cand"])] = o["logits"][idx]
+    extra = []  # (b, n) of selected nodes never expanded
+    for b in range(B):
+        if (b, -1) not in z_of:
+            continue
+        out[b, 0] = z_of[(b, -1)]
+        for n in range(1, int(tree["num_nodes"][b]) + 1):
+            ci = int(tree["node_cand"][b, n])
+            if (b, ci) in z_of:
+                out[b, n] = z_of[(b, ci)]
+            else:
+                extra.append((b, n))
+    if not extra:
+        return out
+    pad = ((0, 0), (0, 0), (0, n1), (0, 0))
+    kx, vx = np.pad(kcache, pad), np.pad(vcache, pad)
+    hidden, toks, seq, pos, slot, anc = [], [], [], [], [], []
+    for b, n in extra:
+        c = int(ctx_len[b])
+        p = int(tree["parent"][b, n])
+        hidden.append(h_of[(b, -1 if p == 0 else int(tree["node_cand"][b, p]))])
+        toks.append(int(tree["tokens"][b, n]))
+        seq.append(b)
+        pos.append(int(tree["position"][b, n]))
+        slot.append(S + n)
+        chain, a = [], p
+        while a > 0:
+            chain.append(int(tree["draft_slot"][b, a]))
+            a = int(tree["parent"][b, a])
+        anc.append([c + i for i in range(n_new)] + chain[::-1] + [S + n])
+    A = max(len(a) for a in anc)
+    anc_arr = np.full((len(extra), A), -1, np.int64)
+    for i, a in enumerate(anc):
+        anc_arr[i, :len(a)] = a
+    res = draft_pass(cfg, W, kx, vx, 1, np.stack(hidden), toks, seq, pos, slot, ctx_len, anc_arr)
+    for i, (b, n) in enumerate(extra):
+        out[b, n] = res["logits"][i]
+    return out

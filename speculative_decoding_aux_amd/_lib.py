@@ -59,7 +59,7 @@ EXPORTS = ["spec_create", "spec_destroy", "spec_last_error", "spec_workspace_byt
            "spec_verify_tree", "spec_verify_tree_static", "spec_compact_kv", "spec_decode_metadata", "spec_rejection_sample",
            "spec_target_forward",
            "spec_profile_enable", "spec_profile_read"]
-SPEC_PROF_LM_HEAD, SPEC_PROF_ATTENTION, SPEC_PROF_VERIFY, SPEC_PROF_TOPK = 0, 1, 2, 3
+SPEC_PROF_LM_HEAD, SPEC_PROF_ATTENTION, SPEC_PROF_VERIFY, SPEC_PROF_TOPK, SPEC_PROF_LM_HEAD_TILED = 0, 1, 2, 3, 4
 
 _lib = None
 

@@ -160,9 +160,10 @@ SPEC_DEV double block_sum(double v, double* red) {
   return t;
 }
 
-// (value desc, id asc) ordering used by every top-k and argmax.
+// (value desc, id asc) ordering used by every top-k and argmax (bitwise
+// combination: both comparisons are evaluated, so no branch is emitted).
 SPEC_DEV bool better(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
+  return (va > vb) | ((va == vb) & (ia < ib));
 }
 
 // ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw; SC'11) ----------------------

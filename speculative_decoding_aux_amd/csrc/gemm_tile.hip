@@ -69,11 +69,13 @@ SPEC_DEV TileGeo tile_geo(int t, int M, int N, int K, int kc) {
   const int r = t - q.split * per;
   int strip = r, mb = 0;
   if (nmb > 1) {
-    const int grp = r / (8 * nmb), rem = r % (8 * nmb);
-    strip = grp * 8 + rem % 8;
-    mb = rem / 8;
-    if (strip >= nstrip) {  // the last group is short: spread its ids over what is left
-      const int base = (nstrip / 8) * 8, left = nstrip - base;
+    const int grp = r / (8 * nmb);
+    if ((grp + 1) * 8 <= nstrip) {  // a full group of 8 strips
+      const int rem = r % (8 * nmb);
+      strip = grp * 8 + rem % 8;
+      mb = rem / 8;
+    } else {  // the last group is short: its ids cover the strips that are left
+      const int base = grp * 8, left = nstrip - base;
       const int u = r - base * nmb;
       strip = base + u % left;
       mb = u / left;
@@ -107,16 +109,15 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   constexpr int IW = BN * CH / 64, IX = BM * CH / 64;
   constexpr int NW = (IW + NWAVE - 1) / NWAVE, NX = (IX + NWAVE - 1) / NWAVE, NI = NW + NX;
   static_assert(FB >= 1 && WGN * WGM == NWAVE && BM % (16 * WGM) == 0, "tile shape");
-  static_assert((BK == 32 || BK == 64) && NS >= 2 && NS <= 4, "stages");
+  static_assert((BK == 32 || BK == 64) && NS >= 2 && NS <= 6, "stages");
   static_assert(!REC || WGN == 2, "strip records assume two waves across the strip");
-  // one LDS object per stage
-  // (with three stages the fourth object holds the records' exchange: the
-  // (max, sum) of the wn = 1 half of each row)
-  static_assert(!REC || NS < 4, "record exchange lives in the unused fourth stage");
+  // one LDS object per stage, and the records' exchange (the (max, sum) of
+  // the wn = 1 half of each row)
   __shared__ u32x4_t w0[BN * CH], w1[BN * CH], w2[NS > 2 ? BN * CH : 1],
-      w3[NS > 3 ? BN * CH : (REC ? BM / 2 : 1)];
-  __shared__ u32x4_t x0[BM * CH], x1[BM * CH], x2[NS > 2 ? BM * CH : 1], x3[NS > 3 ? BM * CH : 1];
-  float2* const xr = (float2*)w3;
+      w3[NS > 3 ? BN * CH : 1], w4[NS > 4 ? BN * CH : 1], w5[NS > 5 ? BN * CH : 1];
+  __shared__ u32x4_t x0[BM * CH], x1[BM * CH], x2[NS > 2 ? BM * CH : 1], x3[NS > 3 ? BM * CH : 1],
+      x4[NS > 4 ? BM * CH : 1], x5[NS > 5 ? BM * CH : 1];
+  __shared__ float2 xr[REC ? BM : 1];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wn = wave % WGN, wm = wave / WGN;
@@ -156,14 +157,18 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     if constexpr (S == 0) return (SPEC_LDS u32x4_t*)w0;
     else if constexpr (S == 1) return (SPEC_LDS u32x4_t*)w1;
     else if constexpr (S == 2) return (SPEC_LDS u32x4_t*)w2;
-    else return (SPEC_LDS u32x4_t*)w3;
+    else if constexpr (S == 3) return (SPEC_LDS u32x4_t*)w3;
+    else if constexpr (S == 4) return (SPEC_LDS u32x4_t*)w4;
+    else return (SPEC_LDS u32x4_t*)w5;
   };
   auto xbuf = [](auto sc) -> SPEC_LDS u32x4_t* {
     constexpr int S = decltype(sc)::value;
     if constexpr (S == 0) return (SPEC_LDS u32x4_t*)x0;
     else if constexpr (S == 1) return (SPEC_LDS u32x4_t*)x1;
     else if constexpr (S == 2) return (SPEC_LDS u32x4_t*)x2;
-    else return (SPEC_LDS u32x4_t*)x3;
+    else if constexpr (S == 3) return (SPEC_LDS u32x4_t*)x3;
+    else if constexpr (S == 4) return (SPEC_LDS u32x4_t*)x4;
+    else return (SPEC_LDS u32x4_t*)x5;
   };
 
   int S = 0;  // K steps of all the block's tiles

@@ -60,7 +60,7 @@ struct spec_ctx {
   bool prof = false;
   static constexpr int kProfCap = 4096;
   std::vector<hipEvent_t> ev[SPEC_PROF_NLABELS][2];
-  int used[SPEC_PROF_NLABELS] = {0, 0, 0, 0};
+  int used[SPEC_PROF_NLABELS] = {};
 };
 
 namespace {
@@ -518,7 +518,7 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
       // tiled LM head writing per-strip (max, sum exp) records; the top-k
       // rescans only the k best strips of each row
       {
-        ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
+        ProfScope ps(ctx, SPEC_PROF_LM_HEAD_TILED, s);
         SPEC_HIP(ctx, gemm_tile_records(ws.nrm, H, w->lm_head, H, z, M, Vd, H, ws.topk_part, s));
       }
       ProfScope ps(ctx, SPEC_PROF_TOPK, s);

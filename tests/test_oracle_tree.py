@@ -343,3 +343,52 @@ def test_root_pass_over_new_rows_equals_sequential_single_rows():
                                        tree["score"][b, n] + (z2[top2] - logsumexp(z2)), atol=3e-5)
             for m in kids:
                 assert tree["position"][b, m] == c + n_new + 1 and tree["draft_slot"][b, m] == -1
+
+
+# ----------------------------------------- draft logits of every tree node
+def test_node_draft_logits_of_a_chain_equal_the_next_pass():
+    """The last node of a depth-D chain was never expanded; its logits (one
+    extra recurrent pass at its position, on its parent's state) equal the
+    logits of pass D + 1 of the depth-(D+1) chain built from the same inputs,
+    where the node is run by the tree construction itself.  Expanded nodes
+    carry the logits their children were ranked by."""
+    D = 3
+    cfg = _tiny_tree_cfg(top_k=1, depth=D, total_tokens=D, dtype="f32", batch=2)
+    cfg2 = _tiny_tree_cfg(top_k=1, depth=D + 1, total_tokens=D + 1, dtype="f32", batch=2)
+    W = gen.make_weights(cfg, 34)
+    inp = gen.make_step_inputs(cfg2, 34)
+    rec, rec2 = [], []
+    kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
+    tree = ot.build_tree(cfg, W, kc, vc, inp["aux"], inp["in_tokens"], inp["ctx_len"], record=rec)
+    z = ot.node_draft_logits(cfg, W, kc, vc, inp["ctx_len"], tree, rec)
+    ot.build_tree(cfg2, W, inp["k_cache"].copy(), inp["v_cache"].copy(), inp["aux"], inp["in_tokens"],
+                  inp["ctx_len"], record=rec2)
+    for b in range(2):
+        for n in range(D):  # expanded nodes: the argmax of row n is node n + 1
+            assert int(np.argmax(z[b, n])) == tree["tokens"][b, n + 1]
+            np.testing.assert_array_equal(z[b, n], rec[n][1]["logits"][b])
+        np.testing.assert_allclose(z[b, D], rec2[D][1]["logits"][b], rtol=0, atol=1e-5)
+
+
+def test_node_draft_logits_of_a_tree():
+    """In a tree, every node with children ranks them as the top-k of its
+    row; rows of unused nodes are zero; never-expanded nodes get finite rows
+    whose values differ from their parent's."""
+    cfg = _tiny_tree_cfg(top_k=3, depth=3, total_tokens=9, batch=2)
+    W = gen.make_weights(cfg, 35)
+    inp = gen.make_step_inputs(cfg, 35)
+    rec = []
+    kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
+    tree = ot.build_tree(cfg, W, kc, vc, inp["aux"], inp["in_tokens"], inp["ctx_len"], record=rec)
+    z = ot.node_draft_logits(cfg, W, kc, vc, inp["ctx_len"], tree, rec)
+    for b in range(2):
+        nn = int(tree["num_nodes"][b])
+        for n in range(nn + 1):
+            kids = [m for m in range(1, nn + 1) if tree["parent"][b, m] == n]
+            top = np.argsort(-z[b, n].astype(np.float64), kind="stable")[:3].tolist()
+            for m in kids:
+                assert tree["tokens"][b, m] in top
+            assert np.isfinite(z[b, n]).all() and np.abs(z[b, n]).max() > 0
+            if n:
+                assert not np.array_equal(z[b, n], z[b, tree["parent"][b, n]])
+        assert not z[b, nn + 1:].any()
