@@ -596,7 +596,9 @@ def bench_target_forward(args):
     from speculative_decoding_aux_amd.tensors import to_device, upload_target_weights
     from synth import configs, gen
 
-    cfg = configs.get(args.config)
+    # the target has the workload's dimensions and its full vocabulary head
+    cfg = configs.get(args.config, cand_rank=0, num_candidates=0, sliding_window=0)
+    cfg["draft_vocab"] = cfg["vocab"]
     Lr, B, N, dt = args.target_forward, cfg["batch"], cfg["total_tokens"], cfg["dtype"]
     n1 = N + 1
     seed = configs.SEEDS[args.config] + 600

@@ -67,8 +67,9 @@ typedef struct spec_ctx spec_ctx;
 
 /* Shapes of the draft and of the tree; copied by spec_create.
  * Limits: head_dim in {64, 128}; n_q_heads a multiple of n_kv_heads with
- * n_q_heads/n_kv_heads * max(top_k, max_new) <= 64; top_k <= 16;
- * total_tokens + 1 <= 64; depth <= total_tokens; max_new + depth <= 64;
+ * n_q_heads/n_kv_heads <= 32 (bf16) / 64 (f32); top_k <= 16; max_new <= 64;
+ * total_tokens + 1 <= 64; depth <= total_tokens (spec_build_tree further
+ * needs n_new + depth <= 64);
  * hidden, intermediate, n_q_heads*head_dim and cand_rank multiples of 32 for
  * bf16 (of 4 for f32); hidden <= 8192 (bf16) / 4096 (f32);
  * top_k <= num_candidates <= 256 when cand_rank > 0. */
@@ -369,7 +370,9 @@ typedef struct spec_target_weights {
  * norm and the LM head.
  * The context's config gives the target's shapes (vocab = draft_vocab = V,
  * sliding_window 0) and the tree (total_tokens N, depth); it must be created
- * with max_new >= N + 1 (rows per sequence of the forward).
+ * with max_new >= N + 1 (rows per sequence of the forward) and kv_capacity
+ * >= the target cache's slots.  Any tree of up to 64 nodes is served (the
+ * attention takes the nodes' query vectors in groups of rows).
  * Outputs: logits [B, N+1, V] float32 (the verify step's target logits) and
  * aux_hidden [B, N+1, 3H] in the storage type (low | mid | high). */
 spec_status spec_target_forward(spec_ctx* ctx, const spec_target_weights* w,

@@ -233,14 +233,15 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
                                                        const T* __restrict__ vc, int64_t sseq,
                                                        int64_t shead, int S, KvPages pg,
                                                        const int* __restrict__ ctx_len,
-                                                       const int* __restrict__ pos, int R, int nq,
-                                                       int nkv, int window, int chunk,
-                                                       float* __restrict__ part) {
+                                                       const int* __restrict__ pos, int R, int r0,
+                                                       int Rg, int nq, int nkv, int window,
+                                                       int chunk, float* __restrict__ part) {
   extern __shared__ float smem[];
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int nch = gridDim.x;
   const int G = nq / nkv;
-  const int QV = R * G;
+  // rows r0 .. r0 + Rg - 1 of each sequence (see attn_ctx_mfma_kernel)
+  const int QV = Rg * G, QVF = R * G;
   float* qs = smem;                  // [QV][HD]
   float* sc = qs + QV * HD;          // [QV][kTile]
   float* mrow = sc + QV * kTile;     // [QV]
@@ -259,13 +260,13 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
 
   for (int i = threadIdx.x; i < QV * HD; i += blockDim.x) {
     const int qv = i / HD, d = i % HD;
-    const int r = qv / G, h = kvh * G + qv % G;
+    const int r = r0 + qv / G, h = kvh * G + qv % G;
     qs[i] = St<T>::load(q, ((int64_t)(b * R + r) * nq + h) * HD + d);
   }
   for (int i = threadIdx.x; i < QV; i += blockDim.x) {
     mrow[i] = -INFINITY;
     lrow[i] = 0.f;
-    lo[i] = window > 0 ? max(0, pos[b * R + i / G] - window + 1) : 0;
+    lo[i] = window > 0 ? max(0, pos[b * R + r0 + i / G] - window + 1) : 0;
   }
   __syncthreads();
 
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
     __syncthreads();
   }
   // partial record per query vector: O[HD], m, l
-  float* pb = part + (((int64_t)(b * nkv + kvh) * nch + c) * QV) * (HD + 2);
+  float* pb = part + (((int64_t)(b * nkv + kvh) * nch + c) * QVF + r0 * G) * (HD + 2);
 #pragma unroll
   for (int j = 0; j < (64 + NG - 1) / NG; ++j) {
     const int qv = grp + j * NG;
@@ -387,7 +388,7 @@ template <int HD, int QT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_ctx_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     int64_t sseq, int64_t shead, int S, KvPages pg, const int* __restrict__ ctx_len,
-    const int* __restrict__ pos, int R, int nq, int nkv, int window, int chunk,
+    const int* __restrict__ pos, int R, int r0, int Rg, int nq, int nkv, int window, int chunk,
     float* __restrict__ part) {
   constexpr int DS = HD / 32;        // 32-dim steps of S^T
   constexpr int DT = HD / 16;        // 16-dim tiles of O^T
@@ -409,7 +410,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   __shared__ int ptab[kAttnMaxChunkPages];
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int nch = gridDim.x;
-  const int G = nq / nkv, QV = R * G;
+  // this launch's query vectors: rows r0 .. r0 + Rg - 1 of each sequence
+  // (local index qv = (r - r0) * G + head), recorded at r * G + head of the
+  // R * G vectors of the sequence
+  const int G = nq / nkv, QV = Rg * G, QVF = R * G;
   const int lane = threadIdx.x & 63, g = lane >> 4, col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // scores in log2 units (x * log2 e / sqrt(hd)), so the softmax uses the
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   for (int t = 0; t < QT; ++t) {
     const int qv = t * 16 + col;
     const bool ok = qv < QV;
-    const int r = ok ? qv / G : 0, h = kvh * G + (ok ? qv % G : 0);
+    const int r = r0 + (ok ? qv / G : 0), h = kvh * G + (ok ? qv % G : 0);
     if (wave == 0) {
       const bf16_t* qp = q + ((int64_t)(b * R + r) * nq + h) * HD + g * 8;
 #pragma unroll
@@ -638,7 +642,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     __syncthreads();
   }
   if (wave == 0) {
-    float* pb = part + (((int64_t)(b * nkv + kvh) * nch + c) * QV) * (HD + 2);
+    float* pb = part + (((int64_t)(b * nkv + kvh) * nch + c) * QVF + r0 * G) * (HD + 2);
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const int qv = t * 16 + col;
@@ -659,26 +663,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 template <typename T, int HD>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int G = a.nq / a.nkv;
-  const int QV = a.R * G;
   const dim3 grid(a.nchunks, a.nkv, a.B);
-  if (std::is_same<T, bf16_t>::value && QV <= 32) {
-    if (QV <= 16) {
+  // query vectors go in groups of rows: up to 32 vectors per launch on the
+  // bf16 MFMA path (two 16-vector tiles), 64 on the scalar path; each group
+  // streams the context chunk again, so one group is the common case (the
+  // draft's beam rows) and several only serve large trees (the target's
+  // verification forward)
+  const bool mfma = std::is_same<T, bf16_t>::value;
+  const int rg = std::max(1, (mfma ? 32 : 64) / G);
+  for (int r0 = 0; r0 < a.R; r0 += rg) {
+    const int Rg = std::min(rg, a.R - r0);
+    const int QV = Rg * G;
+    if (mfma && QV <= 16) {
       SPEC_LAUNCH((attn_ctx_mfma_kernel<HD, 1>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
-                         (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq,
-                         a.kv.stride_head, a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
-                         a.window, a.chunk, a.part);
-    } else {
+                  (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
+                  a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, r0, Rg, a.nq, a.nkv, a.window,
+                  a.chunk, a.part);
+    } else if (mfma) {
       SPEC_LAUNCH((attn_ctx_mfma_kernel<HD, 2>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
-                         (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq,
-                         a.kv.stride_head, a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, a.nq, a.nkv,
-                         a.window, a.chunk, a.part);
+                  (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
+                  a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, r0, Rg, a.nq, a.nkv, a.window,
+                  a.chunk, a.part);
+    } else {
+      const size_t lds = (size_t)QV * (HD + kTile + 3) * sizeof(float) + QV * sizeof(int);
+      SPEC_LAUNCH((attn_ctx_kernel<T, HD>), grid, dim3(256), lds, s, (const T*)a.q,
+                  (const T*)a.kv.k, (const T*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
+                  a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, r0, Rg, a.nq, a.nkv, a.window,
+                  a.chunk, a.part);
     }
-  } else {
-    const size_t lds = (size_t)QV * (HD + kTile + 3) * sizeof(float) + QV * sizeof(int);
-    SPEC_LAUNCH((attn_ctx_kernel<T, HD>), grid, dim3(256), lds, s, (const T*)a.q,
-                       (const T*)a.kv.k, (const T*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
-                       a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, a.nq, a.nkv, a.window, a.chunk,
-                       a.part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -166,9 +166,9 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
   const int r_max = std::max(c.max_new, c.top_k);
   const int kmul = bf16 ? 32 : 4;
   if ((c.head_dim != 64 && c.head_dim != 128) || c.top_k > 16 || c.total_tokens + 1 > 64 ||
-      c.depth > c.total_tokens || G * r_max > 64 || c.hidden % kmul ||
-      c.intermediate % kmul || (c.n_q_heads * c.head_dim) % kmul ||
-      c.max_new + c.depth > 64 || c.hidden > (bf16 ? 8192 : 4096))
+      c.depth > c.total_tokens || G > (bf16 ? 32 : 64) || r_max > 64 || c.hidden % kmul ||
+      c.intermediate % kmul || (c.n_q_heads * c.head_dim) % kmul || c.max_new > 64 ||
+      c.hidden > (bf16 ? 8192 : 4096))
     return SPEC_EUNSUPPORTED;
   if (c.cand_rank) {
     if (c.cand_rank % kmul || c.num_candidates <= 0 || c.num_candidates > 256 ||
@@ -720,6 +720,8 @@ spec_status spec_build_tree(spec_ctx* ctx, const spec_weights* w, const spec_kv*
   const spec_config& c = ctx->cfg;
   SPEC_REQ(ctx, B > 0 && B <= c.max_batch && n_new > 0 && n_new <= c.max_new, SPEC_EINVAL,
            "bad B or n_new");
+  SPEC_REQ(ctx, n_new + c.depth <= 64, SPEC_EUNSUPPORTED,
+           "n_new + depth = %d above 64 (extra keys per row)", n_new + c.depth);
   SPEC_REQ(ctx, draft_kv->slots >= c.kv_capacity, SPEC_EINVAL, "draft KV has fewer slots than kv_capacity");
   SPEC_REQ(ctx, aux_hidden && aligned16(aux_hidden) && in_tokens && ctx_len, SPEC_EINVAL,
            "null or misaligned argument");

@@ -6,7 +6,8 @@ within the activation tolerance of the draft tests, greedy verification
 with the GPU's logits equal to verification with the oracle's wherever the
 oracle's argmax gaps exceed the tolerance.  Chains (also deeper than the
 config's draft depth) and random trees, float32 and bf16, 8 layers (aux
-layers 2, 4, 5)."""
+layers 2, 4, 5); trees and chains of 32 and 64 nodes with 4 q-heads per
+kv-head (more query vectors than one attention launch takes)."""
 
 import numpy as np
 import pytest
@@ -33,6 +34,17 @@ CASES = {
     "deep_chain_f32": (dict(BASE, dtype="f32", top_k=4, depth=3, total_tokens=16), "chain", 1e-4),
     "tree_bf16_hd128": (dict(BASE, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128, top_k=2,
                              depth=4, total_tokens=7), "tree", 2e-2),
+    # the verified trees of the Qwen3-4B (1 + 31 nodes) and Qwen3-8B (1 + 63
+    # nodes) workloads with 4 q-heads per kv-head: 128 and 256 query vectors
+    # per kv-head, taken by the attention in groups of rows
+    "tree31_gqa4_bf16": (dict(BASE, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128, top_k=8,
+                              depth=5, total_tokens=31), "tree", 2e-2),
+    "tree63_gqa4_bf16": (dict(BASE, dtype="bf16", n_q_heads=8, n_kv_heads=2, head_dim=128, top_k=8,
+                              depth=7, total_tokens=63, batch=2), "tree", 2e-2),
+    "tree31_gqa4_f32": (dict(BASE, dtype="f32", n_q_heads=8, n_kv_heads=2, top_k=8, depth=5,
+                             total_tokens=31, batch=2), "tree", 1e-4),
+    "chain63_gqa4_bf16": (dict(BASE, dtype="bf16", n_q_heads=8, n_kv_heads=2, top_k=8, depth=7,
+                               total_tokens=63, batch=2), "chain", 2e-2),
 }
 
 
