@@ -230,6 +230,19 @@ spec_status spec_tree_from_topk(spec_ctx* ctx, int32_t B, int32_t n_new, const i
                                 const int32_t* ctx_len, const int32_t* topk_ids,
                                 const float* topk_logp, spec_tree* out, void* stream);
 
+/* The candidate table that the last spec_build_tree (or spec_tree_from_topk)
+ * call left in the context: the candidates the tree of total_draft_tokens is
+ * selected from ("Eaglet", "Approach 1: YAML Recipe").  For sequence b and
+ * candidate c, in append order (depth by depth, beam node by beam node,
+ * child rank by child rank): tokens[b, c] (target ids), parent[b, c]
+ * (candidate index of the parent, -1 at depth 1), slot[b, c] (the draft-KV
+ * slot of a candidate that was expanded, else -1) and score[b, c]
+ * (cumulative log-prob).  Arrays are [B, C] with C = top_k + (depth - 1) *
+ * top_k^2; entries of sequences past the capacity cutoff are unspecified.
+ * Device-to-device copies, asynchronous on stream. */
+spec_status spec_tree_candidates(spec_ctx* ctx, int32_t B, int32_t* tokens, int32_t* parent,
+                                 int32_t* slot, float* score, void* stream);
+
 /* Draft side of one step for B sequences ("Eaglet": tree of draft_top_k,
  * draft_depth, total_draft_tokens; vLLM Neuron page, "The propose() Method").
  *   aux_hidden[B, n_new, 3H]: concatenated aux states of the new rows;

@@ -71,12 +71,20 @@ def _ancestor_slots(cands, ci):
     return out[::-1]
 
 
-def build_tree_core(cfg, B, n_new, ctx_len, in_tokens, pass_fn):
+def build_tree_core(cfg, B, n_new, ctx_len, in_tokens, pass_fn, choose=None):
     """Tree construction with a pluggable draft.
 
     ``pass_fn(d, rows)`` runs draft pass d (1 = root) over ``rows`` (dicts with
     b, token, pos, slot, anc, src, cand, rank, i, path) and returns one
-    (ids[k], logp[k]) pair per row, ids in the target vocabulary."""
+    (ids[k], logp[k]) pair per row, ids in the target vocabulary.
+
+    ``choose(kind, b, depth, ranked, C)``, if given, may replace a ranking
+    decision: kind "beam" (the beam of depth ``depth``, the first k of
+    ``ranked``) or "select" (the tree, the first N of ``ranked``); ``ranked``
+    lists candidate indices by (score desc, index asc) and ``C`` is the
+    sequence's candidate list.  It returns the chosen indices (a test that
+    replays another implementation's choices at near-ties uses it); without
+    it the rule above applies."""
     k, D, N = cfg["top_k"], cfg["depth"], cfg["total_tokens"]
     cap = cfg["kv_capacity"]
     ctx_len = np.asarray(ctx_len)
@@ -105,7 +113,8 @@ def build_tree_core(cfg, B, n_new, ctx_len, in_tokens, pass_fn):
             c0 = int(ctx_len[b])
             C = cands[b]
             pool = [ci for ci, c in enumerate(C) if c["depth"] == d - 1]
-            beam = sorted(pool, key=lambda ci: (-float(C[ci]["score"]), ci))[:k]
+            ranked = sorted(pool, key=lambda ci: (-float(C[ci]["score"]), ci))
+            beam = ranked[:k] if choose is None else choose("beam", b, d - 1, ranked, C)
             for j, ci in enumerate(beam):
                 C[ci]["slot"] = c0 + n_new + (d - 2) * k + j
                 anc = [c0 + i for i in range(n_new)] + _ancestor_slots(C, ci) + [C[ci]["slot"]]
@@ -145,7 +154,8 @@ def build_tree_core(cfg, B, n_new, ctx_len, in_tokens, pass_fn):
             continue
         tree["draft_slot"][b, 0] = c0 + n_new - 1
         C = cands[b]
-        best = sorted(range(len(C)), key=lambda ci: (-float(C[ci]["score"]), ci))[:N]
+        ranked = sorted(range(len(C)), key=lambda ci: (-float(C[ci]["score"]), ci))
+        best = ranked[:N] if choose is None else choose("select", b, D, ranked, C)
         sel = sorted(best)
         node_of = {ci: n + 1 for n, ci in enumerate(sel)}
         tree["num_nodes"][b] = len(sel)
@@ -164,11 +174,13 @@ def build_tree_core(cfg, B, n_new, ctx_len, in_tokens, pass_fn):
     return tree
 
 
-def model_pass_fn(cfg, W, kcache, vcache, aux, ctx_len, record=None):
+def model_pass_fn(cfg, W, kcache, vcache, aux, ctx_len, record=None, topk_fn=None):
     """The draft model as a pass function for build_tree_core.
 
     ``record``, if given, is a list that receives each pass's rows and output
-    dict (for tests that compare stage by stage)."""
+    dict (for tests that compare stage by stage).  ``topk_fn(d, row, z, ids,
+    lp)``, if given, may replace a row's top-k (ids in the target vocabulary,
+    log-probs) given its logits z over the head's rows (EAGLE-3 heads)."""
     k = cfg["top_k"]
     d2t = W.get("d2t")
     state = {}
@@ -197,19 +209,24 @@ def model_pass_fn(cfg, W, kcache, vcache, aux, ctx_len, record=None):
             else:
                 pos, lp = topk_logprobs(out["logits"][i], k)
                 ids = d2t[pos] if d2t is not None else pos
+                if topk_fn is not None:
+                    ids, lp = topk_fn(d, rows[i], out["logits"][i], ids, lp)
             res.append((np.asarray(ids, np.int64), lp))
         return res
 
     return fn
 
 
-def build_tree(cfg, W, kcache, vcache, aux, in_tokens, ctx_len, record=None):
+def build_tree(cfg, W, kcache, vcache, aux, in_tokens, ctx_len, record=None, topk_fn=None,
+               choose=None):
     """Full draft side of one speculation step: root pass, D-1 expansions and
-    the final selection.  kcache/vcache are updated in place."""
+    the final selection.  kcache/vcache are updated in place.  ``topk_fn``
+    and ``choose`` are the decision hooks of model_pass_fn and
+    build_tree_core (identity when None)."""
     in_tokens = np.asarray(in_tokens)
     B, n_new = in_tokens.shape
-    fn = model_pass_fn(cfg, W, kcache, vcache, aux, ctx_len, record)
-    return build_tree_core(cfg, B, n_new, ctx_len, in_tokens, fn)
+    fn = model_pass_fn(cfg, W, kcache, vcache, aux, ctx_len, record, topk_fn)
+    return build_tree_core(cfg, B, n_new, ctx_len, in_tokens, fn, choose)
 
 
 def table_pass_fn(ids_tab, lp_tab):

@@ -55,7 +55,7 @@ class SpecTargetWeights(ctypes.Structure):
 
 
 EXPORTS = ["spec_create", "spec_destroy", "spec_last_error", "spec_workspace_bytes", "spec_version",
-           "spec_draft_step", "spec_topk_logprobs", "spec_retrieve_candidates", "spec_tree_from_topk", "spec_build_tree",
+           "spec_draft_step", "spec_topk_logprobs", "spec_retrieve_candidates", "spec_tree_from_topk", "spec_tree_candidates", "spec_build_tree",
            "spec_verify_tree", "spec_verify_tree_static", "spec_compact_kv", "spec_decode_metadata", "spec_rejection_sample",
            "spec_target_forward",
            "spec_profile_enable", "spec_profile_read"]
@@ -94,6 +94,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_retrieve_candidates.restype = c_i32
     lib.spec_tree_from_topk.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, P(SpecTree), c_vp]
     lib.spec_tree_from_topk.restype = c_i32
+    lib.spec_tree_candidates.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.spec_tree_candidates.restype = c_i32
     lib.spec_build_tree.argtypes = [c_vp, P(SpecWeights), P(SpecKV), c_i32, c_i32, c_vp, c_vp, c_vp,
                                     P(SpecTree), c_vp]
     lib.spec_build_tree.restype = c_i32

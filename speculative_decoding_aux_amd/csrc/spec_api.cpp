@@ -706,6 +706,22 @@ spec_status spec_tree_from_topk(spec_ctx* ctx, int32_t B, int32_t n_new, const i
   return SPEC_OK;
 }
 
+spec_status spec_tree_candidates(spec_ctx* ctx, int32_t B, int32_t* tokens, int32_t* parent,
+                                 int32_t* slot, float* score, void* stream) {
+  if (!ctx) return SPEC_EINVAL;
+  const spec_config& c = ctx->cfg;
+  SPEC_REQ(ctx, B > 0 && B <= c.max_batch, SPEC_EINVAL, "bad B");
+  SPEC_REQ(ctx, tokens && parent && slot && score, SPEC_EINVAL, "null argument");
+  Workspace& w = ctx->ws;
+  hipStream_t s = STREAM(stream);
+  const size_t n = (size_t)B * ctx->cmax * 4;  // [B, C] rows, contiguous in the workspace
+  SPEC_HIP(ctx, hipMemcpyAsync(tokens, w.tr_tok, n, hipMemcpyDeviceToDevice, s));
+  SPEC_HIP(ctx, hipMemcpyAsync(parent, w.tr_par, n, hipMemcpyDeviceToDevice, s));
+  SPEC_HIP(ctx, hipMemcpyAsync(slot, w.tr_slot, n, hipMemcpyDeviceToDevice, s));
+  SPEC_HIP(ctx, hipMemcpyAsync(score, w.tr_score, n, hipMemcpyDeviceToDevice, s));
+  return SPEC_OK;
+}
+
 spec_status spec_build_tree(spec_ctx* ctx, const spec_weights* w, const spec_kv* draft_kv,
                             int32_t B, int32_t n_new, const void* aux_hidden,
                             const int32_t* in_tokens, const int32_t* ctx_len, spec_tree* out,

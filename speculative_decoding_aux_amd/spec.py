@@ -190,6 +190,20 @@ def spec_retrieve_candidates(ctx: SpecContext, scores: torch.Tensor, K: int):
     return ids
 
 
+def spec_tree_candidates(ctx: SpecContext, B: int) -> dict:
+    """The candidate table of the context's last tree build: tokens, parent,
+    slot and score, each [B, C] (C = top_k + (depth - 1) * top_k^2)."""
+    cfg, dev = ctx.cfg, ctx.device
+    k, D = cfg["top_k"], cfg["depth"]
+    C = k + (D - 1) * k * k
+    out = {f: torch.empty(B, C, dtype=torch.int32, device=dev) for f in ("tokens", "parent", "slot")}
+    out["score"] = torch.empty(B, C, dtype=torch.float32, device=dev)
+    st = ctx.lib.spec_tree_candidates(ctx.h, B, _p(out["tokens"]), _p(out["parent"]), _p(out["slot"]),
+                                      _p(out["score"]), _stream())
+    ctx._check(st)
+    return out
+
+
 def spec_tree_from_topk(ctx: SpecContext, B, n_new, in_tokens, ctx_len, ids_tab, lp_tab) -> Tree:
     dev = ctx.device
     tree = Tree(B, ctx.cfg["total_tokens"] + 1, dev)
