@@ -226,8 +226,11 @@ SPEC_DEV void for_row_batches(const float* __restrict__ row, int lo, int hi, F&&
 }
 
 // Online (max m, sum s of exp(v - m)) update with a batch of 16 values:
-// one rescale per batch at most; the batch's terms are summed in float64.
+// one rescale per batch at most.  Each term is exp2((v - m) log2 e) (the
+// difference taken first, so the batch maximum's term is exactly 1); the 16
+// terms are summed in float32 and the batch sum is added in float64.
 SPEC_DEV void lse_update16(const float (&v)[16], float& m, double& s) {
+  constexpr float kL2e = 1.4426950408889634f;
   float bm = v[0];
 #pragma unroll
   for (int e = 1; e < 16; ++e) bm = fmaxf(bm, v[e]);
@@ -236,8 +239,8 @@ SPEC_DEV void lse_update16(const float (&v)[16], float& m, double& s) {
     s = m == -INFINITY ? 0.0 : s * exp((double)m - (double)bm);
     m = bm;
   }
-  double a = 0.0;
+  float a = 0.f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) a += (double)expf(v[e] - m);
-  s += a;
+  for (int e = 0; e < 16; ++e) a += __builtin_amdgcn_exp2f((v[e] - m) * kL2e);
+  s += (double)a;
 }

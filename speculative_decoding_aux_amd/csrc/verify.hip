@@ -209,22 +209,30 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
         if (p.m != -INFINITY) z += p.z * exp((double)p.m - (double)m);
       }
       z = wave_sum(z);
-      // children in node order, tested one after another
-      double zrem = 1.0;
-      int ord = 0;
-      for (int x = 1; x <= nn && next < 0; ++x) {
-        if (pr[x] != cur) continue;
-        const int tok = clampi(tk[x], 0, V - 1);
+      // each child's probability and uniform, loaded by its own lane (node
+      // lane + 1; its rank among the children in node order picks the
+      // uniform); then the children are tested one after another
+      const unsigned long long kids = __ballot(xl <= nn && prl == cur);
+      double p = 0.0;
+      float u = 0.f;
+      if ((kids >> lane) & 1) {
+        const int tok = clampi(tkl, 0, V - 1);
         const float l = logits[(int64_t)(b * n1 + cur) * V + tok];
         const float zv = temp == 1.0f ? l : l * (1.0f / temp);
-        const double p = exp((double)zv - (double)m) / z;
-        const float u = accept_u[((int64_t)(b * n1 + cur)) * k + min(ord, k - 1)];
-        if ((double)u <= p / zrem) {
-          next = x;
+        p = exp((double)zv - (double)m) / z;
+        const int ord = __popcll(kids & ((1ull << lane) - 1));
+        u = accept_u[((int64_t)(b * n1 + cur)) * k + min(ord, k - 1)];
+      }
+      double zrem = 1.0;
+      for (unsigned long long rem = kids; rem && next < 0; rem &= rem - 1) {
+        const int i = __ffsll((long long)rem) - 1;
+        const double pi = __shfl(p, i, 64);
+        const float ui = __shfl(u, i, 64);
+        if ((double)ui <= pi / zrem) {
+          next = i + 1;
         } else {
-          zrem -= p;
+          zrem -= pi;
         }
-        ++ord;
       }
     }
     if (next < 0 || depth >= D) break;
@@ -257,11 +265,12 @@ __global__ __launch_bounds__(256) void verify_gumbel_kernel(
   const int nn = min(num_nodes[b], N);
   const int n = clampi(stop[b], 0, N);
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  if (t == 0) {
-    int cnt = 0;
-    for (int x = 1; x <= nn && cnt < 64; ++x)
-      if (parent[(int64_t)b * n1 + x] == n) kids[cnt++] = tokens[(int64_t)b * n1 + x];
-    nkids = cnt;
+  if (t < 64) {  // node t + 1 (nn <= 63): one load per lane, children compacted in node order
+    const int x = t + 1;
+    const bool kid = x <= nn && parent[(int64_t)b * n1 + x] == n;
+    const unsigned long long bal = __ballot(kid);
+    if (kid) kids[__popcll(bal & ((1ull << t) - 1))] = tokens[(int64_t)b * n1 + x];
+    if (t == 0) nkids = __popcll(bal);
   }
   __syncthreads();
   const int nk = nkids;
