@@ -42,15 +42,28 @@ __global__ void root_setup_kernel(int B, int n_new, const int* __restrict__ in_t
 }
 
 // Tree step of sequence b after pass d, by a 256-thread block (every thread
-// calls it).  Dynamic LDS: (2 cmax + 256) ints.
+// calls it).  The sequence's candidate arrays are mirrored in LDS for the
+// step (one coalesced read of the candidates so far), so the ancestor walks
+// and the ranking read LDS, not dependent global loads; every global write
+// goes to the mirror too.  Dynamic LDS: expand_lds_ints(cmax) ints.
 SPEC_DEV void expand_seq(int b, int d, int n_new, const int* __restrict__ ctx_len,
                          const int* __restrict__ in_tokens, int k, int D, int N,
                          const int* __restrict__ ids, const float* __restrict__ logp, int ld,
                          int root_stride, int root_off, TreeState st, int* __restrict__ beam,
                          PassRows nx, TreeOut out) {
-  extern __shared__ int sh[];  // node_of[cmax] | counts[256] | scores[cmax]
+  extern __shared__ int sh[];
   const int t = threadIdx.x;
   const int cmax = st.cmax;
+  // node_of | counts[256] | scores | parent, slot, token, source, score mirrors | beam[64]
+  int* node_of = sh;
+  int* counts = sh + cmax;
+  float* ss = (float*)(sh + cmax + 256);
+  int* lpar = sh + 2 * cmax + 256;
+  int* lslot = lpar + cmax;
+  int* ltok = lslot + cmax;
+  int* lsrc = ltok + cmax;
+  float* lsc = (float*)(lsrc + cmax);
+  int* lbm = (int*)(lsc + cmax);
   int* ctok = st.tok + (int64_t)b * cmax;
   int* cpar = st.parent + (int64_t)b * cmax;
   int* cslot = st.slot + (int64_t)b * cmax;
@@ -62,27 +75,43 @@ SPEC_DEV void expand_seq(int b, int d, int n_new, const int* __restrict__ ctx_le
   const int K2 = k * k;
 
   if (act) {
+    // 0. mirror the candidates of passes 1 .. d-1 and the current beam
+    const int have = d == 1 ? 0 : k + (d - 2) * K2;
+    for (int x = t; x < have; x += blockDim.x) {
+      lpar[x] = cpar[x];
+      lslot[x] = cslot[x];
+      ltok[x] = ctok[x];
+      lsrc[x] = csrc[x];
+      lsc[x] = csc[x];
+    }
+    if (d > 1)
+      for (int j = t; j < k; j += blockDim.x) lbm[j] = bm[j];
+    __syncthreads();
     // 1. append the children produced by pass d
     if (d == 1) {
       const int row = b * root_stride + root_off;
       if (t < k) {
-        ctok[t] = ids[(int64_t)row * ld + t];
-        cpar[t] = -1;
-        cslot[t] = -1;
-        csrc[t] = row;
-        csc[t] = logp[(int64_t)row * ld + t];
+        const int tk = ids[(int64_t)row * ld + t];
+        const float sc = logp[(int64_t)row * ld + t];
+        ctok[t] = ltok[t] = tk;
+        cpar[t] = lpar[t] = -1;
+        cslot[t] = lslot[t] = -1;
+        csrc[t] = lsrc[t] = row;
+        csc[t] = lsc[t] = sc;
       }
     } else {
-      const int base = k + (d - 2) * K2;
       for (int x = t; x < K2; x += blockDim.x) {
         const int jb = x / k, jc = x % k;
         const int row = b * k + jb;
-        const int p = bm[jb];
-        ctok[base + x] = ids[(int64_t)row * ld + jc];
-        cpar[base + x] = p;
-        cslot[base + x] = -1;
-        csrc[base + x] = row;
-        csc[base + x] = csc[p] + logp[(int64_t)row * ld + jc];
+        const int p = lbm[jb];
+        const int c = have + x;
+        const int tk = ids[(int64_t)row * ld + jc];
+        const float sc = lsc[p] + logp[(int64_t)row * ld + jc];
+        ctok[c] = ltok[c] = tk;
+        cpar[c] = lpar[c] = p;
+        cslot[c] = lslot[c] = -1;
+        csrc[c] = lsrc[c] = row;
+        csc[c] = lsc[c] = sc;
       }
     }
     __syncthreads();
@@ -93,14 +122,13 @@ SPEC_DEV void expand_seq(int b, int d, int n_new, const int* __restrict__ ctx_le
     const int lo = d == 1 ? 0 : k + (d - 2) * K2;
     const int cnt = d == 1 ? k : K2;
     if (act) {
-      float* ss = (float*)(sh + cmax + 256);
-      for (int x = t; x < cnt; x += blockDim.x) ss[x] = csc[lo + x];
+      for (int x = t; x < cnt; x += blockDim.x) ss[x] = lsc[lo + x];
       __syncthreads();
       for (int x = t; x < cnt; x += blockDim.x) {
         const float sc = ss[x];
         int rank = 0;
         for (int y = 0; y < cnt; ++y) rank += better(ss[y], y, sc, x) ? 1 : 0;
-        if (rank < k) bm[rank] = lo + x;
+        if (rank < k) bm[rank] = lbm[rank] = lo + x;
       }
       __syncthreads();
     }
@@ -108,16 +136,16 @@ SPEC_DEV void expand_seq(int b, int d, int n_new, const int* __restrict__ ctx_le
       const int r = b * k + j;
       nx.pos[r] = ctx + n_new - 1 + d;
       if (act) {
-        const int c = bm[j];
+        const int c = lbm[j];
         const int sl = ctx + n_new + (d - 1) * k + j;
-        cslot[c] = sl;
-        nx.tok[r] = ctok[c];
+        cslot[c] = sl;  // the mirror is not read again in this step
+        nx.tok[r] = ltok[c];
         nx.slot[r] = sl;
-        nx.src[r] = csrc[c];
+        nx.src[r] = lsrc[c];
         int* a = nx.anc + (int64_t)r * nx.A;
         for (int i = 0; i < n_new; ++i) a[i] = ctx + i;
         // ancestors of a depth-d candidate sit at depths 1 .. d-1, then itself
-        for (int p = cpar[c]; p >= 0; p = cpar[p]) a[n_new + cand_depth(p, k) - 1] = cslot[p];
+        for (int p = lpar[c]; p >= 0; p = lpar[p]) a[n_new + cand_depth(p, k) - 1] = lslot[p];
         a[n_new + d - 1] = sl;
         int na = n_new + d;
         for (; na < nx.A; ++na) a[na] = -1;
@@ -135,10 +163,7 @@ SPEC_DEV void expand_seq(int b, int d, int n_new, const int* __restrict__ ctx_le
   // 3. final selection (d == D)
   const int n1 = N + 1;
   const int ncand = act ? k + (D - 1) * K2 : 0;
-  int* node_of = sh;
-  int* counts = sh + cmax;
-  float* ss = (float*)(sh + cmax + 256);
-  for (int c = t; c < ncand; c += blockDim.x) ss[c] = csc[c];
+  for (int c = t; c < ncand; c += blockDim.x) ss[c] = lsc[c];
   __syncthreads();
   for (int c = t; c < ncand; c += blockDim.x) {
     const float sc = ss[c];
@@ -194,16 +219,16 @@ SPEC_DEV void expand_seq(int b, int d, int n_new, const int* __restrict__ ctx_le
   for (int c = t; c < ncand; c += blockDim.x) {
     const int n = node_of[c];
     if (n < 0) continue;
-    const int pc = cpar[c];
+    const int pc = lpar[c];
     const int dep = cand_depth(c, k);
-    out.tokens[ob + n] = ctok[c];
+    out.tokens[ob + n] = ltok[c];
     out.parent[ob + n] = pc < 0 ? 0 : node_of[pc];
     out.depth[ob + n] = dep;
     out.position[ob + n] = ctx + n_new - 1 + dep;
-    out.draft_slot[ob + n] = cslot[c];
-    out.score[ob + n] = csc[c];
+    out.draft_slot[ob + n] = lslot[c];
+    out.score[ob + n] = lsc[c];
     uint64_t mask = 1ull | (1ull << n);
-    for (int p = pc; p >= 0; p = cpar[p]) mask |= 1ull << node_of[p];
+    for (int p = pc; p >= 0; p = lpar[p]) mask |= 1ull << node_of[p];
     out.anc_mask[ob + n] = mask;
   }
 }
@@ -345,10 +370,15 @@ hipError_t tree_root_setup(int B, int n_new, const int* in_tokens, const int* ct
   return hipGetLastError();
 }
 
+// Dynamic LDS of expand_seq: node_of, scores and five candidate mirrors of
+// cmax entries, 256 scan counts and the beam (k <= 64).
+static size_t expand_lds_bytes(int cmax) { return (size_t)(7 * cmax + 256 + 64) * sizeof(int); }
+
 hipError_t tree_expand(int d, int B, int n_new, const int* ctx_len, const int* in_tokens, int k,
                        int D, int N, const int* ids, const float* logp, int ld, int root_stride,
                        int root_off, TreeState st, PassRows next, TreeOut out, hipStream_t s) {
-  const size_t lds = (size_t)(2 * st.cmax + 256) * sizeof(int);
+  const size_t lds = expand_lds_bytes(st.cmax);
+  if (k > 64 || lds > 64 * 1024) return hipErrorInvalidValue;
   SPEC_LAUNCH(tree_expand_kernel, dim3(B), dim3(256), lds, s, d, n_new, ctx_len, in_tokens,
                      k, D, N, ids, logp, ld, root_stride, root_off, st, st.beam, next, out);
   return hipGetLastError();
@@ -364,7 +394,8 @@ hipError_t chain_tail(bool bf16, int d, int B, int M, int n_new, const int* ctx_
   const float* pv = (const float*)part;
   const int* pi = (const int*)(pv + (size_t)M * nch);
   const topkdev::Part* pp = (const topkdev::Part*)(pi + (size_t)M * nch);
-  const size_t lds = (size_t)(2 * st.cmax + 256) * sizeof(int);
+  const size_t lds = expand_lds_bytes(st.cmax);
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
   if (bf16) {
     const ChainPrologue<bf16_t> pro{(const bf16_t*)embed, V, (const bf16_t*)hid,
                                     (const bf16_t*)w_in, (const bf16_t*)w_hid, eps, H,
