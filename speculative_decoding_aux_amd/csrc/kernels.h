@@ -140,6 +140,12 @@ hipError_t topk_merge_records(int M, int n, int k, int km, int nch, void* part, 
                               int* ids, int ldi, float* logp, int ldl, hipStream_t s);
 // Candidate retrieval: the best K (value desc, id asc) of each row, K <= 256.
 hipError_t topk_large(const float* z, int M, int n, int K, int* ids, void* part, hipStream_t s);
+// The same with the maximum of every 128-column strip of each row already
+// known (rec: float2 [M][nstrip], .x the maximum, as gemm_tile_records
+// writes; nstrip = ceil(n / 128)): only the strips that can hold one of the
+// K best are read.
+hipError_t topk_large_strips(const float* z, int M, int n, int K, const void* rec, int nstrip,
+                             int* ids, hipStream_t s);
 // Gathered exact rescoring: out[m, j] = dot(x[m], W[ids[m, j]]) (float32 accumulate).
 hipError_t gather_dot(bool bf16, const void* x, const void* W, int H, int V, const int* ids, int M,
                       int K, float* out, hipStream_t s);

@@ -209,6 +209,11 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
     // strip records of the tiled LM head (one per row and 128-column strip)
     if (bf16 && !c.cand_rank && lp.nsplit == 1 && lp.tile)
       tk = std::max(tk, (size_t)m * gemm_tile_strips(c.draft_vocab) * 8);
+    // EAGLE-4: strip records of the tiled candidate score GEMM
+    if (bf16 && c.cand_rank) {
+      const GemmPlan sp = gemm_plan(m, c.vocab, c.cand_rank, true);
+      if (sp.nsplit == 1 && sp.tile) tk = std::max(tk, (size_t)m * gemm_tile_strips(c.vocab) * 8);
+    }
   }
   ctx->topk_bytes = tk;
   {
@@ -556,18 +561,29 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
   }
   {
     const GemmPlan p = gemm_plan(M, V, r, bf);
-    if (p.nsplit == 1) {
-      ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
-      SPEC_HIP(ctx, gemm(bf, ws.lowrank, r, w->cand_up, r, sc, M, V, r, p, s, 1));
-    } else {
+    if (bf && p.tile && p.nsplit == 1) {
+      // tiled score GEMM writing every 128-column strip's maximum with the
+      // scores: the retrieval then reads only the strips that can hold one
+      // of the K best
       {
         ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
-        SPEC_HIP(ctx, gemm(bf, ws.lowrank, r, w->cand_up, r, P, M, V, r, p, s, 1));
+        SPEC_HIP(ctx, gemm_tile_records(ws.lowrank, r, w->cand_up, r, sc, M, V, r, ws.topk_part, s));
       }
-      SPEC_HIP(ctx, gemm_epilogue(bf, EPI_F32, sc, nullptr, P, p.nsplit, M, V, s));
+      SPEC_HIP(ctx, topk_large_strips(sc, M, V, K, ws.topk_part, gemm_tile_strips(V), cid, s));
+    } else {
+      if (p.nsplit == 1) {
+        ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
+        SPEC_HIP(ctx, gemm(bf, ws.lowrank, r, w->cand_up, r, sc, M, V, r, p, s, 1));
+      } else {
+        {
+          ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
+          SPEC_HIP(ctx, gemm(bf, ws.lowrank, r, w->cand_up, r, P, M, V, r, p, s, 1));
+        }
+        SPEC_HIP(ctx, gemm_epilogue(bf, EPI_F32, sc, nullptr, P, p.nsplit, M, V, s));
+      }
+      SPEC_HIP(ctx, topk_large(sc, M, V, K, cid, nullptr, s));
     }
   }
-  SPEC_HIP(ctx, topk_large(sc, M, V, K, cid, nullptr, s));
   SPEC_HIP(ctx, gather_dot(bf, ws.nrm, w->lm_head, H, V, cid, M, K, cz, s));
   {
     int nch, ch;

@@ -287,48 +287,26 @@ SPEC_DEV void radix_topk_row(const float* __restrict__ row, int n, int K, int* _
 // good), so a radix select over the group maxima gives a threshold; the
 // groups at or above it (at most kLargeCand of them, else the full-row
 // select runs) are rescanned and their values sorted.
-constexpr int kLargeGroups = 8192, kLargeCand = 256;
+// STRIPS: the score GEMM has already written every 128-column strip's
+// maximum (rec[row][strip].x); by the same argument the K best values lie in
+// the strips at or above the K-th best strip maximum, so pass 1 reads only
+// those strips (at most kStripCand of them), in groups of 16 consecutive
+// columns, instead of the whole row.
+constexpr int kLargeGroups = 8192, kLargeCand = 256, kStripCand = 512, kStripW = 128;
+template <bool STRIPS>
 __global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict__ z, int n,
-                                                         int K, int* __restrict__ ids) {
+                                                         int K, const float2* __restrict__ rec,
+                                                         int nstrip, int* __restrict__ ids) {
   __shared__ float gmax[kLargeGroups];
   __shared__ float cv[kLargeCand * 16];
   __shared__ int ci[kLargeCand * 16];
   __shared__ int hist[256], cg[kLargeCand];
+  __shared__ int cstr[STRIPS ? kStripCand : 1];
   __shared__ int sh[8];
   const int r = blockIdx.x, t = threadIdx.x;
   const float* row = z + (int64_t)r * n;
-  const int G = (n + 4095) / 4096 * 256;  // groups: batch j of thread t is group 256 j + t
-  const bool fast = ((uintptr_t)row & 15) == 0 && G <= kLargeGroups && K <= kLargeCand;
-  if (fast) {
-    for (int g = t; g < G; g += 256) gmax[g] = -INFINITY;
-    __syncthreads();
-    // two batches per thread per step (eight 16-byte loads in flight); the
-    // batch at x0 = 4096 j + 4 t holds row[x0 + 1024 i + e] and is group 256 j + t
-    for (int x0 = 4 * t; x0 < n; x0 += 8192) {
-      float4 w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int x = x0 + 1024 * i;
-        if (x + 3 < n) {
-          w[i] = *(const float4*)(row + x);
-        } else {
-          w[i].x = x < n ? row[x] : -INFINITY;
-          w[i].y = x + 1 < n ? row[x + 1] : -INFINITY;
-          w[i].z = x + 2 < n ? row[x + 2] : -INFINITY;
-          w[i].w = -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float bm = -INFINITY;
-#pragma unroll
-        for (int i = 4 * h; i < 4 * h + 4; ++i)
-          bm = fmaxf(fmaxf(bm, fmaxf(w[i].x, w[i].y)), fmaxf(w[i].z, w[i].w));
-        const int xb = x0 + 4096 * h;
-        if (xb < n) gmax[(xb >> 12) * 256 + t] = bm;
-      }
-    }
-    // radix select of the K-th best group maximum (by key)
+  // K-th best key (okey) of vals[0, cnt) by radix select, left in sh[3]
+  auto kth_key = [&](const float* vals, int cnt) {
     if (t == 0) {
       sh[3] = 0;  // prefix
       sh[4] = 0;  // mask
@@ -339,8 +317,8 @@ __global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict
       hist[t] = 0;
       __syncthreads();
       const uint32_t pre = (uint32_t)sh[3], msk = (uint32_t)sh[4];
-      for (int g = t; g < G; g += 256) {
-        const uint32_t key = okey(gmax[g]);
+      for (int g = t; g < cnt; g += 256) {
+        const uint32_t key = okey(vals[g]);
         if ((key & msk) == pre) atomicAdd(&hist[(key >> p) & 255], 1);
       }
       __syncthreads();
@@ -378,6 +356,98 @@ __global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict
       }
       __syncthreads();
     }
+    return (uint32_t)sh[3];
+  };
+  int G;       // groups of 16 values
+  bool fast;
+  if constexpr (!STRIPS) {
+    G = (n + 4095) / 4096 * 256;  // batch j of thread t is group 256 j + t
+    fast = ((uintptr_t)row & 15) == 0 && G <= kLargeGroups && K <= kLargeCand;
+  } else {
+    G = 0;
+    fast = ((uintptr_t)row & 15) == 0 && nstrip == (n + kStripW - 1) / kStripW &&
+           nstrip <= kLargeGroups && K <= kLargeCand;
+  }
+  // column of value e of group g
+  auto gx = [&](int g, int e) -> int {
+    if constexpr (STRIPS) return cstr[g >> 3] * kStripW + (g & 7) * 16 + e;
+    else return (g >> 8) * 4096 + 4 * (g & 255) + 1024 * (e >> 2) + (e & 3);
+  };
+  if (fast) {
+    if constexpr (!STRIPS) {
+      for (int g = t; g < G; g += 256) gmax[g] = -INFINITY;
+      __syncthreads();
+      // two batches per thread per step (eight 16-byte loads in flight); the
+      // batch at x0 = 4096 j + 4 t holds row[x0 + 1024 i + e] and is group 256 j + t
+      for (int x0 = 4 * t; x0 < n; x0 += 8192) {
+        float4 w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int x = x0 + 1024 * i;
+          if (x + 3 < n) {
+            w[i] = *(const float4*)(row + x);
+          } else {
+            w[i].x = x < n ? row[x] : -INFINITY;
+            w[i].y = x + 1 < n ? row[x + 1] : -INFINITY;
+            w[i].z = x + 2 < n ? row[x + 2] : -INFINITY;
+            w[i].w = -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float bm = -INFINITY;
+#pragma unroll
+          for (int i = 4 * h; i < 4 * h + 4; ++i)
+            bm = fmaxf(fmaxf(bm, fmaxf(w[i].x, w[i].y)), fmaxf(w[i].z, w[i].w));
+          const int xb = x0 + 4096 * h;
+          if (xb < n) gmax[(xb >> 12) * 256 + t] = bm;
+        }
+      }
+    } else {
+      // the strips at or above the K-th best strip maximum
+      const float2* pr = rec + (int64_t)r * nstrip;
+      for (int q = t; q < nstrip; q += 256) gmax[q] = pr[q].x;
+      __syncthreads();
+      const uint32_t T1 = kth_key(gmax, nstrip);
+      if (t == 0) sh[0] = 0;
+      __syncthreads();
+      for (int q = t; q < nstrip; q += 256)
+        if (okey(gmax[q]) >= T1) {
+          const int slot = atomicAdd(&sh[0], 1);
+          if (slot < kStripCand) cstr[slot] = q;
+        }
+      __syncthreads();
+      const int C1 = sh[0];
+      fast = C1 <= kStripCand;
+      if (fast) {
+        // their groups of 16 consecutive columns (4 loads of 16 bytes each)
+        G = C1 * (kStripW / 16);
+        __syncthreads();  // every thread has read sh[0] and gmax
+        for (int g = t; g < G; g += 256) {
+          const int x0 = gx(g, 0);
+          float bm = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int x = x0 + 4 * i;
+            float4 w;
+            if (x + 3 < n) {
+              w = *(const float4*)(row + x);
+            } else {
+              w.x = x < n ? row[x] : -INFINITY;
+              w.y = x + 1 < n ? row[x + 1] : -INFINITY;
+              w.z = x + 2 < n ? row[x + 2] : -INFINITY;
+              w.w = -INFINITY;
+            }
+            bm = fmaxf(fmaxf(bm, fmaxf(w.x, w.y)), fmaxf(w.z, w.w));
+          }
+          gmax[g] = bm;
+        }
+      }
+    }
+  }
+  if (fast) {
+    // radix select of the K-th best group maximum (by key)
+    kth_key(gmax, G);
     const uint32_t T = (uint32_t)sh[3];
     if (t == 0) sh[0] = 0;
     __syncthreads();
@@ -394,7 +464,7 @@ __global__ __launch_bounds__(256) void topk_large_kernel(const float* __restrict
         float v = -INFINITY;
         int id = kIdNone;
         const int g = cg[q >> 4], e = q & 15;
-        const int x = (g >> 8) * 4096 + 4 * (g & 255) + 1024 * (e >> 2) + (e & 3);
+        const int x = gx(g, e);
         if (x < n) {
           v = row[x];
           id = x;
@@ -552,7 +622,6 @@ __global__ __launch_bounds__(256) void gather_dot_vec_kernel(const bf16_t* __res
 // the k best elements of the row lie in its k best strips: those are picked
 // from the records and only their k * 128 logits are rescanned.  The row
 // logsumexp comes from the records alone (merged across waves in float64).
-constexpr int kStripW = 128;
 
 template <int KM>
 __global__ __launch_bounds__(256) void topk_strip_merge_kernel(int n, int k, int nstrip,
@@ -762,7 +831,15 @@ hipError_t topk_merge_records(int M, int n, int k, int km, int nch, void* part, 
 
 hipError_t topk_large(const float* z, int M, int n, int K, int* ids, void* part, hipStream_t s) {
   (void)part;
-  SPEC_LAUNCH(topk_large_kernel, dim3(M), dim3(256), 0, s, z, n, K, ids);
+  SPEC_LAUNCH(topk_large_kernel<false>, dim3(M), dim3(256), 0, s, z, n, K, nullptr, 0, ids);
+  return hipGetLastError();
+}
+
+hipError_t topk_large_strips(const float* z, int M, int n, int K, const void* rec, int nstrip,
+                             int* ids, hipStream_t s) {
+  if (!rec || nstrip != (n + kStripW - 1) / kStripW) return hipErrorInvalidValue;
+  SPEC_LAUNCH(topk_large_kernel<true>, dim3(M), dim3(256), 0, s, z, n, K, (const float2*)rec,
+              nstrip, ids);
   return hipGetLastError();
 }
 
