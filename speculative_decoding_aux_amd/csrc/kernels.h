@@ -189,8 +189,12 @@ hipError_t chain_tail(bool bf16, int d, int B, int M, int n_new, const int* ctx_
 struct VerifyPlan {
   int nch, chunk;    // statistics pass: vocab chunks per node row
   int gch, gchunk;   // Gumbel pass: vocab chunks per stop row
+  bool level;        // level mode: statistics only of the rows the walks reach
+  int lch, lchunk;   // level mode: vocab chunks per current row
 };
-VerifyPlan verify_plan(int B, int N, int V);
+// Level mode is chosen when the tree's rows outweigh the D + 2 launches it
+// takes.
+VerifyPlan verify_plan(int B, int N, int D, int V);
 size_t verify_ws_bytes(const VerifyPlan& p, int B, int N);
 hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const int* parent,
                   const int* num_nodes, const float* logits, int mode, float temperature,

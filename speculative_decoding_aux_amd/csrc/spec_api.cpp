@@ -219,7 +219,7 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
   {
     size_t vb = 0;
     for (int b = 1; b <= c.max_batch; ++b)
-      vb = std::max({vb, verify_ws_bytes(verify_plan(b, c.total_tokens, c.vocab), b,
+      vb = std::max({vb, verify_ws_bytes(verify_plan(b, c.total_tokens, c.depth, c.vocab), b,
                                          c.total_tokens),
                      sample_ws_bytes(sample_plan(b, c.vocab), b, c.total_tokens)});
     ctx->verify_bytes = vb;
@@ -821,7 +821,7 @@ spec_status spec_verify_tree(spec_ctx* ctx, int32_t B, const spec_tree* tree,
   if (mode == SPEC_VERIFY_STOCHASTIC)
     SPEC_REQ(ctx, accept_u && temperature > 0.f, SPEC_EINVAL,
              "stochastic verification needs accept_u and temperature > 0");
-  const VerifyPlan vp = verify_plan(B, c.total_tokens, c.vocab);
+  const VerifyPlan vp = verify_plan(B, c.total_tokens, c.depth, c.vocab);
   SPEC_REQ(ctx, verify_ws_bytes(vp, B, c.total_tokens) <= ctx->verify_bytes, SPEC_EUNSUPPORTED,
            "workspace too small");
   ProfScope ps(ctx, SPEC_PROF_VERIFY, STREAM(stream));
@@ -854,7 +854,7 @@ spec_status spec_verify_tree_static(int32_t B, int32_t total_tokens, int32_t dep
   if (mode == SPEC_VERIFY_STOCHASTIC && (!accept_u || !(temperature > 0.f)))
     return bad(SPEC_EINVAL,
                "spec_verify_tree_static: stochastic verification needs accept_u and temperature > 0");
-  const VerifyPlan vp = verify_plan(B, total_tokens, vocab);
+  const VerifyPlan vp = verify_plan(B, total_tokens, depth, vocab);
   if (verify_ws_bytes(vp, B, total_tokens) > kStaticVerifyScratchBytes) {
     char buf[160];
     snprintf(buf, sizeof buf,

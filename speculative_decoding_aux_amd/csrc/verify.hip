@@ -8,6 +8,9 @@
 // Stage 2, walk (one wave per sequence): merge the chunk records of the nodes
 // on the walk and run the acceptance walk from the root; greedy writes the
 // bonus token, stochastic records the node where the walk stopped.
+// Level mode (large rows): stages 1 and 2 run level by level, the statistics
+// of only the node each walk has reached (at most depth + 1 rows a sequence
+// instead of every node's).
 // Stage 3, stochastic only: Gumbel-max over that node's row with its children
 // excluded, which samples the residual distribution (or the node's own
 // distribution when it has no children).  U is drawn in-kernel from
@@ -40,21 +43,13 @@ struct GPart {  // per (sequence, vocab chunk) of the stop node's row
   int gid;
 };
 
-__global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
-                                                           const int* __restrict__ num_nodes,
-                                                           const float* __restrict__ logits,
-                                                           int mode, float temp, int chunk,
-                                                           VPart* __restrict__ part) {
+// Statistics record of ids [lo, hi) of one logits row (lo a multiple of
+// 1024), by a 256-thread block; valid in thread 0.
+SPEC_DEV VPart chunk_stats(const float* __restrict__ lrow, int lo, int hi, int mode, float temp) {
   __shared__ float rf[4];
   __shared__ int ri[4];
   __shared__ double rz[4];
-  const int c = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
-  const int n1 = N + 1;
-  const int b = row / n1, n = row % n1;
-  if (n > num_nodes[b]) return;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const float* lrow = logits + (int64_t)row * V;
-  const int lo = c * chunk, hi = min(V, lo + chunk);
   const bool vec = ((uintptr_t)lrow & 15) == 0;  // chunk starts are multiples of 1024
   VPart rec;
   if (mode == 0) {
@@ -100,9 +95,8 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
       rec.m = rf[0];
       rec.arg = ri[0];
       rec.z = 0.0;
-      part[(int64_t)row * nch + c] = rec;
     }
-    return;
+    return rec;
   }
   const float invT = 1.0f / temp;
   float m = -INFINITY;
@@ -146,8 +140,102 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
     rec.m = bm;
     rec.z = bz;
     rec.arg = 0;
-    part[(int64_t)row * nch + c] = rec;
   }
+  return rec;
+}
+
+
+__global__ __launch_bounds__(256) void verify_stats_kernel(int N, int V,
+                                                           const int* __restrict__ num_nodes,
+                                                           const float* __restrict__ logits,
+                                                           int mode, float temp, int chunk,
+                                                           VPart* __restrict__ part) {
+  const int c = blockIdx.x, row = blockIdx.y, nch = gridDim.x;
+  const int n1 = N + 1;
+  const int b = row / n1, n = row % n1;
+  if (n > num_nodes[b]) return;
+  const int lo = c * chunk, hi = min(V, lo + chunk);
+  const VPart rec = chunk_stats(logits + (int64_t)row * V, lo, hi, mode, temp);
+  if (threadIdx.x == 0) part[(int64_t)row * nch + c] = rec;
+}
+
+// One step of the acceptance walk of sequence b at node cur, by one wave:
+// merge cur's chunk records pb[0, nch) and return the accepted child (-1:
+// none); greedy also leaves the argmax in *emit.  Lane l holds node l + 1's
+// token tkl and parent prl (-2 past the tree's nn nodes).
+SPEC_DEV int walk_step(int b, int cur, int n1, int nn, int k, int V, int tkl, int prl,
+                       const float* __restrict__ logits, int mode, float temp,
+                       const float* __restrict__ accept_u, int nch, const VPart* __restrict__ pb,
+                       int* emit) {
+  const int lane = threadIdx.x & 63;
+  const int xl = lane + 1;
+  // merge the chunk records of node cur
+  float m = -INFINITY;
+  int arg = 0x7fffffff;
+  for (int c = lane; c < nch; c += 64) {
+    const VPart p = pb[c];
+    if (mode == 0) {
+      if (better(p.m, p.arg, m, arg)) {
+        m = p.m;
+        arg = p.arg;
+      }
+    } else {
+      m = fmaxf(m, p.m);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, 64);
+    const int oa = __shfl_xor(arg, o, 64);
+    if (mode == 0) {
+      if (better(om, oa, m, arg)) {
+        m = om;
+        arg = oa;
+      }
+    } else {
+      m = fmaxf(m, om);
+    }
+  }
+  int next = -1;
+  if (mode == 0) {
+    // child whose token is the argmax (first in node order)
+    const unsigned long long bal = __ballot(xl <= nn && prl == cur && tkl == arg);
+    if (bal) next = __ffsll((long long)bal);  // node lane + 1 of the lowest hit
+    *emit = arg;
+  } else {
+    double z = 0.0;
+    for (int c = lane; c < nch; c += 64) {
+      const VPart p = pb[c];
+      if (p.m != -INFINITY) z += p.z * exp((double)p.m - (double)m);
+    }
+    z = wave_sum(z);
+    // each child's probability and uniform, loaded by its own lane (node
+    // lane + 1; its rank among the children in node order picks the
+    // uniform); then the children are tested one after another
+    const unsigned long long kids = __ballot(xl <= nn && prl == cur);
+    double p = 0.0;
+    float u = 0.f;
+    if ((kids >> lane) & 1) {
+      const int tok = clampi(tkl, 0, V - 1);
+      const float l = logits[(int64_t)(b * n1 + cur) * V + tok];
+      const float zv = temp == 1.0f ? l : l * (1.0f / temp);
+      p = exp((double)zv - (double)m) / z;
+      const int ord = __popcll(kids & ((1ull << lane) - 1));
+      u = accept_u[((int64_t)(b * n1 + cur)) * k + min(ord, k - 1)];
+    }
+    double zrem = 1.0;
+    for (unsigned long long rem = kids; rem && next < 0; rem &= rem - 1) {
+      const int i = __ffsll((long long)rem) - 1;
+      const double pi = __shfl(p, i, 64);
+      const float ui = __shfl(u, i, 64);
+      if ((double)ui <= pi / zrem) {
+        next = i + 1;
+      } else {
+        zrem -= pi;
+      }
+    }
+  }
+  return next;
 }
 
 __global__ __launch_bounds__(64) void verify_walk_kernel(
@@ -168,73 +256,8 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
   const int xl = lane + 1;
   const int tkl = xl <= nn ? tk[xl] : -1, prl = xl <= nn ? pr[xl] : -2;
   while (true) {
-    const VPart* pb = part + (int64_t)(b * n1 + cur) * nch;
-    // merge the chunk records of node cur
-    float m = -INFINITY;
-    int arg = 0x7fffffff;
-    for (int c = lane; c < nch; c += 64) {
-      const VPart p = pb[c];
-      if (mode == 0) {
-        if (better(p.m, p.arg, m, arg)) {
-          m = p.m;
-          arg = p.arg;
-        }
-      } else {
-        m = fmaxf(m, p.m);
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float om = __shfl_xor(m, o, 64);
-      const int oa = __shfl_xor(arg, o, 64);
-      if (mode == 0) {
-        if (better(om, oa, m, arg)) {
-          m = om;
-          arg = oa;
-        }
-      } else {
-        m = fmaxf(m, om);
-      }
-    }
-    int next = -1;
-    if (mode == 0) {
-      // child whose token is the argmax (first in node order)
-      const unsigned long long bal = __ballot(xl <= nn && prl == cur && tkl == arg);
-      if (bal) next = __ffsll((long long)bal);  // node lane + 1 of the lowest hit
-      emit = arg;
-    } else {
-      double z = 0.0;
-      for (int c = lane; c < nch; c += 64) {
-        const VPart p = pb[c];
-        if (p.m != -INFINITY) z += p.z * exp((double)p.m - (double)m);
-      }
-      z = wave_sum(z);
-      // each child's probability and uniform, loaded by its own lane (node
-      // lane + 1; its rank among the children in node order picks the
-      // uniform); then the children are tested one after another
-      const unsigned long long kids = __ballot(xl <= nn && prl == cur);
-      double p = 0.0;
-      float u = 0.f;
-      if ((kids >> lane) & 1) {
-        const int tok = clampi(tkl, 0, V - 1);
-        const float l = logits[(int64_t)(b * n1 + cur) * V + tok];
-        const float zv = temp == 1.0f ? l : l * (1.0f / temp);
-        p = exp((double)zv - (double)m) / z;
-        const int ord = __popcll(kids & ((1ull << lane) - 1));
-        u = accept_u[((int64_t)(b * n1 + cur)) * k + min(ord, k - 1)];
-      }
-      double zrem = 1.0;
-      for (unsigned long long rem = kids; rem && next < 0; rem &= rem - 1) {
-        const int i = __ffsll((long long)rem) - 1;
-        const double pi = __shfl(p, i, 64);
-        const float ui = __shfl(u, i, 64);
-        if ((double)ui <= pi / zrem) {
-          next = i + 1;
-        } else {
-          zrem -= pi;
-        }
-      }
-    }
+    const int next = walk_step(b, cur, n1, nn, k, V, tkl, prl, logits, mode, temp, accept_u, nch,
+                               part + (int64_t)(b * n1 + cur) * nch, &emit);
     if (next < 0 || depth >= D) break;
     if (lane == 0) {
       out_tokens[(int64_t)b * (D + 1) + depth] = tk[next];
@@ -248,6 +271,79 @@ __global__ __launch_bounds__(64) void verify_walk_kernel(
     else stop[b] = cur;
     accepted_len[b] = depth;
   }
+}
+
+// Level mode (trees whose rows are large): launch r = 0..D+1 takes every
+// walk from level r - 1 to level r and reads chunk c of the row of the node
+// it reached, so only the rows of nodes the walks reach are read.  Launch r's
+// workgroups (c, b) all repeat the step of sequence b from level r - 1 (the
+// previous launch's records of that level: the kernel boundary makes them
+// visible, no workgroup waits for another), workgroup c = 0 writes the step's
+// outputs and the reached node; records and nodes alternate between two
+// buffers by the parity of the level.  Launch D + 1 (one workgroup a
+// sequence) only steps.  node[.][b] = -1 once b's walk has stopped.
+__global__ __launch_bounds__(256) void verify_level_kernel(
+    int r, int N, int D, int k, int V, const int* __restrict__ tokens,
+    const int* __restrict__ parent, const int* __restrict__ num_nodes,
+    const float* __restrict__ logits, int mode, float temp, const float* __restrict__ accept_u,
+    int nch, int chunk, VPart* __restrict__ part0, VPart* __restrict__ part1,
+    int* __restrict__ node0, int* __restrict__ node1, int* __restrict__ stop,
+    int* __restrict__ out_tokens, int* __restrict__ accepted_len,
+    int* __restrict__ accepted_nodes) {
+  __shared__ int reached;
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int n1 = N + 1;
+  int* nprev = (r & 1) ? node0 : node1;  // level r - 1
+  int* ncur = (r & 1) ? node1 : node0;   // level r
+  const VPart* pprev = (r & 1) ? part0 : part1;
+  VPart* pcur = (r & 1) ? part1 : part0;
+  int node;
+  if (r == 0) {
+    node = 0;
+    if (c == 0) {
+      for (int j = t; j <= D; j += 256) out_tokens[(int64_t)b * (D + 1) + j] = -1;
+      for (int j = t; j < D; j += 256) accepted_nodes[(int64_t)b * D + j] = -1;
+      if (t == 0) ncur[b] = 0;
+    }
+  } else {
+    const int prev = nprev[b];
+    if (prev < 0) {  // stopped before level r - 1 (uniform in the block)
+      if (c == 0 && t == 0) ncur[b] = -1;
+      return;
+    }
+    if (t < 64) {
+      const int lane = t;
+      const int nn = min(num_nodes[b], N);
+      const int* tk = tokens + (int64_t)b * n1;
+      const int* pr = parent + (int64_t)b * n1;
+      const int xl = lane + 1;
+      const int tkl = xl <= nn ? tk[xl] : -1, prl = xl <= nn ? pr[xl] : -2;
+      int emit = -1;
+      const int next = walk_step(b, prev, n1, nn, k, V, tkl, prl, logits, mode, temp, accept_u,
+                                 nch, pprev + (int64_t)b * nch, &emit);
+      const int go = (next >= 0 && r - 1 < D) ? next : -1;
+      if (lane == 0) {
+        reached = go;
+        if (c == 0) {
+          if (go >= 0) {
+            out_tokens[(int64_t)b * (D + 1) + r - 1] = tk[go];
+            accepted_nodes[(int64_t)b * D + r - 1] = go;
+          } else {
+            if (mode == 0) out_tokens[(int64_t)b * (D + 1) + r - 1] = emit;
+            else stop[b] = prev;
+            accepted_len[b] = r - 1;
+          }
+          ncur[b] = go;
+        }
+      }
+    }
+    __syncthreads();
+    node = reached;
+    if (node < 0 || r > D) return;  // uniform in the block
+  }
+  const int lo = c * chunk, hi = min(V, lo + chunk);
+  const VPart rec = chunk_stats(logits + (int64_t)(b * n1 + node) * V, lo, hi, mode, temp);
+  if (t == 0) pcur[(int64_t)b * nch + c] = rec;
 }
 
 // Gumbel-max over a chunk of the stop node's row, children excluded.
@@ -400,7 +496,7 @@ __global__ __launch_bounds__(256) void compact_kernel(char* __restrict__ kb, cha
 
 }  // namespace
 
-VerifyPlan verify_plan(int B, int N, int V) {
+VerifyPlan verify_plan(int B, int N, int D, int V) {
   VerifyPlan p;
   const int rows = B * (N + 1);
   // statistics: about 2048 blocks, chunks of at least 4096 ids
@@ -413,14 +509,24 @@ VerifyPlan verify_plan(int B, int N, int V) {
   g = std::max(1, std::min(g, std::max(1, (V + 2047) / 2048)));
   p.gchunk = ((V + g - 1) / g + 1023) / 1024 * 1024;
   p.gch = (V + p.gchunk - 1) / p.gchunk;
+  // level mode once the rows of every node cost more than the D + 2 launches
+  // it takes, a few microseconds each (about 32 MB of logits per launch)
+  p.level = D >= 1 && (double)rows * V * 4.0 > (double)(D + 2) * 32.0 * (1 << 20);
+  // level mode: about 1024 blocks over the B current rows, chunks of >= 4096 ids
+  int lc = (1024 + B - 1) / std::max(1, B);
+  lc = std::max(1, std::min(lc, std::max(1, (V + 4095) / 4096)));
+  p.lchunk = ((V + lc - 1) / lc + 1023) / 1024 * 1024;
+  p.lch = (V + p.lchunk - 1) / p.lchunk;
   return p;
 }
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 size_t verify_ws_bytes(const VerifyPlan& p, int B, int N) {
-  return align256((size_t)B * (N + 1) * p.nch * sizeof(VPart)) +
-         align256((size_t)B * p.gch * sizeof(GPart)) + align256((size_t)B * sizeof(int));
+  // level mode: records and reached nodes of two levels
+  const size_t recs = p.level ? 2 * (size_t)B * p.lch : (size_t)B * (N + 1) * p.nch;
+  return align256(recs * sizeof(VPart)) + align256((size_t)B * p.gch * sizeof(GPart)) +
+         3 * align256((size_t)B * sizeof(int));
 }
 
 hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const int* parent,
@@ -428,20 +534,37 @@ hipError_t verify(int B, int N, int D, int k, int V, const int* tokens, const in
                   const float* accept_u, uint64_t seed, int* out_tokens, int* accepted_len,
                   int* accepted_nodes, void* ws, const VerifyPlan& p, hipStream_t s) {
   const int rows = B * (N + 1);
+  const size_t recs = p.level ? 2 * (size_t)B * p.lch : (size_t)rows * p.nch;
   char* w = (char*)ws;
   VPart* part = (VPart*)w;
-  w += align256((size_t)rows * p.nch * sizeof(VPart));
+  w += align256(recs * sizeof(VPart));
   GPart* gpart = (GPart*)w;
   w += align256((size_t)B * p.gch * sizeof(GPart));
   int* stop = (int*)w;
-  SPEC_LAUNCH(verify_stats_kernel, dim3(p.nch, rows), dim3(256), 0, s, N, V, num_nodes,
-                     logits, mode, temperature, p.chunk, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  SPEC_LAUNCH(verify_walk_kernel, dim3(B), dim3(64), 0, s, N, D, k, V, tokens, parent,
-                     num_nodes, logits, mode, temperature, accept_u, p.nch, (const VPart*)part,
-                     stop, out_tokens, accepted_len, accepted_nodes);
-  e = hipGetLastError();
+  w += align256((size_t)B * sizeof(int));
+  int* node0 = (int*)w;
+  w += align256((size_t)B * sizeof(int));
+  int* node1 = (int*)w;
+  hipError_t e = hipSuccess;
+  if (p.level) {
+    VPart* part1 = part + (size_t)B * p.lch;
+    for (int r = 0; r <= D + 1 && e == hipSuccess; ++r) {
+      SPEC_LAUNCH(verify_level_kernel, dim3(r <= D ? p.lch : 1, B), dim3(256), 0, s, r, N, D, k,
+                  V, tokens, parent, num_nodes, logits, mode, temperature, accept_u, p.lch,
+                  p.lchunk, part, part1, node0, node1, stop, out_tokens, accepted_len,
+                  accepted_nodes);
+      e = hipGetLastError();
+    }
+  } else {
+    SPEC_LAUNCH(verify_stats_kernel, dim3(p.nch, rows), dim3(256), 0, s, N, V, num_nodes,
+                logits, mode, temperature, p.chunk, part);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SPEC_LAUNCH(verify_walk_kernel, dim3(B), dim3(64), 0, s, N, D, k, V, tokens, parent,
+                num_nodes, logits, mode, temperature, accept_u, p.nch, (const VPart*)part, stop,
+                out_tokens, accepted_len, accepted_nodes);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess || mode == 0) return e;
   SPEC_LAUNCH(verify_gumbel_kernel, dim3(p.gch, B), dim3(256), 0, s, N, V, tokens, parent,
                      num_nodes, logits, temperature, (uint32_t)(seed & 0xffffffffu),
