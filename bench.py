@@ -103,14 +103,14 @@ def measured_traffic(workload, kernel="lm_head"):
     return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["kernel_source_sha256"] else None
 
 
-def kernel_figures(cfg, rows, lm, lmt, att, ver):
+def kernel_figures(cfg, rows, lm, lmt, att, ver, alen=None):
     """Per-label launch figures of the sampled steps: average launch time,
     algorithmic bytes (and, for the LM head, GEMM flops) per launch, achieved
     rates and their fractions of the published peaks.  LM head: the launches
     up to 64 rows (root pass, chains) and the tiled launches of the beam
     passes apart; attention: the visible context K and V of every (sequence,
-    kv head) once per pass (the window at most); verify: every node row's
-    target logits once."""
+    kv head) once per pass (the window at most); verify: the target-logit rows
+    of the nodes the acceptance walks reach, once (alen: accepted lengths)."""
     es = 2 if cfg["dtype"] == "bf16" else 4
     B, nkv, hd = cfg["batch"], cfg["n_kv_heads"], cfg["head_dim"]
     ctx = min(cfg["ctx"], cfg["sliding_window"]) if cfg["sliding_window"] else cfg["ctx"]
@@ -138,7 +138,11 @@ def kernel_figures(cfg, rows, lm, lmt, att, ver):
                 flops = sum(2.0 * m * cfg["draft_vocab"] * cfg["hidden"] for m in rs) / len(rs)
                 rate(name, nl, ms, byts, flops)
     rate("attention", att[0], att[1], B * nkv * ctx * hd * 2 * es)
-    rate("verify", ver[0], ver[1], B * (cfg["total_tokens"] + 1) * cfg["vocab"] * 4)
+    # verify: the target-logit rows the walks need, (accepted + 1) per sequence
+    vrows = int(np.sum(alen + 1)) if alen is not None else B * (cfg["total_tokens"] + 1)
+    rate("verify", ver[0], ver[1], vrows * cfg["vocab"] * 4)
+    if "verify" in out:
+        out["verify"]["rows_needed"] = vrows
     return out
 
 
@@ -368,7 +372,8 @@ def main():
         nv, msv = ctx.profile_read(L.SPEC_PROF_VERIFY)
         ctx.profile(False)
         rows = pass_rows(cfg)
-        kern = kernel_figures(cfg, rows, (n, ms), (nt, mst), (na, msa), (nv, msv))
+        kern = kernel_figures(cfg, rows, (n, ms), (nt, mst), (na, msa), (nv, msv),
+                              vout[1].cpu().numpy())
         # the roofline kernel: the LM head launch that takes the most time per
         # step (the tiled beam-pass head of tree workloads beyond 64 rows)
         tiled = "lm_head_tiled" in kern and nt * mst >= n * ms
