@@ -8,7 +8,10 @@
 // one chunk of one (sequence, kv-head) once for all R rows x G q-heads of that
 // kv-head (online softmax in float32, partial (max, sum, O) per query vector).
 // A combine kernel merges the chunk partials with the few extra keys of each
-// row and normalises.  Scores are q.k / sqrt(hd).
+// row and normalises.  When one workgroup can take a (sequence, kv-head)'s
+// whole context (all rows in one launch, a short context per wave), it also
+// attends the rows' extra keys and writes the normalised output itself: no
+// partials and no combine launch.  Scores are q.k / sqrt(hd).
 #include <type_traits>
 
 #include "common.h"
@@ -357,10 +360,10 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
 
 
 // ---- bf16 context attention on MFMA -----------------------------------------
-// Each wave walks blocks of 16 keys, wave w taking blocks w, w + 4, ... of the
-// chunk, one block ahead of use: the V rows go into a wave-private LDS stage
-// by global_load_lds_dwordx4 (two stages per wave, 32 KB per workgroup at hd
-// 128) and the K rows load straight into registers in MFMA fragment layout as
+// Each wave walks blocks of 16 keys, wave w taking blocks w, w + NW, ... of
+// the chunk (NW = 4 or 8 waves), one block ahead of use: the V rows go into a
+// wave-private LDS stage by global_load_lds_dwordx4 (two stages per wave, 8 KB
+// per wave at hd 128) and the K rows load straight into registers in MFMA fragment layout as
 // soon as the previous block's scores are done, so the key loop has no
 // workgroup barrier, every load is 16 bytes wide and several workgroups share
 // a CU.
@@ -373,8 +376,8 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
 // j ^ 2((r >> 2) & 3), so the four key rows of one read hit distinct bank
 // groups.  P goes in as two bf16 parts (hi + lo), keeping the float32 softmax
 // weights to about 16 bits.  The query fragments sit in LDS, shared by the
-// four waves.  Online softmax runs per query column (shuffles across the four
-// lane groups); the four waves are merged pairwise through LDS at the end.
+// waves.  Online softmax runs per query column (shuffles across the four
+// lane groups); the waves are merged pairwise through LDS at the end.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 SPEC_DEV uint2 pack4(const float (&v)[4]) {
@@ -384,30 +387,40 @@ SPEC_DEV uint2 pack4(const float (&v)[4]) {
 
 SPEC_DEV int v_swz(int r) { return 2 * ((r >> 2) & 3); }
 
-template <int HD, int QT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void attn_ctx_mfma_kernel(
+template <int HD, int QT, int NW, bool FUSE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 3))) void attn_ctx_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     int64_t sseq, int64_t shead, int S, KvPages pg, const int* __restrict__ ctx_len,
     const int* __restrict__ pos, int R, int r0, int Rg, int nq, int nkv, int window, int chunk,
-    float* __restrict__ part) {
+    const int* __restrict__ anc, int A, float* __restrict__ part, bf16_t* __restrict__ out) {
   constexpr int DS = HD / 32;        // 32-dim steps of S^T
   constexpr int DT = HD / 16;        // 16-dim tiles of O^T
   constexpr int CH = HD / 8;         // 16-byte chunks per row
   constexpr int BLK = 16 * CH;       // 16-byte units per 16-row V block
   constexpr int NI = BLK / 64;       // DMA instructions per V block
   constexpr int NL = DS + NI;        // vector loads per block (K fragments + V DMA)
+  constexpr int KS = NW * 16;        // keys from one of a wave's blocks to its next
   static_assert(NL < 64 && NI < 64, "vmcnt range");
   static_assert(HD == 64 || HD == 128, "head dim");
+  static_assert(NW == 4 || NW == 8, "waves");
   // two V stages, one LDS object each; a wave owns BLK units of each
-  __shared__ u32x4_t v0s[4 * BLK], v1s[4 * BLK];
+  __shared__ u32x4_t v0s[NW * BLK], v1s[NW * BLK];
   // query fragments (B operand of S^T), [t][ds][lane], shared by the waves
   __shared__ u32x4_t qsh[QT * DS * 64];
-  // merge buffers: [QT][DT][64] accumulators per slot (slot 0 in V stage 0,
-  // slot 1 in V stage 1, free after the key loop), [2][QT][64] max and sum
-  static_assert(QT * DT * 64 * 16 <= 4 * BLK * 16, "merge slot fits in a V stage");
-  __shared__ float mm[2 * QT * 64], ml[2 * QT * 64];
-  // paged caches: the blocks of the pages this chunk touches, read once
-  __shared__ int ptab[kAttnMaxChunkPages];
+  // merge buffers: slots of [QT][DT][64] accumulators in the V stages (free
+  // after the key loop), [NW / 2][QT][64] max and sum
+  constexpr int SLOT = QT * DT * 64;
+  constexpr int CAP = NW * BLK / SLOT;  // merge slots per V stage
+  static_assert(CAP >= 1 && 2 * CAP >= NW / 2, "merge slots fit in the V stages");
+  __shared__ float mm[NW / 2 * QT * 64], ml[NW / 2 * QT * 64];
+  // paged caches: the blocks of the pages this chunk touches, read once;
+  // with eight waves the table also pads the workgroup's LDS past half of a
+  // CU's 160 KB, so no CU takes two of them
+  constexpr int LDS0 = 2 * NW * BLK * 16 + QT * DS * 64 * 16 + 2 * (NW / 2) * QT * 64 * 4;
+  constexpr int PTAB = NW == 8 && (84 * 1024 - LDS0) / 4 > kAttnMaxChunkPages
+                           ? (84 * 1024 - LDS0) / 4
+                           : kAttnMaxChunkPages;
+  __shared__ int ptab[PTAB];
   const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int nch = gridDim.x;
   // this launch's query vectors: rows r0 .. r0 + Rg - 1 of each sequence
@@ -427,14 +440,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   const int k0 = start + c * chunk;
   const int k1 = min(ctx, k0 + chunk);
   const int first = k0 + wave * 16;
-  const int nblk = first < k1 ? (k1 - first + 63) / 64 : 0;
+  const int nblk = first < k1 ? (k1 - first + KS - 1) / KS : 0;
 
   // every key the kernel touches lies in [kmin, kmax] (clamped reads past
   // the end included)
   const int kmax = max(k1 - 1, 0), kmin = min(k0, kmax);
   const int pg0 = pg.tbl ? kmin / pg.bs : 0;
   const int npg = pg.tbl ? min(kmax / pg.bs - pg0 + 1, kAttnMaxChunkPages) : 0;
-  for (int i = threadIdx.x; i < npg; i += 256) {
+  for (int i = threadIdx.x; i < npg; i += 64 * NW) {
     const int page = min(pg0 + i, pg.mb - 1);
     const int blk = pg.tbl[(int64_t)b * pg.mb + page];
     ptab[i] = blk < 0 ? 0 : (blk >= pg.nblk ? pg.nblk - 1 : blk);
@@ -480,14 +493,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   };
   u32x4_t kf[DS];  // K fragments: loaded for block i + 1 once block i's scores are done
   auto issue_k = [&](int i) {
-    const int base = first + min(i, max(nblk - 1, 0)) * 64;
+    const int base = first + min(i, max(nblk - 1, 0)) * KS;
     const bf16_t* kp = kb + koff(min(base + col, max(k1 - 1, 0))) + g * 8;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) kf[ds] = *(const u32x4_t*)(kp + ds * 32);
   };
   // V rows of block i (past the end: the last block again, never used)
   auto issue_v = [&](auto sc, int i) {
-    const int base = first + min(i, max(nblk - 1, 0)) * 64;
+    const int base = first + min(i, max(nblk - 1, 0)) * KS;
     // unit u of a block is row u / CH at position u % CH, holding chunk
     // (u % CH) ^ v_swz(row)
 #pragma unroll
@@ -498,18 +511,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     }
   };
 
-  auto block = [&](auto sc, auto sn, int i) {
-    // refill the other V stage (read by this wave's previous block, whose LDS
-    // reads have completed) with block i + 1, then wait for everything issued
-    // before it: this block's V stage and K fragments
-    wait_vm_lgkm0<NL>();
-    asm volatile("" ::: "memory");
-    issue_v(sn, i + 1);
-    wait_vm_lgkm0<NI>();
-    asm volatile("" ::: "memory");
-    if (i >= nblk) return;
-    const int kb0 = first + i * 64;
-    const SPEC_LDS bf16_t* vs = (const SPEC_LDS bf16_t*)(vbuf(sc) + wave * BLK);
+  // One 16-key block: V rows in LDS at vs, K fragments in kf.  S^T tiles by
+  // MFMA, then after_s() (the K fragments are free), then the online softmax
+  // per query column over the keys vis(t, e) admits (key 4g + e of the block
+  // for this lane's query vector of tile t) and O^T += V^T . P^T.
+  auto attend = [&](const SPEC_LDS bf16_t* vs, auto after_s, auto vis) {
     f32x4 sc4[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
             __builtin_bit_cast(bf16x8, kf[ds]),
             __builtin_bit_cast(bf16x8, qsh[(t * DS + ds) * 64 + lane]), sc4[t], 0, 0, 0);
     }
-    issue_k(i + 1);  // the K fragments are consumed
+    after_s();
     uint2 pf[QT], pl[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -528,8 +534,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       float tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int key = kb0 + 4 * g + e;
-        v[e] = (key < k1 && key >= loq[t]) ? sc4[t][e] * scale : -INFINITY;
+        v[e] = vis(t, e) ? sc4[t][e] * scale : -INFINITY;
         tmax = fmaxf(tmax, v[e]);
       }
       {
@@ -594,6 +599,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       }
     }
   };
+
+  auto block = [&](auto sc, auto sn, int i) {
+    // refill the other V stage (read by this wave's previous block, whose LDS
+    // reads have completed) with block i + 1, then wait for everything issued
+    // before it: this block's V stage and K fragments
+    wait_vm_lgkm0<NL>();
+    asm volatile("" ::: "memory");
+    issue_v(sn, i + 1);
+    wait_vm_lgkm0<NI>();
+    asm volatile("" ::: "memory");
+    if (i >= nblk) return;
+    const int kb0 = first + i * KS;
+    attend((const SPEC_LDS bf16_t*)(vbuf(sc) + wave * BLK), [&] { issue_k(i + 1); },
+           [&](int t, int e) {
+             const int key = kb0 + 4 * g + e;
+             return key < k1 && key >= loq[t];
+           });
+  };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   if (nblk > 0) {
@@ -605,27 +628,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     }
   }
   wait_vm_lgkm0<0>();  // the repeated loads past the end
-  __syncthreads();      // every wave is done with the V stages
-  f32x4* const mo0 = (f32x4*)v0s;
-  f32x4* const mo1 = (f32x4*)v1s;
 
-  // merge waves pairwise through LDS: (2,3) -> (0,1), then 1 -> 0
+  if constexpr (FUSE) {
+    // The whole context is this workgroup's (one chunk): the rows' extra keys
+    // (root rows, tree ancestors, itself) are attended here as well, wave w
+    // taking rows w, w + NW, ...  A row's list holds its slots (-1: none)
+    // with consecutive positions ending at the row's own; lane l takes entry
+    // l, and the keys go in blocks of 16 through the same MFMA step, visible
+    // to the query vectors of that row only.
+    for (int rr = wave; rr < Rg; rr += NW) {
+      const int grow = b * R + r0 + rr;
+      const int pq = pos[grow];
+      const int sl = lane < A ? anc[(int64_t)grow * A + lane] : -1;
+      const unsigned long long vmask = __ballot(sl >= 0);
+      const int nvalid = __popcll(vmask);
+      const int rank = __popcll(vmask & ((1ull << lane) - 1ull));
+      const bool vis = sl >= 0 && sl < S && (window <= 0 || pq - (nvalid - 1 - rank) > pq - window);
+      const unsigned long long kmask = __ballot(vis);
+      // each lane's entry as an element offset (an in-range row when hidden)
+      const int64_t soff = kv_slot_off(pg, b, vis ? sl : 0, sseq, HD);
+      for (int j0 = 0; j0 < 64 && (kmask >> j0) != 0ull; j0 += 16) {
+        wait_vm_lgkm0<0>();  // the stage's previous reads are done
+        asm volatile("" ::: "memory");
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const int half = round == 0 ? 2 : 1;
+        for (int j = 0; j < NI; ++j) {
+          const int u = j * 64 + lane, row = u / CH;
+          const int64_t ro = __shfl(soff, (j0 + row) & 63, 64);
+          dma16(vb + ro + ((u % CH) ^ v_swz(row)) * 8, vbuf(S0{}) + wave * BLK + j * 64);
+        }
+        {
+          const bf16_t* kp = kb + __shfl(soff, (j0 + col) & 63, 64) + g * 8;
+#pragma unroll
+          for (int ds = 0; ds < DS; ++ds) kf[ds] = *(const u32x4_t*)(kp + ds * 32);
+        }
+        wait_vm_lgkm0<0>();
+        asm volatile("" ::: "memory");
+        attend((const SPEC_LDS bf16_t*)(vbuf(S0{}) + wave * BLK), [] {}, [&](int t, int e) {
+          const int qv = t * 16 + col, key = j0 + 4 * g + e;
+          return qv < QV && qv / G == rr && key < 64 && ((kmask >> key) & 1ull);
+        });
+      }
+    }
+    wait_vm_lgkm0<0>();
+  }
+  __syncthreads();  // every wave is done with the V stages
+  auto slotp = [&](int sl) -> f32x4* {
+    return (f32x4*)(sl < CAP ? v0s : v1s) + (sl % CAP) * SLOT;
+  };
+
+  // merge the waves pairwise through LDS, the upper half into the lower
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half /= 2) {
     if (wave >= half && wave < 2 * half) {
       const int slot = wave - half;
+      f32x4* mo = slotp(slot);
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
         mm[(slot * QT + t) * 64 + lane] = mrun[t];
         ml[(slot * QT + t) * 64 + lane] = lrun[t];
-        f32x4* mo = slot ? mo1 : mo0;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) mo[(t * DT + dt) * 64 + lane] = o[t][dt];
       }
     }
     __syncthreads();
     if (wave < half) {
+      const f32x4* mo = slotp(wave);
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
         const float mb = mm[(wave * QT + t) * 64 + lane], lb = ml[(wave * QT + t) * 64 + lane];
@@ -634,7 +701,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         const float eb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - M);
         lrun[t] = lrun[t] * ea + lb * eb;
         mrun[t] = M;
-        const f32x4* mo = wave ? mo1 : mo0;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[t][dt] = o[t][dt] * ea + mo[(t * DT + dt) * 64 + lane] * eb;
       }
@@ -642,48 +708,108 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     __syncthreads();
   }
   if (wave == 0) {
-    float* pb = part + (((int64_t)(b * nkv + kvh) * nch + c) * QVF + r0 * G) * (HD + 2);
+    if constexpr (FUSE) {
+      // normalised output of each query vector: dims dt*16 + 4g .. +3
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      const int qv = t * 16 + col;
-      if (qv >= QV) continue;
-      float* rec = pb + (int64_t)qv * (HD + 2);
+      for (int t = 0; t < QT; ++t) {
+        const int qv = t * 16 + col;
+        if (qv >= QV) continue;
+        const int r = r0 + qv / G, h = kvh * G + qv % G;
+        const float inv = lrun[t] > 0.f ? 1.f / lrun[t] : 0.f;
+        bf16_t* op = out + ((int64_t)(b * R + r) * nq + h) * HD + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt) {
+          const float w[4] = {o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv,
+                              o[t][dt][3] * inv};
+          *(uint2*)(op + dt * 16) = pack4(w);
+        }
+      }
+    } else {
+      float* pb = part + (((int64_t)(b * nkv + kvh) * nch + c) * QVF + r0 * G) * (HD + 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rec[dt * 16 + 4 * g + i] = o[t][dt][i];
-      if (g == 0) {
-        rec[HD] = mrun[t] * 0.6931471805599453f;  // log2 units -> natural
-        rec[HD + 1] = lrun[t];
+      for (int t = 0; t < QT; ++t) {
+        const int qv = t * 16 + col;
+        if (qv >= QV) continue;
+        float* rec = pb + (int64_t)qv * (HD + 2);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rec[dt * 16 + 4 * g + i] = o[t][dt][i];
+        if (g == 0) {
+          rec[HD] = mrun[t] * 0.6931471805599453f;  // log2 units -> natural
+          rec[HD + 1] = lrun[t];
+        }
       }
     }
   }
 }
 
+// One-chunk attention: at most this many 16-key blocks per wave.
+constexpr int kFuseMaxBlocks = 24;
+
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 1;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int HD, int QT, int NW, bool FUSE>
+void launch_ctx(const AttnArgs& a, dim3 grid, size_t lds, int r0, int Rg, int chunk,
+                hipStream_t s) {
+  SPEC_LAUNCH((attn_ctx_mfma_kernel<HD, QT, NW, FUSE>), grid, dim3(64 * NW), lds, s,
+              (const bf16_t*)a.q, (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq,
+              a.kv.stride_head, a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, r0, Rg, a.nq, a.nkv,
+              a.window, chunk, a.anc, a.A, a.part, (bf16_t*)a.out);
+}
+
 template <typename T, int HD>
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int G = a.nq / a.nkv;
+  const bool mfma = std::is_same<T, bf16_t>::value;
+  if (mfma) {
+    // All of a sequence's rows in one launch and a short context per wave:
+    // one workgroup per (sequence, kv-head) takes the whole context and the
+    // rows' extra keys and writes the output (no chunk records, no combine).
+    // Eight waves when the workgroups fit the CUs one each (their LDS keeps
+    // a second one off a CU), else four, two per CU.
+    const int span = a.window > 0 ? std::min(a.window, a.kv.slots) : a.kv.slots;
+    const int nw = a.B * a.nkv <= cu_count() ? 8 : 4;
+    const bool pages_ok = !a.kv.pg.tbl || span / a.kv.pg.bs + 2 <= kAttnMaxChunkPages;
+    if (a.R * G <= 32 && a.A <= 64 && pages_ok && span <= nw * 16 * kFuseMaxBlocks) {
+      const int chunk = (span + nw * 16 - 1) / (nw * 16) * (nw * 16);
+      const dim3 grid(1, a.nkv, a.B);
+      const bool one = a.R * G <= 16;
+      if (nw == 8) {
+        if (one) launch_ctx<HD, 1, 8, true>(a, grid, 0, 0, a.R, chunk, s);
+        else launch_ctx<HD, 2, 8, true>(a, grid, 0, 0, a.R, chunk, s);
+      } else {
+        if (one) launch_ctx<HD, 1, 4, true>(a, grid, 0, 0, a.R, chunk, s);
+        else launch_ctx<HD, 2, 4, true>(a, grid, 0, 0, a.R, chunk, s);
+      }
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(a.nchunks, a.nkv, a.B);
   // query vectors go in groups of rows: up to 32 vectors per launch on the
   // bf16 MFMA path (two 16-vector tiles), 64 on the scalar path; each group
   // streams the context chunk again, so one group is the common case (the
   // draft's beam rows) and several only serve large trees (the target's
   // verification forward)
-  const bool mfma = std::is_same<T, bf16_t>::value;
   const int rg = std::max(1, (mfma ? 32 : 64) / G);
   for (int r0 = 0; r0 < a.R; r0 += rg) {
     const int Rg = std::min(rg, a.R - r0);
     const int QV = Rg * G;
     if (mfma && QV <= 16) {
-      SPEC_LAUNCH((attn_ctx_mfma_kernel<HD, 1>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
-                  (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
-                  a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, r0, Rg, a.nq, a.nkv, a.window,
-                  a.chunk, a.part);
+      launch_ctx<HD, 1, 4, false>(a, grid, 0, r0, Rg, a.chunk, s);
     } else if (mfma) {
-      SPEC_LAUNCH((attn_ctx_mfma_kernel<HD, 2>), grid, dim3(256), 0, s, (const bf16_t*)a.q,
-                  (const bf16_t*)a.kv.k, (const bf16_t*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
-                  a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, r0, Rg, a.nq, a.nkv, a.window,
-                  a.chunk, a.part);
+      launch_ctx<HD, 2, 4, false>(a, grid, 0, r0, Rg, a.chunk, s);
     } else {
       const size_t lds = (size_t)QV * (HD + kTile + 3) * sizeof(float) + QV * sizeof(int);
       SPEC_LAUNCH((attn_ctx_kernel<T, HD>), grid, dim3(256), lds, s, (const T*)a.q,
