@@ -100,17 +100,19 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W, int ldw,
     float* __restrict__ P, int M, int N, int K, int kc, int ntiles, float2* __restrict__ rec) {
   constexpr int NWAVE = NTH / 64;
-  constexpr int WGN = BN / 64, WGM = NWAVE / WGN;  // wave grid
-  constexpr int WM = BM / WGM;                     // X rows per wave
-  constexpr int FA = 4, FB = WM / 16;
+  constexpr int WGN = BN % 64 == 0 ? BN / 64 : 2, WGM = NWAVE / WGN;  // wave grid
+  constexpr int WN = BN / WGN, WM = BM / WGM;  // weight rows and X rows per wave
+  constexpr int FA = WN / 16, FB = WM / 16;
   constexpr int CH = BK / 8;                       // 16-byte chunks per stage row
   // wave-level DMA instructions per stage, dealt round-robin to the waves
   // (repeats load the same bytes)
   constexpr int IW = BN * CH / 64, IX = BM * CH / 64;
   constexpr int NW = (IW + NWAVE - 1) / NWAVE, NX = (IX + NWAVE - 1) / NWAVE, NI = NW + NX;
-  static_assert(FB >= 1 && WGN * WGM == NWAVE && BM % (16 * WGM) == 0, "tile shape");
+  static_assert(FA >= 1 && FB >= 1 && WGN * WGM == NWAVE && BN % (16 * WGN) == 0 &&
+                    BM % (16 * WGM) == 0,
+                "tile shape");
   static_assert((BK == 32 || BK == 64) && NS >= 2 && NS <= 6, "stages");
-  static_assert(!REC || WGN == 2, "strip records assume two waves across the strip");
+  static_assert(!REC || (WGN == 2 && WN == 64), "strip records assume two waves across the strip");
   // one LDS object per stage, and the records' exchange (the (max, sum) of
   // the wn = 1 half of each row)
   __shared__ u32x4_t w0[BN * CH], w1[BN * CH], w2[NS > 2 ? BN * CH : 1],
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
 #pragma unroll
     for (int b = 0; b < FB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int sw = chunk_swz<CH>(c);  // rows of a fragment start at multiples of 16
-  const int rowa = (wn * 64 + c) * CH, rowb = (wm * WM + c) * CH;
+  const int rowa = (wn * WN + c) * CH, rowb = (wm * WM + c) * CH;
 
   // lane holds Y[m0 + wm*WM + 16b + c][n0 + wn*64 + 16a + 4g + r]
   auto epilogue = [&](const TileGeo& q) __attribute__((always_inline)) {
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       if (m >= M) continue;
 #pragma unroll
       for (int a = 0; a < FA; ++a) {
-        const int n = q.n0 + wn * 64 + 16 * a + 4 * g;
+        const int n = q.n0 + wn * WN + 16 * a + 4 * g;
         float* dst = Pb + (int64_t)m * N + n;
         if (n + 3 < N && (N & 3) == 0) {
           *(float4*)dst = make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
       // lane groups of the wave by shuffles, the two waves of a row via LDS
       constexpr float kL2e = 1.4426950408889634f;
       const bool full = q.n0 + BN <= N;
-      const int nl = N - (q.n0 + wn * 64 + 4 * g);  // this lane's columns below N: 16a + r < nl
+      const int nl = N - (q.n0 + wn * WN + 4 * g);  // this lane's columns below N: 16a + r < nl
       float rm[FB], rs[FB];
 #pragma unroll
       for (int b = 0; b < FB; ++b) {
@@ -336,25 +338,40 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
 
 }  // namespace
 
-// Beam-pass tile: 128 weight rows x 256 X rows, K stages of 64, three stages
-// (144 KB of LDS, one block per CU, two waves per SIMD).
+// Beam-pass tile: 128 (or 96) weight rows x 256 X rows, K stages of 64, three
+// stages (144 KB of LDS, one block per CU, two waves per SIMD).
 constexpr int kTileBN = 128, kTileBM = 256, kTileBK = 64, kTileThreads = 512, kTileStages = 3;
+constexpr int kTileBNNarrow = 96;
 
 bool gemm_tile_ok(int M, int K) { return M > 64 && K % kTileBK == 0; }
 
 GemmPlan gemm_tile_plan(int M, int N, int K) {
-  GemmPlan p;
-  const int strips = (N + kTileBN - 1) / kTileBN;
-  const int mblocks = (M + kTileBM - 1) / kTileBM;
-  const int ktiles = K / kTileBK;
   // One block per CU: split K only while the grid is short of 256 blocks
   // (every split costs an M x N float32 partial), keeping >= 4 stages per split.
-  int ns = 256 / std::max(1, strips * mblocks);
-  ns = std::max(1, std::min(ns, std::max(1, ktiles / 4)));
-  const int per = (ktiles + ns - 1) / ns;
-  p.kc = per * kTileBK;
-  p.nsplit = (ktiles + per - 1) / per;
-  return p;
+  // Of the two strip widths, the one with the least work on the busiest CU:
+  // rounds of tiles x (strip width + a fixed cost per step of 32 rows) x steps
+  // per tile.
+  GemmPlan best;
+  int64_t best_cost = 0;
+  for (const int bn : {kTileBN, kTileBNNarrow}) {
+    GemmPlan p;
+    p.bn = bn;
+    const int strips = (N + bn - 1) / bn;
+    const int mblocks = (M + kTileBM - 1) / kTileBM;
+    const int ktiles = K / kTileBK;
+    int ns = 256 / std::max(1, strips * mblocks);
+    ns = std::max(1, std::min(ns, std::max(1, ktiles / 4)));
+    const int per = (ktiles + ns - 1) / ns;
+    p.kc = per * kTileBK;
+    p.nsplit = (ktiles + per - 1) / per;
+    const int64_t tiles = (int64_t)strips * mblocks * p.nsplit;
+    const int64_t cost = (tiles + 255) / 256 * (bn + 32) * per;
+    if (bn == kTileBN || cost < best_cost) {
+      best = p;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 namespace {
@@ -374,24 +391,22 @@ int tile_grid(int ntiles) {
   return std::min(ntiles, cus[dev]);
 }
 
-template <bool REC>
+template <bool REC, int BN>
 hipError_t launch_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
                        int K, int kc, int nsplit, float2* rec, hipStream_t s) {
   if (M <= 0 || N <= 0 || K % kTileBK != 0 || kc % kTileBK != 0 || kc <= 0 || nsplit < 1 ||
       (int64_t)(nsplit - 1) * kc >= K)
     return hipErrorInvalidValue;
-  const int ntiles = ((N + kTileBN - 1) / kTileBN) * ((M + kTileBM - 1) / kTileBM) * nsplit;
+  const int ntiles = ((N + BN - 1) / BN) * ((M + kTileBM - 1) / kTileBM) * nsplit;
   const int grid = tile_grid(ntiles);
   if (grid < ntiles)
-    SPEC_LAUNCH(
-        (gemm_dma_kernel<kTileBN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, true>),
-        dim3(grid), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M,
-        N, K, kc, ntiles, rec);
+    SPEC_LAUNCH((gemm_dma_kernel<BN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, true>),
+                dim3(grid), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W,
+                ldw, P, M, N, K, kc, ntiles, rec);
   else
-    SPEC_LAUNCH(
-        (gemm_dma_kernel<kTileBN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, false>),
-        dim3(ntiles), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M,
-        N, K, kc, ntiles, rec);
+    SPEC_LAUNCH((gemm_dma_kernel<BN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, false>),
+                dim3(ntiles), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W,
+                ldw, P, M, N, K, kc, ntiles, rec);
   return hipGetLastError();
 }
 
@@ -399,14 +414,17 @@ hipError_t launch_tile(const void* X, int ldx, const void* W, int ldw, float* P,
 
 hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N, int K,
                      const GemmPlan& plan, hipStream_t s) {
-  return launch_tile<false>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit, nullptr, s);
+  if (plan.bn == kTileBNNarrow)
+    return launch_tile<false, kTileBNNarrow>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit,
+                                             nullptr, s);
+  return launch_tile<false, kTileBN>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit, nullptr, s);
 }
 
 int gemm_tile_strips(int N) { return (N + kTileBN - 1) / kTileBN; }
 
 hipError_t gemm_tile_records(const void* X, int ldx, const void* W, int ldw, float* z, int M,
                              int N, int K, void* rec, hipStream_t s) {
-  return launch_tile<true>(X, ldx, W, ldw, z, M, N, K, K, 1, (float2*)rec, s);
+  return launch_tile<true, kTileBN>(X, ldx, W, ldw, z, M, N, K, K, 1, (float2*)rec, s);
 }
 
 }  // namespace spec
