@@ -72,7 +72,8 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
                          int nq, int nkv, int window, int nch, const float* __restrict__ part,
                          T* __restrict__ out) {
   constexpr int DPL = HD / 64;  // dims per lane
-  constexpr int PC = 4;         // chunk records prefetched
+  constexpr int PC = 8;         // chunk records prefetched
+  constexpr int CG = 16;        // chunk records in flight per group after them
   constexpr int KB = 8;         // extra keys per batch
   const int lane = threadIdx.x & 63;
   const int G = nq / nkv, kvh = h / G;
@@ -152,13 +153,15 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
         for (int i = 0; i < DPL; ++i) o[i] += po[c][i] * w;
       }
     }
-    // the remaining chunk records, four chunks' loads in flight at a time
-    for (int c0 = PC; c0 < nch; c0 += 4) {
-      float mq[4], oq[4][DPL];
+    // the remaining chunk records, CG chunks' loads in flight at a time (the
+    // maxima of the first 64 chunks are already in the lanes)
+    for (int c0 = PC; c0 < nch; c0 += CG) {
+      float mq[CG], oq[CG][DPL];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < CG; ++u) {
         const int c = c0 + u;
-        mq[u] = c < nch ? pb[c * cstride + HD] : -INFINITY;
+        const float sm = __shfl(pm, c & 63, 64);
+        mq[u] = c >= nch ? -INFINITY : (c < 64 ? sm : pb[c * cstride + HD]);
         if (c < nch) {
           load_dims<float, DPL>(pb + c * cstride + DPL * lane, oq[u]);
         } else {
@@ -167,7 +170,7 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < CG; ++u) {
         if (mq[u] == -INFINITY) continue;
         const float w = expf(mq[u] - m);
 #pragma unroll
