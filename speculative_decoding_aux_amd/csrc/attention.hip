@@ -280,9 +280,13 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
   const T* vb = vc + kvh * shead;
   constexpr int NG = 256 / HD;          // PV thread groups
   const int d = threadIdx.x % HD, grp = threadIdx.x / HD;
-  float acc[(64 + NG - 1) / NG];
+  constexpr int NJ = (64 + NG - 1) / NG;  // accumulators per thread, enough for 64 vectors
+  // the ones this thread's group uses (uniform across a wave: a group is one
+  // or two whole waves), so the unused ones are skipped by scalar branches
+  const int jn = __builtin_amdgcn_readfirstlane(QV > grp ? (QV - grp + NG - 1) / NG : 0);
+  float acc[NJ];
 #pragma unroll
-  for (int j = 0; j < (64 + NG - 1) / NG; ++j) acc[j] = 0.f;
+  for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
 
   for (int t0 = k0; t0 < k1; t0 += kTile) {
     // scores: lane = key, wave w takes query vectors w, w+4, ...
@@ -326,9 +330,9 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
     // O[qv][d] = O * scale + sum_key p[qv][key] * V[key][d]
     const int nk = min(kTile, k1 - t0);
 #pragma unroll
-    for (int j = 0; j < (64 + NG - 1) / NG; ++j) {
-      const int qv = grp + j * NG;
-      if (qv < QV) acc[j] *= srow[qv];
+    for (int j = 0; j < NJ; ++j) {
+      if (j >= jn) break;
+      acc[j] *= srow[grp + j * NG];
     }
     // V rows in batches of 8 keys: the loads of a batch are independent
     for (int kk0 = 0; kk0 < nk; kk0 += 8) {
@@ -340,9 +344,9 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
       for (int u = 0; u < 8; ++u) {
         if (kk0 + u >= nk) break;
 #pragma unroll
-        for (int j = 0; j < (64 + NG - 1) / NG; ++j) {
-          const int qv = grp + j * NG;
-          if (qv < QV) acc[j] += sc[qv * kTile + kk0 + u] * v8[u];
+        for (int j = 0; j < NJ; ++j) {
+          if (j >= jn) break;
+          acc[j] += sc[(grp + j * NG) * kTile + kk0 + u] * v8[u];
         }
       }
     }
@@ -351,9 +355,9 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
   // partial record per query vector: O[HD], m, l
   float* pb = part + (((int64_t)(b * nkv + kvh) * nch + c) * QVF + r0 * G) * (HD + 2);
 #pragma unroll
-  for (int j = 0; j < (64 + NG - 1) / NG; ++j) {
-    const int qv = grp + j * NG;
-    if (qv < QV) pb[qv * (HD + 2) + d] = acc[j];
+  for (int j = 0; j < NJ; ++j) {
+    if (j >= jn) break;
+    pb[(grp + j * NG) * (HD + 2) + d] = acc[j];
   }
   for (int i = threadIdx.x; i < QV; i += blockDim.x) {
     pb[i * (HD + 2) + HD] = mrow[i];
