@@ -254,6 +254,7 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
   float* lrow = mrow + QV;
   float* srow = lrow + QV;
   int* lo = (int*)(srow + QV);       // [QV]
+  float* red = (float*)(lo + QV);    // [NG][QV][HD] when the keys are split
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const float inv_sqrt = 1.0f / sqrtf((float)HD);
 
@@ -284,6 +285,9 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
   // the ones this thread's group uses (uniform across a wave: a group is one
   // or two whole waves), so the unused ones are skipped by scalar branches
   const int jn = __builtin_amdgcn_readfirstlane(QV > grp ? (QV - grp + NG - 1) / NG : 0);
+  // few query vectors (at most half the groups): every group takes every
+  // vector over its own keys (key % NG == group), the groups summed at the end
+  const bool ksplit = 2 * QV <= NG;
   float acc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) acc[j] = 0.f;
@@ -329,6 +333,28 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
     __syncthreads();
     // O[qv][d] = O * scale + sum_key p[qv][key] * V[key][d]
     const int nk = min(kTile, k1 - t0);
+    if (ksplit) {
+      constexpr int KPG = kTile / NG;  // keys per group per tile
+#pragma unroll
+      for (int qv = 0; qv < NG / 2; ++qv)
+        if (qv < QV) acc[qv] *= srow[qv];
+      float vk[KPG];
+#pragma unroll
+      for (int u = 0; u < KPG; ++u) {
+        const int kk = grp + NG * u;
+        vk[u] = kk < nk ? St<T>::load(vb, kv_slot_off(pg, b, t0 + kk, sseq, HD) + d) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < KPG; ++u) {
+        const int kk = grp + NG * u;
+        if (kk >= nk) break;
+#pragma unroll
+        for (int qv = 0; qv < NG / 2; ++qv)
+          if (qv < QV) acc[qv] += sc[qv * kTile + kk] * vk[u];
+      }
+      __syncthreads();
+      continue;
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (j >= jn) break;
@@ -354,10 +380,23 @@ __global__ __launch_bounds__(256) void attn_ctx_kernel(const T* __restrict__ q,
   }
   // partial record per query vector: O[HD], m, l
   float* pb = part + (((int64_t)(b * nkv + kvh) * nch + c) * QVF + r0 * G) * (HD + 2);
+  if (ksplit) {
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    if (j >= jn) break;
-    pb[(grp + j * NG) * (HD + 2) + d] = acc[j];
+    for (int qv = 0; qv < NG / 2; ++qv)
+      if (qv < QV) red[(grp * QV + qv) * HD + d] = acc[qv];
+    __syncthreads();
+    for (int i = threadIdx.x; i < QV * HD; i += blockDim.x) {
+      float o = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) o += red[gg * QV * HD + i];
+      pb[(i / HD) * (HD + 2) + i % HD] = o;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (j >= jn) break;
+      pb[(grp + j * NG) * (HD + 2) + d] = acc[j];
+    }
   }
   for (int i = threadIdx.x; i < QV; i += blockDim.x) {
     pb[i * (HD + 2) + HD] = mrow[i];
@@ -818,7 +857,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     } else if (mfma) {
       launch_ctx<HD, 2, 4, false>(a, grid, 0, r0, Rg, a.chunk, s);
     } else {
-      const size_t lds = (size_t)QV * (HD + kTile + 3) * sizeof(float) + QV * sizeof(int);
+      const size_t lds = (size_t)QV * (HD + kTile + 3) * sizeof(float) + QV * sizeof(int) +
+                         (2 * QV <= 256 / HD ? (size_t)(256 / HD) * QV * HD * sizeof(float) : 0);
       SPEC_LAUNCH((attn_ctx_kernel<T, HD>), grid, dim3(256), lds, s, (const T*)a.q,
                   (const T*)a.kv.k, (const T*)a.kv.v, a.kv.stride_seq, a.kv.stride_head,
                   a.kv.slots, a.kv.pg, a.ctx_len, a.pos, a.R, r0, Rg, a.nq, a.nkv, a.window,
