@@ -436,6 +436,46 @@ __global__ __launch_bounds__(256) void epi_f32(float* __restrict__ Y, const floa
   Y[idx] = a;
 }
 
+// Split-K LM head whose logits are materialised: z = the sum of the nsplit
+// partials (in split order) and one (max, sum of exp(v - max)) record per row
+// and 128-column strip, the layout the strip top-k reads.  One wave per
+// (row, strip), two columns per lane.
+__global__ __launch_bounds__(256) void epi_f32_rec_kernel(float* __restrict__ z,
+                                                          const float* __restrict__ P, int nsplit,
+                                                          int M, int N, int nstrip,
+                                                          float2* __restrict__ rec) {
+  constexpr float kL2e = 1.4426950408889634f;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, strip)
+  if (w >= (int64_t)M * nstrip) return;                             // uniform in the wave
+  const int m = int(w / nstrip), st = int(w % nstrip);
+  const int64_t ss = (int64_t)M * N;
+  float v[2];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = st * 128 + 2 * lane + j;
+    v[j] = 0.f;
+    if (n < N) {
+      const float* p = P + (int64_t)m * N + n;
+      float a = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) a += p[sp * ss];
+      z[(int64_t)m * N + n] = a;
+      v[j] = a;
+      mx = fmaxf(mx, a);
+    }
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (st * 128 + 2 * lane + j < N) sum += __builtin_amdgcn_exp2f((v[j] - mx) * kL2e);
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) rec[(int64_t)m * nstrip + st] = make_float2(mx, sum);
+}
+
 // Few splits over many outputs: one thread per 4 consecutive outputs (16-byte
 // partial loads), splits summed in order from 0 - the same additions, in the
 // same order, as epi_kernel for nsplit <= kEpiGroups.
@@ -723,6 +763,15 @@ hipError_t gemm_lmhead_topk(const void* X, int ldx, const void* W, int ldw, floa
     if (cw1) launch_lmhead<4, 1>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
     else launch_lmhead<4, 2>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t gemm_epilogue_records(const float* P, int nsplit, int M, int N, float* z, void* rec,
+                                 hipStream_t s) {
+  const int nstrip = (N + 127) / 128;
+  const int64_t waves = (int64_t)M * nstrip;
+  SPEC_LAUNCH(epi_f32_rec_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, z, P, nsplit,
+              M, N, nstrip, (float2*)rec);
   return hipGetLastError();
 }
 

@@ -44,6 +44,11 @@ enum EpiOp { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_F32 = 3 };
 // (gate | up) and writes N; EPI_F32 writes float32 sums to Y.
 hipError_t gemm_epilogue(bool bf16, int op, void* Y, const void* R, const float* P, int nsplit,
                          int M, int N, hipStream_t s);
+// Float32 logits z[M, N] = the sum of the nsplit partials, plus one (max, sum
+// exp) record per row and 128-column strip (float2 [M][ceil(N / 128)]) for
+// topk_merge_strips.  P may be z itself when nsplit == 1.
+hipError_t gemm_epilogue_records(const float* P, int nsplit, int M, int N, float* z, void* rec,
+                                 hipStream_t s);
 
 // Paged KV (vLLM Neuron page, "KV Cache Sharing": the physical slot of a
 // logical position is block_table[pos / block_size] * block_size + pos %

@@ -532,6 +532,21 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
                                       s));
       return SPEC_OK;
     }
+    if (io.k_out <= 8 && (size_t)M * gemm_tile_strips(Vd) * 8 <= ctx->topk_bytes) {
+      // logits with per-strip (max, sum exp) records as the partials are
+      // summed; the top-k rescans only the k best strips of each row
+      float* src = p.nsplit == 1 ? z : P;
+      {
+        ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
+        SPEC_HIP(ctx, gemm(bf, ws.nrm, H, w->lm_head, H, src, M, Vd, H, p, s, 1));
+      }
+      SPEC_HIP(ctx, gemm_epilogue_records(src, p.nsplit, M, Vd, z, ws.topk_part, s));
+      ProfScope ps(ctx, SPEC_PROF_TOPK, s);
+      SPEC_HIP(ctx, topk_merge_strips(z, M, Vd, io.k_out, gemm_tile_strips(Vd), 128,
+                                      ws.topk_part, w->d2t, io.ids, io.ld_out, io.logp, io.ld_out,
+                                      s));
+      return SPEC_OK;
+    }
     if (p.nsplit == 1) {
       ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
       SPEC_HIP(ctx, gemm(bf, ws.nrm, H, w->lm_head, H, z, M, Vd, H, p, s, 1));
