@@ -117,28 +117,28 @@ SPEC_DEV void stream_acc(const bf16_t* __restrict__ X, int ldx, const bf16_t* __
 // last one, keeping every wave's load count uniform.
 template <int MT, int CW>
 SPEC_DEV void stream_acc_lds(const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W,
-                             int ldw, int M, int N, int K, int m0, int n0, f32x4 (&acc)[CW][MT],
-                             SPEC_LDS u32x4_t* xs0, SPEC_LDS u32x4_t* xs1) {
+                             int ldw, int M, int N, int k0, int kn, int m0, int n0,
+                             f32x4 (&acc)[CW][MT], SPEC_LDS u32x4_t* xs0, SPEC_LDS u32x4_t* xs1) {
   constexpr int NXI = 2 * MT;  // DMA instructions per wave per iteration (16*MT rows x 32 chunks)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
   const bf16_t* wp[CW];
 #pragma unroll
-  for (int w = 0; w < CW; ++w) wp[w] = W + (int64_t)min(n0 + 16 * w + c, N - 1) * ldw + g * 8;
+  for (int w = 0; w < CW; ++w) wp[w] = W + (int64_t)min(n0 + 16 * w + c, N - 1) * ldw + k0 + g * 8;
   const bf16_t* xsrc[NXI];
   int xdst[NXI];
 #pragma unroll
   for (int j = 0; j < NXI; ++j) {
     xdst[j] = (wave * NXI + j) * 64;
     const int u = xdst[j] + lane, row = u >> 5, pos = u & 31;
-    xsrc[j] = X + (int64_t)min(m0 + row, M - 1) * ldx + 8 * (pos ^ (row & 15));
+    xsrc[j] = X + (int64_t)min(m0 + row, M - 1) * ldx + k0 + 8 * (pos ^ (row & 15));
   }
 #pragma unroll
   for (int w = 0; w < CW; ++w)
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nit = K / 256;
+  const int nit = kn / 256;
   auto issue = [&](SPEC_LDS u32x4_t* xs, int it) __attribute__((always_inline)) {
     const int k = min(it, nit - 1) * 256;
 #pragma unroll
@@ -218,21 +218,30 @@ SPEC_DEV void store_tiles(const f32x4 (&acc)[CW][MT], float* __restrict__ P, int
   }
 }
 
-template <int MT, int TAG, int CW>
+template <int MT, int TAG, int CW, bool XL>
 __global__ __launch_bounds__(256) void gemm_bf16_stream(const bf16_t* __restrict__ X, int ldx,
                                                          const bf16_t* __restrict__ W, int ldw,
                                                          float* __restrict__ P, int M, int N, int K,
                                                          int kc) {
+  __shared__ u32x4_t xs0[XL ? 16 * MT * 32 : 1], xs1[XL ? 16 * MT * 32 : 1];
   const int wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * (64 * CW) + wave * (16 * CW);
-  if (n0 >= N) return;
   const int split = blockIdx.y;
   const int k0 = split * kc;
   const int k1 = min(K, k0 + kc);
   const int m0 = blockIdx.z * (16 * MT);
   f32x4 acc[CW][MT];
-  stream_acc<MT, CW>(X, ldx, W, ldw, M, N, k0, k1, m0, n0, acc);
-  store_tiles<MT, CW>(acc, P + (int64_t)split * M * N, M, N, m0, n0);
+  if constexpr (XL) {
+    // every wave takes part in the block's shared X loads (one past N streams
+    // the clamped last weight rows and stores nothing)
+    stream_acc_lds<MT, CW>(X, ldx, W, ldw, M, N, k0, k1 - k0, m0, n0, acc,
+                           (SPEC_LDS u32x4_t*)xs0, (SPEC_LDS u32x4_t*)xs1);
+    if (n0 < N) store_tiles<MT, CW>(acc, P + (int64_t)split * M * N, M, N, m0, n0);
+  } else {
+    if (n0 >= N) return;
+    stream_acc<MT, CW>(X, ldx, W, ldw, M, N, k0, k1, m0, n0, acc);
+    store_tiles<MT, CW>(acc, P + (int64_t)split * M * N, M, N, m0, n0);
+  }
 }
 
 // LM head with the vocab top-k fused: after the (unsplit) contraction each
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(256) void gemm_lmhead_topk_kernel(
   if constexpr (XL) {
     // every wave takes part in the shared X loads (an inactive one streams
     // the clamped last weight rows and stores nothing)
-    stream_acc_lds<MT, CW>(X, ldx, W, ldw, M, N, K, m0, n0, acc, (SPEC_LDS u32x4_t*)xs0,
+    stream_acc_lds<MT, CW>(X, ldx, W, ldw, M, N, 0, K, m0, n0, acc, (SPEC_LDS u32x4_t*)xs0,
                            (SPEC_LDS u32x4_t*)xs1);
     if (active && z) store_tiles<MT, CW>(acc, z, M, N, m0, n0);
   } else if (active) {
@@ -667,12 +676,15 @@ GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split) {
   const int mblocks = (M + 63) / 64;
   const int target = (cw == 1 || M > 16) ? 1024 : 2048;  // workgroups in flight
   int ns = (target + strips * mblocks - 1) / (strips * mblocks);
-  const int kblocks = (K + 127) / 128;
+  // K in blocks of 128, or of 512 where the activation rows go through LDS
+  // (17-64 rows, see stream_acc_lds), whose K steps come in pairs of 256
+  const int kb = M > 16 && K % 512 == 0 ? 512 : 128;
+  const int kblocks = (K + kb - 1) / kb;
   ns = std::max(1, std::min(std::min(ns, kblocks), std::min(kMaxSplit, std::max(1, max_split))));
   // vocab-wide heads have >= 1024 strips already: no split, so the top-k can
   // be fused into the epilogue and no M x N partials are written
   if (N >= 65536) ns = 1;
-  const int kc = ((kblocks + ns - 1) / ns) * 128;
+  const int kc = ((kblocks + ns - 1) / ns) * kb;
   p.kc = kc;
   p.nsplit = (K + kc - 1) / kc;
   return p;
@@ -682,17 +694,22 @@ template <int TAG, int CW>
 static void launch_stream(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
                           int K, const GemmPlan& plan, hipStream_t s) {
   const int strips = (N + 64 * CW - 1) / (64 * CW);
+  // X through LDS once per block where it holds two or more 16-row tiles and
+  // every split's K range is whole pairs of 256-wide steps
+  const bool xl = K % 512 == 0 && plan.kc % 512 == 0 && ldx % 8 == 0 && ((uintptr_t)X & 15) == 0;
+#define SPEC_STREAM(MT, XLV, GZ)                                                                \
+  SPEC_LAUNCH((gemm_bf16_stream<MT, TAG, CW, XLV>), dim3(strips, plan.nsplit, GZ), dim3(256), 0, \
+              s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc)
   if (M <= 16) {
-    SPEC_LAUNCH((gemm_bf16_stream<1, TAG, CW>), dim3(strips, plan.nsplit, 1), dim3(256), 0,
-                       s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc);
+    SPEC_STREAM(1, false, 1);
   } else if (M <= 32) {
-    SPEC_LAUNCH((gemm_bf16_stream<2, TAG, CW>), dim3(strips, plan.nsplit, 1), dim3(256), 0,
-                       s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc);
+    if (xl) SPEC_STREAM(2, true, 1);
+    else SPEC_STREAM(2, false, 1);
   } else {
-    SPEC_LAUNCH((gemm_bf16_stream<4, TAG, CW>), dim3(strips, plan.nsplit, (M + 63) / 64),
-                       dim3(256), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K,
-                       plan.kc);
+    if (xl) SPEC_STREAM(4, true, (M + 63) / 64);
+    else SPEC_STREAM(4, false, (M + 63) / 64);
   }
+#undef SPEC_STREAM
 }
 
 hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
