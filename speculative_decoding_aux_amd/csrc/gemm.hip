@@ -676,9 +676,9 @@ GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split) {
   const int mblocks = (M + 63) / 64;
   const int target = (cw == 1 || M > 16) ? 1024 : 2048;  // workgroups in flight
   int ns = (target + strips * mblocks - 1) / (strips * mblocks);
-  // K in blocks of 128, or of 512 where the activation rows go through LDS
-  // (17-64 rows, see stream_acc_lds), whose K steps come in pairs of 256
-  const int kb = M > 16 && K % 512 == 0 ? 512 : 128;
+  // K in blocks of 512 where the activation rows go through LDS (see
+  // stream_acc_lds: K steps in pairs of 256), else of 128
+  const int kb = K % 512 == 0 ? 512 : 128;
   const int kblocks = (K + kb - 1) / kb;
   ns = std::max(1, std::min(std::min(ns, kblocks), std::min(kMaxSplit, std::max(1, max_split))));
   // vocab-wide heads have >= 1024 strips already: no split, so the top-k can
@@ -694,14 +694,15 @@ template <int TAG, int CW>
 static void launch_stream(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
                           int K, const GemmPlan& plan, hipStream_t s) {
   const int strips = (N + 64 * CW - 1) / (64 * CW);
-  // X through LDS once per block where it holds two or more 16-row tiles and
-  // every split's K range is whole pairs of 256-wide steps
+  // X through LDS once per block (the four waves share its rows) where every
+  // split's K range is whole pairs of 256-wide steps
   const bool xl = K % 512 == 0 && plan.kc % 512 == 0 && ldx % 8 == 0 && ((uintptr_t)X & 15) == 0;
 #define SPEC_STREAM(MT, XLV, GZ)                                                                \
   SPEC_LAUNCH((gemm_bf16_stream<MT, TAG, CW, XLV>), dim3(strips, plan.nsplit, GZ), dim3(256), 0, \
               s, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, P, M, N, K, plan.kc)
   if (M <= 16) {
-    SPEC_STREAM(1, false, 1);
+    if (xl) SPEC_STREAM(1, true, 1);
+    else SPEC_STREAM(1, false, 1);
   } else if (M <= 32) {
     if (xl) SPEC_STREAM(2, true, 1);
     else SPEC_STREAM(2, false, 1);
