@@ -100,7 +100,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
     const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W, int ldw,
     float* __restrict__ P, int M, int N, int K, int kc, int ntiles, float2* __restrict__ rec) {
   constexpr int NWAVE = NTH / 64;
-  constexpr int WGN = BN % 64 == 0 ? BN / 64 : 2, WGM = NWAVE / WGN;  // wave grid
+  constexpr int WGN = BN % 64 == 0 ? BN / 64 : (BN % 32 == 0 ? 2 : 1), WGM = NWAVE / WGN;  // wave grid
   constexpr int WN = BN / WGN, WM = BM / WGM;  // weight rows and X rows per wave
   constexpr int FA = WN / 16, FB = WM / 16;
   constexpr int CH = BK / 8;                       // 16-byte chunks per stage row
@@ -338,22 +338,22 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
 
 }  // namespace
 
-// Beam-pass tile: 128 (or 96) weight rows x 256 X rows, K stages of 64, three
-// stages (144 KB of LDS, one block per CU, two waves per SIMD).
+// Beam-pass tile: 128 (or 96 or 112) weight rows x 256 X rows, K stages of 64,
+// three stages (up to 144 KB of LDS, one block per CU, two waves per SIMD).
 constexpr int kTileBN = 128, kTileBM = 256, kTileBK = 64, kTileThreads = 512, kTileStages = 3;
-constexpr int kTileBNNarrow = 96;
+constexpr int kTileBNNarrow = 96, kTileBN112 = 112;
 
 bool gemm_tile_ok(int M, int K) { return M > 64 && K % kTileBK == 0; }
 
 GemmPlan gemm_tile_plan(int M, int N, int K) {
   // One block per CU: split K only while the grid is short of 256 blocks
   // (every split costs an M x N float32 partial), keeping >= 4 stages per split.
-  // Of the two strip widths, the one with the least work on the busiest CU:
+  // Of the strip widths, the one with the least work on the busiest CU:
   // rounds of tiles x (strip width + a fixed cost per step of 32 rows) x steps
   // per tile.
   GemmPlan best;
   int64_t best_cost = 0;
-  for (const int bn : {kTileBN, kTileBNNarrow}) {
+  for (const int bn : {kTileBN, kTileBNNarrow, kTileBN112}) {
     GemmPlan p;
     p.bn = bn;
     const int strips = (N + bn - 1) / bn;
@@ -417,6 +417,9 @@ hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, i
   if (plan.bn == kTileBNNarrow)
     return launch_tile<false, kTileBNNarrow>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit,
                                              nullptr, s);
+  if (plan.bn == kTileBN112)
+    return launch_tile<false, kTileBN112>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit,
+                                          nullptr, s);
   return launch_tile<false, kTileBN>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit, nullptr, s);
 }
 

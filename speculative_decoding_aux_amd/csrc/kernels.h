@@ -12,7 +12,7 @@ struct GemmPlan {
   int nsplit = 1;
   int kc = 0;         // K elements per split
   bool tile = false;  // LDS-tiled kernel (beam passes, M > 64) instead of weight streaming
-  int bn = 128;       // tiled kernel: weight rows per tile (128 or 96)
+  int bn = 128;       // tiled kernel: weight rows per tile (128, 112 or 96)
 };
 // max_split caps the split-K depth of the weight-streaming kernel (M <= 64).
 GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split = 32);
