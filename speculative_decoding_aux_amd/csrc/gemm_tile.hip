@@ -95,10 +95,15 @@ SPEC_DEV TileGeo tile_geo(int t, int M, int N, int K, int kc) {
 // Otherwise every block owns one tile.
 // REC (unsplit launches, BN = 128): also write, per row and BN-column strip,
 // the record (max, sum of exp(v - max)) that the vocab top-k merges.
-template <int BN, int BM, int BK, int NTH, int NS, bool REC, bool PERSIST>
+// SWI (unsplit, one tile per block, two waves across): W is [gate (N/2) |
+// up (N/2)] and tile s takes gate rows s*BN/2 .. and the same up rows, the
+// first wave across holding gate and the second up; the epilogue writes
+// silu(gate) * up as bf16 to Y[M][N/2] (the up values cross through LDS).
+template <int BN, int BM, int BK, int NTH, int NS, bool REC, bool PERSIST, bool SWI = false>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void gemm_dma_kernel(
     const bf16_t* __restrict__ X, int ldx, const bf16_t* __restrict__ W, int ldw,
-    float* __restrict__ P, int M, int N, int K, int kc, int ntiles, float2* __restrict__ rec) {
+    float* __restrict__ P, int M, int N, int K, int kc, int ntiles, float2* __restrict__ rec,
+    bf16_t* __restrict__ Y) {
   constexpr int NWAVE = NTH / 64;
   constexpr int WGN = BN % 64 == 0 ? BN / 64 : (BN % 32 == 0 ? 2 : 1), WGM = NWAVE / WGN;  // wave grid
   constexpr int WN = BN / WGN, WM = BM / WGM;  // weight rows and X rows per wave
@@ -113,6 +118,8 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
                 "tile shape");
   static_assert((BK == 32 || BK == 64) && NS >= 2 && NS <= 6, "stages");
   static_assert(!REC || (WGN == 2 && WN == 64), "strip records assume two waves across the strip");
+  static_assert(!SWI || (WGN == 2 && !REC && !PERSIST && NS >= 2 && WGM * WM * WN * 4 <= 2 * BM * BK * 2),
+                "SwiGLU epilogue: gate and up waves, one tile per block, up values fit two X stages");
   // one LDS object per stage, and the records' exchange (the (max, sum) of
   // the wn = 1 half of each row)
   __shared__ u32x4_t w0[BN * CH], w1[BN * CH], w2[NS > 2 ? BN * CH : 1],
@@ -150,7 +157,14 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
   const bf16_t* gx[NX];
   auto point = [&](const TileGeo& q) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NW; ++j) gw[j] = W + (int64_t)min(q.n0 + rw[j], N - 1) * ldw + q.k0 + ow[j];
+    for (int j = 0; j < NW; ++j) {
+      int row = min(q.n0 + rw[j], N - 1);
+      if constexpr (SWI) {  // local rows [0, BN/2) gate, [BN/2, BN) the matching up rows
+        const int r = rw[j] % BN, hn = N / 2;
+        row = min(r < BN / 2 ? q.n0 / 2 + r : hn + q.n0 / 2 + r - BN / 2, N - 1);
+      }
+      gw[j] = W + (int64_t)row * ldw + q.k0 + ow[j];
+    }
 #pragma unroll
     for (int j = 0; j < NX; ++j) gx[j] = X + (int64_t)min(q.m0 + rx[j], M - 1) * ldx + q.k0 + ox[j];
   };
@@ -207,6 +221,53 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
 
   // lane holds Y[m0 + wm*WM + 16b + c][n0 + wn*64 + 16a + 4g + r]
   auto epilogue = [&](const TileGeo& q) __attribute__((always_inline)) {
+    if constexpr (SWI) {
+      // the up wave (wn = 1) of each row block hands its values to the gate
+      // wave (wn = 0) through the (now idle) X stages; then silu(g) * u
+      float* ex = (float*)(wm < WGM / 2 ? (SPEC_LDS u32x4_t*)x0 : (SPEC_LDS u32x4_t*)x1) +
+                  (wm % (WGM / 2)) * WM * WN;
+      block_barrier();  // every wave is done with the stages
+      if (wn == 1) {
+#pragma unroll
+        for (int b = 0; b < FB; ++b)
+#pragma unroll
+          for (int a = 0; a < FA; ++a)
+            *(f32x4*)(ex + (16 * b + c) * WN + 16 * a + 4 * g) = acc[a][b];
+      }
+      wait_lgkm0();
+      block_barrier();
+      if (wn == 0) {
+        const int hn = N / 2;
+#pragma unroll
+        for (int b = 0; b < FB; ++b) {
+          const int m = q.m0 + wm * WM + 16 * b + c;
+          if (m >= M) continue;
+#pragma unroll
+          for (int a = 0; a < FA; ++a) {
+            const int n = q.n0 / 2 + 16 * a + 4 * g;
+            const f32x4 u = *(const f32x4*)(ex + (16 * b + c) * WN + 16 * a + 4 * g);
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float gt = acc[a][b][r];
+              v[r] = gt / (1.f + expf(-gt)) * u[r];
+            }
+            bf16_t* dst = Y + (int64_t)m * hn + n;
+            if (n + 3 < hn) {
+              uint2 w2;
+              w2.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+              w2.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+              *(uint2*)dst = w2;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (n + r < hn) dst[r] = f32_to_bf16(v[r]);
+            }
+          }
+        }
+      }
+      return;
+    }
     float* Pb = P + (int64_t)q.split * M * N;
 #pragma unroll
     for (int b = 0; b < FB; ++b) {
@@ -391,22 +452,29 @@ int tile_grid(int ntiles) {
   return std::min(ntiles, cus[dev]);
 }
 
-template <bool REC, int BN>
+template <bool REC, int BN, bool SWI = false>
 hipError_t launch_tile(const void* X, int ldx, const void* W, int ldw, float* P, int M, int N,
-                       int K, int kc, int nsplit, float2* rec, hipStream_t s) {
+                       int K, int kc, int nsplit, float2* rec, hipStream_t s,
+                       bf16_t* Y = nullptr) {
   if (M <= 0 || N <= 0 || K % kTileBK != 0 || kc % kTileBK != 0 || kc <= 0 || nsplit < 1 ||
       (int64_t)(nsplit - 1) * kc >= K)
     return hipErrorInvalidValue;
   const int ntiles = ((N + BN - 1) / BN) * ((M + kTileBM - 1) / kTileBM) * nsplit;
   const int grid = tile_grid(ntiles);
-  if (grid < ntiles)
+  if constexpr (SWI) {
+    if (grid < ntiles || nsplit != 1 || N % BN != 0 || !Y) return hipErrorInvalidValue;
+    SPEC_LAUNCH((gemm_dma_kernel<BN, kTileBM, kTileBK, kTileThreads, kTileStages, false, false, true>),
+                dim3(ntiles), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W,
+                ldw, P, M, N, K, kc, ntiles, rec, Y);
+  } else if (grid < ntiles) {
     SPEC_LAUNCH((gemm_dma_kernel<BN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, true>),
                 dim3(grid), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W,
-                ldw, P, M, N, K, kc, ntiles, rec);
-  else
+                ldw, P, M, N, K, kc, ntiles, rec, Y);
+  } else {
     SPEC_LAUNCH((gemm_dma_kernel<BN, kTileBM, kTileBK, kTileThreads, kTileStages, REC, false>),
                 dim3(ntiles), dim3(kTileThreads), 0, s, (const bf16_t*)X, ldx, (const bf16_t*)W,
-                ldw, P, M, N, K, kc, ntiles, rec);
+                ldw, P, M, N, K, kc, ntiles, rec, Y);
+  }
   return hipGetLastError();
 }
 
@@ -424,6 +492,21 @@ hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, i
 }
 
 int gemm_tile_strips(int N) { return (N + kTileBN - 1) / kTileBN; }
+
+bool gemm_tile_swiglu_ok(int M, int N, int K, const GemmPlan& plan) {
+  if (!plan.tile || plan.nsplit != 1 || plan.bn != kTileBNNarrow || N % kTileBNNarrow != 0 ||
+      K % kTileBK != 0)
+    return false;
+  const int ntiles = (N / kTileBNNarrow) * ((M + kTileBM - 1) / kTileBM);
+  return tile_grid(ntiles) >= ntiles;
+}
+
+hipError_t gemm_tile_swiglu(const void* X, int ldx, const void* W, int ldw, void* Y, int M, int N,
+                            int K, const GemmPlan& plan, hipStream_t s) {
+  if (!gemm_tile_swiglu_ok(M, N, K, plan)) return hipErrorInvalidValue;
+  return launch_tile<false, kTileBNNarrow, true>(X, ldx, W, ldw, nullptr, M, N, K, plan.kc, 1,
+                                                 nullptr, s, (bf16_t*)Y);
+}
 
 hipError_t gemm_tile_records(const void* X, int ldx, const void* W, int ldw, float* z, int M,
                              int N, int K, void* rec, hipStream_t s) {

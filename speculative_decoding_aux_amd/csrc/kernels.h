@@ -25,6 +25,12 @@ hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, i
 // exp(v - max)) per row and 128-column strip, float2 [M][strips], for the
 // vocab top-k.
 int gemm_tile_strips(int N);
+// gate|up projection with the SwiGLU fused: W [gate (N/2) | up (N/2)] rows,
+// Y[M][N/2] = bf16(silu(X.gate^T) * X.up^T) with no partials, where the plan
+// is one unsplit launch of 96-row tiles, at most one per CU (_ok says so).
+bool gemm_tile_swiglu_ok(int M, int N, int K, const GemmPlan& plan);
+hipError_t gemm_tile_swiglu(const void* X, int ldx, const void* W, int ldw, void* Y, int M, int N,
+                            int K, const GemmPlan& plan, hipStream_t s);
 hipError_t gemm_tile_records(const void* X, int ldx, const void* W, int ldw, float* z, int M,
                              int N, int K, void* rec, hipStream_t s);
 // tag 1 launches a separately named instance (the LM head and score GEMMs).

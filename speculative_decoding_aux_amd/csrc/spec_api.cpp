@@ -480,8 +480,12 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
   }
   {
     const GemmPlan p = gemm_plan(M, 2 * I, H, bf);
-    SPEC_HIP(ctx, gemm(bf, ws.mn, H, w->w_gate_up, H, P, M, 2 * I, H, p, s));
-    SPEC_HIP(ctx, gemm_epilogue(bf, EPI_SWIGLU, ws.s, nullptr, P, p.nsplit, M, I, s));
+    if (bf && gemm_tile_swiglu_ok(M, 2 * I, H, p)) {
+      SPEC_HIP(ctx, gemm_tile_swiglu(ws.mn, H, w->w_gate_up, H, ws.s, M, 2 * I, H, p, s));
+    } else {
+      SPEC_HIP(ctx, gemm(bf, ws.mn, H, w->w_gate_up, H, P, M, 2 * I, H, p, s));
+      SPEC_HIP(ctx, gemm_epilogue(bf, EPI_SWIGLU, ws.s, nullptr, P, p.nsplit, M, I, s));
+    }
   }
   {
     const GemmPlan p = gemm_plan(M, H, I, bf, kResidNormSplit);
@@ -1036,8 +1040,12 @@ spec_status spec_target_forward(spec_ctx* ctx, const spec_target_weights* tw,
     }
     {
       const GemmPlan p = gemm_plan(M, 2 * I, H, bf);
-      SPEC_HIP(ctx, gemm(bf, ws.mn, H, y.w_gate_up, H, P, M, 2 * I, H, p, s));
-      SPEC_HIP(ctx, gemm_epilogue(bf, EPI_SWIGLU, ws.s, nullptr, P, p.nsplit, M, I, s));
+      if (bf && gemm_tile_swiglu_ok(M, 2 * I, H, p)) {
+        SPEC_HIP(ctx, gemm_tile_swiglu(ws.mn, H, y.w_gate_up, H, ws.s, M, 2 * I, H, p, s));
+      } else {
+        SPEC_HIP(ctx, gemm(bf, ws.mn, H, y.w_gate_up, H, P, M, 2 * I, H, p, s));
+        SPEC_HIP(ctx, gemm_epilogue(bf, EPI_SWIGLU, ws.s, nullptr, P, p.nsplit, M, I, s));
+      }
     }
     {
       const GemmPlan p = gemm_plan(M, H, I, bf);
