@@ -673,14 +673,6 @@ __global__ __launch_bounds__(256) void topk_strip_merge_kernel(int n, int k, int
     }
   }
   __syncthreads();
-  float bm = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) bm = fmaxf(bm, smax[w]);
-  double bs = 0.0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-    if (smax[w] != -INFINITY) bs += (double)ssum[w] * exp((double)smax[w] - (double)bm);
-  const double lse = (double)bm + log(bs);
   if (wave == 0) {  // the k best strips
     List<1> one;
     one.init();
@@ -700,19 +692,34 @@ __global__ __launch_bounds__(256) void topk_strip_merge_kernel(int n, int k, int
     }
   }
   __syncthreads();
-  // candidate q = t + 256 h: column q % 128 of the (q / 128)-th best strip
+  // candidate q = t + 256 h: column q % 128 of the (q / 128)-th best strip;
+  // the loads go out first, the row logsumexp is taken while they fly
   constexpr int CPT = KM * kStripW / 256;
-  List<KM < CPT ? KM : CPT> cand;
-  cand.init();
+  float cz[CPT];
+  int cx[CPT];
 #pragma unroll
   for (int h = 0; h < CPT; ++h) {
     const int q = t + 256 * h, rank = q / kStripW;
     const int st = sel[rank];
-    if (rank < k && st != kIdNone) {
-      const int x = st * kStripW + q % kStripW;
-      if (x < n) cand.insert(row[x], x);
-    }
+    cx[h] = rank < k && st != kIdNone ? st * kStripW + q % kStripW : n;
+    cz[h] = cx[h] < n ? row[cx[h]] : -INFINITY;
   }
+  double lse = 0.0;
+  if (wave == 0) {
+    float bm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) bm = fmaxf(bm, smax[w]);
+    double bs = 0.0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (smax[w] != -INFINITY) bs += (double)ssum[w] * exp((double)smax[w] - (double)bm);
+    lse = (double)bm + log(bs);
+  }
+  List<KM < CPT ? KM : CPT> cand;
+  cand.init();
+#pragma unroll
+  for (int h = 0; h < CPT; ++h)
+    if (cx[h] < n) cand.insert(cz[h], cx[h]);
   float cv[KM];
   int cid[KM];
   wave_merge<KM < CPT ? KM : CPT, KM>(cand, k, cv, cid);
