@@ -14,8 +14,14 @@
 // top-k set) by radix selection over key intervals: each level histograms the
 // candidate interval into at most 2048 power-of-two-wide bins in LDS, keeps
 // the bin where the running count or mass from the top crosses the target,
-// and stops when that bin holds one token.  Masses are exp(l/T - max) in
-// float32 summed in float64.  A draft is accepted iff u <= p_f(x).
+// and stops when that bin holds one token.  The first level (4096 bins of
+// the top 12 key bits) counts the row in the same pass as the maximum; when
+// the bins from the k-th best token's up hold at most the 8192 keys LDS
+// takes, the second pass copies them there and both cuts are taken on that
+// list, else the second pass histograms the masses and the cut bins are
+// collected (or, when too full, rescanned) one at a time.  Masses are
+// exp(l/T - max) in float32 summed in float64.  A draft is accepted iff
+// u <= p_f(x).
 // Stage 2, vocabulary chunks of each request's stop row (first rejection, or
 // the bonus row): the Gumbel-max over the kept tokens with the rejected draft
 // excluded, U from the Philox4x32-10 stream of the tree verifier with
@@ -401,7 +407,18 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(
   const float T = temperature[r];
   const bool greedy = !(T > 0.f) || uniform == nullptr;
   const int x = j < n ? drafts[start + j] : -1;
-  // pass 1: max / argmax
+  const int k = greedy || !top_k ? 0 : top_k[r];
+  const float p = greedy || !top_p ? 1.0f : top_p[r];
+  const bool use_k = k > 0 && k < V, use_p = p < 1.0f;
+  const bool hist = use_k || use_p;  // the row needs the first-level histogram
+  if (hist) {
+    for (int i = t; i < kL0Bins; i += kRowThreads) {
+      s.l0_cnt[i] = 0;
+      s.l0_mass[i] = 0.0;
+    }
+    __syncthreads();
+  }
+  // pass 1: max / argmax, and the first-level counts (they need no maximum)
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   for_row(row, V, [&](float l, int v) {
@@ -409,6 +426,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(
       bv = l;
       bi = v;
     }
+    if (hist) atomicAdd(&s.l0_cnt[(int)(tok_key(l, v) >> kL0Shift)], 1u);
   });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -424,11 +442,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(
     s.red_f[w] = bv;
     s.red_i[w] = bi;
   }
-  for (int i = t; i < kL0Bins; i += kRowThreads) {
-    s.l0_cnt[i] = 0;
-    s.l0_mass[i] = 0.0;
-  }
-  __syncthreads();
+  __syncthreads();  // also orders the counts before their use
   for (int i = 0; i < kRowThreads / 64; ++i)
     if (better(s.red_f[i], s.red_i[i], bv, bi)) {
       bv = s.red_f[i];
@@ -447,86 +461,118 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(
   }
   const float invT = 1.0f / T;
   const float zmax = bv * invT;
-  const int k = top_k ? top_k[r] : 0;
-  const float p = top_p ? top_p[r] : 1.0f;
-  const bool use_k = k > 0 && k < V, use_p = p < 1.0f;
-  // pass 2: first-level histogram (count and mass) over the whole row
-  double sum = 0.0;
-  for_row(row, V, [&](float l, int v) {
-    const int b = (int)(tok_key(l, v) >> kL0Shift);
-    const double e = l == -INFINITY ? 0.0 : (double)expf(l * invT - zmax);
-    sum += e;
-    if (use_k || use_p) {
-      atomicAdd(&s.l0_cnt[b], 1u);
-      if (e != 0.0) atomicAdd(&s.l0_mass[b], e);
-    }
-  });
-  double S = block_sum(sum, s.red_d);  // also orders the histogram before its use
-  unsigned long long kstar = 0;        // kept iff key >= kstar
-  int cbin = -1;                       // first-level bin whose keys are in s.cand
-  int ncand = 0;
-  int bk = -1;                         // first-level bin of the k-th best token
+  // the first-level bin of the k-th best token, from the counts
+  int bk = -1;
+  unsigned int above = 0, cbk = 0;
   if (use_k) {
-    // the first-level bin holding the k-th best token, then the token itself
     scan_pick<false>(s.l0_cnt, s.l0_mass, kL0Bins, (unsigned int)k, 0.0, s);
     bk = s.sel_bin;
-    const unsigned int above = s.sel_above_cnt;
-    const unsigned int cbk = s.l0_cnt[bk];
-    double above_mass = 0.0;
-    for (int b = kL0Bins - 1 - t; b > bk; b -= kRowThreads) above_mass += s.l0_mass[b];
-    above_mass = block_sum(above_mass, s.red_d);
-    double unused;
-    if (cbk <= (unsigned int)kCap) {
-      ncand = collect_bin(row, V, bk, s);
-      cbin = bk;
-      const CandSrc cs{s.cand, ncand};
-      kstar = radix_select<false>(cs, invT, zmax, bin_lo(bk), bin_hi(bk), (unsigned int)k - above,
-                                  0.0, &unused, s);
-      S = above_mass + mass_in(cs, invT, zmax, kstar, bin_hi(bk), s);
-    } else {
-      const RowSrc rs{row, V};
-      kstar = radix_select<false>(rs, invT, zmax, bin_lo(bk), bin_hi(bk), (unsigned int)k - above,
-                                  0.0, &unused, s);
-      S = above_mass + mass_in(rs, invT, zmax, kstar, bin_hi(bk), s);
-    }
-    // the top-k set as a first-level histogram: bins below bk emptied, bin
-    // bk reduced to its kept part
-    const int bkeep = bk;
-    for (int b = t; b < bkeep; b += kRowThreads) {
-      s.l0_cnt[b] = 0;
-      s.l0_mass[b] = 0.0;
-    }
-    __syncthreads();
-    if (t == 0) {
-      s.l0_cnt[bkeep] = (unsigned int)k - above;
-      s.l0_mass[bkeep] = S - above_mass;
-    }
-    __syncthreads();
+    above = s.sel_above_cnt;
+    cbk = s.l0_cnt[bk];
   }
-  if (use_p) {
-    const double target = (double)p * S;
-    scan_pick<true>(s.l0_cnt, s.l0_mass, kL0Bins, 0u, target, s);
-    const int bp = s.sel_bin;
-    const double above_mass = s.sel_above_mass;
-    const unsigned int cbp = s.l0_cnt[bp];
+  // Top-k sets that fit in LDS: pass 2 collects the keys of every bin from
+  // bk up (the whole top-k set and the rest of bin bk), and both cuts are
+  // then taken on that list: no mass histogram and no further row pass.
+  double S = 0.0;
+  unsigned long long kstar = 0;  // kept iff key >= kstar
+  if (use_k && above + cbk <= (unsigned int)kCap) {
+    const unsigned long long glo = bin_lo(bk);
+    if (t == 0) s.ncand = 0;
     __syncthreads();
-    // in the top-k cut's bin only its kept part counts; its tokens are in
-    // LDS when the top-k selection collected them, else the row is scanned
-    const unsigned long long lo = bp == bk ? kstar : bin_lo(bp);
-    const bool have = bp == cbin;
-    double upto = 0.0;
-    if (have || (bp != bk && cbp <= (unsigned int)kCap)) {
-      if (!have) {
-        ncand = collect_bin(row, V, bp, s);
-        cbin = bp;
+    for_row(row, V, [&](float l, int v) {
+      const unsigned long long key = tok_key(l, v);
+      const bool in = key >= glo;
+      const unsigned long long m = __ballot(in);
+      if (m) {
+        const int lane = t & 63;
+        const int leader = __ffsll((long long)m) - 1;
+        int base = 0;
+        if (lane == leader) base = atomicAdd(&s.ncand, __popcll(m));
+        base = __shfl(base, leader, 64);
+        const int pos = base + __popcll(m & ((1ull << lane) - 1));
+        if (in && pos < kCap) s.cand[pos] = key;
       }
-      const CandSrc cs{s.cand, ncand};
-      kstar = radix_select<true>(cs, invT, zmax, lo, bin_hi(bp), 0u, target - above_mass, &upto, s);
-    } else {
-      const RowSrc rs{row, V};
-      kstar = radix_select<true>(rs, invT, zmax, lo, bin_hi(bp), 0u, target - above_mass, &upto, s);
+    });
+    __syncthreads();
+    const CandSrc cs{s.cand, min(s.ncand, kCap)};
+    const unsigned long long ktop = tok_key(bv, bi);  // the best key of the row
+    double unused;
+    kstar = radix_select<false>(cs, invT, zmax, glo, bin_hi(bk), (unsigned int)k - above, 0.0,
+                                &unused, s);
+    S = mass_in(cs, invT, zmax, kstar, ktop, s);
+    if (use_p) {
+      double upto = 0.0;
+      kstar = radix_select<true>(cs, invT, zmax, kstar, ktop, 0u, (double)p * S, &upto, s);
+      S = upto;
     }
-    S = above_mass + upto;
+  } else {
+    // pass 2: the first-level masses and the row's mass
+    double sum = 0.0;
+    for_row(row, V, [&](float l, int v) {
+      const double e = l == -INFINITY ? 0.0 : (double)expf(l * invT - zmax);
+      sum += e;
+      if (hist && e != 0.0) atomicAdd(&s.l0_mass[(int)(tok_key(l, v) >> kL0Shift)], e);
+    });
+    S = block_sum(sum, s.red_d);  // also orders the histogram before its use
+    int cbin = -1;                // first-level bin whose keys are in s.cand
+    int ncand = 0;
+    if (use_k) {
+      // the k-th best token in bin bk
+      double above_mass = 0.0;
+      for (int b = kL0Bins - 1 - t; b > bk; b -= kRowThreads) above_mass += s.l0_mass[b];
+      above_mass = block_sum(above_mass, s.red_d);
+      double unused;
+      if (cbk <= (unsigned int)kCap) {
+        ncand = collect_bin(row, V, bk, s);
+        cbin = bk;
+        const CandSrc cs{s.cand, ncand};
+        kstar = radix_select<false>(cs, invT, zmax, bin_lo(bk), bin_hi(bk), (unsigned int)k - above,
+                                    0.0, &unused, s);
+        S = above_mass + mass_in(cs, invT, zmax, kstar, bin_hi(bk), s);
+      } else {
+        const RowSrc rs{row, V};
+        kstar = radix_select<false>(rs, invT, zmax, bin_lo(bk), bin_hi(bk), (unsigned int)k - above,
+                                    0.0, &unused, s);
+        S = above_mass + mass_in(rs, invT, zmax, kstar, bin_hi(bk), s);
+      }
+      // the top-k set as a first-level histogram: bins below bk emptied, bin
+      // bk reduced to its kept part
+      for (int b = t; b < bk; b += kRowThreads) {
+        s.l0_cnt[b] = 0;
+        s.l0_mass[b] = 0.0;
+      }
+      __syncthreads();
+      if (t == 0) {
+        s.l0_cnt[bk] = (unsigned int)k - above;
+        s.l0_mass[bk] = S - above_mass;
+      }
+      __syncthreads();
+    }
+    if (use_p) {
+      const double target = (double)p * S;
+      scan_pick<true>(s.l0_cnt, s.l0_mass, kL0Bins, 0u, target, s);
+      const int bp = s.sel_bin;
+      const double above_mass = s.sel_above_mass;
+      const unsigned int cbp = s.l0_cnt[bp];
+      __syncthreads();
+      // in the top-k cut's bin only its kept part counts; its tokens are in
+      // LDS when the top-k selection collected them, else the row is scanned
+      const unsigned long long lo = bp == bk ? kstar : bin_lo(bp);
+      const bool have = bp == cbin;
+      double upto = 0.0;
+      if (have || (bp != bk && cbp <= (unsigned int)kCap)) {
+        if (!have) {
+          ncand = collect_bin(row, V, bp, s);
+          cbin = bp;
+        }
+        const CandSrc cs{s.cand, ncand};
+        kstar = radix_select<true>(cs, invT, zmax, lo, bin_hi(bp), 0u, target - above_mass, &upto, s);
+      } else {
+        const RowSrc rs{row, V};
+        kstar = radix_select<true>(rs, invT, zmax, lo, bin_hi(bp), 0u, target - above_mass, &upto, s);
+      }
+      S = above_mass + upto;
+    }
   }
   out.kstar = kstar;
   out.skept = S;

@@ -154,3 +154,40 @@ def test_degenerate_filters(k, p, T):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), want_out)
     np.testing.assert_array_equal(acc.cpu().numpy(), want_acc)
+
+
+@pytest.mark.parametrize("k,p", [(5000, 1.0), (5000, 0.9), (9000, 1.0), (40000, 0.5)])
+def test_large_top_k_sets(k, p):
+    """Logits uniform on [0, 16) put 4096 of the 65536 tokens in each of the
+    eight first-level bins of [8, 16) (sign, exponent and three mantissa
+    bits): with top-k 5000 the keys of the cut's bin and the bins above it
+    fill the 8192 that LDS holds, with 9000 and 40000 the tokens above the
+    cut are more than LDS holds and only the cut's bin is collected.  The
+    draft tokens are raised above the rest, so that some are accepted."""
+    announce(f"rejection sample large top-k k={k} p={p}")
+    V, B, L = 65536, 8, 4
+    rng = np.random.default_rng(4100 + k)
+    for s in range(40):
+        d = gen.flat_batch(5300 + s, B, L, V, greedy_frac=0.0)
+        meta = osm.spec_decode_metadata(d["cu_num_scheduled_tokens"], d["num_draft_tokens"])
+        cu, _, tgt, bonus = meta
+        lg = rng.uniform(0.0, 16.0, d["logits"].shape).astype(np.float32)
+        lg[tgt, d["draft_token_ids"]] = rng.uniform(17.0, 26.0, len(tgt)).astype(np.float32)
+        d["logits"] = lg
+        d["temperature"][:] = 1.0
+        d["top_k"][:] = k
+        d["top_p"][:] = p
+        if _margins_ok(d, meta):
+            break
+    else:
+        pytest.fail("no seed with clear decision margins")
+    want_out, want_acc = osm.rejection_sample(cu, d["draft_token_ids"], d["logits"], tgt, bonus,
+                                              d["temperature"], d["top_k"], d["top_p"], d["uniform"],
+                                              d["seed"], L)
+    ctx = _ctx(V, B, L)
+    out, acc = S.spec_rejection_sample(ctx, cu, d["draft_token_ids"], torch.from_numpy(d["logits"]).to(DEV),
+                                       tgt, bonus, d["temperature"], d["top_k"], d["top_p"], d["uniform"],
+                                       d["seed"], L)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), want_out)
+    np.testing.assert_array_equal(acc.cpu().numpy(), want_acc)
