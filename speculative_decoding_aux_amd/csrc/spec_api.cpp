@@ -407,6 +407,11 @@ KvPages kv_pages(const spec_kv* kv) {
   return pg;
 }
 
+// Split-K depth of a GEMM whose partials one resid_norm workgroup per row
+// sums: as many H-wide float32 partials as kResidNormSplit rows of 4096 (the
+// bound resid_norm_ok applies at few rows), so narrower layers split deeper.
+static int resid_norm_split(int H) { return std::max(1, kResidNormSplit * 4096 / std::max(1, H)); }
+
 spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, const PassIO& io,
                      hipStream_t s) {
   const spec_config& c = ctx->cfg;
@@ -468,7 +473,7 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
   // (at few rows the O and down GEMMs split K less, so that one launch per row
   // can sum the splits and take the norm)
   {
-    const GemmPlan p = gemm_plan(M, H, nqd, bf, kResidNormSplit);
+    const GemmPlan p = gemm_plan(M, H, nqd, bf, resid_norm_split(H));
     SPEC_HIP(ctx, gemm(bf, ws.o, nqd, w->wo, nqd, P, M, H, nqd, p, s));
     if (resid_norm_ok(bf, M, H, p.nsplit, P, ws.g, ws.h1, w->post_attn_norm, ws.mn)) {
       SPEC_HIP(ctx, resid_norm(bf, P, p.nsplit, M, H, ws.g, ws.h1, w->post_attn_norm, c.rms_eps,
@@ -488,7 +493,7 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
     }
   }
   {
-    const GemmPlan p = gemm_plan(M, H, I, bf, kResidNormSplit);
+    const GemmPlan p = gemm_plan(M, H, I, bf, resid_norm_split(H));
     SPEC_HIP(ctx, gemm(bf, ws.s, I, w->w_down, I, P, M, H, I, p, s));
     // S8: final norm (then the LM head; S9: top-k with log-probs)
     if (resid_norm_ok(bf, M, H, p.nsplit, P, ws.h1, io.hidden_out, w->final_norm, ws.nrm)) {
@@ -1029,7 +1034,7 @@ spec_status spec_target_forward(spec_ctx* ctx, const spec_target_weights* tw,
       SPEC_HIP(ctx, attention(bf, a, s));
     }
     {
-      const GemmPlan p = gemm_plan(M, H, nqd, bf, kResidNormSplit);
+      const GemmPlan p = gemm_plan(M, H, nqd, bf, resid_norm_split(H));
       SPEC_HIP(ctx, gemm(bf, ws.o, nqd, y.wo, nqd, P, M, H, nqd, p, s));
       if (resid_norm_ok(bf, M, H, p.nsplit, P, h, ws.h1, y.mlp_norm, ws.mn)) {
         SPEC_HIP(ctx, resid_norm(bf, P, p.nsplit, M, H, h, ws.h1, y.mlp_norm, c.rms_eps, ws.mn, s));
