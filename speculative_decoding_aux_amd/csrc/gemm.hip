@@ -674,9 +674,9 @@ GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split) {
   const int cw = gemm_cw(M, N);
   const int strips = (N + 64 * cw - 1) / (64 * cw);
   const int mblocks = (M + 63) / 64;
-  // workgroups in flight: beyond 16 rows each split's M x N float32 partial
-  // costs more, and 512 workgroups of four waves still stream at full rate
-  const int target = M > 16 ? 512 : (cw == 1 ? 1024 : 2048);
+  // workgroups in flight: 512 of four waves stream the weights at full rate;
+  // more only add split-K partials
+  const int target = 512;
   int ns = (target + strips * mblocks - 1) / (strips * mblocks);
   // K in blocks of 512 where the activation rows go through LDS (see
   // stream_acc_lds: K steps in pairs of 256), else of 128
