@@ -655,9 +655,12 @@ __global__ __launch_bounds__(256) void qkv_epi_rows_kernel(
 
 // Columns per wave: 16 for the very wide LM head at M <= 32 (one long K sweep
 // per wave, no split, twice the strips), 32 otherwise (twice the loads in
-// flight, and each activation fragment feeds two weight tiles).
+// flight, and each activation fragment feeds two weight tiles).  With the
+// top-k fused into the epilogue only up to 16 rows: every strip adds a record
+// list per row that the merge reads.
 static constexpr int kMaxSplit = 32;  // bounds the epilogue's reduction depth
 static int gemm_cw(int M, int N) { return (M <= 32 && N >= 65536) ? 1 : 2; }
+static int lmhead_cw(int M, int N) { return (M <= 16 && N >= 65536) ? 1 : 2; }
 
 GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split) {
   GemmPlan p;
@@ -736,7 +739,7 @@ hipError_t gemm(bool bf16, const void* X, int ldx, const void* W, int ldw, float
 }
 
 int gemm_strips(int M, int N) {
-  const int cw = gemm_cw(M, N);
+  const int cw = lmhead_cw(M, N);
   return (N + 64 * cw - 1) / (64 * cw);
 }
 
@@ -772,7 +775,7 @@ hipError_t gemm_lmhead_topk(const void* X, int ldx, const void* W, int ldw, floa
   float* pv = (float*)part;
   int* pi = (int*)(pv + (size_t)M * nch * km);
   topkdev::Part* pp = (topkdev::Part*)(pi + (size_t)M * nch * km);
-  const bool cw1 = gemm_cw(M, N) == 1;
+  const bool cw1 = lmhead_cw(M, N) == 1;
   if (M <= 16) {
     if (cw1) launch_lmhead<1, 1>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
     else launch_lmhead<1, 2>(X, ldx, W, ldw, z, M, N, K, km, pv, pi, pp, s);
