@@ -142,6 +142,68 @@ __global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restri
   }
 }
 
+// Short rows (n <= kSmallRow, one chunk): one wave per row takes the k best
+// and the log-probs in one launch (four rows per 256-thread block), with the
+// partial kernel's per-value steps and the merge's output rule.
+constexpr int kSmallRow = 512;
+
+template <int KM>
+__global__ __launch_bounds__(256) void topk_small_kernel(const float* __restrict__ z, int M, int n,
+                                                         int ldz, int k,
+                                                         const int* __restrict__ id_map,
+                                                         const int* __restrict__ rowmap,
+                                                         int* __restrict__ ids, int ldi,
+                                                         float* __restrict__ logp, int ldl) {
+  constexpr int U = kSmallRow / 64;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= M) return;  // whole waves
+  const float* row = z + (int64_t)r * ldz;
+  const int* rm = rowmap ? rowmap + (int64_t)r * n : nullptr;
+  float v[U];
+  int id[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {  // every load issued before the first is used
+    const int x = min(lane + 64 * u, n - 1);
+    v[u] = row[x];
+    id[u] = rm ? rm[x] : x;
+  }
+  List<KM> L;
+  L.init();
+  float m = -INFINITY;
+  double sm = 0.0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (lane + 64 * u >= n) continue;
+    L.insert(v[u], id[u]);
+    if (v[u] > m) {
+      sm = (m == -INFINITY ? 0.0 : sm * (double)expf(m - v[u])) + 1.0;
+      m = v[u];
+    } else {
+      sm += (double)expf(v[u] - m);
+    }
+  }
+  const float wm = wave_max(m);
+  double ws = m == -INFINITY ? 0.0 : sm * (double)expf(m - wm);
+  ws = wave_sum(ws);
+  const float lse = (float)((double)wm + log(ws));
+  float ov[KM];
+  int oi[KM];
+  wave_merge<KM, KM>(L, k, ov, oi);
+  if (lane < k) {
+    float bv = 0.f;
+    int bi = 0;
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j == lane) {
+        bv = ov[j];
+        bi = oi[j];
+      }
+    ids[(int64_t)r * ldi + lane] = rowmap ? bi : (id_map ? id_map[clampi(bi, 0, n - 1)] : bi);
+    logp[(int64_t)r * ldl + lane] = bv - lse;
+  }
+}
+
 // Merge of per-chunk records of a row (merge_row): one 256-thread block per row.
 template <int KM>
 __global__ __launch_bounds__(256) void topk_merge_kernel(int n, int k, int nch,
@@ -760,6 +822,11 @@ template <int KM>
 hipError_t launch_topk(const float* z, int M, int n, int ldz, int k, const int* id_map,
                        const int* rowmap, int* ids, int ldi, float* logp, int ldl, void* part,
                        int nch, int chunk, hipStream_t s) {
+  if (nch == 1 && n >= 1 && n <= kSmallRow) {
+    SPEC_LAUNCH(topk_small_kernel<KM>, dim3((M + 3) / 4), dim3(256), 0, s, z, M, n, ldz, k, id_map,
+                rowmap, ids, ldi, logp, ldl);
+    return hipGetLastError();
+  }
   float* pv = (float*)part;
   int* pi = (int*)(pv + (size_t)M * nch * KM);
   Part* pp = (Part*)(pi + (size_t)M * nch * KM);

@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("M,n,k,mapped", [(4, 128256, 1, False), (1, 32000, 8, True), (8, 32000, 8, True),
                                           (256, 151936, 8, False), (3, 1000, 16, False), (2, 37, 5, False),
-                                          (64, 4096, 3, False)])
+                                          (64, 4096, 3, False), (5, 128, 8, True), (7, 500, 16, False),
+                                          (2, 512, 4, False)])
 def test_topk_logprobs_match_oracle(M, n, k, mapped):
     announce(f"topk M={M} n={n} k={k}")
     z = gen.random_logits(M * 7 + n, "topk", (M, n))
