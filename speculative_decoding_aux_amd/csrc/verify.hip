@@ -448,47 +448,55 @@ __global__ __launch_bounds__(64) void verify_emit_kernel(int D, int nch,
   if (lane == 0) out_tokens[(int64_t)b * (D + 1) + clampi(accepted_len[b], 0, D)] = gi;
 }
 
-// One block per (sequence, layer, kv-head): read every accepted row, then write.
+// One block per (sequence, layer, group of HG kv-heads): for each head of the
+// group, read every accepted row, then write (heads touch disjoint rows, so
+// only the read-then-write order within a head needs the barrier).  Grouping
+// heads keeps the block count near what the chip dispatches quickly when the
+// cache has many layers and sequences.
 template <int VEC_PER_ROW>
 __global__ __launch_bounds__(256) void compact_kernel(char* __restrict__ kb, char* __restrict__ vb,
                                                       int64_t sl_bytes, int64_t ss_bytes,
                                                       int64_t sh_bytes, int slots, KvPages pg,
                                                       const int* __restrict__ base,
                                                       const int* __restrict__ nodes,
-                                                      const int* __restrict__ alen, int max_accept) {
-  const int b = blockIdx.x, layer = blockIdx.y, h = blockIdx.z, t = threadIdx.x;
+                                                      const int* __restrict__ alen, int max_accept,
+                                                      int nkv, int hg) {
+  const int b = blockIdx.x, layer = blockIdx.y, t = threadIdx.x;
   const int a = clampi(alen[b], 0, max_accept);
   const int bs = base[b];
-  const int64_t off = layer * sl_bytes + h * sh_bytes;  // + the row of (b, slot)
   constexpr int kRow = VEC_PER_ROW * 16;
   constexpr int kPer = (2 * 64 * VEC_PER_ROW + 255) / 256;  // up to 64 rows of K and V
-  u32x4_t buf[kPer];
   const int total = 2 * a * VEC_PER_ROW;
+  const int h1 = min(nkv, (blockIdx.z + 1) * hg);
+  for (int h = blockIdx.z * hg; h < h1; ++h) {
+    const int64_t off = layer * sl_bytes + h * sh_bytes;  // + the row of (b, slot)
+    u32x4_t buf[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = t + 256 * i;
-    if (e < total) {
-      const int kv = e / (a * VEC_PER_ROW), rem = e % (a * VEC_PER_ROW);
-      const int j = rem / VEC_PER_ROW, q = rem % VEC_PER_ROW;
-      const int src = bs + nodes[(int64_t)b * max_accept + j];
-      if (src >= 0 && src < slots) {
-        const char* p = (kv ? vb : kb) + off + kv_slot_off(pg, b, src, ss_bytes, kRow) + q * 16;
-        buf[i] = *(const u32x4_t*)p;
+    for (int i = 0; i < kPer; ++i) {
+      const int e = t + 256 * i;
+      if (e < total) {
+        const int kv = e / (a * VEC_PER_ROW), rem = e % (a * VEC_PER_ROW);
+        const int j = rem / VEC_PER_ROW, q = rem % VEC_PER_ROW;
+        const int src = bs + nodes[(int64_t)b * max_accept + j];
+        if (src >= 0 && src < slots) {
+          const char* p = (kv ? vb : kb) + off + kv_slot_off(pg, b, src, ss_bytes, kRow) + q * 16;
+          buf[i] = *(const u32x4_t*)p;
+        }
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int e = t + 256 * i;
-    if (e < total) {
-      const int kv = e / (a * VEC_PER_ROW), rem = e % (a * VEC_PER_ROW);
-      const int j = rem / VEC_PER_ROW, q = rem % VEC_PER_ROW;
-      const int src = bs + nodes[(int64_t)b * max_accept + j];
-      const int dst = bs + 1 + j;
-      if (src >= 0 && src < slots && dst >= 0 && dst < slots) {
-        char* p = (kv ? vb : kb) + off + kv_slot_off(pg, b, dst, ss_bytes, kRow) + q * 16;
-        *(u32x4_t*)p = buf[i];
+    for (int i = 0; i < kPer; ++i) {
+      const int e = t + 256 * i;
+      if (e < total) {
+        const int kv = e / (a * VEC_PER_ROW), rem = e % (a * VEC_PER_ROW);
+        const int j = rem / VEC_PER_ROW, q = rem % VEC_PER_ROW;
+        const int src = bs + nodes[(int64_t)b * max_accept + j];
+        const int dst = bs + 1 + j;
+        if (src >= 0 && src < slots && dst >= 0 && dst < slots) {
+          char* p = (kv ? vb : kb) + off + kv_slot_off(pg, b, dst, ss_bytes, kRow) + q * 16;
+          *(u32x4_t*)p = buf[i];
+        }
       }
     }
   }
@@ -601,17 +609,20 @@ hipError_t compact(bool bf16, KvFull kv, int B, const int* base, const int* node
                    const int* alen, int max_accept, hipStream_t s) {
   const int esz = bf16 ? 2 : 4;
   const int row_bytes = kv.hd * esz;
-  const dim3 grid(B, kv.layers, kv.nkv);
+  // heads per block: about 1024 blocks in all
+  const int64_t units = (int64_t)B * kv.layers * kv.nkv;
+  const int hg = (int)std::max<int64_t>(1, std::min<int64_t>(kv.nkv, units / 1024));
+  const dim3 grid(B, kv.layers, (kv.nkv + hg - 1) / hg);
   const int64_t sl = kv.stride_layer * esz, ss = kv.stride_seq * esz, sh = kv.stride_head * esz;
   if (row_bytes == 256) {
     SPEC_LAUNCH(compact_kernel<16>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
-                       sh, kv.slots, kv.pg, base, nodes, alen, max_accept);
+                       sh, kv.slots, kv.pg, base, nodes, alen, max_accept, kv.nkv, hg);
   } else if (row_bytes == 128) {
     SPEC_LAUNCH(compact_kernel<8>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
-                       sh, kv.slots, kv.pg, base, nodes, alen, max_accept);
+                       sh, kv.slots, kv.pg, base, nodes, alen, max_accept, kv.nkv, hg);
   } else {
     SPEC_LAUNCH(compact_kernel<32>, grid, dim3(256), 0, s, (char*)kv.k, (char*)kv.v, sl, ss,
-                       sh, kv.slots, kv.pg, base, nodes, alen, max_accept);
+                       sh, kv.slots, kv.pg, base, nodes, alen, max_accept, kv.nkv, hg);
   }
   return hipGetLastError();
 }
