@@ -447,7 +447,8 @@ __global__ __launch_bounds__(256) void epi_f32(float* __restrict__ Y, const floa
 
 // Split-K LM head whose logits are materialised: z = the sum of the nsplit
 // partials (in split order) and one (max, sum of exp(v - max)) record per row
-// and 128-column strip, the layout the strip top-k reads.  One wave per
+// and 128-column strip, the layout the strip top-k reads (with z == P and one
+// split, only the records of an output already written).  One wave per
 // (row, strip), two columns per lane.
 __global__ __launch_bounds__(256) void epi_f32_rec_kernel(float* __restrict__ z,
                                                           const float* __restrict__ P, int nsplit,
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(256) void epi_f32_rec_kernel(float* __restrict__ z,
       const float* p = P + (int64_t)m * N + n;
       float a = 0.f;
       for (int sp = 0; sp < nsplit; ++sp) a += p[sp * ss];
-      z[(int64_t)m * N + n] = a;
+      if (z != P) z[(int64_t)m * N + n] = a;  // z == P: records of a finished output
       v[j] = a;
       mx = fmaxf(mx, a);
     }

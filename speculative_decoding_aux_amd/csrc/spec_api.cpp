@@ -209,11 +209,9 @@ spec_status spec_create(const spec_config* cfg_in, spec_ctx** out) {
     // strip records of the tiled LM head (one per row and 128-column strip)
     if (bf16 && !c.cand_rank && lp.nsplit == 1 && lp.tile)
       tk = std::max(tk, (size_t)m * gemm_tile_strips(c.draft_vocab) * 8);
-    // EAGLE-4: strip records of the tiled candidate score GEMM
-    if (bf16 && c.cand_rank) {
-      const GemmPlan sp = gemm_plan(m, c.vocab, c.cand_rank, true);
-      if (sp.nsplit == 1 && sp.tile) tk = std::max(tk, (size_t)m * gemm_tile_strips(c.vocab) * 8);
-    }
+    // EAGLE-4: strip records of the candidate scores (one per row and
+    // 128-column strip, from the tiled score GEMM or the records epilogue)
+    if (bf16 && c.cand_rank) tk = std::max(tk, (size_t)m * gemm_tile_strips(c.vocab) * 8);
   }
   ctx->topk_bytes = tk;
   {
@@ -592,6 +590,24 @@ spec_status run_pass(spec_ctx* ctx, const spec_weights* w, const spec_kv* kv, co
       {
         ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
         SPEC_HIP(ctx, gemm_tile_records(ws.lowrank, r, w->cand_up, r, sc, M, V, r, ws.topk_part, s));
+      }
+      SPEC_HIP(ctx, topk_large_strips(sc, M, V, K, ws.topk_part, gemm_tile_strips(V), cid, s));
+    } else if (bf) {
+      // weight-streaming score GEMM, then one pass over its output (or the
+      // split-K sum) writing the strip records, so that the retrieval again
+      // reads only the strips that can hold one of the K best
+      if (p.nsplit == 1) {
+        {
+          ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
+          SPEC_HIP(ctx, gemm(bf, ws.lowrank, r, w->cand_up, r, sc, M, V, r, p, s, 1));
+        }
+        SPEC_HIP(ctx, gemm_epilogue_records(sc, 1, M, V, sc, ws.topk_part, s));
+      } else {
+        {
+          ProfScope ps(ctx, SPEC_PROF_LM_HEAD, s);
+          SPEC_HIP(ctx, gemm(bf, ws.lowrank, r, w->cand_up, r, P, M, V, r, p, s, 1));
+        }
+        SPEC_HIP(ctx, gemm_epilogue_records(P, p.nsplit, M, V, sc, ws.topk_part, s));
       }
       SPEC_HIP(ctx, topk_large_strips(sc, M, V, K, ws.topk_part, gemm_tile_strips(V), cid, s));
     } else {
