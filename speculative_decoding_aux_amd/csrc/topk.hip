@@ -685,6 +685,78 @@ __global__ __launch_bounds__(256) void gather_dot_vec_kernel(const bf16_t* __res
 // from the records and only their k * 128 logits are rescanned.  The row
 // logsumexp comes from the records alone (merged across waves in float64).
 
+// The same selection by one wave per row (four rows per 256-thread block):
+// the row's records and its k best strips' logits each pass through the
+// lanes once, with no exchange between waves and no barrier.
+template <int KM>
+__global__ __launch_bounds__(256) void topk_strip_merge_wave_kernel(
+    int M, int n, int k, int nstrip, const float* __restrict__ z, const float2* __restrict__ rec,
+    const int* __restrict__ id_map, int* __restrict__ ids, int ldi, float* __restrict__ logp,
+    int ldl) {
+  constexpr float kL2e = 1.4426950408889634f;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= M) return;  // whole waves
+  const float2* pr = rec + (int64_t)r * nstrip;
+  const float* row = z + (int64_t)r * n;
+  List<KM> L;
+  L.init();
+  float m = -INFINITY, s = 0.f;
+  // eight records per lane in flight at a time, then inserted
+  for (int j0 = lane; j0 < nstrip; j0 += 64 * 8) {
+    float2 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = pr[min(j0 + 64 * u, nstrip - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + 64 * u >= nstrip || p[u].x == -INFINITY) continue;
+      L.insert(p[u].x, j0 + 64 * u);
+      const float nm = fmaxf(m, p[u].x);
+      s = (m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f((m - nm) * kL2e)) +
+          p[u].y * __builtin_amdgcn_exp2f((p[u].x - nm) * kL2e);
+      m = nm;
+    }
+  }
+  float sv[KM];
+  int si[KM];
+  wave_merge<KM, KM>(L, k, sv, si);  // the k best strips, in every lane
+  // candidate h of the lane: column lane + 64 (h & 1) of the (h / 2)-th best strip
+  constexpr int CPL = KM * kStripW / 64;
+  float cz[CPL];
+  int cx[CPL];
+#pragma unroll
+  for (int h = 0; h < CPL; ++h) {
+    const int st = (h >> 1) < k ? si[h >> 1] : kIdNone;
+    cx[h] = st != kIdNone ? st * kStripW + lane + 64 * (h & 1) : n;
+    cz[h] = row[min(cx[h], n - 1)];
+  }
+  // row logsumexp from the records (lanes combined in float64)
+  const float wm = wave_max(m);
+  double ws = m == -INFINITY ? 0.0 : (double)s * exp((double)m - (double)wm);
+  ws = wave_sum(ws);
+  const double lse = (double)wm + log(ws);
+  List<KM> C;
+  C.init();
+#pragma unroll
+  for (int h = 0; h < CPL; ++h)
+    if (cx[h] < n) C.insert(cz[h], cx[h]);
+  float ov[KM];
+  int oi[KM];
+  wave_merge<KM, KM>(C, k, ov, oi);
+  if (lane < k) {
+    float v = 0.f;
+    int id = 0;
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j == lane) {
+        v = ov[j];
+        id = oi[j];
+      }
+    ids[(int64_t)r * ldi + lane] = id_map ? id_map[clampi(id, 0, n - 1)] : id;
+    logp[(int64_t)r * ldl + lane] = (float)((double)v - lse);
+  }
+}
+
 template <int KM>
 __global__ __launch_bounds__(256) void topk_strip_merge_kernel(int n, int k, int nstrip,
                                                                const float* __restrict__ z,
@@ -883,8 +955,15 @@ hipError_t topk_merge_strips(const float* z, int M, int n, int k, int nstrip, in
                              int ldl, hipStream_t s) {
   if (k < 1 || k > 8 || sw != kStripW || nstrip != (n + kStripW - 1) / kStripW)
     return hipErrorInvalidValue;
-  SPEC_LAUNCH(topk_strip_merge_kernel<8>, dim3(M), dim3(256), 0, s, n, k, nstrip, z,
-                     (const float2*)rec, id_map, ids, ldi, logp, ldl);
+  // up to 512 strips (vocabularies up to 65536) a wave per row; beyond, a
+  // block per row, four waves sharing the records
+  if (nstrip <= 512) {
+    SPEC_LAUNCH(topk_strip_merge_wave_kernel<8>, dim3((M + 3) / 4), dim3(256), 0, s, M, n, k,
+                nstrip, z, (const float2*)rec, id_map, ids, ldi, logp, ldl);
+  } else {
+    SPEC_LAUNCH(topk_strip_merge_kernel<8>, dim3(M), dim3(256), 0, s, n, k, nstrip, z,
+                (const float2*)rec, id_map, ids, ldi, logp, ldl);
+  }
   return hipGetLastError();
 }
 
