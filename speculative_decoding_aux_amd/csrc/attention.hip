@@ -72,7 +72,7 @@ SPEC_DEV void combine_qv(int r, int h, const T* __restrict__ q, const T* __restr
                          int nq, int nkv, int window, int nch, const float* __restrict__ part,
                          T* __restrict__ out) {
   constexpr int DPL = HD / 64;  // dims per lane
-  constexpr int PC = 8;         // chunk records prefetched
+  constexpr int PC = 32;        // chunk records prefetched (the first round trip)
   constexpr int CG = 16;        // chunk records in flight per group after them
   constexpr int KB = 8;         // extra keys per batch
   const int lane = threadIdx.x & 63;
