@@ -678,9 +678,10 @@ GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split) {
   const int cw = gemm_cw(M, N);
   const int strips = (N + 64 * cw - 1) / (64 * cw);
   const int mblocks = (M + 63) / 64;
-  // workgroups in flight: 512 of four waves stream the weights at full rate;
+  // workgroups in flight: 512 of four waves stream the weights at full rate
+  // beyond 16 rows, 768 at up to 16 rows (shorter MFMA work per weight byte);
   // more only add split-K partials
-  const int target = 512;
+  const int target = M <= 16 ? 768 : 512;
   int ns = (target + strips * mblocks - 1) / (strips * mblocks);
   // K in blocks of 512 where the activation rows go through LDS (see
   // stream_acc_lds: K steps in pairs of 256), else of 128
