@@ -136,11 +136,14 @@ def test_capacity_cutoff_sequence_emits_one_token():
     np.testing.assert_array_equal(out.cpu().numpy(), want[0])
 
 
-@pytest.mark.parametrize("name,layers,B", [("tiny_chain", 1, 1), ("llama8b_chain", 32, 4),
-                                           ("qwen8b_tree", 3, 32)])
-def test_compaction_bit_exact(name, layers, B):
-    announce(f"compaction {name} layers={layers} B={B}")
-    cfg = configs.get(name, batch=B)
+@pytest.mark.parametrize("name,layers,B,ctx", [("tiny_chain", 1, 1, None), ("llama8b_chain", 32, 4, None),
+                                               ("qwen8b_tree", 3, 32, None),
+                                               # 4096 and 8192 (sequence, layer, head) units: blocks of
+                                               # four and of all eight kv-heads
+                                               ("qwen8b_tree", 32, 16, 64), ("eagle4_llama8b", 16, 64, 64)])
+def test_compaction_bit_exact(name, layers, B, ctx):
+    announce(f"compaction {name} layers={layers} B={B} ctx={ctx}")
+    cfg = configs.get(name, batch=B, **({} if ctx is None else {"ctx": ctx}))
     D = cfg["depth"]
     slots = cfg["ctx"] + cfg["total_tokens"] + 8
     kv = gen.make_target_kv(cfg, 3, slots, layers)
