@@ -657,11 +657,11 @@ __global__ __launch_bounds__(256) void qkv_epi_rows_kernel(
 // Columns per wave: 16 for the very wide LM head at M <= 32 (one long K sweep
 // per wave, no split, twice the strips), 32 otherwise (twice the loads in
 // flight, and each activation fragment feeds two weight tiles).  With the
-// top-k fused into the epilogue only up to 16 rows: every strip adds a record
-// list per row that the merge reads.
+// top-k fused into the epilogue always 32: every strip adds a record list per
+// row that the merge reads, and the weight stream runs as fast either way.
 static constexpr int kMaxSplit = 32;  // bounds the epilogue's reduction depth
 static int gemm_cw(int M, int N) { return (M <= 32 && N >= 65536) ? 1 : 2; }
-static int lmhead_cw(int M, int N) { return (M <= 16 && N >= 65536) ? 1 : 2; }
+static int lmhead_cw(int, int) { return 2; }
 
 GemmPlan gemm_plan(int M, int N, int K, bool bf16, int max_split) {
   GemmPlan p;
