@@ -399,10 +399,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void g
 
 }  // namespace
 
-// Beam-pass tile: 128 (or 96 or 112) weight rows x 256 X rows, K stages of 64,
+// Beam-pass tile: 128 (or 96, 112 or 64) weight rows x 256 X rows, K stages of 64,
 // three stages (up to 144 KB of LDS, one block per CU, two waves per SIMD).
 constexpr int kTileBN = 128, kTileBM = 256, kTileBK = 64, kTileThreads = 512, kTileStages = 3;
-constexpr int kTileBNNarrow = 96, kTileBN112 = 112;
+constexpr int kTileBNNarrow = 96, kTileBN112 = 112, kTileBN64 = 64;
 
 bool gemm_tile_ok(int M, int K) { return M > 64 && K % kTileBK == 0; }
 
@@ -410,11 +410,11 @@ GemmPlan gemm_tile_plan(int M, int N, int K) {
   // One block per CU: split K only while the grid is short of 256 blocks
   // (every split costs an M x N float32 partial), keeping >= 4 stages per split.
   // Of the strip widths, the one with the least work on the busiest CU:
-  // rounds of tiles x (strip width + a fixed cost per step of 32 rows) x steps
-  // per tile.
+  // rounds of tiles x (strip width + a fixed cost per step of 32 rows) x (steps
+  // per tile + 6 for filling the stages and writing the tile).
   GemmPlan best;
   int64_t best_cost = 0;
-  for (const int bn : {kTileBN, kTileBNNarrow, kTileBN112}) {
+  for (const int bn : {kTileBN, kTileBNNarrow, kTileBN112, kTileBN64}) {
     GemmPlan p;
     p.bn = bn;
     const int strips = (N + bn - 1) / bn;
@@ -426,7 +426,7 @@ GemmPlan gemm_tile_plan(int M, int N, int K) {
     p.kc = per * kTileBK;
     p.nsplit = (ktiles + per - 1) / per;
     const int64_t tiles = (int64_t)strips * mblocks * p.nsplit;
-    const int64_t cost = (tiles + 255) / 256 * (bn + 32) * per;
+    const int64_t cost = (tiles + 255) / 256 * (bn + 32) * (per + 6);
     if (bn == kTileBN || cost < best_cost) {
       best = p;
       best_cost = cost;
@@ -488,6 +488,9 @@ hipError_t gemm_tile(const void* X, int ldx, const void* W, int ldw, float* P, i
   if (plan.bn == kTileBN112)
     return launch_tile<false, kTileBN112>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit,
                                           nullptr, s);
+  if (plan.bn == kTileBN64)
+    return launch_tile<false, kTileBN64>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit,
+                                         nullptr, s);
   return launch_tile<false, kTileBN>(X, ldx, W, ldw, P, M, N, K, plan.kc, plan.nsplit, nullptr, s);
 }
 
